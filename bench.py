@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Throughput of the speculative-verify GDN route on one MI355X.
+
+One step = one speculative round over L independent layer instances of the
+workload (default: 4 lanes in an 8-slot pool, 16-node random draft trees,
+H_k=16, H_v=32, d_k=d_v=128, 8192 conv channels): for every instance the tree
+conv step and the tree verify, then for every instance the replay commit of the
+round's accepted paths.  L=64 instances (~1.9 GB) keep the working set far
+above the 256 MB last-level cache, so every layer reads its inputs from HBM.
+
+value = C*N*L / step time: verified draft tokens per second, each instance
+counted as one single-layer verify.  Inputs are resident in HBM before timing.
+
+The JSON line also carries the roofline of the dominant kernel (algorithmic
+bytes per launch / mean launch time measured with HIP events on the launch
+stream) and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="tree-c4-n16")
+    ap.add_argument("--instances", type=int, default=64)
+    ap.add_argument("--rounds", type=int, default=4, help="distinct tree/acceptance draws cycled over steps")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--kernel-reps", type=int, default=20, help="repetitions of each per-kernel timing loop")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-only", action="store_true", help="skip the CPU oracle and per-kernel loops")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(wl, accept_depths):
+    """Every input read once and every output written once, at the library's layouts (fp32)."""
+    C, N, Ch, Hv, dk, dv = wl.n_seqs, wl.n_nodes, wl.channels, wl.n_v_heads, wl.d_k, wl.d_v
+    W, R = wl.d_conv - 1, wl.log_row
+    conv = 4 * Ch * (C * (W + N + N + N * W) + wl.d_conv)
+    verify = 4 * (C * Hv * dk * dv + C * N * Ch + 2 * C * N * Hv + 2 * Hv + C * N * Hv * dv + C * N * Hv * R)
+    commit = sum(4 * (2 * Hv * dk * dv + 2 * W * Ch) + a * 4 * Hv * R for a in accept_depths if a > 0)
+    return dict(conv=conv, verify=verify, commit=commit)
+
+
+def cpu_baseline(wl, seconds, seed):
+    """The fp64 oracle on single-layer instances of the workload, until `seconds` of CPU work."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import gdn_oracle as O
+    from workloads import layer_params, round_inputs, round_structure
+
+    st = round_structure(wl, 0, seed)
+    done, t_used = 0, 0.0
+    with threadpool_limits(limits=1):
+        while t_used < seconds:
+            lp, ri = layer_params(wl, done, seed), round_inputs(wl, done, 0, seed)
+            t0 = time.perf_counter()
+            r = O.verify_round(ri["x"], ri["ba"], lp["conv_w"], lp["conv_hist"], lp["state"], lp["dt_bias"], lp["A"],
+                               st["slot_ids"], st["parents"], wl.n_k_heads)
+            pool, hist = lp["state"].astype(np.float64), lp["conv_hist"].astype(np.float64)
+            O.replay_commit(r["replay_log"], r["commit_win"], st["slot_ids"], st["parents"], st["accept_node"], pool,
+                            hist)
+            t_used += time.perf_counter() - t0
+            done += 1
+    return dict(value=wl.n_seqs * wl.n_nodes * done / t_used, unit="verify tokens/s", cores=1, kind="oracle",
+                sample=f"{done} single-layer rounds (conv+verify+commit) of {wl.name}, fp64 numpy, 1 BLAS thread, "
+                       f"{t_used:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the route needs no collective, "
+              "so multi-GPU throughput is the per-GPU figure times the lane-sharded GPU count.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_deltanet_speculative_amd as gdn
+    from workloads import WORKLOADS, layer_params, path_to_root, round_inputs, round_structure
+
+    wl = WORKLOADS[args.workload]
+    sh = gdn.Shape(**wl.shape_dict())
+    C, N, P, Ch, Hv, dk, dv = sh.n_seqs, sh.n_nodes, sh.n_slots, sh.channels, sh.n_v_heads, sh.d_k, sh.d_v
+    L = args.instances
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t_gen = time.time()
+    rounds = [round_structure(wl, r, args.seed) for r in range(args.rounds)]
+    slot_ids = d(rounds[0]["slot_ids"])
+    parents = [d(r["parents"]) for r in rounds]
+    accepts = [d(r["accept_node"]) for r in rounds]
+    depths = [[len(path_to_root(r["parents"][c], int(e))) if e >= 0 else 0 for c, e in enumerate(r["accept_node"])]
+              for r in rounds]
+    inst = []
+    for l in range(L):
+        lp, ri = layer_params(wl, l, args.seed), round_inputs(wl, l, 0, args.seed)
+        ba = d(ri["ba"])
+        inst.append(dict(
+            x=d(ri["x"]), ba=ba, beta=ba[..., :Hv], alpha=ba[..., Hv:], conv_w=d(lp["conv_w"]),
+            conv_hist=d(lp["conv_hist"]), state=d(lp["state"]), dt_bias=d(lp["dt_bias"]), A=d(lp["A"]),
+            conv_out=torch.empty((C, N, Ch), device=dev), commit_win=torch.empty((C, N, Ch, 3), device=dev),
+            out=torch.empty((C, N, Hv, dv), device=dev), log=torch.empty((C, N, Hv, sh.log_row), device=dev),
+            status=torch.zeros(1, dtype=torch.int32, device=dev),
+        ))
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+
+    def conv(b, r):
+        gdn.conv_tree_step(sh, b["x"], b["conv_w"], b["conv_hist"], slot_ids, parents[r], conv_out=b["conv_out"],
+                           commit_win=b["commit_win"], status=b["status"])
+
+    def verify(b, r):
+        gdn.tree_verify(sh, b["conv_out"], b["beta"], b["alpha"], b["dt_bias"], b["A"], b["state"], slot_ids,
+                        parents[r], out=b["out"], replay_log=b["log"], status=b["status"])
+
+    def commit(b, r):
+        gdn.replay_commit(sh, b["log"], b["commit_win"], slot_ids, parents[r], accepts[r], b["state"], b["conv_hist"],
+                          b["status"])
+
+    def step(k):
+        r = k % args.rounds
+        for b in inst:
+            conv(b, r)
+            verify(b, r)
+        for b in inst:
+            commit(b, r)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    assert all(int(b["status"].item()) == 0 for b in inst), "device status bits set"
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for k in range(args.steps):
+        step(args.warmup + k)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # per-kernel mean launch time: each kernel alone over the L instances, HIP events on its stream
+    kern = {}
+    if not args.profile_only:
+        for name, fn in (("conv_tree_step", conv), ("tree_verify", verify), ("replay_commit", commit)):
+            for b in inst:
+                fn(b, 0)
+            torch.cuda.synchronize()
+            ev0.record()
+            for rep in range(args.kernel_reps):
+                for b in inst:
+                    fn(b, rep % args.rounds)
+            ev1.record()
+            torch.cuda.synchronize()
+            kern[name] = ev0.elapsed_time(ev1) * 1e3 / (args.kernel_reps * L)  # us per launch
+
+    mean_depths = np.mean([np.mean(dd) for dd in depths]) if depths else 0.0
+    ab = algorithmic_bytes(wl, [int(round(mean_depths))] * C)
+    ab_rounds = [algorithmic_bytes(wl, dd) for dd in depths]
+    commit_bytes = float(np.mean([a["commit"] for a in ab_rounds]))
+    roofline = None
+    if kern:
+        dom = max(("conv_tree_step", "tree_verify", "replay_commit"), key=lambda k: kern[k])
+        bytes_per = {"conv_tree_step": ab["conv"], "tree_verify": ab["verify"], "replay_commit": commit_bytes}[dom]
+        achieved = bytes_per / (kern[dom] * 1e-6) / 1e9
+        roofline = dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                        bytes_per_launch=int(bytes_per), us_per_launch=round(kern[dom], 3))
+
+    cpu = None
+    if not args.no_cpu_baseline and not args.profile_only:
+        cpu = cpu_baseline(wl, args.cpu_seconds, args.seed)
+
+    tokens = C * N * L
+    step_bytes = L * (ab["conv"] + ab["verify"]) + L * commit_bytes
+    line = {
+        "metric": "GDN verify tokens/s (C=4, 16-node trees, d=128); achieved HBM GB/s vs peak",
+        "value": round(tokens / (ms_step * 1e-3), 1),
+        "unit": "verify tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "lanes": C, "nodes": N, "slots": P, "k_heads": wl.n_k_heads,
+                   "v_heads": Hv, "d_k": dk, "d_v": dv, "conv_channels": Ch, "layer_instances": L,
+                   "step": "conv+verify per instance, then commit per instance"},
+        "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "kernel_us": {k: round(v, 3) for k, v in kern.items()},
+        "kernel_gbs": {k: round(b / (kern[k] * 1e-6) / 1e9, 1) for k, b in
+                       (("conv_tree_step", ab["conv"]), ("tree_verify", ab["verify"]),
+                        ("replay_commit", commit_bytes)) if k in kern},
+        "verify_only_tokens_per_s": (round(C * N / ((kern["conv_tree_step"] + kern["tree_verify"]) * 1e-6), 1)
+                                     if kern else None),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "setup_s": round(t_gen, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,28 @@
+"""MI355X-native speculative-verify Gated DeltaNet route.
+
+Three calls over one caller stream, each a thin binding of the C ABI in
+include/gdn_verify.h (libgdnverify.so, hand-written gfx950 HIP kernels):
+
+    conv_tree_step  -> conv_out, commit_win
+    tree_verify     -> out, replay_log          (persistent state read-only)
+    replay_commit   -> advances state_pool / conv_hist of accepting slots
+
+The library is loaded on first use and must have been built
+(`python -m gated_deltanet_speculative_amd.build`); there is no fallback path.
+"""
+
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    GdnError,
+    LIB_PATH,
+    Shape,
+    STATUS_ACCEPT,
+    STATUS_PARENT,
+    STATUS_SLOT_DUP,
+    STATUS_SLOT_RANGE,
+    conv_tree_step,
+    load_library,
+    replay_commit,
+    strerror,
+    tree_verify,
+)

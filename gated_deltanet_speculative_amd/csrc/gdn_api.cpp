@@ -1,0 +1,145 @@
+// Host entry points of the C ABI: argument validation, byte-range alias checks and
+// kernel dispatch on the caller's stream.  Every check runs before anything is
+// enqueued; no entry point allocates, synchronises or keeps state between calls.
+#include <cstdint>
+#include <initializer_list>
+
+#include "gdn_internal.h"
+
+namespace {
+
+struct Range {
+    const void *p;
+    size_t bytes;
+};
+
+bool overlap(const Range &a, const Range &b) {
+    if (!a.p || !b.p || !a.bytes || !b.bytes) return false;
+    const char *a0 = static_cast<const char *>(a.p), *b0 = static_cast<const char *>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// every output range against every input and every other output
+bool any_alias(std::initializer_list<Range> outs, std::initializer_list<Range> ins) {
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (const Range &i : ins)
+            if (overlap(*o, i)) return true;
+        for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlap(*o, *o2)) return true;
+    }
+    return false;
+}
+
+bool aligned(std::initializer_list<const void *> ps, uintptr_t a) {
+    for (const void *p : ps)
+        if (reinterpret_cast<uintptr_t>(p) % a) return false;
+    return true;
+}
+
+bool pow2_width(int v) { return v == 16 || v == 32 || v == 64 || v == 128; }
+
+int check_shape(const gdn_shape *sh, gdn::Dims *d) {
+    if (!sh) return GDN_ERR_NULL;
+    if (sh->n_seqs <= 0 || sh->n_nodes <= 0 || sh->n_slots <= 0 || sh->n_k_heads <= 0 || sh->n_v_heads <= 0 ||
+        sh->d_k <= 0 || sh->d_v <= 0 || sh->d_conv <= 0)
+        return GDN_ERR_SHAPE;
+    if (sh->n_v_heads % sh->n_k_heads != 0) return GDN_ERR_SHAPE;
+    if (sh->d_conv != 4 || !pow2_width(sh->d_k) || !pow2_width(sh->d_v) || sh->n_nodes > GDN_MAX_NODES ||
+        sh->n_seqs > GDN_MAX_SEQS)
+        return GDN_ERR_UNSUPPORTED;
+    const int64_t ch = 2ll * sh->n_k_heads * sh->d_k + (int64_t)sh->n_v_heads * sh->d_v;
+    if (ch > (1 << 24) || (int64_t)sh->n_slots * sh->n_v_heads > (1 << 24)) return GDN_ERR_UNSUPPORTED;
+    *d = gdn::Dims{sh->n_seqs, sh->n_nodes, sh->n_slots, sh->n_k_heads, sh->n_v_heads, sh->d_k, sh->d_v, (int)ch};
+    return GDN_OK;
+}
+
+constexpr size_t F = sizeof(float), I = sizeof(int32_t);
+
+}  // namespace
+
+extern "C" {
+
+int gdn_conv_tree_step(const gdn_shape *sh, const float *x, const float *conv_w, const float *conv_hist,
+                       const int32_t *slot_ids, const int32_t *parents, float *conv_out, float *commit_win,
+                       int32_t *status, hipStream_t stream) {
+    gdn::Dims d;
+    if (int r = check_shape(sh, &d)) return r;
+    if (!x || !conv_w || !conv_hist || !slot_ids || !parents || !conv_out || !commit_win) return GDN_ERR_NULL;
+    if (!aligned({x, conv_w, conv_hist, conv_out, commit_win}, 16) || !aligned({slot_ids, parents, status}, 4))
+        return GDN_ERR_ALIGN;
+    const size_t cnc = (size_t)d.C * d.N * d.Ch;
+    if (any_alias({{conv_out, cnc * F}, {commit_win, cnc * 3 * F}, {status, I}},
+                  {{x, cnc * F}, {conv_w, (size_t)d.Ch * 4 * F}, {conv_hist, (size_t)d.P * d.Ch * 3 * F},
+                   {slot_ids, (size_t)d.C * I}, {parents, (size_t)d.C * d.N * I}}))
+        return GDN_ERR_ALIAS;
+    return gdn::launch_conv_tree_step(d, x, conv_w, conv_hist, slot_ids, parents, conv_out, commit_win, status,
+                                      stream) == hipSuccess
+               ? GDN_OK
+               : GDN_ERR_HIP;
+}
+
+int gdn_tree_verify(const gdn_shape *sh, const float *qkv, const float *beta_logits, const float *alpha_logits,
+                    int64_t gate_stride, const float *dt_bias, const float *A, const float *state_pool,
+                    const int32_t *slot_ids, const int32_t *parents, float *out, float *replay_log,
+                    int32_t *status, hipStream_t stream) {
+    gdn::Dims d;
+    if (int r = check_shape(sh, &d)) return r;
+    if (!qkv || !beta_logits || !alpha_logits || !dt_bias || !A || !state_pool || !slot_ids || !parents || !out ||
+        !replay_log)
+        return GDN_ERR_NULL;
+    if (gate_stride < d.Hv) return GDN_ERR_SHAPE;
+    if (!aligned({qkv, state_pool, out}, 16) ||
+        !aligned({beta_logits, alpha_logits, dt_bias, A, slot_ids, parents, replay_log, status}, 4))
+        return GDN_ERR_ALIGN;
+    const size_t rows = (size_t)d.C * d.N;
+    const size_t gate_bytes = ((rows - 1) * (size_t)gate_stride + d.Hv) * F;
+    const size_t R = 1 + (size_t)d.dk + d.dv;
+    if (any_alias({{out, rows * d.Hv * d.dv * F}, {replay_log, rows * d.Hv * R * F}, {status, I}},
+                  {{qkv, rows * d.Ch * F}, {beta_logits, gate_bytes}, {alpha_logits, gate_bytes},
+                   {dt_bias, (size_t)d.Hv * F}, {A, (size_t)d.Hv * F},
+                   {state_pool, (size_t)d.P * d.Hv * d.dk * d.dv * F}, {slot_ids, (size_t)d.C * I},
+                   {parents, rows * I}}))
+        return GDN_ERR_ALIAS;
+    return gdn::launch_tree_verify(d, qkv, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids,
+                                   parents, out, replay_log, status, stream) == hipSuccess
+               ? GDN_OK
+               : GDN_ERR_HIP;
+}
+
+int gdn_replay_commit(const gdn_shape *sh, const float *replay_log, const float *commit_win,
+                      const int32_t *slot_ids, const int32_t *parents, const int32_t *accept_node,
+                      float *state_pool, float *conv_hist, int32_t *status, hipStream_t stream) {
+    gdn::Dims d;
+    if (int r = check_shape(sh, &d)) return r;
+    if (!replay_log || !commit_win || !slot_ids || !parents || !accept_node || !state_pool || !conv_hist || !status)
+        return GDN_ERR_NULL;
+    if (!aligned({commit_win, state_pool, conv_hist}, 16) ||
+        !aligned({replay_log, slot_ids, parents, accept_node, status}, 4))
+        return GDN_ERR_ALIGN;
+    const size_t rows = (size_t)d.C * d.N;
+    const size_t R = 1 + (size_t)d.dk + d.dv;
+    if (any_alias({{state_pool, (size_t)d.P * d.Hv * d.dk * d.dv * F}, {conv_hist, (size_t)d.P * d.Ch * 3 * F},
+                   {status, I}},
+                  {{replay_log, rows * d.Hv * R * F}, {commit_win, rows * d.Ch * 3 * F}, {slot_ids, (size_t)d.C * I},
+                   {parents, rows * I}, {accept_node, (size_t)d.C * I}}))
+        return GDN_ERR_ALIAS;
+    return gdn::launch_replay_commit(d, replay_log, commit_win, slot_ids, parents, accept_node, state_pool, conv_hist,
+                                     status, stream) == hipSuccess
+               ? GDN_OK
+               : GDN_ERR_HIP;
+}
+
+const char *gdn_strerror(int code) {
+    switch (code) {
+        case GDN_OK: return "success";
+        case GDN_ERR_NULL: return "a required pointer is NULL";
+        case GDN_ERR_SHAPE: return "invalid shape (non-positive dimension, H_v not a multiple of H_k, or gate_stride < H_v)";
+        case GDN_ERR_UNSUPPORTED: return "unsupported shape (d_conv != 4, head width not in {16,32,64,128}, too many nodes or lanes)";
+        case GDN_ERR_ALIAS: return "an output buffer overlaps an input or another output";
+        case GDN_ERR_HIP: return "HIP kernel launch failed";
+        case GDN_ERR_ALIGN: return "a buffer is misaligned (dense float buffers need 16 bytes, others 4)";
+        default: return "unknown error code";
+    }
+}
+
+}  // extern "C"

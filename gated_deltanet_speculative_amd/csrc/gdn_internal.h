@@ -1,0 +1,49 @@
+// Internal declarations shared by the host entry points and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_verify.h"
+
+namespace gdn {
+
+struct Dims {
+    int C, N, P, Hk, Hv, dk, dv, Ch;
+};
+
+// Per-lane validity on the device, evaluated cooperatively by every thread of a
+// workgroup.  Returns the lane's GDN_STATUS_* bits (0 = lane is valid); `s` is the
+// lane's slot id and must not be -1.  Uses one LDS word; contains barriers, so
+// every thread of the workgroup must call it.
+__device__ inline int lane_status_bits(const int32_t *__restrict__ slot_ids, const int32_t *__restrict__ parents,
+                                       const Dims &d, int c, int s, int *lds_word) {
+    int bits = 0;
+    if (s < -1 || s >= d.P) bits |= GDN_STATUS_SLOT_RANGE;
+    for (int o = threadIdx.x; o < d.C; o += blockDim.x)
+        if (o != c && slot_ids[o] == s) bits |= GDN_STATUS_SLOT_DUP;
+    for (int i = threadIdx.x; i < d.N; i += blockDim.x) {
+        const int p = parents[(int64_t)c * d.N + i];
+        if (p < -1 || p >= i) bits |= GDN_STATUS_PARENT;
+    }
+    if (threadIdx.x == 0) *lds_word = 0;
+    __syncthreads();
+    if (bits) atomicOr(lds_word, bits);
+    __syncthreads();
+    return *lds_word;
+}
+
+hipError_t launch_conv_tree_step(const Dims &d, const float *x, const float *conv_w, const float *conv_hist,
+                                 const int32_t *slot_ids, const int32_t *parents, float *conv_out,
+                                 float *commit_win, int32_t *status, hipStream_t stream);
+
+hipError_t launch_tree_verify(const Dims &d, const float *qkv, const float *beta_logits, const float *alpha_logits,
+                              int64_t gate_stride, const float *dt_bias, const float *A, const float *state_pool,
+                              const int32_t *slot_ids, const int32_t *parents, float *out, float *replay_log,
+                              int32_t *status, hipStream_t stream);
+
+hipError_t launch_replay_commit(const Dims &d, const float *replay_log, const float *commit_win,
+                                const int32_t *slot_ids, const int32_t *parents, const int32_t *accept_node,
+                                float *state_pool, float *conv_hist, int32_t *status, hipStream_t stream);
+
+}  // namespace gdn

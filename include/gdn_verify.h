@@ -1,0 +1,184 @@
+/*
+ * gdn_verify.h -- C ABI of the speculative-verify Gated DeltaNet route on MI355X (gfx950).
+ *
+ * One speculative round of one GDN layer is three calls on ONE caller stream:
+ *
+ *   gdn_conv_tree_step  tree-parent causal conv + SiLU over slot-mapped history,
+ *                       plus one commit window per draft node;
+ *   gdn_tree_verify     gated delta-rule recurrence over each lane's draft tree,
+ *                       reading the slot's persistent state read-only and writing
+ *                       the attention output and a replay log;
+ *   gdn_replay_commit   after the host has chosen the accepted node of every lane,
+ *                       advances the live recurrent state and conv history of the
+ *                       accepting slots (an all-or-nothing transaction).
+ *
+ * Sources (page title, then section):
+ *   "perf(qwen35): fuse the DFlash2 concurrent verify Gated DeltaNet route",
+ *       Summary and Optimizations (the three operations and their inputs/outputs),
+ *       closing paragraph of Optimizations (tap/accumulation order; persistent state
+ *       read-only during verification; replay-log commit after acceptance).
+ *   "qwen35: DSpark speculative decoding (Qwen3.8-27B drafters)", commit messages
+ *       (raw gates sigmoid(beta), softplus(alpha + dt_bias) * A; stacked
+ *       ssm_beta|ssm_alpha projection; one l2_norm over q|k; q/k heads broadcast).
+ *   "perf(qwen38): various DFlash2 optimizations concurrency C1-C5", Summary item 3
+ *       (state size 128, replay width 257), Correctness and verification (padded and
+ *       permuted slots, transaction preflight), review of the replay-log commit
+ *       (commit must be ordered after the producer on the same stream).
+ *   "llama-cpp-bonsai-gdn-conv.patch", ssm-conv.cu / ssm-conv.cuh / models.h /
+ *       qwen35.cpp hunks (history layout [d_conv-1, channels] per sequence, token
+ *       layout channels-contiguous, weight [channels][d_conv], state and output
+ *       shapes, channel count).
+ *
+ * Conventions common to all calls
+ *   - Every tensor is float32 or int32, C order (row-major), in device memory,
+ *     allocated and owned by the caller.  The library allocates nothing, keeps no
+ *     pointer or device state between calls, and is re-entrant.
+ *   - Every call validates its arguments on the host, enqueues its kernels on
+ *     `stream` and returns without synchronising.  Verify and commit of a round
+ *     must be issued on the same stream (or the caller orders them).
+ *   - Output buffers must not overlap any input or each other (checked on byte
+ *     ranges, GDN_ERR_ALIAS); the commit's two in-place pools must not overlap its
+ *     inputs or each other.
+ *   - Dense float buffers (x, conv_w, conv_hist, conv_out, commit_win, qkv, state_pool,
+ *     out) must be 16-byte aligned; every other buffer 4-byte aligned (GDN_ERR_ALIGN).
+ *   - Host errors are returned synchronously and nothing is enqueued.
+ *   - Lane errors found on the device are OR-ed into *status as GDN_STATUS_* bits
+ *     (caller zeroes *status before the round).  Conv and verify write nothing for
+ *     an offending lane; the commit mutates nothing at all if *status is non-zero
+ *     after its preflight, including bits left there by the round's conv/verify.
+ *   - A lane whose slot id is -1 is a padding lane: nothing is read or written for it.
+ *
+ * Notation: C = n_seqs lanes, N = n_nodes draft nodes per lane, P = n_slots pool
+ * slots, H_k q/k heads, H_v value heads (H_v % H_k == 0; value head h uses q/k head
+ * h % H_k), Ch = 2*H_k*d_k + H_v*d_v conv channels ordered q | k | v with each head a
+ * contiguous block, W = d_conv - 1 = 3, R = 1 + d_k + d_v replay-log row width.
+ */
+#ifndef GDN_VERIFY_H
+#define GDN_VERIFY_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Host return codes. */
+#define GDN_OK 0
+#define GDN_ERR_NULL 1        /* a required pointer is NULL                                  */
+#define GDN_ERR_SHAPE 2       /* non-positive dimension, H_v % H_k != 0, gate_stride < H_v   */
+#define GDN_ERR_UNSUPPORTED 3 /* d_conv != 4, d_k/d_v not in {16,32,64,128}, N > 64, C > 1024 */
+#define GDN_ERR_ALIAS 4       /* an output byte range overlaps an input or another output    */
+#define GDN_ERR_HIP 5         /* a kernel launch failed                                      */
+#define GDN_ERR_ALIGN 6       /* a dense float buffer is not 16-byte aligned, or an int32 /
+                                 gate buffer not 4-byte aligned                              */
+
+/* Device status bits (OR-ed into *status). */
+#define GDN_STATUS_SLOT_RANGE 1 /* slot id outside [-1, P)                                   */
+#define GDN_STATUS_SLOT_DUP 2   /* the same non-negative slot id used by two lanes           */
+#define GDN_STATUS_PARENT 4     /* parents[c][i] outside [-1, i-1]                           */
+#define GDN_STATUS_ACCEPT 8     /* accept_node[c] outside [-1, N) (commit only)              */
+
+#define GDN_MAX_NODES 64
+#define GDN_MAX_SEQS 1024
+
+typedef struct gdn_shape {
+    int32_t n_seqs;    /* C, 1..GDN_MAX_SEQS                                     */
+    int32_t n_nodes;   /* N, 1..GDN_MAX_NODES; parent[i] in [-1, i-1]            */
+    int32_t n_slots;   /* P >= 1                                                 */
+    int32_t n_k_heads; /* H_k >= 1                                               */
+    int32_t n_v_heads; /* H_v, a multiple of H_k                                 */
+    int32_t d_k;       /* 16, 32, 64 or 128                                      */
+    int32_t d_v;       /* 16, 32, 64 or 128                                      */
+    int32_t d_conv;    /* must be 4                                              */
+} gdn_shape;
+
+/*
+ * Tree conv step ("perf(qwen35): fuse the DFlash2 concurrent verify Gated DeltaNet
+ * route", Optimizations, first bullet; tap order from "llama-cpp-bonsai-gdn-conv.patch",
+ * ssm-conv.cu hunk).
+ *
+ * For lane c (slot s = slot_ids[c]) and node i, let E(i) be the slot's history
+ * columns conv_hist[s][:, 0..2] (oldest first) followed by the tokens x[c][a] of the
+ * nodes a on i's root path (root child first, i last).  Then
+ *   conv_out[c][i][ch]      = silu( sum_{j=0..3} conv_w[ch][j] * E(i)[-4 + j][ch] )
+ *   commit_win[c][i][ch][j] = E(i)[-3 + j][ch],  j = 0..2   (bit-exact copies)
+ * i.e. tap 0 multiplies the oldest column, no bias.  commit_win[c][i] is exactly the
+ * history slot s must hold if node i becomes the last accepted token.
+ *
+ *   x          [C][N][Ch]     projected tokens                       (read)
+ *   conv_w     [Ch][4]        depthwise taps                         (read)
+ *   conv_hist  [P][Ch][3]     persistent history pool, READ-ONLY here
+ *   slot_ids   [C]            int32, -1 = padding lane               (read)
+ *   parents    [C][N]         int32 draft-tree parents               (read)
+ *   conv_out   [C][N][Ch]     written for valid lanes
+ *   commit_win [C][N][Ch][3]  written for valid lanes
+ *   status     int32*         may be NULL; SLOT_RANGE / SLOT_DUP / PARENT bits
+ */
+int gdn_conv_tree_step(const gdn_shape *sh, const float *x, const float *conv_w, const float *conv_hist,
+                       const int32_t *slot_ids, const int32_t *parents, float *conv_out, float *commit_win,
+                       int32_t *status, hipStream_t stream);
+
+/*
+ * Read-only slot-mapped tree verify ("perf(qwen35): fuse the DFlash2 concurrent
+ * verify Gated DeltaNet route", Optimizations, second and third bullets; gates from
+ * "qwen35: DSpark speculative decoding", raw-gate commit message).
+ *
+ * For lane c (slot s), value head h (q/k head kh = h % H_k) and nodes i in index
+ * order, with q = qkv[c][i][kh*d_k ..], k = qkv[c][i][H_k*d_k + kh*d_k ..],
+ * v = qkv[c][i][2*H_k*d_k + h*d_v ..], b = beta_logits[(c*N+i)*gate_stride + h],
+ * a = alpha_logits[(c*N+i)*gate_stride + h]:
+ *   q^ = q/|q|, k^ = k/|k|;  beta = sigmoid(b);  g = exp(softplus(a + dt_bias[h]) * A[h])
+ *   S' = g * S_parent   (S_parent = state_pool[s][h] for a root child, else the state
+ *                        after the parent node; states of [d_k][d_v], value index fastest)
+ *   delta = beta * (v - S'^T k^);  S_i = S' + k^ delta^T;  out[c][i][h] = S_i^T q^ / sqrt(d_k)
+ *   replay_log[c][i][h] = (g, k^[0..d_k), delta[0..d_v))            (R floats)
+ * state_pool is bit-identical afterwards; no per-node state is written.
+ *
+ *   qkv            [C][N][Ch]          conv output of the round           (read)
+ *   beta_logits    strided, see above  e.g. the stacked b|a projection [C][N][2*H_v]
+ *   alpha_logits   strided, see above  with alpha_logits = beta_logits + H_v
+ *   gate_stride    floats between consecutive tokens' gate rows, >= H_v
+ *   dt_bias, A     [H_v]               (A negative, e.g. -exp(A_log))
+ *   state_pool     [P][H_v][d_k][d_v]  persistent, READ-ONLY here
+ *   slot_ids, parents                  as above
+ *   out            [C][N][H_v][d_v]    written for valid lanes
+ *   replay_log     [C][N][H_v][R]      written for valid lanes
+ *   status         int32*              may be NULL
+ */
+int gdn_tree_verify(const gdn_shape *sh, const float *qkv, const float *beta_logits, const float *alpha_logits,
+                    int64_t gate_stride, const float *dt_bias, const float *A, const float *state_pool,
+                    const int32_t *slot_ids, const int32_t *parents, float *out, float *replay_log,
+                    int32_t *status, hipStream_t stream);
+
+/*
+ * Replay-log commit ("perf(qwen35): fuse the DFlash2 concurrent verify Gated DeltaNet
+ * route", closing paragraph of Optimizations; "perf(qwen38): various DFlash2
+ * optimizations concurrency C1-C5", Summary item 3 and the transaction preflight).
+ *
+ * Preflight over every non-padding lane: slot range, duplicate slots, parents and
+ * accept_node[c] in [-1, N).  If *status is then non-zero nothing is written.
+ * Otherwise every non-padding lane with e = accept_node[c] >= 0 replays the logged
+ * transitions of e's root path, in path order, into its slot:
+ *   S <- g_t * S + k^_t delta_t^T    for state_pool[s][h], every h,
+ * and sets conv_hist[s] = commit_win[c][e] (bit-exact copy).  Lanes with e = -1 and
+ * slots used by no accepting lane are bit-identical afterwards.
+ *
+ *   replay_log, commit_win   outputs of this round's verify / conv    (read)
+ *   slot_ids, parents        the round's mapping and trees            (read)
+ *   accept_node [C]          int32 deepest accepted node, -1 = none   (read)
+ *   state_pool, conv_hist    updated in place
+ *   status                   int32*, REQUIRED (GDN_ERR_NULL otherwise)
+ */
+int gdn_replay_commit(const gdn_shape *sh, const float *replay_log, const float *commit_win,
+                      const int32_t *slot_ids, const int32_t *parents, const int32_t *accept_node,
+                      float *state_pool, float *conv_hist, int32_t *status, hipStream_t stream);
+
+/* Static description of a GDN_OK / GDN_ERR_* code. */
+const char *gdn_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_VERIFY_H */

@@ -1,0 +1,135 @@
+"""The C-ABI library without a GPU: it loads, exports every function the header
+declares, and its host-side validation returns the documented error codes
+before anything is enqueued (fake, never-dereferenced pointer values)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_speculative_amd as gdn
+from gated_deltanet_speculative_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "gdn_verify.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="library not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char \*)\s*(gdn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function():
+    names = _declared()
+    assert names == sorted(_lib.EXPORTED)
+    lib = gdn.load_library()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror_codes():
+    assert gdn.strerror(0) == "success"
+    assert "overlaps" in gdn.strerror(4)
+    assert "unknown" in gdn.strerror(99)
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
+
+
+def _shape(**kw):
+    base = dict(n_seqs=2, n_nodes=4, n_slots=4, n_k_heads=2, n_v_heads=4, d_k=16, d_v=16, d_conv=4)
+    base.update(kw)
+    return gdn.Shape(**base)
+
+
+def _ptrs(n, stride=1 << 28):
+    return [FAKE + k * stride for k in range(n)]
+
+
+def _conv(sh, ptrs, status=None):
+    lib = gdn.load_library()
+    cs = sh.c_struct() if sh is not None else None
+    return lib.gdn_conv_tree_step(ctypes.byref(cs) if cs else None, *ptrs, status, None)
+
+
+def _verify(sh, ptrs, gate_stride, status=None):
+    lib = gdn.load_library()
+    cs = sh.c_struct()
+    p = list(ptrs)
+    return lib.gdn_tree_verify(ctypes.byref(cs), p[0], p[1], p[2], gate_stride, *p[3:], status, None)
+
+
+def _commit(sh, ptrs, status):
+    lib = gdn.load_library()
+    cs = sh.c_struct()
+    return lib.gdn_replay_commit(ctypes.byref(cs), *ptrs, status, None)
+
+
+def test_null_shape_and_pointers():
+    assert _conv(None, _ptrs(7)) == _lib.GDN_ERR_NULL
+    p = _ptrs(7)
+    p[2] = None
+    assert _conv(_shape(), p) == _lib.GDN_ERR_NULL
+    p = _ptrs(10)
+    p[0] = None
+    assert _verify(_shape(), p, 8) == _lib.GDN_ERR_NULL
+    assert _commit(_shape(), _ptrs(7), None) == _lib.GDN_ERR_NULL  # commit needs its status word
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_seqs=0), _lib.GDN_ERR_SHAPE),
+    (dict(n_nodes=-1), _lib.GDN_ERR_SHAPE),
+    (dict(n_v_heads=3), _lib.GDN_ERR_SHAPE),
+    (dict(d_conv=3), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(d_k=48), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(d_v=256), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(n_nodes=65), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(n_seqs=1025), _lib.GDN_ERR_UNSUPPORTED),
+])
+def test_shape_rejections(kw, code):
+    assert _conv(_shape(**kw), _ptrs(7)) == code
+    assert _verify(_shape(**kw), _ptrs(10), 8) == code
+    assert _commit(_shape(**kw), _ptrs(7), FAKE + (9 << 28)) == code
+
+
+def test_gate_stride_below_heads_rejected():
+    assert _verify(_shape(), _ptrs(10), 3) == _lib.GDN_ERR_SHAPE
+
+
+def test_misaligned_rejected():
+    p = _ptrs(7)
+    p[0] += 4  # x not 16-byte aligned
+    assert _conv(_shape(), p) == _lib.GDN_ERR_ALIGN
+    p = _ptrs(10)
+    p[1] += 2  # gate rows not 4-byte aligned
+    assert _verify(_shape(), p, 8) == _lib.GDN_ERR_ALIGN
+    p = _ptrs(10)
+    p[1] += 4  # a 4-byte offset is fine for the gates (e.g. the alpha half of b|a) ...
+    p[5] += 8  # ... but not for the state pool
+    assert _verify(_shape(), p, 8) == _lib.GDN_ERR_ALIGN
+
+
+def test_alias_rejected():
+    sh = _shape()
+    p = _ptrs(7)
+    p[5] = p[0] + 64  # conv_out inside x
+    assert _conv(sh, p) == _lib.GDN_ERR_ALIAS
+    p = _ptrs(7)
+    p[6] = p[5] + 16  # commit_win overlaps conv_out
+    assert _conv(sh, p) == _lib.GDN_ERR_ALIAS
+    p = _ptrs(7)
+    assert _conv(sh, p, status=p[3]) == _lib.GDN_ERR_ALIAS  # status inside slot_ids
+    p = _ptrs(10)
+    p[8] = p[5] + 16  # out overlaps the state pool
+    assert _verify(sh, p, 8) == _lib.GDN_ERR_ALIAS
+    p = _ptrs(10)
+    p[9] = p[1] + 4 * 8 * 7  # replay log inside the strided gate rows
+    assert _verify(sh, p, 8) == _lib.GDN_ERR_ALIAS
+    p = _ptrs(7)
+    p[6] = p[5]  # conv_hist == state_pool
+    assert _commit(sh, p, FAKE + (9 << 28)) == _lib.GDN_ERR_ALIAS
+    p = _ptrs(7)
+    p[5] = p[0]  # state pool over the replay log
+    assert _commit(sh, p, FAKE + (9 << 28)) == _lib.GDN_ERR_ALIAS

@@ -12,4 +12,5 @@ from .gen import (  # noqa: F401
     round_inputs,
     round_structure,
     path_to_root,
+    synth_case,
 )

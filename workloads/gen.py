@@ -165,3 +165,30 @@ def round_inputs(wl: Workload, layer: int, rnd: int, seed: int = 0) -> dict:
     x = _normal(rng, 1.0, (wl.n_seqs, wl.n_nodes, wl.channels))
     ba = _normal(rng, 1.0, (wl.n_seqs, wl.n_nodes, 2 * wl.n_v_heads))
     return dict(x=x, ba=ba)
+
+
+def synth_case(C: int, N: int, P: int, Hk: int, Hv: int, dk: int, dv: int, seed: int, tree: bool = True,
+               slots=None) -> dict:
+    """One layer and one round at an arbitrary shape, with the workload distributions.
+
+    Draw order: conv_w, conv_hist, state, dt_bias, A, slot permutation, parents
+    (random trees or chains), x, ba.  `slots` overrides the drawn slot ids.
+    """
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 1000, C, N, P, Hk, Hv, dk, dv])))
+    ch = 2 * Hk * dk + Hv * dv
+    out = dict(
+        conv_w=_normal(rng, 0.5, (ch, 4)),
+        conv_hist=_normal(rng, 1.0, (P, ch, 3)),
+        state=_normal(rng, 0.1, (P, Hv, dk, dv)),
+        dt_bias=_normal(rng, 0.5, (Hv,)),
+        A=(-np.exp(rng.uniform(-1.0, 1.0, Hv))).astype(np.float32),
+    )
+    perm = rng.permutation(P)[:C].astype(np.int32)
+    out["slot_ids"] = perm if slots is None else np.asarray(slots, np.int32)
+    if tree:
+        out["parents"] = np.stack([_random_parents(rng, N) for _ in range(C)]).astype(np.int32)
+    else:
+        out["parents"] = np.tile(np.arange(-1, N - 1, dtype=np.int32), (C, 1))
+    out["x"] = _normal(rng, 1.0, (C, N, ch))
+    out["ba"] = _normal(rng, 1.0, (C, N, 2 * Hv))
+    return out
