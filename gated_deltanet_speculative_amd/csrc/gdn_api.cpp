@@ -134,7 +134,7 @@ const char *gdn_strerror(int code) {
         case GDN_OK: return "success";
         case GDN_ERR_NULL: return "a required pointer is NULL";
         case GDN_ERR_SHAPE: return "invalid shape (non-positive dimension, H_v not a multiple of H_k, or gate_stride < H_v)";
-        case GDN_ERR_UNSUPPORTED: return "unsupported shape (d_conv != 4, head width not in {16,32,64,128}, too many nodes or lanes)";
+        case GDN_ERR_UNSUPPORTED: return "unsupported shape (d_conv != 4, head width not in {16,32,64,128}, more than 32 nodes or 1024 lanes)";
         case GDN_ERR_ALIAS: return "an output buffer overlaps an input or another output";
         case GDN_ERR_HIP: return "HIP kernel launch failed";
         case GDN_ERR_ALIGN: return "a buffer is misaligned (dense float buffers need 16 bytes, others 4)";

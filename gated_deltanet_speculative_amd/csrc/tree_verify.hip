@@ -7,194 +7,431 @@
 // speculative decoding", raw-gate commit message; log row width 1 + d_k + d_v from
 // "perf(qwen38): various DFlash2 optimizations concurrency C1-C5", Summary item 3.
 //
-// Design.  The recurrence is separable in value columns, and unrolling it along a
-// node's root path gives, with G_i the product of decays on the path of i,
-//   S_i = G_i S0 + sum_{a on path(i)} (G_i/G_a) k^_a delta_a^T,
-// so per value column j:
-//   u_i[j]   = G_i (k^_i . S0[:,j]) + sum_{a strict ancestor} (G_i/G_a)(k^_a.k^_i) delta_a[j]
-//   delta_i  = beta_i (v_i - u_i)
-//   o_i[j]   = (G_i (q^_i . S0[:,j]) + sum_{a on path(i)} (G_i/G_a)(k^_a.q^_i) delta_a[j]) / sqrt(d_k)
-// The only O(d_k d_v) work is the dense product [K^;Q^] S0 (2N rows); per-node states
-// are never formed, the slot's state is read exactly once per value column and the
-// tree enters only through N x N ancestor-masked coefficient matrices.  Decay ratios
-// are exp(L_i - L_a) of cumulative log-decays, which cannot overflow.
+// Formulation.  Unrolling the recurrence along a node's root path, with G_i the product
+// of the decays on path(i), gives S_i = G_i S0 + sum_{a on path(i)} (G_i/G_a) k^_a d_a^T.
+// For value column j this yields a triangular system over the tree
+//   d_i = beta_i (v_i - G_i k^_i.S0 - sum_{a strict ancestor} (G_i/G_a)(k^_a.k^_i) d_a)
+//   o_i = (G_i q^_i.S0 + sum_{a on path(i)} (G_i/G_a)(k^_a.q^_i) d_a) / sqrt(d_k).
+// With Ck[a][i] = (G_i/G_a) k^_a.k^_i on strict ancestors, Cq[a][i] = (G_i/G_a) k^_a.q^_i
+// on the path, T = (I + diag(beta) Ck^T)^-1, M1 = T diag(beta):
+//   d = M1 V - K' S0,                 K' = T diag(beta G) K^
+//   o = (Q' S0 + W V) / sqrt(d_k),    Q' = diag(G) Q^ - Cq^T K',  W = Cq^T M1.
+// Everything but the slot's state S0 is known before S0 arrives, so a workgroup first
+// builds the (2N) x (d_k + N) matrix A = [[-K', M1], [Q'/sqrt(d_k), W/sqrt(d_k)]] from
+// q, k, gates and the tree while its S0 block is in flight, then one MFMA product
+// A x [S0; V] yields the delta rows (replay log) and output rows directly from the
+// accumulators.  Per-node states are never formed and S0 is read once.  q and k are
+// never normalised explicitly: their norms come from the diagonal of the Gram product
+// and fold into the coefficients.  Decay ratios are exp(L_i - L_a) of cumulative
+// log-decays, which cannot overflow.
 //
-// One workgroup per (lane, value head, block of 32 value columns).
+// Mapping: one workgroup (4 waves) per (lane, value head, block of 32 value columns);
+// products run on v_mfma_f32_16x16x4_f32 from LDS.  N is padded to NP (16 or 32) with
+// zero rows.  Barriers wait only for LDS traffic, so the state block requested at the
+// start stays in flight through the whole tree phase.
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 
-template <int DK, int DV>
-struct VerifyCfg {
-    static constexpr int JB = DV < 32 ? DV : 32;  // value columns per workgroup
-    static constexpr int NB = DV / JB;            // column blocks per head
-    static size_t lds_bytes(int N) {
-        return sizeof(float) * (size_t)(2 * N * DK + DK * JB + 3 * N * JB + 2 * N * N);
-    }
-};
+typedef float v4f __attribute__((ext_vector_type(4)));
 
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+// Workgroup barrier for LDS communication only: waits for this wave's LDS operations,
+// not for its outstanding global loads, so prefetched data keeps streaming in.
+__device__ inline void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt left open
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
-template <int DK, int DV>
+template <int DK, int DV, int NP>
+struct VerifyLayout {
+    static constexpr int JB = DV < 32 ? DV : 32;  // value columns per workgroup
+    static constexpr int NB = DV / JB;            // column blocks per head
+    static constexpr int R = 1 + DK + DV;         // replay-log row
+    static constexpr int KA = DK + NP;            // contraction length of the main product
+    // row strides (floats) are 4 mod 8 so 16 rows read with ds_read_b128 hit distinct banks
+    static constexpr int SA = (KA + 7) / 8 * 8 + 4;  // A: [2NP][SA]
+    static constexpr int SBT = SA;                   // [S0; V] transposed: [JB][SBT]
+    static constexpr int SG = NP + 4;                // small matrices
+    static constexpr int OFF_CQ = 2 * NP * SA;       // Cq^T [NP][SG] (own region)
+    static constexpr int OFF_X = OFF_CQ + NP * SG;   // late: [S0; V]^T; early aliases:
+    static constexpr int OFF_G = OFF_X;              //   Gram [2NP][SG]
+    static constexpr int OFF_CK = OFF_G + 2 * NP * SG;  // Ck^T [NP][SG]
+    static constexpr int OFF_MK = OFF_CK + NP * SG;     // -T diag(beta G / |k|) [NP][SG]
+    static constexpr int X_FLOATS = (JB * SBT > 4 * NP * SG) ? JB * SBT : 4 * NP * SG;
+    static constexpr int LDS_FLOATS = OFF_X + X_FLOATS;
+};
+
+// One 16x16 tile of A[m0.., 0:K] x B[0:K, n0..] with both operands k-contiguous:
+// A(m, k) = A[m*AM + k], B(k, n) = B[n*BN + k].  Each 16-wide k chunk is read with one
+// ds_read_b128 per operand; lane group g = l/16 supplies k = k0 + 4g + s in MFMA step s,
+// a permutation of the contraction index shared by both operands.  Lane l receives
+// rows 4*(l/16) + v (v = 0..3) of column l % 16.
+template <int K, int AM, int BN>
+__device__ inline v4f mma_kc(const float *A, const float *B) {
+    const int l = threadIdx.x & 63;
+    const float *a = A + (l & 15) * AM + 4 * (l >> 4);
+    const float *b = B + (l & 15) * BN + 4 * (l >> 4);
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        const v4f av = *reinterpret_cast<const v4f *>(a + k0);
+        const v4f bv = *reinterpret_cast<const v4f *>(b + k0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[0], bv[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[1], bv[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[2], bv[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[3], bv[3], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// Same tile with A k-contiguous and B row-major in k: B(k, n) = B[k*BK + n].
+template <int K, int AM, int BK>
+__device__ inline v4f mma_kr(const float *A, const float *B) {
+    const int l = threadIdx.x & 63;
+    const float *a = A + (l & 15) * AM + (l >> 4);
+    const float *b = B + (l >> 4) * BK + (l & 15);
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k0], b[k0 * BK], acc, 0, 0, 0);
+    return acc;
+}
+
+// 1 / max(|x|, 1e-6) from |x|^2, and the gate nonlinearities, on the hardware
+// transcendental units (about 1 ulp each; the outputs carry a 2e-4 tolerance)
+__device__ inline float inv_norm(float sq) { return fminf(__builtin_amdgcn_rsqf(sq), 1e6f); }
+__device__ inline float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ inline float fast_softplus(float x) {
+    return fmaxf(x, 0.f) + 0.6931471805599453f * __builtin_amdgcn_logf(1.0f + fast_exp(-fabsf(x)));
+}
+__device__ inline float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + fast_exp(-x)); }
+
+template <int DK, int DV, int NP>
 __global__ __launch_bounds__(kThreads) void tree_verify_kernel(
     Dims d, const float *__restrict__ qkv, const float *__restrict__ beta_logits,
     const float *__restrict__ alpha_logits, int64_t gate_stride, const float *__restrict__ dt_bias,
-    const float *__restrict__ A, const float *__restrict__ state_pool, const int32_t *__restrict__ slot_ids,
+    const float *__restrict__ A_decay, const float *__restrict__ state_pool, const int32_t *__restrict__ slot_ids,
     const int32_t *__restrict__ parents, float *__restrict__ out, float *__restrict__ replay_log,
     int32_t *__restrict__ status) {
-    using Cfg = VerifyCfg<DK, DV>;
-    constexpr int JB = Cfg::JB;
-    constexpr int R = 1 + DK + DV;
+    using Ly = VerifyLayout<DK, DV, NP>;
+    constexpr int JB = Ly::JB, R = Ly::R, KA = Ly::KA, SA = Ly::SA, SBT = Ly::SBT, SG = Ly::SG;
+    constexpr int Q4 = JB / 4;  // 4-float groups per block row
     extern __shared__ float lds[];
-    __shared__ int s_bits;
-    __shared__ int s_par[GDN_MAX_NODES];
-    __shared__ float s_beta[GDN_MAX_NODES], s_lg[GDN_MAX_NODES], s_L[GDN_MAX_NODES];
-    __shared__ unsigned long long s_anc[GDN_MAX_NODES];
+    float *Am = lds;                // A: rows 0..NP-1 delta rows, NP..2NP-1 output rows
+    float *CqT = lds + Ly::OFF_CQ;  // Cq^T[i][a]
+    float *BmT = lds + Ly::OFF_X;   // [S0 block; V block]^T, written last
+    float *Gm = lds + Ly::OFF_G;    // early aliases of the [S0; V] region
+    float *CkT = lds + Ly::OFF_CK;
+    float *Mk = lds + Ly::OFF_MK;
+    __shared__ int s_wbits[kWaves];
+    __shared__ float s_beta[NP], s_g[NP], s_L[NP], s_G[NP], s_rk[NP], s_rq[NP], s_gq[NP];
+    __shared__ unsigned int s_anc[NP];
 
     const int jb = blockIdx.x, h = blockIdx.y, c = blockIdx.z;
-    const int s = slot_ids[c];
-    if (s == -1) return;  // padding lane
-    const int bits = lane_status_bits(slot_ids, parents, d, c, s, &s_bits);
-    if (bits) {
-        if (jb == 0 && h == 0 && threadIdx.x == 0 && status) atomicOr(status, bits);
-        return;
-    }
-
-    const int N = d.N, Ch = d.Ch, Hv = d.Hv, tid = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int N = d.N, Hv = d.Hv;
     const int kh = h % d.Hk;
     const int j0 = jb * JB;
-    float *qh = lds;            // [N][DK] normalised queries
-    float *kk = qh + N * DK;    // [N][DK] normalised keys
-    float *S0 = kk + N * DK;    // [DK][JB] state columns j0 .. j0+JB
-    float *PK = S0 + DK * JB;   // [N][JB] k^_i . S0[:,j]
-    float *PQ = PK + N * JB;    // [N][JB] q^_i . S0[:,j]
-    float *Vd = PQ + N * JB;    // [N][JB] v, overwritten in place by delta
-    float *Ck = Vd + N * JB;    // [N][N]  Ck[a*N+i] = (G_i/G_a) k^_a.k^_i, a strict ancestor of i
-    float *Cq = Ck + N * N;     // [N][N]  Cq[a*N+i] = (G_i/G_a) k^_a.q^_i, a on path(i)
 
-    // ---- gates and tree bookkeeping
-    if (tid < N) {
-        const int64_t row = (int64_t)c * N + tid;
-        s_par[tid] = parents[row];
-        const float b = beta_logits[row * gate_stride + h];
-        const float a = alpha_logits[row * gate_stride + h] + dt_bias[h];
-        s_beta[tid] = 1.0f / (1.0f + expf(-b));
-        s_lg[tid] = (fmaxf(a, 0.0f) + log1pf(expf(-fabsf(a)))) * A[h];  // log g = softplus(a + dt_bias) * A
-    }
-    __syncthreads();
-    if (tid < N) {
-        float L = 0.0f;
-        unsigned long long m = 0ull;
-        for (int a = tid; a >= 0; a = s_par[a]) {
-            L += s_lg[a];
-            m |= 1ull << a;
-        }
-        s_L[tid] = L;
-        s_anc[tid] = m;
-    }
+    // ---- loads, in the order they are consumed (global loads complete in order): tree
+    //      and gates, duplicate-slot check, raw q/k, the V block, then the state block.
+    //      Indices are clamped and out-of-range values selected to zero, so every load
+    //      is unconditional and all of them are in flight together.
+    const int tn = tid < N ? tid : 0;
+    const int64_t trow = (int64_t)c * N + tn;
+    const int par_raw = parents[trow];
+    const float braw = beta_logits[trow * gate_stride + h];
+    const float araw = alpha_logits[trow * gate_stride + h] + dt_bias[h];
+    const float Ah = A_decay[h];
+    const int so = slot_ids[tid < d.C ? tid : 0];  // this thread's share of the duplicate check
+    const int s = slot_ids[c];
 
-    // ---- q/k L2 normalisation (one wave per vector), replay-log g and k^ (column block 0)
-    const int wave = tid >> 6, lane = tid & 63;
-    float *logc = replay_log + ((int64_t)c * N * Hv + h) * R;  // row (c, i, h) at logc + i*Hv*R
-    for (int vec = wave; vec < 2 * N; vec += kThreads / 64) {
-        const int i = vec >> 1;
-        const bool is_k = vec & 1;
-        const float *src = qkv + ((int64_t)c * N + i) * Ch + (is_k ? d.Hk * DK : 0) + kh * DK;
-        float v0 = lane < DK ? src[lane] : 0.0f;
-        float v1 = lane + 64 < DK ? src[lane + 64] : 0.0f;
-        const float inv = 1.0f / fmaxf(sqrtf(wave_sum(v0 * v0 + v1 * v1)), 1e-6f);
-        v0 *= inv;
-        v1 *= inv;
-        float *dst = (is_k ? kk : qh) + i * DK;
-        if (lane < DK) dst[lane] = v0;
-        if (lane + 64 < DK) dst[lane + 64] = v1;
-        if (is_k && jb == 0) {
-            float *lrow = logc + (int64_t)i * Hv * R;
-            if (lane < DK) lrow[1 + lane] = v0;
-            if (lane + 64 < DK) lrow[1 + lane + 64] = v1;
-            if (lane == 0) lrow[0] = expf(s_lg[i]);
+    constexpr int QF4 = 2 * NP * (DK / 4), QPT = (QF4 + kThreads - 1) / kThreads;
+    v4f qreg[QPT];  // row r < NP: k of node r; row NP + i: q of node i
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+        const int f = min(tid + kThreads * u, QF4 - 1), r = f / (DK / 4), q = f - r * (DK / 4);
+        const int i = r < NP ? r : r - NP;
+        const float *src = qkv + ((int64_t)c * N + (i < N ? i : 0)) * d.Ch + (r < NP ? d.Hk * DK : 0) + kh * DK;
+        const v4f x = reinterpret_cast<const v4f *>(src)[q];
+        qreg[u] = i < N ? x : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    constexpr int VF4 = NP * Q4, VPT = (VF4 + kThreads - 1) / kThreads;
+    v4f vreg[VPT];
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+        const int f = min(tid + kThreads * u, VF4 - 1), i = f / Q4, q = f - i * Q4;
+        const v4f x = reinterpret_cast<const v4f *>(qkv + ((int64_t)c * N + (i < N ? i : 0)) * d.Ch + 2 * d.Hk * DK +
+                                                    h * DV + j0)[q];
+        vreg[u] = i < N ? x : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    if (s == -1) return;  // padding lane
+    const bool s_ok = s >= 0 && s < d.P;
+    constexpr int SF4 = DK * Q4, SPT = (SF4 + kThreads - 1) / kThreads;
+    v4f sreg[SPT];
+    {
+        const float *Sg = state_pool + ((int64_t)(s_ok ? s : 0) * Hv + h) * DK * DV + j0;
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int f = min(tid + kThreads * u, SF4 - 1), r = f / Q4, q = f - r * Q4;
+            sreg[u] = reinterpret_cast<const v4f *>(Sg + (int64_t)r * DV)[q];
         }
     }
-    // ---- state columns and values
-    const float *Sg = state_pool + (((int64_t)s * Hv + h) * DK) * DV + j0;
-    for (int idx = tid; idx < DK * JB / 4; idx += kThreads) {
-        const int r = idx / (JB / 4), q = idx - r * (JB / 4);
-        reinterpret_cast<float4 *>(S0)[idx] = reinterpret_cast<const float4 *>(Sg + (int64_t)r * DV)[q];
-    }
-    for (int idx = tid; idx < N * JB; idx += kThreads) {
-        const int i = idx / JB, j = idx - i * JB;
-        Vd[idx] = qkv[((int64_t)c * N + i) * Ch + 2 * d.Hk * DK + h * DV + j0 + j];
-    }
-    __syncthreads();
 
-    // ---- ancestor-masked coefficient matrices
-    for (int idx = tid; idx < N * N; idx += kThreads) {
-        const int a = idx / N, i = idx - a * N;
-        float ck = 0.0f, cq = 0.0f;
-        if (a <= i && ((s_anc[i] >> a) & 1ull)) {
-            const float r = expf(s_L[i] - s_L[a]);
-            float dq = 0.0f, dk = 0.0f;
-            for (int k = 0; k < DK; ++k) {
-                dq = fmaf(kk[a * DK + k], qh[i * DK + k], dq);
-                dk = fmaf(kk[a * DK + k], kk[i * DK + k], dk);
+    // ---- lane validity (slot range, duplicate slot, parents); nothing is written for a bad lane
+    int bits = s_ok ? 0 : GDN_STATUS_SLOT_RANGE;
+    if (tid < d.C && tid != c && so == s) bits |= GDN_STATUS_SLOT_DUP;
+    for (int o = tid + kThreads; o < d.C; o += kThreads)  // lanes beyond the first 256
+        if (o != c && slot_ids[o] == s) bits |= GDN_STATUS_SLOT_DUP;
+    if (tid < N && (par_raw < -1 || par_raw >= tid)) bits |= GDN_STATUS_PARENT;
+    {
+        int wb = 0;
+#pragma unroll
+        for (int b = 0; b < 3; ++b)
+            if (__builtin_amdgcn_ballot_w64((bits >> b) & 1)) wb |= 1 << b;
+        if (lane == 0) s_wbits[wave] = wb;
+    }
+    // raw q/k rows into A (k rows 0..NP-1, q rows NP..2NP-1)
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+        const int f = min(tid + kThreads * u, QF4 - 1), r = f / (DK / 4), q = f - r * (DK / 4);
+        *reinterpret_cast<v4f *>(Am + r * SA + 4 * q) = qreg[u];
+    }
+    lds_barrier();
+    {
+        int all = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) all |= s_wbits[w];
+        if (all) {
+            if (jb == 0 && h == 0 && tid == 0 && status) atomicOr(status, all);
+            return;
+        }
+    }
+
+    // ---- tree, wave 0: cumulative log-decay L_i and ancestor set by pointer jumping
+    //      (log2(NP) rounds of lane shuffles, independent of the tree depth)
+    if (wave == 0) {
+        const bool real = lane < N;
+        int jump = real ? par_raw : -1;
+        float L = 0.f;
+        if (real) L = fast_softplus(araw) * Ah;  // log g = softplus(a + dt_bias) * A
+        if (lane < NP) s_g[lane] = fast_exp(L);
+        unsigned int anc = real ? 1u << lane : 0u;
+#pragma unroll
+        for (int r = 1; r < NP; r <<= 1) {
+            const int src = jump < 0 ? lane : jump;
+            const float Lj = __shfl(L, src);
+            const unsigned int aj = __shfl(anc, src);
+            const int jj = __shfl(jump, src);
+            if (jump >= 0) {
+                L += Lj;
+                anc |= aj;
+                jump = jj;
             }
-            cq = r * dq;
-            ck = a < i ? r * dk : 0.0f;
         }
-        Ck[idx] = ck;
-        Cq[idx] = cq;
-    }
-    // ---- [K^; Q^] S0 for this column block
-    for (int idx = tid; idx < 2 * N * JB; idx += kThreads) {
-        const int r = idx / JB, j = idx - r * JB;
-        const float *vec = r < N ? kk + r * DK : qh + (r - N) * DK;
-        float acc = 0.0f;
-        for (int k = 0; k < DK; ++k) acc = fmaf(vec[k], S0[k * JB + j], acc);
-        (r < N ? PK : PQ)[(r < N ? r : r - N) * JB + j] = acc;
-    }
-    __syncthreads();
-
-    // ---- forward substitution over nodes (parents precede children), one thread per column
-    if (tid < JB) {
-        const int j = tid;
-        for (int i = 0; i < N; ++i) {
-            float u = expf(s_L[i]) * PK[i * JB + j];
-            for (int a = 0; a < i; ++a) u = fmaf(Ck[a * N + i], Vd[a * JB + j], u);
-            Vd[i * JB + j] = s_beta[i] * (Vd[i * JB + j] - u);
+        if (lane < NP) {
+            s_L[lane] = L;
+            s_G[lane] = real ? fast_exp(L) : 0.f;
+            s_anc[lane] = anc;
+            s_beta[lane] = real ? fast_sigmoid(braw) : 0.f;
         }
     }
-    __syncthreads();
+    // ---- Gram of the raw vectors: Gm[r][a] = (row r of A) . k_a; the diagonal tiles of
+    //      Q Q^T give |q_i|^2
+    {
+        constexpr int NT = NP / 16, TG = 2 * NP / 16 * NT, TQ = NP / 16;
+        for (int t = wave; t < TG + TQ; t += kWaves) {
+            if (t < TG) {
+                const int mt = t / NT, nt = t - mt * NT;
+                const v4f acc = mma_kc<DK, SA, SA>(Am + mt * 16 * SA, Am + nt * 16 * SA);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    Gm[(mt * 16 + 4 * (lane >> 4) + v) * SG + nt * 16 + (lane & 15)] = acc[v];
+                    if (mt == nt && 4 * (lane >> 4) + v == (lane & 15)) s_rk[mt * 16 + (lane & 15)] = inv_norm(acc[v]);
+                }
+            } else {
+                const int qt = t - TG;
+                const float *Qb = Am + (NP + qt * 16) * SA;
+                const v4f acc = mma_kc<DK, SA, SA>(Qb, Qb);
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (4 * (lane >> 4) + v == (lane & 15)) s_rq[qt * 16 + (lane & 15)] = inv_norm(acc[v]);
+            }
+        }
+    }
+    lds_barrier();
 
-    // ---- outputs and the delta part of the log rows
-    const float scale = 1.0f / sqrtf((float)DK);
-    for (int idx = tid; idx < N * JB; idx += kThreads) {
-        const int i = idx / JB, j = idx - i * JB;
-        float o = expf(s_L[i]) * PQ[idx];
-        for (int a = 0; a <= i; ++a) o = fmaf(Cq[a * N + i], Vd[a * JB + j], o);
-        out[(((int64_t)c * N + i) * Hv + h) * DV + j0 + j] = o * scale;
-        logc[(int64_t)i * Hv * R + 1 + DK + j0 + j] = Vd[idx];
+    // ---- decayed, ancestor-masked, norm-scaled coefficients (stored transposed) and the
+    //      replay-log header (g, k^) of every node, once per (lane, head)
+    //      (CkT[i][a] carries beta_i: it is the strictly lower matrix of the solve below)
+    for (int p = tid; p < NP * NP; p += kThreads) {
+        const int i = p / NP, a = p - i * NP;
+        const bool on = (s_anc[i] >> a) & 1u;
+        const float r = on ? fast_exp(s_L[i] - s_L[a]) * s_rk[a] : 0.f;
+        CkT[i * SG + a] = (on && a < i) ? r * Gm[a * SG + i] * (s_rk[i] * s_beta[i]) : 0.f;
+        CqT[i * SG + a] = on ? r * Gm[(NP + i) * SG + a] * s_rq[i] : 0.f;
+    }
+    if (tid < NP) s_gq[tid] = s_G[tid] * s_rq[tid];
+    if (jb == 0) {
+        float *logc = replay_log + ((int64_t)c * N * Hv + h) * R;
+        for (int f = tid; f < N * DK; f += kThreads) {
+            const int i = f / DK, e = f - i * DK;
+            float *lrow = logc + (int64_t)i * Hv * R;
+            lrow[1 + e] = Am[i * SA + e] * s_rk[i];
+            if (e == 0) lrow[0] = s_g[i];
+        }
+    }
+    lds_barrier();
+
+    // ---- T = (I + diag(beta) Ck^T)^-1 by forward substitution, one column per thread;
+    //      M1 = T diag(beta) goes into A (rows 0..NP-1, columns DK..),
+    //      Mk = -T diag(beta G / |k|) multiplies the raw k rows
+    if (tid < NP) {
+        const int a = tid;
+        float t[NP];
+        // row i of the solve matrix is read (i / 4 + 1 four-float groups) while row i - 1
+        // is being solved, so each row costs its FMA chain rather than an LDS round trip
+        v4f cur[NP / 4], nxt[NP / 4];
+        cur[0] = *reinterpret_cast<const v4f *>(CkT);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            if (i + 1 < NP)
+#pragma unroll
+                for (int m4 = 0; m4 <= (i + 1) / 4; ++m4)
+                    nxt[m4] = *reinterpret_cast<const v4f *>(CkT + (i + 1) * SG + 4 * m4);
+            float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) {
+                if (m & 1) s1 = fmaf(cur[m / 4][m % 4], t[m], s1);
+                else s0 = fmaf(cur[m / 4][m % 4], t[m], s0);
+            }
+            t[i] = i < a ? 0.f : (i == a ? 1.f : -(s0 + s1));
+#pragma unroll
+            for (int m4 = 0; m4 < NP / 4; ++m4) cur[m4] = nxt[m4];
+        }
+        const float ba = s_beta[a], ga = ba * s_G[a] * s_rk[a];
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            Am[i * SA + DK + a] = t[i] * ba;
+            Mk[i * SG + a] = -t[i] * ga;
+        }
+    }
+    lds_barrier();
+
+    const float isd = 1.0f / sqrtf((float)DK);
+    // ---- -K' = Mk K (in place over the k rows once every tile has read them) and
+    //      W / sqrt(d_k) = Cq^T M1 / sqrt(d_k) (rows NP.., columns DK.. of A)
+    {
+        constexpr int NTK = DK / 16, TK = NP / 16 * NTK, TKW = (TK + kWaves - 1) / kWaves;
+        v4f kacc[TKW];
+#pragma unroll
+        for (int u = 0; u < TKW; ++u) {
+            const int t = wave + kWaves * u;
+            if (t < TK) {
+                const int mt = t / NTK, nt = t - mt * NTK;
+                kacc[u] = mma_kr<NP, SG, SA>(Mk + mt * 16 * SG, Am + nt * 16);
+            }
+        }
+        constexpr int NTW = NP / 16;
+        for (int t = wave; t < NTW * NTW; t += kWaves) {
+            const int mt = t / NTW, nt = t - mt * NTW;
+            const v4f acc = mma_kr<NP, SG, SA>(CqT + mt * 16 * SG, Am + DK + nt * 16);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                Am[(NP + mt * 16 + 4 * (lane >> 4) + v) * SA + DK + nt * 16 + (lane & 15)] = acc[v] * isd;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int u = 0; u < TKW; ++u) {
+            const int t = wave + kWaves * u;
+            if (t < TK) {
+                const int mt = t / NTK, nt = t - mt * NTK;
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    Am[(mt * 16 + 4 * (lane >> 4) + v) * SA + nt * 16 + (lane & 15)] = kacc[u][v];
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---- Q' / sqrt(d_k) = (diag(G / |q|) Q + Cq^T (-K')) / sqrt(d_k) in place over the
+    //      q rows; meanwhile the state and V blocks become the transposed right operand
+    {
+        constexpr int NTK = DK / 16, TQ = NP / 16 * NTK;
+        for (int t = wave; t < TQ; t += kWaves) {
+            const int mt = t / NTK, nt = t - mt * NTK;
+            const v4f acc = mma_kr<NP, SG, SA>(CqT + mt * 16 * SG, Am + nt * 16);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = mt * 16 + 4 * (lane >> 4) + v;
+                float *q = Am + (NP + i) * SA + nt * 16 + (lane & 15);
+                *q = fmaf(s_gq[i], *q, acc[v]) * isd;
+            }
+        }
+    }
+    // (indices clamped as at load time: surplus threads rewrite the last element with the
+    // value they loaded for it, so the stores need no condition)
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+        const int f = min(tid + kThreads * u, SF4 - 1), r = f / Q4, q = f - r * Q4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) BmT[(4 * q + e) * SBT + r] = sreg[u][e];
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+        const int f = min(tid + kThreads * u, VF4 - 1), i = f / Q4, q = f - i * Q4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) BmT[(4 * q + e) * SBT + DK + i] = vreg[u][e];
+    }
+    lds_barrier();
+
+    // ---- [delta; o] = A x [S0; V]
+    {
+        constexpr int NTJ = JB / 16, TM = 2 * NP / 16 * NTJ;
+        float *logc = replay_log + ((int64_t)c * N * Hv + h) * R;
+        for (int t = wave; t < TM; t += kWaves) {
+            const int mt = t / NTJ, nt = t - mt * NTJ;
+            const v4f acc = mma_kc<KA, SA, SBT>(Am + mt * 16 * SA, BmT + nt * 16 * SBT);
+            const int col = j0 + nt * 16 + (lane & 15);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = mt * 16 + 4 * (lane >> 4) + v;
+                if (row < NP) {
+                    if (row < N) logc[(int64_t)row * Hv * R + 1 + DK + col] = acc[v];
+                } else if (row - NP < N) {
+                    out[(((int64_t)c * N + row - NP) * Hv + h) * DV + col] = acc[v];
+                }
+            }
+        }
     }
 }
 
-template <int DK, int DV>
+template <int DK, int DV, int NP>
 hipError_t launch(const Dims &d, const float *qkv, const float *bl, const float *al, int64_t gs, const float *dt,
                   const float *A, const float *pool, const int32_t *slots, const int32_t *parents, float *out,
                   float *log, int32_t *status, hipStream_t stream) {
-    using Cfg = VerifyCfg<DK, DV>;
-    const size_t lds = Cfg::lds_bytes(d.N);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&tree_verify_kernel<DK, DV>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((tree_verify_kernel<DK, DV>), dim3(Cfg::NB, d.Hv, d.C), dim3(kThreads), lds, stream, d, qkv,
+    using Ly = VerifyLayout<DK, DV, NP>;
+    const size_t lds = sizeof(float) * Ly::LDS_FLOATS;
+    // the LDS limit is a property of the kernel, set once (also keeps stream capture clean)
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&tree_verify_kernel<DK, DV, NP>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((tree_verify_kernel<DK, DV, NP>), dim3(Ly::NB, d.Hv, d.C), dim3(kThreads), lds, stream, d, qkv,
                        bl, al, gs, dt, A, pool, slots, parents, out, log, status);
     return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_np(const Dims &d, const float *qkv, const float *bl, const float *al, int64_t gs, const float *dt,
+                     const float *A, const float *pool, const int32_t *slots, const int32_t *parents, float *out,
+                     float *log, int32_t *status, hipStream_t stream) {
+    if (d.N <= 16) return launch<DK, DV, 16>(d, qkv, bl, al, gs, dt, A, pool, slots, parents, out, log, status, stream);
+    return launch<DK, DV, 32>(d, qkv, bl, al, gs, dt, A, pool, slots, parents, out, log, status, stream);
 }
 
 }  // namespace
@@ -203,10 +440,10 @@ hipError_t launch_tree_verify(const Dims &d, const float *qkv, const float *beta
                               int64_t gate_stride, const float *dt_bias, const float *A, const float *state_pool,
                               const int32_t *slot_ids, const int32_t *parents, float *out, float *replay_log,
                               int32_t *status, hipStream_t stream) {
-#define GDN_VERIFY_CASE(K, V)                                                                                   \
-    if (d.dk == K && d.dv == V)                                                                                 \
-        return launch<K, V>(d, qkv, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids, \
-                            parents, out, replay_log, status, stream);
+#define GDN_VERIFY_CASE(K, V)                                                                                      \
+    if (d.dk == K && d.dv == V)                                                                                    \
+        return launch_np<K, V>(d, qkv, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids, \
+                               parents, out, replay_log, status, stream);
 #define GDN_VERIFY_ROW(K) GDN_VERIFY_CASE(K, 16) GDN_VERIFY_CASE(K, 32) GDN_VERIFY_CASE(K, 64) GDN_VERIFY_CASE(K, 128)
     GDN_VERIFY_ROW(16) GDN_VERIFY_ROW(32) GDN_VERIFY_ROW(64) GDN_VERIFY_ROW(128)
 #undef GDN_VERIFY_ROW

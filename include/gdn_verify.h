@@ -67,7 +67,7 @@ extern "C" {
 #define GDN_OK 0
 #define GDN_ERR_NULL 1        /* a required pointer is NULL                                  */
 #define GDN_ERR_SHAPE 2       /* non-positive dimension, H_v % H_k != 0, gate_stride < H_v   */
-#define GDN_ERR_UNSUPPORTED 3 /* d_conv != 4, d_k/d_v not in {16,32,64,128}, N > 64, C > 1024 */
+#define GDN_ERR_UNSUPPORTED 3 /* d_conv != 4, d_k/d_v not in {16,32,64,128}, N > 32, C > 1024 */
 #define GDN_ERR_ALIAS 4       /* an output byte range overlaps an input or another output    */
 #define GDN_ERR_HIP 5         /* a kernel launch failed                                      */
 #define GDN_ERR_ALIGN 6       /* a dense float buffer is not 16-byte aligned, or an int32 /
@@ -79,7 +79,7 @@ extern "C" {
 #define GDN_STATUS_PARENT 4     /* parents[c][i] outside [-1, i-1]                           */
 #define GDN_STATUS_ACCEPT 8     /* accept_node[c] outside [-1, N) (commit only)              */
 
-#define GDN_MAX_NODES 64
+#define GDN_MAX_NODES 32
 #define GDN_MAX_SEQS 1024
 
 typedef struct gdn_shape {

@@ -85,7 +85,7 @@ def test_null_shape_and_pointers():
     (dict(d_conv=3), _lib.GDN_ERR_UNSUPPORTED),
     (dict(d_k=48), _lib.GDN_ERR_UNSUPPORTED),
     (dict(d_v=256), _lib.GDN_ERR_UNSUPPORTED),
-    (dict(n_nodes=65), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(n_nodes=33), _lib.GDN_ERR_UNSUPPORTED),
     (dict(n_seqs=1025), _lib.GDN_ERR_UNSUPPORTED),
 ])
 def test_shape_rejections(kw, code):
