@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true", help="skip the CPU oracle and per-kernel loops")
+    ap.add_argument("--eager", action="store_true", help="launch every call directly instead of replaying graphs")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after the run, launch 4 plain device copies of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -53,6 +56,21 @@ def algorithmic_bytes(wl, accept_depths):
     verify = 4 * (C * Hv * dk * dv + C * N * Ch + 2 * C * N * Hv + 2 * Hv + C * N * Hv * dv + C * N * Hv * R)
     commit = sum(4 * (2 * Hv * dk * dv + 2 * W * Ch) + a * 4 * Hv * R for a in accept_depths if a > 0)
     return dict(conv=conv, verify=verify, commit=commit)
+
+
+def measured_traffic(workload, kernel):
+    """Fabric bytes per launch of `kernel` from the committed counter summary
+    (profiles/traffic_<workload>.json: FETCH_SIZE + WRITE_SIZE, copy-calibrated), or
+    None when there is none or the kernel's source changed since it was measured."""
+    from gated_deltanet_speculative_amd.rocprof_summary import source_sha256
+
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get("kernels", {}).get(kernel)
+    if not rec or rec.get("source_sha256") != source_sha256(kernel):
+        return None
+    return int(round(rec["read_bytes"] + rec["write_bytes"]))
 
 
 def cpu_baseline(wl, seconds, seed):
@@ -156,7 +174,10 @@ def main():
             fn()
         return g
 
-    graphs = [capture(lambda r=r: step(r)) for r in range(args.rounds)]
+    if args.eager:
+        graphs = [type("Eager", (), {"replay": (lambda self, r=r: step(r))})() for r in range(args.rounds)]
+    else:
+        graphs = [capture(lambda r=r: step(r)) for r in range(args.rounds)]
     for r in range(args.rounds):
         graphs[r].replay()
     torch.cuda.synchronize()
@@ -185,6 +206,14 @@ def main():
             torch.cuda.synchronize()
             kern[name] = ev0.elapsed_time(ev1) * 1e3 / (args.kernel_reps * L)  # us per launch
 
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty(n, device=dev)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
     mean_depths = np.mean([np.mean(dd) for dd in depths]) if depths else 0.0
     ab = algorithmic_bytes(wl, [int(round(mean_depths))] * C)
     ab_rounds = [algorithmic_bytes(wl, dd) for dd in depths]
@@ -195,7 +224,7 @@ def main():
         bytes_per = {"conv_tree_step": ab["conv"], "tree_verify": ab["verify"], "replay_commit": commit_bytes}[dom]
         achieved = bytes_per / (kern[dom] * 1e-6) / 1e9
         roofline = dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(wl.name, dom),
                         bytes_per_launch=int(bytes_per), us_per_launch=round(kern[dom], 3))
 
     cpu = None
