@@ -6,6 +6,7 @@ include/gdn_verify.h (libgdnverify.so, hand-written gfx950 HIP kernels):
     conv_tree_step  -> conv_out, commit_win
     tree_verify     -> out, replay_log          (persistent state read-only)
     replay_commit   -> advances state_pool / conv_hist of accepting slots
+    replay_commit_layers -> the same for every layer of a round, one launch
 
 The library is loaded on first use and must have been built
 (`python -m gated_deltanet_speculative_amd.build`); there is no fallback path.
@@ -15,6 +16,7 @@ from ._lib import (  # noqa: F401
     EXPORTED,
     GdnError,
     LIB_PATH,
+    MAX_LAYERS,
     Shape,
     STATUS_ACCEPT,
     STATUS_PARENT,
@@ -23,6 +25,7 @@ from ._lib import (  # noqa: F401
     conv_tree_step,
     load_library,
     replay_commit,
+    replay_commit_layers,
     strerror,
     tree_verify,
 )

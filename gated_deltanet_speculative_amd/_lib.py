@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libgdnverify.so")
 
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP, GDN_ERR_ALIGN = range(7)
 STATUS_SLOT_RANGE, STATUS_SLOT_DUP, STATUS_PARENT, STATUS_ACCEPT = 1, 2, 4, 8
-EXPORTED = ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_replay_commit", "gdn_strerror")
+EXPORTED = ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_replay_commit", "gdn_replay_commit_layers", "gdn_strerror")
+MAX_LAYERS = 64
 
 
 class GdnError(RuntimeError):
@@ -73,7 +74,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdn_conv_tree_step.argtypes = [sp] + [vp] * 9
     lib.gdn_tree_verify.argtypes = [sp, vp, vp, vp, i64] + [vp] * 9
     lib.gdn_replay_commit.argtypes = [sp] + [vp] * 9
-    for f in ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_replay_commit"):
+    lib.gdn_replay_commit_layers.argtypes = [sp, i32] + [vp] * 9
+    for f in ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_replay_commit", "gdn_replay_commit_layers"):
         getattr(lib, f).restype = i32
     lib.gdn_strerror.argtypes = [ctypes.c_int]
     lib.gdn_strerror.restype = ctypes.c_char_p
@@ -215,4 +217,41 @@ def replay_commit(sh: Shape, replay_log, commit_win, slot_ids, parents, accept_n
     ]
     cs = sh.c_struct()
     _check(load_library().gdn_replay_commit(ctypes.byref(cs), *args), "gdn_replay_commit")
+    return status
+
+
+def replay_commit_layers(sh: Shape, replay_logs, commit_wins, slot_ids, parents, accept_node, state_pools,
+                         conv_hists, status):
+    """Preflight + replay commit of every layer of the round in one launch.
+
+    replay_logs, commit_wins, state_pools and conv_hists are equal-length sequences
+    (one entry per layer) of tensors laid out as for replay_commit; slot_ids,
+    parents, accept_node and the status word are shared.  All layers commit or none.
+    """
+    C, N, P, Hv, dk, dv, Ch = sh.n_seqs, sh.n_nodes, sh.n_slots, sh.n_v_heads, sh.d_k, sh.d_v, sh.channels
+    if status is None:
+        raise ValueError("replay_commit_layers needs a status word (the round's transaction flag)")
+    L = len(replay_logs)
+    if not (len(commit_wins) == len(state_pools) == len(conv_hists) == L):
+        raise ValueError("replay_commit_layers: per-layer sequences differ in length")
+    if not 1 <= L <= MAX_LAYERS:
+        raise ValueError(f"replay_commit_layers: {L} layers, expected 1..{MAX_LAYERS}")
+    arr = ctypes.c_void_p * L
+    logs = arr(*[_dev(t, f"replay_logs[{l}]", torch.float32, (C, N, Hv, sh.log_row)) for l, t in enumerate(replay_logs)])
+    wins = arr(*[_dev(t, f"commit_wins[{l}]", torch.float32, (C, N, Ch, sh.d_conv - 1))
+                 for l, t in enumerate(commit_wins)])
+    pools = arr(*[_dev(t, f"state_pools[{l}]", torch.float32, (P, Hv, dk, dv)) for l, t in enumerate(state_pools)])
+    hists = arr(*[_dev(t, f"conv_hists[{l}]", torch.float32, (P, Ch, sh.d_conv - 1)) for l, t in enumerate(conv_hists)])
+    args = [
+        ctypes.cast(logs, ctypes.c_void_p), ctypes.cast(wins, ctypes.c_void_p),
+        _dev(slot_ids, "slot_ids", torch.int32, (C,)),
+        _dev(parents, "parents", torch.int32, (C, N)),
+        _dev(accept_node, "accept_node", torch.int32, (C,)),
+        ctypes.cast(pools, ctypes.c_void_p), ctypes.cast(hists, ctypes.c_void_p),
+        _dev(status, "status", torch.int32, (1,)),
+        _stream(state_pools[0]),
+    ]
+    cs = sh.c_struct()
+    _check(load_library().gdn_replay_commit_layers(ctypes.byref(cs), ctypes.c_int32(L), *args),
+           "gdn_replay_commit_layers")
     return status

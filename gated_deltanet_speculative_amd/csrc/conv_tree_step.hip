@@ -11,7 +11,7 @@
 // block's 3 history columns and the lane's N token rows are staged once in LDS as
 // 4-float channel groups, so every ancestor tap a tree node needs is an LDS read and each
 // input byte leaves HBM once.  All global loads (parents, tokens, weights, history) are
-// issued together up front; the tree is walked in LDS.  conv_out rows go out as
+// issued together up front; tree ancestors are found with lane shuffles.  conv_out rows go out as
 // coalesced 16-byte stores; the commit window of 4 channels is 12 consecutive floats,
 // written as three 16-byte stores.
 #include "gdn_internal.h"
@@ -28,14 +28,21 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Workgroup barrier for LDS communication only: waits for this wave's LDS operations,
+// not for its outstanding global loads.
+__device__ inline void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt left open
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __global__ __launch_bounds__(kThreads) void conv_tree_step_kernel(
     Dims d, const float *__restrict__ x, const float *__restrict__ conv_w, const float *__restrict__ conv_hist,
     const int32_t *__restrict__ slot_ids, const int32_t *__restrict__ parents, float *__restrict__ conv_out,
     float *__restrict__ commit_win, int32_t *__restrict__ status) {
     extern __shared__ v4f rows4[];  // [3 + N][kGroups]: history columns 0..2, then token rows
-    __shared__ int s_par[GDN_MAX_NODES];
-    __shared__ int s_src[GDN_MAX_NODES][4];
-    __shared__ int s_bits;
+    __shared__ int s_wbits[kThreads / 64];
 
     const int c = blockIdx.y, tid = threadIdx.x;
     const int N = d.N, Ch = d.Ch;
@@ -45,7 +52,8 @@ __global__ __launch_bounds__(kThreads) void conv_tree_step_kernel(
 
     // ---- every global load first: parents, this thread's duplicate-slot probe, token
     //      rows of the block (into LDS), the 4 taps of this thread's channel group
-    const int par = parents[(int64_t)c * N + (tid < N ? tid : 0)];
+    const int lane = tid & 63;
+    const int par = parents[(int64_t)c * N + (lane < N ? lane : 0)];  // lane i of every wave holds parent i
     const int so = slot_ids[tid < d.C ? tid : 0];
     const v4f *x4 = reinterpret_cast<const v4f *>(x + ((int64_t)c * N) * Ch + ch0);
     const int q = tid % kGroups;  // this thread's channel group (fixed: 256 % 16 == 0)
@@ -62,54 +70,65 @@ __global__ __launch_bounds__(kThreads) void conv_tree_step_kernel(
     const int s = slot_ids[c];
     if (s == -1) return;  // padding lane
     const bool s_ok = s >= 0 && s < d.P;
-    // history block [ch][3] (contiguous), this thread's float of it
+    // ---- history block [ch][3] (contiguous), this thread's float of it
     const int hn = ng * 12;
     const float hv = conv_hist[((int64_t)(s_ok ? s : 0) * Ch + ch0) * 3 + (tid < hn ? tid : 0)];
+    // ---- lane validity (slot range, duplicate slot, parents); nothing is written for a bad lane
+    int bits = s_ok ? 0 : GDN_STATUS_SLOT_RANGE;
+    if (tid < d.C && tid != c && so == s) bits |= GDN_STATUS_SLOT_DUP;
+    for (int o = tid + kThreads; o < d.C; o += kThreads)
+        if (o != c && slot_ids[o] == s) bits |= GDN_STATUS_SLOT_DUP;
+    if (tid < N && (par < -1 || par >= tid)) bits |= GDN_STATUS_PARENT;
+    {
+        int wb = 0;
+#pragma unroll
+        for (int b = 0; b < 3; ++b)
+            if (__builtin_amdgcn_ballot_w64((bits >> b) & 1)) wb |= 1 << b;
+        if ((tid & 63) == 0) s_wbits[tid >> 6] = wb;
+    }
+    // ---- stage the block: token rows, and the history transposed into rows 0..2 (a 64-channel
+    // block has 192 history floats: one per thread)
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
         const int i = tid / kGroups + kRowsPerPass * u;
         if (i < N && q < ng) rows4[(3 + i) * kGroups + q] = xr[u];
     }
-    int bits = s_ok ? 0 : GDN_STATUS_SLOT_RANGE;
-    if (tid < d.C && tid != c && so == s) bits |= GDN_STATUS_SLOT_DUP;
-    for (int o = tid + kThreads; o < d.C; o += kThreads)
-        if (o != c && slot_ids[o] == s) bits |= GDN_STATUS_SLOT_DUP;
-    if (tid < N) {
-        if (par < -1 || par >= tid) bits |= GDN_STATUS_PARENT;
-        s_par[tid] = par;
-    }
-    if (tid == 0) s_bits = 0;
-    if (__syncthreads_or(bits)) {
-        if (bits) atomicOr(&s_bits, bits);
-        __syncthreads();
-        if (blockIdx.x == 0 && tid == 0 && status) atomicOr(status, s_bits);
-        return;
-    }
-    // history transposed into rows 0..2 (a 64-channel block has 192 floats: one per thread)
     if (tid < hn) rows[(tid % 3) * kChBlock + tid / 3] = hv;
-
-    // Window sources of node i, oldest first: LDS row r < 3 is history column r,
-    // row 3 + a is the token of node a.  Newest source is node i itself, then its
-    // ancestors, then history columns 2, 1, 0.
-    if (tid < N) {
-        const int n0 = tid;
-        const int n1 = s_par[n0];
-        const int n2 = n1 >= 0 ? s_par[n1] : -1;
-        const int n3 = n2 >= 0 ? s_par[n2] : -1;
-        const int nn[4] = {n0, n1, n2, n3};
-        const int cnt = 1 + (n1 >= 0) + (n2 >= 0) + (n3 >= 0);
+    lds_barrier();
+    {
+        int all = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) s_src[tid][3 - k] = k < cnt ? 3 + nn[k] : 2 - (k - cnt);
+        for (int w = 0; w < kThreads / 64; ++w) all |= s_wbits[w];
+        if (all) {
+            if (blockIdx.x == 0 && tid == 0 && status) atomicOr(status, all);
+            return;
+        }
     }
-    __syncthreads();
 
-    if (q >= ng) return;
+    // ---- conv + SiLU and the commit windows, one node row per pass.  Window sources of
+    //      node i, oldest first: LDS row r < 3 is history column r, row 3 + a is the token
+    //      of node a; the newest source is node i itself, then its ancestors (found with
+    //      lane shuffles over the parents held by lanes 0..N-1), then history columns 2, 1, 0.
     const int ch = ch0 + 4 * q;
-    for (int i = tid / kGroups; i < N; i += kRowsPerPass) {
-        const v4f t0 = rows4[s_src[i][0] * kGroups + q];
-        const v4f t1 = rows4[s_src[i][1] * kGroups + q];
-        const v4f t2 = rows4[s_src[i][2] * kGroups + q];
-        const v4f t3 = rows4[s_src[i][3] * kGroups + q];
+#pragma unroll
+    for (int u = 0; u < XPT; ++u) {
+        const int i = tid / kGroups + kRowsPerPass * u;
+        const int n0 = i < N ? i : 0;
+        const int n1 = __shfl(par, n0);
+        const int n2s = __shfl(par, n1 >= 0 ? n1 : 0);
+        const int n2 = n1 >= 0 ? n2s : -1;
+        const int n3s = __shfl(par, n2 >= 0 ? n2 : 0);
+        const int n3 = n2 >= 0 ? n3s : -1;
+        if (i >= N || q >= ng) continue;
+        const int cnt = 1 + (n1 >= 0) + (n2 >= 0) + (n3 >= 0);
+        const int nn[4] = {n0, n1, n2, n3};
+        int src[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) src[3 - k] = k < cnt ? 3 + nn[k] : 2 - (k - cnt);
+        const v4f t0 = rows4[src[0] * kGroups + q];
+        const v4f t1 = rows4[src[1] * kGroups + q];
+        const v4f t2 = rows4[src[2] * kGroups + q];
+        const v4f t3 = rows4[src[3] * kGroups + q];
         // sum over taps from the oldest column, as in the pages' kernel
         float za = 0.f, zb = 0.f, zc = 0.f, zd = 0.f;
         za = fmaf(t0.x, wa.x, za); za = fmaf(t1.x, wa.y, za); za = fmaf(t2.x, wa.z, za); za = fmaf(t3.x, wa.w, za);

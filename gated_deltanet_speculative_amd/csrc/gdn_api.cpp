@@ -106,27 +106,63 @@ int gdn_tree_verify(const gdn_shape *sh, const float *qkv, const float *beta_log
                : GDN_ERR_HIP;
 }
 
+int gdn_replay_commit_layers(const gdn_shape *sh, int32_t n_layers, const float *const *replay_logs,
+                             const float *const *commit_wins, const int32_t *slot_ids, const int32_t *parents,
+                             const int32_t *accept_node, float *const *state_pools, float *const *conv_hists,
+                             int32_t *status, hipStream_t stream) {
+    gdn::Dims d;
+    if (int r = check_shape(sh, &d)) return r;
+    if (n_layers < 1 || n_layers > GDN_MAX_LAYERS) return GDN_ERR_UNSUPPORTED;
+    if (!replay_logs || !commit_wins || !state_pools || !conv_hists || !slot_ids || !parents || !accept_node ||
+        !status)
+        return GDN_ERR_NULL;
+    const size_t rows = (size_t)d.C * d.N;
+    const size_t R = 1 + (size_t)d.dk + d.dv;
+    const size_t pool_b = (size_t)d.P * d.Hv * d.dk * d.dv * F, hist_b = (size_t)d.P * d.Ch * 3 * F;
+    const size_t log_b = rows * d.Hv * R * F, win_b = rows * d.Ch * 3 * F;
+    gdn::LayerPtrs lp{};
+    for (int l = 0; l < n_layers; ++l) {
+        if (!replay_logs[l] || !commit_wins[l] || !state_pools[l] || !conv_hists[l]) return GDN_ERR_NULL;
+        if (!aligned({commit_wins[l], state_pools[l], conv_hists[l]}, 16) || !aligned({replay_logs[l]}, 4))
+            return GDN_ERR_ALIGN;
+        lp.replay_log[l] = replay_logs[l];
+        lp.commit_win[l] = commit_wins[l];
+        lp.state_pool[l] = state_pools[l];
+        lp.conv_hist[l] = conv_hists[l];
+    }
+    if (!aligned({slot_ids, parents, accept_node, status}, 4)) return GDN_ERR_ALIGN;
+    // every layer's pools against every input, the status word and every other layer's pools
+    for (int l = 0; l < n_layers; ++l) {
+        const Range outs[2] = {{state_pools[l], pool_b}, {conv_hists[l], hist_b}};
+        for (const Range &o : outs) {
+            if (any_alias({o, {status, I}}, {{slot_ids, (size_t)d.C * I}, {parents, rows * I},
+                                              {accept_node, (size_t)d.C * I}}))
+                return GDN_ERR_ALIAS;
+            for (int m = 0; m < n_layers; ++m) {
+                if (overlap(o, {replay_logs[m], log_b}) || overlap(o, {commit_wins[m], win_b})) return GDN_ERR_ALIAS;
+                if (m == l) {
+                    if (overlap(outs[0], outs[1])) return GDN_ERR_ALIAS;
+                    continue;
+                }
+                if (overlap(o, {state_pools[m], pool_b}) || overlap(o, {conv_hists[m], hist_b})) return GDN_ERR_ALIAS;
+            }
+        }
+    }
+    return gdn::launch_replay_commit(d, n_layers, lp, slot_ids, parents, accept_node, status, stream) == hipSuccess
+               ? GDN_OK
+               : GDN_ERR_HIP;
+}
+
 int gdn_replay_commit(const gdn_shape *sh, const float *replay_log, const float *commit_win,
                       const int32_t *slot_ids, const int32_t *parents, const int32_t *accept_node,
                       float *state_pool, float *conv_hist, int32_t *status, hipStream_t stream) {
-    gdn::Dims d;
-    if (int r = check_shape(sh, &d)) return r;
-    if (!replay_log || !commit_win || !slot_ids || !parents || !accept_node || !state_pool || !conv_hist || !status)
+    if (!replay_log || !commit_win || !state_pool || !conv_hist) {
+        gdn::Dims d;
+        if (int r = check_shape(sh, &d)) return r;
         return GDN_ERR_NULL;
-    if (!aligned({commit_win, state_pool, conv_hist}, 16) ||
-        !aligned({replay_log, slot_ids, parents, accept_node, status}, 4))
-        return GDN_ERR_ALIGN;
-    const size_t rows = (size_t)d.C * d.N;
-    const size_t R = 1 + (size_t)d.dk + d.dv;
-    if (any_alias({{state_pool, (size_t)d.P * d.Hv * d.dk * d.dv * F}, {conv_hist, (size_t)d.P * d.Ch * 3 * F},
-                   {status, I}},
-                  {{replay_log, rows * d.Hv * R * F}, {commit_win, rows * d.Ch * 3 * F}, {slot_ids, (size_t)d.C * I},
-                   {parents, rows * I}, {accept_node, (size_t)d.C * I}}))
-        return GDN_ERR_ALIAS;
-    return gdn::launch_replay_commit(d, replay_log, commit_win, slot_ids, parents, accept_node, state_pool, conv_hist,
-                                     status, stream) == hipSuccess
-               ? GDN_OK
-               : GDN_ERR_HIP;
+    }
+    return gdn_replay_commit_layers(sh, 1, &replay_log, &commit_win, slot_ids, parents, accept_node, &state_pool,
+                                    &conv_hist, status, stream);
 }
 
 const char *gdn_strerror(int code) {

@@ -42,8 +42,16 @@ hipError_t launch_tree_verify(const Dims &d, const float *qkv, const float *beta
                               const int32_t *slot_ids, const int32_t *parents, float *out, float *replay_log,
                               int32_t *status, hipStream_t stream);
 
-hipError_t launch_replay_commit(const Dims &d, const float *replay_log, const float *commit_win,
-                                const int32_t *slot_ids, const int32_t *parents, const int32_t *accept_node,
-                                float *state_pool, float *conv_hist, int32_t *status, hipStream_t stream);
+// Per-layer buffers of a multi-layer commit, passed by value as a kernel argument.
+struct LayerPtrs {
+    const float *replay_log[GDN_MAX_LAYERS];
+    const float *commit_win[GDN_MAX_LAYERS];
+    float *state_pool[GDN_MAX_LAYERS];
+    float *conv_hist[GDN_MAX_LAYERS];
+};
+
+hipError_t launch_replay_commit(const Dims &d, int n_layers, const LayerPtrs &lp, const int32_t *slot_ids,
+                                const int32_t *parents, const int32_t *accept_node, int32_t *status,
+                                hipStream_t stream);
 
 }  // namespace gdn

@@ -1,6 +1,7 @@
 // Replay-log commit for gfx950: after acceptance is known, advance each accepting slot's
 // recurrent state by the logged transitions of its accepted root path and copy the
-// accepted node's commit window into its conv history, as an all-or-nothing transaction.
+// accepted node's commit window into its conv history, as an all-or-nothing transaction,
+// for one layer or for every layer of the round in a single launch.
 //
 // What is computed: "perf(qwen35): fuse the DFlash2 concurrent verify Gated DeltaNet
 // route", closing paragraph of Optimizations (the replay-log commit advances persistent
@@ -12,11 +13,14 @@
 // launch: every workgroup runs the preflight over all lanes itself (slot range,
 // duplicate slots, parents, accept node) and also honours bits already in *status, so
 // all workgroups take the same commit-or-abort decision without a second kernel.  A
-// workgroup owns (lane, value head, 32-row block of the state); it requests its state
-// block before validating, then walks the accepted path in LDS, stages the path's g, k^
-// rows and delta rows, streams the block through S <- g S + k^ delta^T in path order and
-// writes it back.  One extra workgroup row per lane copies the commit window into the
-// history pool.
+// workgroup owns (lane, value head, 32-row block of the state).  It issues every load
+// that does not need the slot id first, then its state block; every wave finds the
+// accepted path by pointer jumping over lane shuffles, and each thread loads the logged
+// g, k^ and delta values of its own state elements for every path node straight into
+// registers while the block streams in, accumulating the replay of the path from a zero
+// state (the transitions are linear: S_final = G S0 + A).  After the preflight (barriers
+// wait for LDS traffic only) it writes G S0 + A back.
+// One extra workgroup row per lane copies the commit window into the history pool.
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -35,149 +39,209 @@ struct CommitCfg {
     static constexpr int FPT = (F4 + kThreads - 1) / kThreads;
 };
 
-// Preflight over every lane, evaluated by each workgroup; returns the status bits.
-// Contains barriers: every thread of the workgroup must call it.
-__device__ int preflight(const Dims &d, const int32_t *__restrict__ slot_ids, const int32_t *__restrict__ parents,
-                         const int32_t *__restrict__ accept_node, unsigned int *bitmap, int *s_bits) {
-    const int tid = threadIdx.x;
-    const bool use_bitmap = d.P <= kBitmapSlots;
-    if (use_bitmap)
-        for (int w = tid; w < (d.P + 31) / 32; w += kThreads) bitmap[w] = 0u;
-    if (tid == 0) *s_bits = 0;
-    __syncthreads();
-    int bits = 0;
-    for (int t = tid; t < d.C; t += kThreads) {
-        const int s = slot_ids[t];
-        if (s == -1) continue;
-        const int e = accept_node[t];
-        if (e < -1 || e >= d.N) bits |= GDN_STATUS_ACCEPT;
-        if (s < -1 || s >= d.P) {
-            bits |= GDN_STATUS_SLOT_RANGE;
-        } else if (use_bitmap) {
-            if (atomicOr(&bitmap[s >> 5], 1u << (s & 31)) & (1u << (s & 31))) bits |= GDN_STATUS_SLOT_DUP;
-        } else {
-            for (int o = 0; o < d.C; ++o)
-                if (o != t && slot_ids[o] == s) bits |= GDN_STATUS_SLOT_DUP;
+// Workgroup barrier for LDS communication only: waits for this wave's LDS operations,
+// not for its outstanding global loads, so requested state keeps streaming in.
+__device__ inline void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt left open
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+constexpr int kPreRows = 4;  // lanes' parent entries checked per thread in the first pass
+
+// Root path of node e as a bit mask, from the parents held by lanes 0..N-1 of the wave
+// (lane i holds parents[i]): pointer jumping, log2(N) rounds of lane shuffles, so the
+// cost does not grow with the depth of the path.  Out-of-range parents end the walk
+// (the preflight rejects them anyway).
+__device__ inline unsigned int path_mask(int par, int lane, int N, int e) {
+    int jump = (lane < N && par >= 0 && par < lane) ? par : -1;
+    unsigned int anc = lane < N ? 1u << lane : 0u;
+#pragma unroll
+    for (int r = 1; r < GDN_MAX_NODES; r <<= 1) {
+        const int src = jump < 0 ? lane : jump;
+        const unsigned int aj = __shfl(anc, src);
+        const int jj = __shfl(jump, src);
+        if (jump >= 0) {
+            anc |= aj;
+            jump = jj;
         }
     }
-    for (int idx = tid; idx < d.C * d.N; idx += kThreads) {
-        const int t = idx / d.N, i = idx - t * d.N;
-        const int p = parents[idx];
-        if (slot_ids[t] != -1 && (p < -1 || p >= i)) bits |= GDN_STATUS_PARENT;
-    }
-    if (bits) atomicOr(s_bits, bits);
-    __syncthreads();
-    return *s_bits;
+    return (e >= 0 && e < N) ? __shfl(anc, e) : 0u;
 }
 
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void replay_commit_kernel(
-    Dims d, const float *__restrict__ replay_log, const float *__restrict__ commit_win,
-    const int32_t *__restrict__ slot_ids, const int32_t *__restrict__ parents, const int32_t *__restrict__ accept_node,
-    float *__restrict__ state_pool, float *__restrict__ conv_hist, int32_t *__restrict__ status) {
+    Dims d, const LayerPtrs lp, const int32_t *__restrict__ slot_ids, const int32_t *__restrict__ parents,
+    const int32_t *__restrict__ accept_node, int32_t *__restrict__ status) {
     using Cfg = CommitCfg<DK, DV>;
     constexpr int RB = Cfg::RB, F4 = Cfg::F4, FPT = Cfg::FPT, R = 1 + DK + DV;
+    constexpr int Q4 = DV / 4;
+    static_assert(kThreads % Q4 == 0, "a thread keeps one 4-column group across its rows");
     __shared__ unsigned int s_bitmap[kBitmapSlots / 32];
-    __shared__ int s_bits, s_m;
-    __shared__ int s_par[GDN_MAX_NODES], s_path[GDN_MAX_NODES];
-    __shared__ float s_g[GDN_MAX_NODES];
-    __shared__ float s_k[GDN_MAX_NODES * RB];
-    __shared__ v4f s_d4[GDN_MAX_NODES * DV / 4];
+    __shared__ int s_wbits[kThreads / 64];
 
-    const int c = blockIdx.z, tid = threadIdx.x;
-    const int N = d.N, Hv = d.Hv;
+    const int c = blockIdx.z, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int N = d.N, Hv = d.Hv, C = d.C;
     const bool hist_copy = blockIdx.y == Hv;
     const int h = hist_copy ? 0 : blockIdx.y;
-    const int r0 = blockIdx.x * RB;
+    const int layer = blockIdx.x / Cfg::NB, rb = blockIdx.x - layer * Cfg::NB;
+    const int r0 = rb * RB;
+    const float *__restrict__ replay_log = lp.replay_log[layer];
+    float *__restrict__ state_pool = lp.state_pool[layer];
 
-    // ---- requests that do not depend on validation: this lane's slot, accept node and
-    //      parents, the round's status word, and the state block (slot clamped into range)
+    // ---- every load that does not need the slot id, issued first: the lane's parents
+    //      (lane i of every wave holds parents[i]) and this thread's share of the
+    //      preflight (one lane's slot and accept node, kPreRows parent entries with the
+    //      slot of their lane)
+    const int par = parents[(int64_t)c * N + (lane < N ? lane : 0)];
+    const int tl = tid < C ? tid : 0;
+    const int so = slot_ids[tl], eo = accept_node[tl];
+    int pp[kPreRows], ps[kPreRows];
+#pragma unroll
+    for (int u = 0; u < kPreRows; ++u) {
+        const int idx = min(tid + kThreads * u, C * N - 1);
+        pp[u] = parents[idx];
+        ps[u] = slot_ids[idx / N];
+    }
     const int s = slot_ids[c], e = accept_node[c];
     const int st_in = *status;
-    const int par = parents[(int64_t)c * N + (tid < N ? tid : 0)];
+    // ---- the state block (slot clamped into range; used only if the round commits)
     const bool s_ok = s >= 0 && s < d.P;
     v4f *S4 = reinterpret_cast<v4f *>(state_pool + (((int64_t)(s_ok ? s : 0) * Hv + h) * DK + r0) * DV);
     v4f sv[FPT];
 #pragma unroll
     for (int u = 0; u < FPT; ++u) sv[u] = S4[min(tid + kThreads * u, F4 - 1)];
 
-    const int bits = preflight(d, slot_ids, parents, accept_node, s_bitmap, &s_bits);
-    if (bits) {
-        if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) atomicOr(status, bits);
-        return;
+    // ---- accepted path (every wave computes it) and the replay of its logged rows.
+    //      The transitions are linear, so S_final = G S0 + A with G the product of the
+    //      path's g and A the same replay started from a zero state; A needs only the
+    //      logged rows, so it is accumulated while the state block streams in.  Path nodes
+    //      are taken 8 at a time with all their loads issued together.
+    const unsigned int pm = path_mask(par, lane, N, e);
+    const int q = tid % Q4;  // this thread's 4-column group (fixed across its rows)
+    const float *logc = replay_log + ((int64_t)c * N * Hv + h) * R;
+    v4f acc[FPT];
+#pragma unroll
+    for (int u = 0; u < FPT; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+    float G = 1.0f;
+    for (unsigned int bm = hist_copy ? 0u : pm; bm;) {
+        constexpr int kChunk = 8;
+        float cg[kChunk], ck[kChunk][FPT];
+        v4f cd[kChunk];
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            const bool has = bm != 0u;
+            const int t = has ? __builtin_ctz(bm) : 0;
+            bm = has ? bm & (bm - 1u) : 0u;
+            const float *lrow = logc + (int64_t)t * Hv * R;
+            const float g = lrow[0];
+            const float d0 = lrow[1 + DK + 4 * q], d1 = lrow[2 + DK + 4 * q];
+            const float d2 = lrow[3 + DK + 4 * q], d3 = lrow[4 + DK + 4 * q];
+            cg[j] = has ? g : 1.0f;
+            cd[j] = has ? v4f{d0, d1, d2, d3} : v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < FPT; ++u) {
+                const float kv = lrow[1 + r0 + min(tid + kThreads * u, F4 - 1) / Q4];
+                ck[j][u] = has ? kv : 0.f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            G *= cg[j];
+#pragma unroll
+            for (int u = 0; u < FPT; ++u) {
+                acc[u].x = fmaf(ck[j][u], cd[j].x, cg[j] * acc[u].x);
+                acc[u].y = fmaf(ck[j][u], cd[j].y, cg[j] * acc[u].y);
+                acc[u].z = fmaf(ck[j][u], cd[j].z, cg[j] * acc[u].z);
+                acc[u].w = fmaf(ck[j][u], cd[j].w, cg[j] * acc[u].w);
+            }
+        }
+    }
+
+    // ---- preflight over every lane (slot range, duplicate slots via an LDS bitmap or a
+    //      scan, parents, accept node); every workgroup reaches the same verdict
+    const bool use_bitmap = d.P <= kBitmapSlots;
+    if (use_bitmap)
+        for (int w = tid; w < (d.P + 31) / 32; w += kThreads) s_bitmap[w] = 0u;
+    lds_barrier();
+    int bits = 0;
+    for (int t = tid; t < C; t += kThreads) {
+        const int st = t == tid ? so : slot_ids[t];
+        if (st == -1) continue;
+        const int et = t == tid ? eo : accept_node[t];
+        if (et < -1 || et >= N) bits |= GDN_STATUS_ACCEPT;
+        if (st < -1 || st >= d.P) {
+            bits |= GDN_STATUS_SLOT_RANGE;
+        } else if (use_bitmap) {
+            if (atomicOr(&s_bitmap[st >> 5], 1u << (st & 31)) & (1u << (st & 31))) bits |= GDN_STATUS_SLOT_DUP;
+        } else {
+            for (int o = 0; o < C; ++o)
+                if (o != t && slot_ids[o] == st) bits |= GDN_STATUS_SLOT_DUP;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kPreRows; ++u) {
+        const int idx = tid + kThreads * u;
+        if (idx < C * N && ps[u] != -1 && (pp[u] < -1 || pp[u] >= idx % N)) bits |= GDN_STATUS_PARENT;
+    }
+    for (int idx = tid + kThreads * kPreRows; idx < C * N; idx += kThreads) {  // beyond the first pass
+        const int p = parents[idx];
+        if (slot_ids[idx / N] != -1 && (p < -1 || p >= idx % N)) bits |= GDN_STATUS_PARENT;
+    }
+    {
+        int wb = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            if (__builtin_amdgcn_ballot_w64((bits >> b) & 1)) wb |= 1 << b;
+        if (lane == 0) s_wbits[wave] = wb;
+    }
+    lds_barrier();
+    {
+        int all = 0;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) all |= s_wbits[w];
+        if (all) {
+            if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) atomicOr(status, all);  // once per lane
+            return;
+        }
     }
     if (st_in != 0 || s < 0 || e < 0) return;  // flagged round, padding lane, or nothing accepted
 
     if (hist_copy) {  // conv history <- commit window of the accepted node
         const int n4 = d.Ch * 3 / 4;
-        const v4f *src = reinterpret_cast<const v4f *>(commit_win + ((int64_t)c * N + e) * d.Ch * 3);
-        v4f *dst = reinterpret_cast<v4f *>(conv_hist + (int64_t)s * d.Ch * 3);
-        for (int idx = blockIdx.x * kThreads + tid; idx < n4; idx += gridDim.x * kThreads) dst[idx] = src[idx];
+        const v4f *src = reinterpret_cast<const v4f *>(lp.commit_win[layer] + ((int64_t)c * N + e) * d.Ch * 3);
+        v4f *dst = reinterpret_cast<v4f *>(lp.conv_hist[layer] + (int64_t)s * d.Ch * 3);
+        for (int idx = rb * kThreads + tid; idx < n4; idx += Cfg::NB * kThreads) dst[idx] = src[idx];
         return;
     }
 
-    // ---- accepted path (root child first), walked in LDS
-    if (tid < N) s_par[tid] = par;
-    __syncthreads();
-    if (tid == 0) {
-        int m = 0;
-        for (int a = e; a >= 0; a = s_par[a]) ++m;
-        s_m = m;
-        for (int a = e, k = m; a >= 0; a = s_par[a]) s_path[--k] = a;
-    }
-    __syncthreads();
-    const int m = s_m;
-    const float *logc = replay_log + ((int64_t)c * N * Hv + h) * R;
-    for (int idx = tid; idx < m * RB; idx += kThreads) {
-        const int t = idx / RB, r = idx - t * RB;
-        const float *lrow = logc + (int64_t)s_path[t] * Hv * R;
-        s_k[idx] = lrow[1 + r0 + r];
-        if (r == 0) s_g[t] = lrow[0];
-    }
-    float *s_d = reinterpret_cast<float *>(s_d4);
-    for (int idx = tid; idx < m * DV; idx += kThreads) {
-        const int t = idx / DV, j = idx - t * DV;
-        s_d[idx] = logc[(int64_t)s_path[t] * Hv * R + 1 + DK + j];
-    }
-    __syncthreads();
-
-    // ---- S <- g S + k^ delta^T along the path, then write the block back
+    // ---- S = G S0 + A, written back
     // (indices clamped as at load time: surplus threads recompute the last group from
-    // the same loaded value and store the identical result)
+    // the same loaded values and store the identical result)
 #pragma unroll
     for (int u = 0; u < FPT; ++u) {
-        const int idx = min(tid + kThreads * u, F4 - 1);
-        const int r = idx / (DV / 4), q = idx - r * (DV / 4);
-        v4f v = sv[u];
-        for (int t = 0; t < m; ++t) {
-            const float g = s_g[t], kr = s_k[t * RB + r];
-            const v4f dl = s_d4[t * (DV / 4) + q];
-            v.x = fmaf(kr, dl.x, g * v.x);
-            v.y = fmaf(kr, dl.y, g * v.y);
-            v.z = fmaf(kr, dl.z, g * v.z);
-            v.w = fmaf(kr, dl.w, g * v.w);
-        }
-        S4[idx] = v;
+        const v4f v = sv[u];
+        S4[min(tid + kThreads * u, F4 - 1)] =
+            v4f{fmaf(G, v.x, acc[u].x), fmaf(G, v.y, acc[u].y), fmaf(G, v.z, acc[u].z), fmaf(G, v.w, acc[u].w)};
     }
 }
 
 template <int DK, int DV>
-hipError_t launch(const Dims &d, const float *log, const float *win, const int32_t *slots, const int32_t *parents,
-                  const int32_t *accept, float *pool, float *hist, int32_t *status, hipStream_t stream) {
-    hipLaunchKernelGGL((replay_commit_kernel<DK, DV>), dim3(CommitCfg<DK, DV>::NB, d.Hv + 1, d.C), dim3(kThreads), 0,
-                       stream, d, log, win, slots, parents, accept, pool, hist, status);
+hipError_t launch(const Dims &d, int n_layers, const LayerPtrs &lp, const int32_t *slots, const int32_t *parents,
+                  const int32_t *accept, int32_t *status, hipStream_t stream) {
+    hipLaunchKernelGGL((replay_commit_kernel<DK, DV>), dim3(CommitCfg<DK, DV>::NB * n_layers, d.Hv + 1, d.C),
+                       dim3(kThreads), 0, stream, d, lp, slots, parents, accept, status);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_replay_commit(const Dims &d, const float *replay_log, const float *commit_win,
-                                const int32_t *slot_ids, const int32_t *parents, const int32_t *accept_node,
-                                float *state_pool, float *conv_hist, int32_t *status, hipStream_t stream) {
-#define GDN_COMMIT_CASE(K, V)                                                                                      \
-    if (d.dk == K && d.dv == V)                                                                                    \
-        return launch<K, V>(d, replay_log, commit_win, slot_ids, parents, accept_node, state_pool, conv_hist, status, \
-                            stream);
+hipError_t launch_replay_commit(const Dims &d, int n_layers, const LayerPtrs &lp, const int32_t *slot_ids,
+                                const int32_t *parents, const int32_t *accept_node, int32_t *status,
+                                hipStream_t stream) {
+#define GDN_COMMIT_CASE(K, V) \
+    if (d.dk == K && d.dv == V) return launch<K, V>(d, n_layers, lp, slot_ids, parents, accept_node, status, stream);
 #define GDN_COMMIT_ROW(K) GDN_COMMIT_CASE(K, 16) GDN_COMMIT_CASE(K, 32) GDN_COMMIT_CASE(K, 64) GDN_COMMIT_CASE(K, 128)
     GDN_COMMIT_ROW(16) GDN_COMMIT_ROW(32) GDN_COMMIT_ROW(64) GDN_COMMIT_ROW(128)
 #undef GDN_COMMIT_ROW

@@ -67,7 +67,8 @@ extern "C" {
 #define GDN_OK 0
 #define GDN_ERR_NULL 1        /* a required pointer is NULL                                  */
 #define GDN_ERR_SHAPE 2       /* non-positive dimension, H_v % H_k != 0, gate_stride < H_v   */
-#define GDN_ERR_UNSUPPORTED 3 /* d_conv != 4, d_k/d_v not in {16,32,64,128}, N > 32, C > 1024 */
+#define GDN_ERR_UNSUPPORTED 3 /* d_conv != 4, d_k/d_v not in {16,32,64,128}, N > 32, C > 1024,
+                                 n_layers outside 1..GDN_MAX_LAYERS                           */
 #define GDN_ERR_ALIAS 4       /* an output byte range overlaps an input or another output    */
 #define GDN_ERR_HIP 5         /* a kernel launch failed                                      */
 #define GDN_ERR_ALIGN 6       /* a dense float buffer is not 16-byte aligned, or an int32 /
@@ -81,6 +82,7 @@ extern "C" {
 
 #define GDN_MAX_NODES 32
 #define GDN_MAX_SEQS 1024
+#define GDN_MAX_LAYERS 64
 
 typedef struct gdn_shape {
     int32_t n_seqs;    /* C, 1..GDN_MAX_SEQS                                     */
@@ -173,6 +175,26 @@ int gdn_tree_verify(const gdn_shape *sh, const float *qkv, const float *beta_log
 int gdn_replay_commit(const gdn_shape *sh, const float *replay_log, const float *commit_win,
                       const int32_t *slot_ids, const int32_t *parents, const int32_t *accept_node,
                       float *state_pool, float *conv_hist, int32_t *status, hipStream_t stream);
+
+/*
+ * Multi-layer replay-log commit: the commit above for every GDN layer of the round in
+ * one launch.  Acceptance is per token, so all layers share slot_ids, parents and
+ * accept_node; each layer l has its own replay log, commit windows, state pool and
+ * history pool.  One preflight and one status word cover the round: either every
+ * layer commits or none does.  (The pages' route issues one commit launch per layer,
+ * "perf(qwen38): various DFlash2 optimizations concurrency C1-C5", launch accounting.)
+ *
+ *   n_layers                 1..GDN_MAX_LAYERS
+ *   replay_logs, commit_wins host arrays of n_layers device pointers (layouts as above)
+ *   state_pools, conv_hists  host arrays of n_layers device pointers, updated in place
+ *   slot_ids, parents, accept_node, status   as in gdn_replay_commit (status REQUIRED)
+ * Every layer's pools must be disjoint from every input and from each other
+ * (GDN_ERR_ALIAS).
+ */
+int gdn_replay_commit_layers(const gdn_shape *sh, int32_t n_layers, const float *const *replay_logs,
+                             const float *const *commit_wins, const int32_t *slot_ids, const int32_t *parents,
+                             const int32_t *accept_node, float *const *state_pools, float *const *conv_hists,
+                             int32_t *status, hipStream_t stream);
 
 /* Static description of a GDN_OK / GDN_ERR_* code. */
 const char *gdn_strerror(int code);

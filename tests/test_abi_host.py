@@ -133,3 +133,42 @@ def test_alias_rejected():
     p = _ptrs(7)
     p[5] = p[0]  # state pool over the replay log
     assert _commit(sh, p, FAKE + (9 << 28)) == _lib.GDN_ERR_ALIAS
+
+
+def _commit_layers(sh, L, per_layer, shared, status, n_layers=None):
+    """per_layer: 4 lists (logs, wins, pools, hists) of L fake pointers; shared: 3 pointers."""
+    lib = gdn.load_library()
+    cs = sh.c_struct()
+    arrs = [(ctypes.c_void_p * L)(*v) for v in per_layer]
+    cast = [ctypes.cast(a, ctypes.c_void_p) for a in arrs]
+    return lib.gdn_replay_commit_layers(ctypes.byref(cs), ctypes.c_int32(L if n_layers is None else n_layers),
+                                        cast[0], cast[1], *shared, cast[2], cast[3], status, None)
+
+
+def _layer_ptrs(L):
+    base = _ptrs(4 * L + 3)
+    return [base[0:L], base[L:2 * L], base[2 * L:3 * L], base[3 * L:4 * L]], base[4 * L:]
+
+
+def test_commit_layers_rejections():
+    sh, st = _shape(), FAKE + (1 << 40)
+    per, shared = _layer_ptrs(3)
+    assert _commit_layers(sh, 3, per, shared, None) == _lib.GDN_ERR_NULL
+    assert _commit_layers(sh, 3, per, shared, st, n_layers=0) == _lib.GDN_ERR_UNSUPPORTED
+    assert _commit_layers(sh, 3, per, shared, st, n_layers=65) == _lib.GDN_ERR_UNSUPPORTED
+    per, shared = _layer_ptrs(3)
+    per[1][2] = None  # one layer's commit windows missing
+    assert _commit_layers(sh, 3, per, shared, st) == _lib.GDN_ERR_NULL
+    per, shared = _layer_ptrs(3)
+    per[2][1] += 8  # one layer's state pool misaligned
+    assert _commit_layers(sh, 3, per, shared, st) == _lib.GDN_ERR_ALIGN
+    per, shared = _layer_ptrs(3)
+    per[3][2] = per[2][0] + 16  # layer 2's history inside layer 0's state pool
+    assert _commit_layers(sh, 3, per, shared, st) == _lib.GDN_ERR_ALIAS
+    per, shared = _layer_ptrs(3)
+    per[2][1] = per[0][2] + 16  # layer 1's state pool inside layer 2's replay log
+    assert _commit_layers(sh, 3, per, shared, st) == _lib.GDN_ERR_ALIAS
+    per, shared = _layer_ptrs(3)
+    assert _commit_layers(sh, 3, per, shared, per[3][1]) == _lib.GDN_ERR_ALIAS  # status in a history pool
+    per, shared = _layer_ptrs(3)
+    assert _commit_layers(_shape(d_conv=5), 3, per, shared, st) == _lib.GDN_ERR_UNSUPPORTED

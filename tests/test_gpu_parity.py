@@ -270,3 +270,72 @@ def test_graph_replay_matches_eager():
         assert int(g.status.item()) == 0
         for a, b in zip(list(bufs) + [g.state, g.conv_hist], ref):
             assert torch.equal(a, b), f"replay {rep} differs from the eager result"
+
+
+def _layer_rounds(wl, layers):
+    sh = gdn.Shape(**wl.shape_dict())
+    rs = round_structure(wl, 0)
+    rounds, cases = [], []
+    for layer in layers:
+        case = dict(layer_params(wl, layer), **rs, **round_inputs(wl, layer, 0))
+        rounds.append(GpuRound(sh, case["x"], case["ba"], case["conv_w"], case["conv_hist"], case["state"],
+                               case["dt_bias"], case["A"], case["slot_ids"], case["parents"]).verify())
+        cases.append(case)
+    torch.cuda.synchronize()
+    return sh, rs, rounds, cases
+
+
+def test_commit_layers_matches_per_layer_and_oracle():
+    """Every layer of chains-c5-n8-l48 committed in one launch: bit-identical to one
+    commit launch per layer, and within the recurrence bar of the oracle on sampled layers."""
+    wl = WORKLOADS["chains-c5-n8-l48"]
+    layers = list(range(wl.n_layers))
+    log(f"[commit-layers] {wl.name} L={len(layers)}")
+    sh, rs, rounds, cases = _layer_rounds(wl, layers)
+    accept = dev(rs["accept_node"])
+    pools = [g.state.clone() for g in rounds]
+    hists = [g.conv_hist.clone() for g in rounds]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gdn.replay_commit_layers(sh, [g.replay_log.t for g in rounds], [g.commit_win.t for g in rounds], rounds[0].slot_ids,
+                             rounds[0].parents, accept, pools, hists, status)
+    for g in rounds:
+        g.commit(rs["accept_node"])
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for l, g in enumerate(rounds):
+        assert int(g.status.item()) == 0
+        assert torch.equal(pools[l], g.state), f"layer {l} state"
+        assert torch.equal(hists[l], g.conv_hist), f"layer {l} history"
+    for l in (0, 23, 47):
+        c = cases[l]
+        ref = oracle_round(sh, c["x"], c["ba"], c["conv_w"], c["conv_hist"], c["state"], c["dt_bias"], c["A"],
+                           c["slot_ids"], c["parents"])
+        st, pool, hist = oracle_commit(sh, ref, c["slot_ids"], c["parents"], c["accept_node"], c["state"],
+                                       c["conv_hist"])
+        assert st == 0
+        assert err_metric(pools[l].cpu().numpy(), pool) <= REC_TOL
+        assert err_metric(hists[l].cpu().numpy(), hist) == 0.0
+
+
+@pytest.mark.parametrize("bad", ["accept", "slot"])
+def test_commit_layers_all_or_nothing(bad):
+    """One bad lane cancels the commit of every layer in the launch."""
+    wl = WORKLOADS["tree-c4-n16"]
+    log(f"[commit-layers transaction] {bad}")
+    sh, rs, rounds, _ = _layer_rounds(wl, [0, 0, 0])  # same inputs, three distinct sets of pools
+    accept = rs["accept_node"].copy()
+    slots = rounds[0].slot_ids.clone()
+    if bad == "accept":
+        accept[2] = sh.n_nodes
+    else:
+        slots[1] = sh.n_slots  # out of range
+    before = [(g.state.clone(), g.conv_hist.clone()) for g in rounds]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gdn.replay_commit_layers(sh, [g.replay_log.t for g in rounds], [g.commit_win.t for g in rounds], slots,
+                             rounds[0].parents, dev(accept), [g.state for g in rounds],
+                             [g.conv_hist for g in rounds], status)
+    torch.cuda.synchronize()
+    want = gdn.STATUS_ACCEPT if bad == "accept" else gdn.STATUS_SLOT_RANGE
+    assert int(status.item()) & want
+    for g, (s0, h0) in zip(rounds, before):
+        assert torch.equal(g.state, s0) and torch.equal(g.conv_hist, h0)
