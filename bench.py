@@ -4,9 +4,12 @@
 One step = one speculative round over L independent layer instances of the
 workload (default: 4 lanes in an 8-slot pool, 16-node random draft trees,
 H_k=16, H_v=32, d_k=d_v=128, 8192 conv channels): for every instance the tree
-conv step and the tree verify, then for every instance the replay commit of the
-round's accepted paths.  L=64 instances (~1.9 GB) keep the working set far
-above the 256 MB last-level cache, so every layer reads its inputs from HBM.
+conv step and the tree verify, then the replay commit of the round's accepted
+paths for all instances in one multi-layer launch (or, with --commit per-layer,
+one commit launch per instance).  All instances share the round's slot ids,
+parents, accept nodes and status word, as the layers of one model round do.
+L=64 instances (~1.9 GB) keep the working set far above the 256 MB last-level
+cache, so every layer reads its inputs from HBM.
 
 value = C*N*L / step time: verified draft tokens per second, each instance
 counted as one single-layer verify.  Inputs are resident in HBM before timing.
@@ -43,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true", help="skip the CPU oracle and per-kernel loops")
     ap.add_argument("--eager", action="store_true", help="launch every call directly instead of replaying graphs")
+    ap.add_argument("--commit", choices=("layers", "per-layer"), default="layers",
+                    help="one multi-layer commit launch per round, or one commit launch per instance")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, launch 4 plain device copies of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -127,6 +132,7 @@ def main():
     accepts = [d(r["accept_node"]) for r in rounds]
     depths = [[len(path_to_root(r["parents"][c], int(e))) if e >= 0 else 0 for c, e in enumerate(r["accept_node"])]
               for r in rounds]
+    status = torch.zeros(1, dtype=torch.int32, device=dev)  # the round's status word, shared by every layer
     inst = []
     for l in range(L):
         lp, ri = layer_params(wl, l, args.seed), round_inputs(wl, l, 0, args.seed)
@@ -136,29 +142,39 @@ def main():
             conv_hist=d(lp["conv_hist"]), state=d(lp["state"]), dt_bias=d(lp["dt_bias"]), A=d(lp["A"]),
             conv_out=torch.empty((C, N, Ch), device=dev), commit_win=torch.empty((C, N, Ch, 3), device=dev),
             out=torch.empty((C, N, Hv, dv), device=dev), log=torch.empty((C, N, Hv, sh.log_row), device=dev),
-            status=torch.zeros(1, dtype=torch.int32, device=dev),
         ))
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
 
     def conv(b, r):
         gdn.conv_tree_step(sh, b["x"], b["conv_w"], b["conv_hist"], slot_ids, parents[r], conv_out=b["conv_out"],
-                           commit_win=b["commit_win"], status=b["status"])
+                           commit_win=b["commit_win"], status=status)
 
     def verify(b, r):
         gdn.tree_verify(sh, b["conv_out"], b["beta"], b["alpha"], b["dt_bias"], b["A"], b["state"], slot_ids,
-                        parents[r], out=b["out"], replay_log=b["log"], status=b["status"])
+                        parents[r], out=b["out"], replay_log=b["log"], status=status)
 
     def commit(b, r):
         gdn.replay_commit(sh, b["log"], b["commit_win"], slot_ids, parents[r], accepts[r], b["state"], b["conv_hist"],
-                          b["status"])
+                          status)
+
+    if L > gdn.MAX_LAYERS and args.commit == "layers":
+        raise SystemExit(f"--instances {L} exceeds the {gdn.MAX_LAYERS} layers of one multi-layer commit")
+    layer_bufs = {k: [b[k] for b in inst] for k in ("log", "commit_win", "state", "conv_hist")}
+
+    def commit_layers(r):
+        gdn.replay_commit_layers(sh, layer_bufs["log"], layer_bufs["commit_win"], slot_ids, parents[r], accepts[r],
+                                 layer_bufs["state"], layer_bufs["conv_hist"], status)
 
     def step(r):
         for b in inst:
             conv(b, r)
             verify(b, r)
-        for b in inst:
-            commit(b, r)
+        if args.commit == "layers":
+            commit_layers(r)
+        else:
+            for b in inst:
+                commit(b, r)
 
     # Warm up eagerly (also runs every kernel's one-time setup), then capture one HIP
     # graph per round draw: a decode loop launches a whole round as one graph replay,
@@ -166,7 +182,7 @@ def main():
     for k in range(args.warmup):
         step(k % args.rounds)
     torch.cuda.synchronize()
-    assert all(int(b["status"].item()) == 0 for b in inst), "device status bits set"
+    assert int(status.item()) == 0, "device status bits set"
 
     def capture(fn):
         g = torch.cuda.CUDAGraph()
@@ -189,14 +205,19 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / args.steps
-    assert all(int(b["status"].item()) == 0 for b in inst), "device status bits set"
+    assert int(status.item()) == 0, "device status bits set"
 
-    # per-kernel mean launch time: each kernel alone over the L instances (one graph of L
-    # back-to-back launches), HIP events on the stream the graph runs on
+    # per-kernel mean time per layer instance: each kernel alone over the L instances (one
+    # graph of L back-to-back launches, or of one multi-layer commit launch), HIP events
+    # on the stream the graph runs on
     kern = {}
     if not args.profile_only:
-        for name, fn in (("conv_tree_step", conv), ("tree_verify", verify), ("replay_commit", commit)):
-            g = capture(lambda fn=fn: [fn(b, 0) for b in inst])
+        timed = [("conv_tree_step", lambda: [conv(b, 0) for b in inst]),
+                 ("tree_verify", lambda: [verify(b, 0) for b in inst])]
+        timed.append(("replay_commit", (lambda: commit_layers(0)) if args.commit == "layers"
+                      else (lambda: [commit(b, 0) for b in inst])))
+        for name, fn in timed:
+            g = capture(fn)
             g.replay()
             torch.cuda.synchronize()
             ev0.record()
@@ -204,7 +225,7 @@ def main():
                 g.replay()
             ev1.record()
             torch.cuda.synchronize()
-            kern[name] = ev0.elapsed_time(ev1) * 1e3 / (args.kernel_reps * L)  # us per launch
+            kern[name] = ev0.elapsed_time(ev1) * 1e3 / (args.kernel_reps * L)  # us per layer instance
 
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20) // 4
@@ -222,10 +243,13 @@ def main():
     if kern:
         dom = max(("conv_tree_step", "tree_verify", "replay_commit"), key=lambda k: kern[k])
         bytes_per = {"conv_tree_step": ab["conv"], "tree_verify": ab["verify"], "replay_commit": commit_bytes}[dom]
+        layers_per_launch = L if (dom == "replay_commit" and args.commit == "layers") else 1
         achieved = bytes_per / (kern[dom] * 1e-6) / 1e9
+        traffic = measured_traffic(wl.name, dom)
         roofline = dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(wl.name, dom),
-                        bytes_per_launch=int(bytes_per), us_per_launch=round(kern[dom], 3))
+                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
+                        bytes_per_launch=int(bytes_per * layers_per_launch),
+                        us_per_launch=round(kern[dom] * layers_per_launch, 3))
 
     cpu = None
     if not args.no_cpu_baseline and not args.profile_only:
@@ -249,7 +273,8 @@ def main():
         "timing": "HIP graph replay of the whole step; inputs resident in HBM",
         "config": {"workload": wl.name, "lanes": C, "nodes": N, "slots": P, "k_heads": wl.n_k_heads,
                    "v_heads": Hv, "d_k": dk, "d_v": dv, "conv_channels": Ch, "layer_instances": L,
-                   "step": "conv+verify per instance, then commit per instance"},
+                   "step": "conv+verify per instance, then " + ("one multi-layer commit" if args.commit == "layers"
+                                                                  else "commit per instance")},
         "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "kernel_us": {k: round(v, 3) for k, v in kern.items()},
         "kernel_gbs": {k: round(b / (kern[k] * 1e-6) / 1e9, 1) for k, b in
