@@ -3,10 +3,10 @@
 
 One step = one speculative round over L independent layer instances of the
 workload (default: 4 lanes in an 8-slot pool, 16-node random draft trees,
-H_k=16, H_v=32, d_k=d_v=128, 8192 conv channels): for every instance the tree
-conv step and the tree verify, then the replay commit of the round's accepted
-paths for all instances in one multi-layer launch (or, with --commit per-layer,
-one commit launch per instance).  All instances share the round's slot ids,
+H_k=16, H_v=32, d_k=d_v=128, 8192 conv channels): for every instance the fused
+tree conv + verify (or, with --route split, the separate conv step and verify),
+then the replay commit of the round's accepted paths for all instances in one
+multi-layer launch (or, with --commit per-layer, one commit launch per instance).  All instances share the round's slot ids,
 parents, accept nodes and status word, as the layers of one model round do.
 L=64 instances (~1.9 GB) keep the working set far above the 256 MB last-level
 cache, so every layer reads its inputs from HBM.
@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true", help="skip the CPU oracle and per-kernel loops")
     ap.add_argument("--eager", action="store_true", help="launch every call directly instead of replaying graphs")
+    ap.add_argument("--route", choices=("fused", "split"), default="fused",
+                    help="fused conv + verify call, or the separate conv step and verify calls")
     ap.add_argument("--commit", choices=("layers", "per-layer"), default="layers",
                     help="one multi-layer commit launch per round, or one commit launch per instance")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -60,7 +62,8 @@ def algorithmic_bytes(wl, accept_depths):
     conv = 4 * Ch * (C * (W + N + N + N * W) + wl.d_conv)
     verify = 4 * (C * Hv * dk * dv + C * N * Ch + 2 * C * N * Hv + 2 * Hv + C * N * Hv * dv + C * N * Hv * R)
     commit = sum(4 * (2 * Hv * dk * dv + 2 * W * Ch) + a * 4 * Hv * R for a in accept_depths if a > 0)
-    return dict(conv=conv, verify=verify, commit=commit)
+    # fused: the conv output is neither written nor read back
+    return dict(conv=conv, verify=verify, conv_verify=conv + verify - 2 * 4 * C * N * Ch, commit=commit)
 
 
 def measured_traffic(workload, kernel):
@@ -154,6 +157,11 @@ def main():
         gdn.tree_verify(sh, b["conv_out"], b["beta"], b["alpha"], b["dt_bias"], b["A"], b["state"], slot_ids,
                         parents[r], out=b["out"], replay_log=b["log"], status=status)
 
+    def conv_verify(b, r):
+        gdn.conv_tree_verify(sh, b["x"], b["conv_w"], b["conv_hist"], b["beta"], b["alpha"], b["dt_bias"], b["A"],
+                             b["state"], slot_ids, parents[r], out=b["out"], replay_log=b["log"],
+                             commit_win=b["commit_win"], status=status)
+
     def commit(b, r):
         gdn.replay_commit(sh, b["log"], b["commit_win"], slot_ids, parents[r], accepts[r], b["state"], b["conv_hist"],
                           status)
@@ -168,8 +176,11 @@ def main():
 
     def step(r):
         for b in inst:
-            conv(b, r)
-            verify(b, r)
+            if args.route == "fused":
+                conv_verify(b, r)
+            else:
+                conv(b, r)
+                verify(b, r)
         if args.commit == "layers":
             commit_layers(r)
         else:
@@ -212,8 +223,11 @@ def main():
     # on the stream the graph runs on
     kern = {}
     if not args.profile_only:
-        timed = [("conv_tree_step", lambda: [conv(b, 0) for b in inst]),
-                 ("tree_verify", lambda: [verify(b, 0) for b in inst])]
+        if args.route == "fused":
+            timed = [("conv_tree_verify", lambda: [conv_verify(b, 0) for b in inst])]
+        else:
+            timed = [("conv_tree_step", lambda: [conv(b, 0) for b in inst]),
+                     ("tree_verify", lambda: [verify(b, 0) for b in inst])]
         timed.append(("replay_commit", (lambda: commit_layers(0)) if args.commit == "layers"
                       else (lambda: [commit(b, 0) for b in inst])))
         for name, fn in timed:
@@ -239,10 +253,12 @@ def main():
     ab = algorithmic_bytes(wl, [int(round(mean_depths))] * C)
     ab_rounds = [algorithmic_bytes(wl, dd) for dd in depths]
     commit_bytes = float(np.mean([a["commit"] for a in ab_rounds]))
+    kernel_bytes = {"conv_tree_step": ab["conv"], "tree_verify": ab["verify"], "conv_tree_verify": ab["conv_verify"],
+                    "replay_commit": commit_bytes}
     roofline = None
     if kern:
-        dom = max(("conv_tree_step", "tree_verify", "replay_commit"), key=lambda k: kern[k])
-        bytes_per = {"conv_tree_step": ab["conv"], "tree_verify": ab["verify"], "replay_commit": commit_bytes}[dom]
+        dom = max(kern, key=lambda k: kern[k])
+        bytes_per = kernel_bytes[dom]
         layers_per_launch = L if (dom == "replay_commit" and args.commit == "layers") else 1
         achieved = bytes_per / (kern[dom] * 1e-6) / 1e9
         traffic = measured_traffic(wl.name, dom)
@@ -256,7 +272,7 @@ def main():
         cpu = cpu_baseline(wl, args.cpu_seconds, args.seed)
 
     tokens = C * N * L
-    step_bytes = L * (ab["conv"] + ab["verify"]) + L * commit_bytes
+    step_bytes = L * (ab["conv_verify"] if args.route == "fused" else ab["conv"] + ab["verify"]) + L * commit_bytes
     line = {
         "metric": "GDN verify tokens/s (C=4, 16-node trees, d=128); achieved HBM GB/s vs peak",
         "value": round(tokens / (ms_step * 1e-3), 1),
@@ -273,14 +289,13 @@ def main():
         "timing": "HIP graph replay of the whole step; inputs resident in HBM",
         "config": {"workload": wl.name, "lanes": C, "nodes": N, "slots": P, "k_heads": wl.n_k_heads,
                    "v_heads": Hv, "d_k": dk, "d_v": dv, "conv_channels": Ch, "layer_instances": L,
-                   "step": "conv+verify per instance, then " + ("one multi-layer commit" if args.commit == "layers"
-                                                                  else "commit per instance")},
+                   "step": ("fused conv+verify" if args.route == "fused" else "conv step + verify")
+                           + " per instance, then " + ("one multi-layer commit" if args.commit == "layers"
+                                                      else "commit per instance")},
         "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "kernel_us": {k: round(v, 3) for k, v in kern.items()},
-        "kernel_gbs": {k: round(b / (kern[k] * 1e-6) / 1e9, 1) for k, b in
-                       (("conv_tree_step", ab["conv"]), ("tree_verify", ab["verify"]),
-                        ("replay_commit", commit_bytes)) if k in kern},
-        "verify_only_tokens_per_s": (round(C * N / ((kern["conv_tree_step"] + kern["tree_verify"]) * 1e-6), 1)
+        "kernel_gbs": {k: round(kernel_bytes[k] / (kern[k] * 1e-6) / 1e9, 1) for k in kern},
+        "verify_only_tokens_per_s": (round(C * N / (sum(v for k, v in kern.items() if k != "replay_commit") * 1e-6), 1)
                                      if kern else None),
         "roofline": roofline,
         "cpu_baseline": cpu,

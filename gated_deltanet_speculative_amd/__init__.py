@@ -5,6 +5,7 @@ include/gdn_verify.h (libgdnverify.so, hand-written gfx950 HIP kernels):
 
     conv_tree_step  -> conv_out, commit_win
     tree_verify     -> out, replay_log          (persistent state read-only)
+    conv_tree_verify -> out, replay_log, commit_win  (the two above fused)
     replay_commit   -> advances state_pool / conv_hist of accepting slots
     replay_commit_layers -> the same for every layer of a round, one launch
 
@@ -23,6 +24,7 @@ from ._lib import (  # noqa: F401
     STATUS_SLOT_DUP,
     STATUS_SLOT_RANGE,
     conv_tree_step,
+    conv_tree_verify,
     load_library,
     replay_commit,
     replay_commit_layers,

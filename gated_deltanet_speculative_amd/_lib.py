@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libgdnverify.so")
 
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP, GDN_ERR_ALIGN = range(7)
 STATUS_SLOT_RANGE, STATUS_SLOT_DUP, STATUS_PARENT, STATUS_ACCEPT = 1, 2, 4, 8
-EXPORTED = ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_replay_commit", "gdn_replay_commit_layers", "gdn_strerror")
+EXPORTED = ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_conv_tree_verify", "gdn_replay_commit",
+            "gdn_replay_commit_layers", "gdn_strerror")
 MAX_LAYERS = 64
 
 
@@ -73,9 +74,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     sp = ctypes.POINTER(_CShape)
     lib.gdn_conv_tree_step.argtypes = [sp] + [vp] * 9
     lib.gdn_tree_verify.argtypes = [sp, vp, vp, vp, i64] + [vp] * 9
+    lib.gdn_conv_tree_verify.argtypes = [sp, vp, vp, vp, vp, vp, i64] + [vp] * 10
     lib.gdn_replay_commit.argtypes = [sp] + [vp] * 9
     lib.gdn_replay_commit_layers.argtypes = [sp, i32] + [vp] * 9
-    for f in ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_replay_commit", "gdn_replay_commit_layers"):
+    for f in ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_conv_tree_verify", "gdn_replay_commit",
+              "gdn_replay_commit_layers"):
         getattr(lib, f).restype = i32
     lib.gdn_strerror.argtypes = [ctypes.c_int]
     lib.gdn_strerror.restype = ctypes.c_char_p
@@ -196,6 +199,43 @@ def tree_verify(sh: Shape, qkv, beta_logits, alpha_logits, dt_bias, A, state_poo
     cs = sh.c_struct()
     _check(load_library().gdn_tree_verify(ctypes.byref(cs), *args), "gdn_tree_verify")
     return out, replay_log, status
+
+
+def conv_tree_verify(sh: Shape, x, conv_w, conv_hist, beta_logits, alpha_logits, dt_bias, A, state_pool, slot_ids,
+                     parents, out=None, replay_log=None, commit_win=None, status=None):
+    """Fused tree conv + verify (the conv output stays on chip).  Returns
+    (out, replay_log, commit_win, status)."""
+    C, N, P, Hv, dk, dv, Ch = sh.n_seqs, sh.n_nodes, sh.n_slots, sh.n_v_heads, sh.d_k, sh.d_v, sh.channels
+    if out is None:
+        out = torch.empty((C, N, Hv, dv), dtype=torch.float32, device=x.device)
+    if replay_log is None:
+        replay_log = torch.empty((C, N, Hv, sh.log_row), dtype=torch.float32, device=x.device)
+    if commit_win is None:
+        commit_win = torch.empty((C, N, Ch, sh.d_conv - 1), dtype=torch.float32, device=x.device)
+    status = _status(status, x)
+    bp, bs = _gate_view(beta_logits, "beta_logits", sh)
+    ap, as_ = _gate_view(alpha_logits, "alpha_logits", sh)
+    if bs != as_:
+        raise ValueError("beta_logits and alpha_logits must share one row stride")
+    args = [
+        _dev(x, "x", torch.float32, (C, N, Ch)),
+        _dev(conv_w, "conv_w", torch.float32, (Ch, sh.d_conv)),
+        _dev(conv_hist, "conv_hist", torch.float32, (P, Ch, sh.d_conv - 1)),
+        bp, ap, bs,
+        _dev(dt_bias, "dt_bias", torch.float32, (Hv,)),
+        _dev(A, "A", torch.float32, (Hv,)),
+        _dev(state_pool, "state_pool", torch.float32, (P, Hv, dk, dv)),
+        _dev(slot_ids, "slot_ids", torch.int32, (C,)),
+        _dev(parents, "parents", torch.int32, (C, N)),
+        _dev(out, "out", torch.float32, (C, N, Hv, dv)),
+        _dev(replay_log, "replay_log", torch.float32, (C, N, Hv, sh.log_row)),
+        _dev(commit_win, "commit_win", torch.float32, (C, N, Ch, sh.d_conv - 1)),
+        status.data_ptr(),
+        _stream(x),
+    ]
+    cs = sh.c_struct()
+    _check(load_library().gdn_conv_tree_verify(ctypes.byref(cs), *args), "gdn_conv_tree_verify")
+    return out, replay_log, commit_win, status
 
 
 def replay_commit(sh: Shape, replay_log, commit_win, slot_ids, parents, accept_node, state_pool, conv_hist,

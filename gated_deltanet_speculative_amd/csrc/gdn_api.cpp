@@ -100,10 +100,65 @@ int gdn_tree_verify(const gdn_shape *sh, const float *qkv, const float *beta_log
                    {state_pool, (size_t)d.P * d.Hv * d.dk * d.dv * F}, {slot_ids, (size_t)d.C * I},
                    {parents, rows * I}}))
         return GDN_ERR_ALIAS;
-    return gdn::launch_tree_verify(d, qkv, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids,
-                                   parents, out, replay_log, status, stream) == hipSuccess
-               ? GDN_OK
-               : GDN_ERR_HIP;
+    gdn::VerifyArgs a{};
+    a.d = d;
+    a.qkv = qkv;
+    a.beta_logits = beta_logits;
+    a.alpha_logits = alpha_logits;
+    a.gate_stride = gate_stride;
+    a.dt_bias = dt_bias;
+    a.A = A;
+    a.state_pool = state_pool;
+    a.slot_ids = slot_ids;
+    a.parents = parents;
+    a.out = out;
+    a.replay_log = replay_log;
+    a.status = status;
+    return gdn::launch_tree_verify(a, stream) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+int gdn_conv_tree_verify(const gdn_shape *sh, const float *x, const float *conv_w, const float *conv_hist,
+                         const float *beta_logits, const float *alpha_logits, int64_t gate_stride,
+                         const float *dt_bias, const float *A, const float *state_pool, const int32_t *slot_ids,
+                         const int32_t *parents, float *out, float *replay_log, float *commit_win, int32_t *status,
+                         hipStream_t stream) {
+    gdn::Dims d;
+    if (int r = check_shape(sh, &d)) return r;
+    if (!x || !conv_w || !conv_hist || !beta_logits || !alpha_logits || !dt_bias || !A || !state_pool ||
+        !slot_ids || !parents || !out || !replay_log || !commit_win)
+        return GDN_ERR_NULL;
+    if (gate_stride < d.Hv) return GDN_ERR_SHAPE;
+    if (!aligned({x, conv_w, conv_hist, state_pool, out, commit_win}, 16) ||
+        !aligned({beta_logits, alpha_logits, dt_bias, A, slot_ids, parents, replay_log, status}, 4))
+        return GDN_ERR_ALIGN;
+    const size_t rows = (size_t)d.C * d.N;
+    const size_t gate_bytes = ((rows - 1) * (size_t)gate_stride + d.Hv) * F;
+    const size_t R = 1 + (size_t)d.dk + d.dv;
+    if (any_alias({{out, rows * d.Hv * d.dv * F}, {replay_log, rows * d.Hv * R * F},
+                   {commit_win, rows * d.Ch * 3 * F}, {status, I}},
+                  {{x, rows * d.Ch * F}, {conv_w, (size_t)d.Ch * 4 * F}, {conv_hist, (size_t)d.P * d.Ch * 3 * F},
+                   {beta_logits, gate_bytes}, {alpha_logits, gate_bytes}, {dt_bias, (size_t)d.Hv * F},
+                   {A, (size_t)d.Hv * F}, {state_pool, (size_t)d.P * d.Hv * d.dk * d.dv * F},
+                   {slot_ids, (size_t)d.C * I}, {parents, rows * I}}))
+        return GDN_ERR_ALIAS;
+    gdn::VerifyArgs a{};
+    a.d = d;
+    a.x = x;
+    a.conv_w = conv_w;
+    a.conv_hist = conv_hist;
+    a.commit_win = commit_win;
+    a.beta_logits = beta_logits;
+    a.alpha_logits = alpha_logits;
+    a.gate_stride = gate_stride;
+    a.dt_bias = dt_bias;
+    a.A = A;
+    a.state_pool = state_pool;
+    a.slot_ids = slot_ids;
+    a.parents = parents;
+    a.out = out;
+    a.replay_log = replay_log;
+    a.status = status;
+    return gdn::launch_tree_verify(a, stream) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 int gdn_replay_commit_layers(const gdn_shape *sh, int32_t n_layers, const float *const *replay_logs,

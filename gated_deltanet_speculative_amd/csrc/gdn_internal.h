@@ -37,10 +37,24 @@ hipError_t launch_conv_tree_step(const Dims &d, const float *x, const float *con
                                  const int32_t *slot_ids, const int32_t *parents, float *conv_out,
                                  float *commit_win, int32_t *status, hipStream_t stream);
 
-hipError_t launch_tree_verify(const Dims &d, const float *qkv, const float *beta_logits, const float *alpha_logits,
-                              int64_t gate_stride, const float *dt_bias, const float *A, const float *state_pool,
-                              const int32_t *slot_ids, const int32_t *parents, float *out, float *replay_log,
-                              int32_t *status, hipStream_t stream);
+// Arguments of the tree verify kernels, passed by value.  The separate route reads the
+// conv output `qkv`; the fused route reads x, conv_w and conv_hist, computes the conv
+// in-kernel and writes commit_win (the unused pointers are null).
+struct VerifyArgs {
+    Dims d;
+    const float *qkv;
+    const float *x, *conv_w, *conv_hist;
+    float *commit_win;
+    const float *beta_logits, *alpha_logits;
+    int64_t gate_stride;
+    const float *dt_bias, *A;
+    const float *state_pool;
+    const int32_t *slot_ids, *parents;
+    float *out, *replay_log;
+    int32_t *status;
+};
+
+hipError_t launch_tree_verify(const VerifyArgs &a, hipStream_t stream);
 
 // Per-layer buffers of a multi-layer commit, passed by value as a kernel argument.
 struct LayerPtrs {

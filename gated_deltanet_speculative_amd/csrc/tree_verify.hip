@@ -28,7 +28,19 @@
 // Mapping: one workgroup (4 waves) per (lane, value head, block of 32 value columns);
 // products run on v_mfma_f32_16x16x4_f32 from LDS.  N is padded to NP (16 or 32) with
 // zero rows.  Barriers wait only for LDS traffic, so the state block requested at the
-// start stays in flight through the whole tree phase.
+// start stays in flight through the whole tree phase.  Workgroup ids are ordered so that
+// the workgroups sharing one (lane, q/k head) are congruent modulo the number of such
+// groups: with round-robin dispatch over the 8 XCDs they land on one XCD and read the
+// shared q/k rows through its L2.
+//
+// Fused route (conv + verify, "perf(qwen35): fuse the DFlash2 concurrent verify Gated
+// DeltaNet route", Optimizations): the workgroup reads the raw projected tokens x of its
+// q/k slab and value block, stages them in LDS, and computes the tree conv + SiLU of its
+// channels in registers (sources of node i, oldest first: the tokens of i's nearest
+// ancestors, then the slot's history columns), writing the results straight into the
+// product operands; the conv output never goes to memory.  The commit windows are
+// written once: value channels by their owning workgroup, the q/k channels split evenly
+// over the workgroups that share them.
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -48,7 +60,7 @@ __device__ inline void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int DK, int DV, int NP>
+template <int DK, int DV, int NP, bool FUSED>
 struct VerifyLayout {
     static constexpr int JB = DV < 32 ? DV : 32;  // value columns per workgroup
     static constexpr int NB = DV / JB;            // column blocks per head
@@ -64,7 +76,13 @@ struct VerifyLayout {
     static constexpr int OFF_CK = OFF_G + 2 * NP * SG;  // Ck^T [NP][SG]
     static constexpr int OFF_MK = OFF_CK + NP * SG;     // -T diag(beta G / |k|) [NP][SG]
     static constexpr int X_FLOATS = (JB * SBT > 4 * NP * SG) ? JB * SBT : 4 * NP * SG;
-    static constexpr int LDS_FLOATS = OFF_X + X_FLOATS;
+    // fused route: raw token rows [NP][SX] (q|k slab, then the value block) staged over
+    // the Cq / late region, which is free until the coefficients are formed
+    static constexpr int SX = 2 * DK + JB;
+    static constexpr int OFF_STG = OFF_CQ;
+    static constexpr int STAGE = FUSED ? NP * SX : 0;
+    static constexpr int TAIL = NP * SG + X_FLOATS;
+    static constexpr int LDS_FLOATS = OFF_CQ + (TAIL > STAGE ? TAIL : STAGE);
 };
 
 // One 16x16 tile of A[m0.., 0:K] x B[0:K, n0..] with both operands k-contiguous:
@@ -110,16 +128,54 @@ __device__ inline float fast_softplus(float x) {
     return fmaxf(x, 0.f) + 0.6931471805599453f * __builtin_amdgcn_logf(1.0f + fast_exp(-fabsf(x)));
 }
 __device__ inline float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + fast_exp(-x)); }
+__device__ inline float fast_silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + fast_exp(-z)); }
 
-template <int DK, int DV, int NP>
-__global__ __launch_bounds__(kThreads) void tree_verify_kernel(
-    Dims d, const float *__restrict__ qkv, const float *__restrict__ beta_logits,
-    const float *__restrict__ alpha_logits, int64_t gate_stride, const float *__restrict__ dt_bias,
-    const float *__restrict__ A_decay, const float *__restrict__ state_pool, const int32_t *__restrict__ slot_ids,
-    const int32_t *__restrict__ parents, float *__restrict__ out, float *__restrict__ replay_log,
-    int32_t *__restrict__ status) {
-    using Ly = VerifyLayout<DK, DV, NP>;
-    constexpr int JB = Ly::JB, R = Ly::R, KA = Ly::KA, SA = Ly::SA, SBT = Ly::SBT, SG = Ly::SG;
+// Tree conv + SiLU of 4 channels at one node.  xi: the node's own tokens; X(n): tokens of
+// node n from the staged rows; hc[j]: history column j (2 = newest); w[e]: the 4 taps of
+// channel e (tap 0 = oldest).  n1..n3 are the node's parent, grandparent and
+// great-grandparent (-1 past the root).  Returns silu(conv) and the 3 newest sources
+// (t1, t2, t3 = the node itself), which form the node's commit window.
+__device__ inline v4f conv_node(v4f xi, const float *stg, int sx, int n1, int n2, int n3, const v4f hc[3],
+                                const v4f w[4], v4f &t1, v4f &t2) {
+    const v4f x1 = *reinterpret_cast<const v4f *>(stg + (n1 > 0 ? n1 : 0) * sx);
+    const v4f x2 = *reinterpret_cast<const v4f *>(stg + (n2 > 0 ? n2 : 0) * sx);
+    const v4f x3 = *reinterpret_cast<const v4f *>(stg + (n3 > 0 ? n3 : 0) * sx);
+    t2 = n1 >= 0 ? x1 : hc[2];
+    t1 = n1 >= 0 ? (n2 >= 0 ? x2 : hc[2]) : hc[1];
+    const v4f t0 = n1 >= 0 ? (n2 >= 0 ? (n3 >= 0 ? x3 : hc[2]) : hc[1]) : hc[0];
+    v4f y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float z = t0[e] * w[e][0];  // taps summed from the oldest column
+        z = fmaf(t1[e], w[e][1], z);
+        z = fmaf(t2[e], w[e][2], z);
+        z = fmaf(xi[e], w[e][3], z);
+        y[e] = fast_silu(z);
+    }
+    return y;
+}
+
+// window of 4 channels in the history layout [ch][3]: 12 consecutive floats
+__device__ inline void store_window(float *dst, v4f t1, v4f t2, v4f t3) {
+    v4f *w = reinterpret_cast<v4f *>(dst);
+    w[0] = v4f{t1.x, t2.x, t3.x, t1.y};
+    w[1] = v4f{t2.y, t3.y, t1.z, t2.z};
+    w[2] = v4f{t3.z, t1.w, t2.w, t3.w};
+}
+
+// history columns of 4 channels from their 12 consecutive floats
+__device__ inline void hist_columns(const float *src, v4f hc[3]) {
+    const v4f *p = reinterpret_cast<const v4f *>(src);
+    const v4f a = p[0], b = p[1], e = p[2];  // ch0: a.x a.y a.z | ch1: a.w b.x b.y | ch2: b.z b.w e.x | ch3: e.y e.z e.w
+    hc[0] = v4f{a.x, a.w, b.z, e.y};
+    hc[1] = v4f{a.y, b.x, b.w, e.z};
+    hc[2] = v4f{a.z, b.y, e.x, e.w};
+}
+
+template <int DK, int DV, int NP, bool FUSED>
+__device__ __forceinline__ void verify_body(const VerifyArgs &args) {
+    using Ly = VerifyLayout<DK, DV, NP, FUSED>;
+    constexpr int JB = Ly::JB, NB = Ly::NB, R = Ly::R, KA = Ly::KA, SA = Ly::SA, SBT = Ly::SBT, SG = Ly::SG;
     constexpr int Q4 = JB / 4;  // 4-float groups per block row
     extern __shared__ float lds[];
     float *Am = lds;                // A: rows 0..NP-1 delta rows, NP..2NP-1 output rows
@@ -132,50 +188,90 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(
     __shared__ float s_beta[NP], s_g[NP], s_L[NP], s_G[NP], s_rk[NP], s_rq[NP], s_gq[NP];
     __shared__ unsigned int s_anc[NP];
 
-    const int jb = blockIdx.x, h = blockIdx.y, c = blockIdx.z;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const Dims d = args.d;
+    const float *__restrict__ state_pool = args.state_pool;
+    const int32_t *__restrict__ slot_ids = args.slot_ids;
+    float *__restrict__ out = args.out;
+    float *__restrict__ replay_log = args.replay_log;
     const int N = d.N, Hv = d.Hv;
-    const int kh = h % d.Hk;
+    // workgroup -> (lane c, q/k head kh, share index ws); ws -> (value head h, column block jb)
+    const int n_groups = d.C * d.Hk;
+    const int grp = blockIdx.x % n_groups, ws = blockIdx.x / n_groups;
+    const int c = grp / d.Hk, kh = grp - c * d.Hk;
+    const int jb = ws % NB, h = kh + d.Hk * (ws / NB);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int j0 = jb * JB;
 
     // ---- loads, in the order they are consumed (global loads complete in order): tree
-    //      and gates, duplicate-slot check, raw q/k, the V block, then the state block.
-    //      Indices are clamped and out-of-range values selected to zero, so every load
-    //      is unconditional and all of them are in flight together.
+    //      and gates, duplicate-slot check, q/k (raw tokens when fused), the V block, then
+    //      the state block.  Indices are clamped and out-of-range values selected to zero,
+    //      so every load is unconditional and all of them are in flight together.
+    const int par = args.parents[(int64_t)c * N + (lane < N ? lane : 0)];  // lane i of every wave: parent of node i
     const int tn = tid < N ? tid : 0;
     const int64_t trow = (int64_t)c * N + tn;
-    const int par_raw = parents[trow];
-    const float braw = beta_logits[trow * gate_stride + h];
-    const float araw = alpha_logits[trow * gate_stride + h] + dt_bias[h];
-    const float Ah = A_decay[h];
+    const float braw = args.beta_logits[trow * args.gate_stride + h];
+    const float araw = args.alpha_logits[trow * args.gate_stride + h] + args.dt_bias[h];
+    const float Ah = args.A[h];
     const int so = slot_ids[tid < d.C ? tid : 0];  // this thread's share of the duplicate check
     const int s = slot_ids[c];
 
-    constexpr int QF4 = 2 * NP * (DK / 4), QPT = (QF4 + kThreads - 1) / kThreads;
-    v4f qreg[QPT];  // row r < NP: k of node r; row NP + i: q of node i
+    // separate route: conv output rows; fused route: raw token rows of the same channels
+    constexpr int G = DK / 2;  // 4-channel groups of one head's q|k slab (kThreads % G == 0)
+    constexpr int QI = (G * NP + kThreads - 1) / kThreads;
+    constexpr int QF4 = 2 * NP * (DK / 4), QPT = FUSED ? QI : (QF4 + kThreads - 1) / kThreads;
+    const int gq = tid % G;
+    const int chq = gq < DK / 4 ? kh * DK + 4 * gq : d.Hk * DK + kh * DK + 4 * (gq - DK / 4);
+    v4f qreg[QPT];  // separate: row r < NP k of node r, NP + i q of node i; fused: x of (node, gq)
 #pragma unroll
     for (int u = 0; u < QPT; ++u) {
-        const int f = min(tid + kThreads * u, QF4 - 1), r = f / (DK / 4), q = f - r * (DK / 4);
-        const int i = r < NP ? r : r - NP;
-        const float *src = qkv + ((int64_t)c * N + (i < N ? i : 0)) * d.Ch + (r < NP ? d.Hk * DK : 0) + kh * DK;
-        const v4f x = reinterpret_cast<const v4f *>(src)[q];
-        qreg[u] = i < N ? x : v4f{0.f, 0.f, 0.f, 0.f};
+        if constexpr (FUSED) {
+            const int i = min((tid + kThreads * u) / G, NP - 1);
+            const v4f x = reinterpret_cast<const v4f *>(args.x + ((int64_t)c * N + (i < N ? i : 0)) * d.Ch + chq)[0];
+            qreg[u] = i < N ? x : v4f{0.f, 0.f, 0.f, 0.f};
+        } else {
+            const int f = min(tid + kThreads * u, QF4 - 1), r = f / (DK / 4), q = f - r * (DK / 4);
+            const int i = r < NP ? r : r - NP;
+            const float *src =
+                args.qkv + ((int64_t)c * N + (i < N ? i : 0)) * d.Ch + (r < NP ? d.Hk * DK : 0) + kh * DK;
+            const v4f x = reinterpret_cast<const v4f *>(src)[q];
+            qreg[u] = i < N ? x : v4f{0.f, 0.f, 0.f, 0.f};
+        }
     }
+    // V block: this thread's 4-column group gv is fixed (kThreads % Q4 == 0); surplus
+    // items are clamped to the last row, so their duplicate writes carry the same value
     constexpr int VF4 = NP * Q4, VPT = (VF4 + kThreads - 1) / kThreads;
+    const int gv = tid % Q4;
+    const int chv = 2 * d.Hk * DK + h * DV + j0 + 4 * gv;
+    const float *vsrc = FUSED ? args.x : args.qkv;
     v4f vreg[VPT];
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-        const int f = min(tid + kThreads * u, VF4 - 1), i = f / Q4, q = f - i * Q4;
-        const v4f x = reinterpret_cast<const v4f *>(qkv + ((int64_t)c * N + (i < N ? i : 0)) * d.Ch + 2 * d.Hk * DK +
-                                                    h * DV + j0)[q];
+        const int i = min((tid + kThreads * u) / Q4, NP - 1);
+        const v4f x = reinterpret_cast<const v4f *>(vsrc + ((int64_t)c * N + (i < N ? i : 0)) * d.Ch + chv)[0];
         vreg[u] = i < N ? x : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    // fused: the taps of this thread's q/k and value channel groups
+    v4f wq[4], wv[4];
+    if constexpr (FUSED) {
+        const v4f *w4 = reinterpret_cast<const v4f *>(args.conv_w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            wq[e] = w4[chq + e];
+            wv[e] = w4[chv + e];
+        }
     }
     if (s == -1) return;  // padding lane
     const bool s_ok = s >= 0 && s < d.P;
+    const int sc = s_ok ? s : 0;
+    v4f hq[3], hv[3];  // fused: history columns of the two channel groups
+    if constexpr (FUSED) {
+        hist_columns(args.conv_hist + ((int64_t)sc * d.Ch + chq) * 3, hq);
+        hist_columns(args.conv_hist + ((int64_t)sc * d.Ch + chv) * 3, hv);
+    }
     constexpr int SF4 = DK * Q4, SPT = (SF4 + kThreads - 1) / kThreads;
     v4f sreg[SPT];
     {
-        const float *Sg = state_pool + ((int64_t)(s_ok ? s : 0) * Hv + h) * DK * DV + j0;
+        const float *Sg = state_pool + ((int64_t)sc * Hv + h) * DK * DV + j0;
 #pragma unroll
         for (int u = 0; u < SPT; ++u) {
             const int f = min(tid + kThreads * u, SF4 - 1), r = f / Q4, q = f - r * Q4;
@@ -188,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(
     if (tid < d.C && tid != c && so == s) bits |= GDN_STATUS_SLOT_DUP;
     for (int o = tid + kThreads; o < d.C; o += kThreads)  // lanes beyond the first 256
         if (o != c && slot_ids[o] == s) bits |= GDN_STATUS_SLOT_DUP;
-    if (tid < N && (par_raw < -1 || par_raw >= tid)) bits |= GDN_STATUS_PARENT;
+    if (tid < N && (par < -1 || par >= tid)) bits |= GDN_STATUS_PARENT;
     {
         int wb = 0;
 #pragma unroll
@@ -196,11 +292,25 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(
             if (__builtin_amdgcn_ballot_w64((bits >> b) & 1)) wb |= 1 << b;
         if (lane == 0) s_wbits[wave] = wb;
     }
-    // raw q/k rows into A (k rows 0..NP-1, q rows NP..2NP-1)
+    float *stg = lds + Ly::OFF_STG;  // fused: staged token rows [NP][SX]
+    if constexpr (FUSED) {
 #pragma unroll
-    for (int u = 0; u < QPT; ++u) {
-        const int f = min(tid + kThreads * u, QF4 - 1), r = f / (DK / 4), q = f - r * (DK / 4);
-        *reinterpret_cast<v4f *>(Am + r * SA + 4 * q) = qreg[u];
+        for (int u = 0; u < QPT; ++u) {
+            const int f = tid + kThreads * u;
+            if (f < G * NP) *reinterpret_cast<v4f *>(stg + (f / G) * Ly::SX + 4 * gq) = qreg[u];
+        }
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int f = tid + kThreads * u;
+            if (f < VF4) *reinterpret_cast<v4f *>(stg + (f / Q4) * Ly::SX + 2 * DK + 4 * gv) = vreg[u];
+        }
+    } else {
+        // conv rows into A (k rows 0..NP-1, q rows NP..2NP-1)
+#pragma unroll
+        for (int u = 0; u < QPT; ++u) {
+            const int f = min(tid + kThreads * u, QF4 - 1), r = f / (DK / 4), q = f - r * (DK / 4);
+            *reinterpret_cast<v4f *>(Am + r * SA + 4 * q) = qreg[u];
+        }
     }
     lds_barrier();
     {
@@ -208,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) all |= s_wbits[w];
         if (all) {
-            if (jb == 0 && h == 0 && tid == 0 && status) atomicOr(status, all);
+            if (ws == 0 && tid == 0 && args.status) atomicOr(args.status, all);
             return;
         }
     }
@@ -217,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(
     //      (log2(NP) rounds of lane shuffles, independent of the tree depth)
     if (wave == 0) {
         const bool real = lane < N;
-        int jump = real ? par_raw : -1;
+        int jump = real ? par : -1;
         float L = 0.f;
         if (real) L = fast_softplus(araw) * Ah;  // log g = softplus(a + dt_bias) * A
         if (lane < NP) s_g[lane] = fast_exp(L);
@@ -241,6 +351,43 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(
             s_beta[lane] = real ? fast_sigmoid(braw) : 0.f;
         }
     }
+    // ---- fused: tree conv + SiLU of the block's channels from the staged rows, into the
+    //      q/k rows of A and the V registers; commit windows of the owned channels
+    if constexpr (FUSED) {
+        // lane i of every wave: parent, grandparent and great-grandparent of node i
+        const int a1 = lane < N ? par : -1;
+        const int a2s = __shfl(a1, a1 >= 0 ? a1 : 0);
+        const int a2 = a1 >= 0 ? a2s : -1;
+        const int a3s = __shfl(a2, a1 >= 0 ? a1 : 0);
+        const int a3 = a1 >= 0 ? a3s : -1;
+        const int n_share = NB * (Hv / d.Hk);
+        const bool own_q = (gq * n_share) / G == ws;  // the q/k windows of group gq are written here
+        float *win = args.commit_win + (int64_t)c * N * d.Ch * 3;
+        const v4f zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < QPT; ++u) {
+            const int f = tid + kThreads * u, i = min(f / G, NP - 1);
+            const int n1 = __shfl(a1, i), n2 = __shfl(a2, i), n3 = __shfl(a3, i);
+            v4f t1, t2;
+            const v4f y = conv_node(qreg[u], stg + 4 * gq, Ly::SX, n1, n2, n3, hq, wq, t1, t2);
+            if (f < G * NP) {
+                const int row = gq < DK / 4 ? NP + i : i, col = 4 * (gq < DK / 4 ? gq : gq - DK / 4);
+                *reinterpret_cast<v4f *>(Am + row * SA + col) = i < N ? y : zero;
+                if (own_q && i < N) store_window(win + ((int64_t)i * d.Ch + chq) * 3, t1, t2, qreg[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int f = tid + kThreads * u, i = min(f / Q4, NP - 1);
+            const int n1 = __shfl(a1, i), n2 = __shfl(a2, i), n3 = __shfl(a3, i);
+            v4f t1, t2;
+            const v4f y = conv_node(vreg[u], stg + 2 * DK + 4 * gv, Ly::SX, n1, n2, n3, hv, wv, t1, t2);
+            if (f < VF4 && i < N) store_window(win + ((int64_t)i * d.Ch + chv) * 3, t1, t2, vreg[u]);
+            vreg[u] = i < N ? y : zero;
+        }
+        lds_barrier();
+    }
+
     // ---- Gram of the raw vectors: Gm[r][a] = (row r of A) . k_a; the diagonal tiles of
     //      Q Q^T give |q_i|^2
     {
@@ -384,9 +531,9 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(
     }
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-        const int f = min(tid + kThreads * u, VF4 - 1), i = f / Q4, q = f - i * Q4;
+        const int i = min((tid + kThreads * u) / Q4, NP - 1);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) BmT[(4 * q + e) * SBT + DK + i] = vreg[u][e];
+        for (int e = 0; e < 4; ++e) BmT[(4 * gv + e) * SBT + DK + i] = vreg[u][e];
     }
     lds_barrier();
 
@@ -412,38 +559,44 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(
 }
 
 template <int DK, int DV, int NP>
-hipError_t launch(const Dims &d, const float *qkv, const float *bl, const float *al, int64_t gs, const float *dt,
-                  const float *A, const float *pool, const int32_t *slots, const int32_t *parents, float *out,
-                  float *log, int32_t *status, hipStream_t stream) {
-    using Ly = VerifyLayout<DK, DV, NP>;
+__global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs args) {
+    verify_body<DK, DV, NP, false>(args);
+}
+
+template <int DK, int DV, int NP>
+__global__ __launch_bounds__(kThreads) void conv_tree_verify_kernel(const VerifyArgs args) {
+    verify_body<DK, DV, NP, true>(args);
+}
+
+template <int DK, int DV, int NP, bool FUSED>
+hipError_t launch(const VerifyArgs &a, hipStream_t stream) {
+    using Ly = VerifyLayout<DK, DV, NP, FUSED>;
     const size_t lds = sizeof(float) * Ly::LDS_FLOATS;
     // the LDS limit is a property of the kernel, set once (also keeps stream capture clean)
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&tree_verify_kernel<DK, DV, NP>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const void *kernel = FUSED ? reinterpret_cast<const void *>(&conv_tree_verify_kernel<DK, DV, NP>)
+                               : reinterpret_cast<const void *>(&tree_verify_kernel<DK, DV, NP>);
+    static const hipError_t attr = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((tree_verify_kernel<DK, DV, NP>), dim3(Ly::NB, d.Hv, d.C), dim3(kThreads), lds, stream, d, qkv,
-                       bl, al, gs, dt, A, pool, slots, parents, out, log, status);
+    const int grid = Ly::NB * a.d.Hv * a.d.C;
+    if constexpr (FUSED)
+        hipLaunchKernelGGL((conv_tree_verify_kernel<DK, DV, NP>), dim3(grid), dim3(kThreads), lds, stream, a);
+    else
+        hipLaunchKernelGGL((tree_verify_kernel<DK, DV, NP>), dim3(grid), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
 }
 
 template <int DK, int DV>
-hipError_t launch_np(const Dims &d, const float *qkv, const float *bl, const float *al, int64_t gs, const float *dt,
-                     const float *A, const float *pool, const int32_t *slots, const int32_t *parents, float *out,
-                     float *log, int32_t *status, hipStream_t stream) {
-    if (d.N <= 16) return launch<DK, DV, 16>(d, qkv, bl, al, gs, dt, A, pool, slots, parents, out, log, status, stream);
-    return launch<DK, DV, 32>(d, qkv, bl, al, gs, dt, A, pool, slots, parents, out, log, status, stream);
+hipError_t launch_np(const VerifyArgs &a, hipStream_t stream) {
+    const bool fused = a.x != nullptr;
+    if (a.d.N <= 16) return fused ? launch<DK, DV, 16, true>(a, stream) : launch<DK, DV, 16, false>(a, stream);
+    return fused ? launch<DK, DV, 32, true>(a, stream) : launch<DK, DV, 32, false>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_tree_verify(const Dims &d, const float *qkv, const float *beta_logits, const float *alpha_logits,
-                              int64_t gate_stride, const float *dt_bias, const float *A, const float *state_pool,
-                              const int32_t *slot_ids, const int32_t *parents, float *out, float *replay_log,
-                              int32_t *status, hipStream_t stream) {
-#define GDN_VERIFY_CASE(K, V)                                                                                      \
-    if (d.dk == K && d.dv == V)                                                                                    \
-        return launch_np<K, V>(d, qkv, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids, \
-                               parents, out, replay_log, status, stream);
+hipError_t launch_tree_verify(const VerifyArgs &a, hipStream_t stream) {
+#define GDN_VERIFY_CASE(K, V) \
+    if (a.d.dk == K && a.d.dv == V) return launch_np<K, V>(a, stream);
 #define GDN_VERIFY_ROW(K) GDN_VERIFY_CASE(K, 16) GDN_VERIFY_CASE(K, 32) GDN_VERIFY_CASE(K, 64) GDN_VERIFY_CASE(K, 128)
     GDN_VERIFY_ROW(16) GDN_VERIFY_ROW(32) GDN_VERIFY_ROW(64) GDN_VERIFY_ROW(128)
 #undef GDN_VERIFY_ROW

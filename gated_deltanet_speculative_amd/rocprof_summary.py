@@ -24,7 +24,8 @@ import statistics
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = {
+KERNEL_SOURCES = {  # (matched in this order: conv_tree_verify before tree_verify)
+    "conv_tree_verify": "csrc/tree_verify.hip",
     "conv_tree_step": "csrc/conv_tree_step.hip",
     "tree_verify": "csrc/tree_verify.hip",
     "replay_commit": "csrc/replay_commit.hip",

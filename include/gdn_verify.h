@@ -12,6 +12,10 @@
  *                       advances the live recurrent state and conv history of the
  *                       accepting slots (an all-or-nothing transaction).
  *
+ * Two further calls cover the same route with fewer launches:
+ *   gdn_conv_tree_verify      the first two calls fused (conv output kept on chip);
+ *   gdn_replay_commit_layers  the commit of every layer of a round in one launch.
+ *
  * Sources (page title, then section):
  *   "perf(qwen35): fuse the DFlash2 concurrent verify Gated DeltaNet route",
  *       Summary and Optimizations (the three operations and their inputs/outputs),
@@ -175,6 +179,29 @@ int gdn_tree_verify(const gdn_shape *sh, const float *qkv, const float *beta_log
 int gdn_replay_commit(const gdn_shape *sh, const float *replay_log, const float *commit_win,
                       const int32_t *slot_ids, const int32_t *parents, const int32_t *accept_node,
                       float *state_pool, float *conv_hist, int32_t *status, hipStream_t stream);
+
+/*
+ * Fused tree conv + verify: gdn_conv_tree_step followed by gdn_tree_verify on its
+ * output, in one launch, without materialising the conv output ("perf(qwen35): fuse
+ * the DFlash2 concurrent verify Gated DeltaNet route", Optimizations: conv, SiLU,
+ * window emission and the read-only recurrence in one route).  out, replay_log and
+ * commit_win are the values the two separate calls produce (the conv output that feeds
+ * the recurrence carries the recurrence tolerance; commit windows are exact copies).
+ *
+ *   x, conv_w, conv_hist          as in gdn_conv_tree_step (conv_hist READ-ONLY)
+ *   beta_logits .. state_pool     as in gdn_tree_verify (state_pool READ-ONLY)
+ *   slot_ids, parents             as above
+ *   out, replay_log               as in gdn_tree_verify
+ *   commit_win                    as in gdn_conv_tree_step
+ *   status                        may be NULL
+ * Alignment: x, conv_w, conv_hist, state_pool, out, commit_win 16 bytes; the rest 4.
+ * Every output must be disjoint from every input and from the other outputs.
+ */
+int gdn_conv_tree_verify(const gdn_shape *sh, const float *x, const float *conv_w, const float *conv_hist,
+                         const float *beta_logits, const float *alpha_logits, int64_t gate_stride,
+                         const float *dt_bias, const float *A, const float *state_pool, const int32_t *slot_ids,
+                         const int32_t *parents, float *out, float *replay_log, float *commit_win, int32_t *status,
+                         hipStream_t stream);
 
 /*
  * Multi-layer replay-log commit: the commit above for every GDN layer of the round in

@@ -172,3 +172,38 @@ def test_commit_layers_rejections():
     assert _commit_layers(sh, 3, per, shared, per[3][1]) == _lib.GDN_ERR_ALIAS  # status in a history pool
     per, shared = _layer_ptrs(3)
     assert _commit_layers(_shape(d_conv=5), 3, per, shared, st) == _lib.GDN_ERR_UNSUPPORTED
+
+
+def _fused(sh, ptrs, gate_stride, status=None):
+    """ptrs: x, conv_w, conv_hist, beta, alpha, dt_bias, A, state_pool, slot_ids, parents, out, replay_log, commit_win"""
+    lib = gdn.load_library()
+    cs = sh.c_struct()
+    p = list(ptrs)
+    return lib.gdn_conv_tree_verify(ctypes.byref(cs), *p[:5], gate_stride, *p[5:], status, None)
+
+
+def test_fused_rejections():
+    sh = _shape()
+    p = _ptrs(13)
+    p[12] = None  # commit windows missing
+    assert _fused(sh, p, 8) == _lib.GDN_ERR_NULL
+    assert _fused(sh, _ptrs(13), 3) == _lib.GDN_ERR_SHAPE  # gate stride below H_v
+    assert _fused(_shape(d_conv=3), _ptrs(13), 8) == _lib.GDN_ERR_UNSUPPORTED
+    assert _fused(_shape(n_nodes=33), _ptrs(13), 8) == _lib.GDN_ERR_UNSUPPORTED
+    p = _ptrs(13)
+    p[2] += 4  # conv history not 16-byte aligned
+    assert _fused(sh, p, 8) == _lib.GDN_ERR_ALIGN
+    p = _ptrs(13)
+    p[12] += 8  # commit windows not 16-byte aligned
+    assert _fused(sh, p, 8) == _lib.GDN_ERR_ALIGN
+    p = _ptrs(13)
+    p[12] = p[0] + 64  # commit windows inside x
+    assert _fused(sh, p, 8) == _lib.GDN_ERR_ALIAS
+    p = _ptrs(13)
+    p[10] = p[12] + 16  # out inside the commit windows
+    assert _fused(sh, p, 8) == _lib.GDN_ERR_ALIAS
+    p = _ptrs(13)
+    p[11] = p[7] + 16  # replay log inside the state pool
+    assert _fused(sh, p, 8) == _lib.GDN_ERR_ALIAS
+    p = _ptrs(13)
+    assert _fused(sh, p, 8, status=p[2] + 4) == _lib.GDN_ERR_ALIAS  # status inside the history pool

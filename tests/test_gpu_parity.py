@@ -21,10 +21,14 @@ def _shape(C, N, P, Hk, Hv, dk, dv):
     return gdn.Shape(C, N, P, Hk, Hv, dk, dv)
 
 
-def _run_case(sh, case, accept=None, lanes=None):
-    """Verify (and optionally commit) on the GPU and in the oracle; returns both sides."""
+ROUTES = ["split", "fused"]
+
+
+def _run_case(sh, case, accept=None, lanes=None, route="split"):
+    """Verify on the GPU (separate conv + verify calls, or the fused call) and in the oracle;
+    returns both sides."""
     g = GpuRound(sh, case["x"], case["ba"], case["conv_w"], case["conv_hist"], case["state"], case["dt_bias"],
-                 case["A"], case["slot_ids"], case["parents"]).verify()
+                 case["A"], case["slot_ids"], case["parents"], fused=route == "fused").verify()
     torch.cuda.synchronize()
     sel = slice(None) if lanes is None else np.asarray(lanes)
     ref = oracle_round(sh, case["x"][sel], case["ba"][sel], case["conv_w"], case["conv_hist"], case["state"],
@@ -32,6 +36,7 @@ def _run_case(sh, case, accept=None, lanes=None):
     return g, ref, sel
 
 
+@pytest.mark.parametrize("route", ROUTES)
 @pytest.mark.parametrize("name,layer,lanes", [
     ("tiny-chain", 0, None),
     ("grouped-chain-n8", 0, None),
@@ -40,12 +45,12 @@ def _run_case(sh, case, accept=None, lanes=None):
     ("chains-c5-n8-l48", 47, None),
     ("stress-c64-n32-l48", 0, [0, 17, 40, 63]),
 ])
-def test_workload_parity(name, layer, lanes):
+def test_workload_parity(name, layer, lanes, route):
     wl = WORKLOADS[name]
     sh = gdn.Shape(**wl.shape_dict())
-    log(f"[parity] {name} layer={layer} lanes={lanes} shape={tuple(sh)}")
+    log(f"[parity] {name} layer={layer} lanes={lanes} route={route} shape={tuple(sh)}")
     case = dict(layer_params(wl, layer), **round_structure(wl, 0), **round_inputs(wl, layer, 0))
-    g, ref, sel = _run_case(sh, case, lanes=lanes)
+    g, ref, sel = _run_case(sh, case, lanes=lanes, route=route)
     assert int(g.status.item()) == 0 and ref["status"] == 0
     assert g.guards_intact()
     errs = compare_verify(g, ref, lanes=sel, ref_is_subset=True)
@@ -86,12 +91,13 @@ SWEEP = [
 ]
 
 
+@pytest.mark.parametrize("route", ROUTES)
 @pytest.mark.parametrize("C,N,P,Hk,Hv,dk,dv,tree", SWEEP)
-def test_shape_sweep(C, N, P, Hk, Hv, dk, dv, tree):
+def test_shape_sweep(C, N, P, Hk, Hv, dk, dv, tree, route):
     sh = _shape(C, N, P, Hk, Hv, dk, dv)
-    log(f"[sweep] shape={tuple(sh)} tree={tree}")
+    log(f"[sweep] shape={tuple(sh)} tree={tree} route={route}")
     case = synth_case(C, N, P, Hk, Hv, dk, dv, seed=7, tree=tree)
-    g, ref, _ = _run_case(sh, case)
+    g, ref, _ = _run_case(sh, case, route=route)
     assert int(g.status.item()) == 0 and g.guards_intact()
     compare_verify(g, ref)
     rng = np.random.default_rng(C * 100 + N)
@@ -105,24 +111,26 @@ def test_shape_sweep(C, N, P, Hk, Hv, dk, dv, tree):
     assert np.array_equal(g.conv_hist.cpu().numpy(), hist.astype(np.float32))
 
 
-def test_many_lanes_small_heads():
+@pytest.mark.parametrize("route", ROUTES)
+def test_many_lanes_small_heads(route):
     C, N, P = 1024, 3, 1100
     sh = _shape(C, N, P, 1, 1, 16, 16)
-    log(f"[max-lanes] shape={tuple(sh)}")
+    log(f"[max-lanes] shape={tuple(sh)} route={route}")
     case = synth_case(C, N, P, 1, 1, 16, 16, seed=3)
     lanes = [0, 511, 1023]
-    g, ref, sel = _run_case(sh, case, lanes=lanes)
+    g, ref, sel = _run_case(sh, case, lanes=lanes, route=route)
     assert int(g.status.item()) == 0 and g.guards_intact()
     compare_verify(g, ref, lanes=sel, ref_is_subset=True)
 
 
-def test_padding_and_invalid_lanes_write_nothing():
+@pytest.mark.parametrize("route", ROUTES)
+def test_padding_and_invalid_lanes_write_nothing(route):
     C, N, P, Hk, Hv, d = 6, 5, 8, 1, 2, 32
     sh = _shape(C, N, P, Hk, Hv, d, d)
-    log("[lanes] padding / invalid parent / duplicate slot / slot out of range")
+    log(f"[lanes] padding / invalid parent / duplicate slot / slot out of range, route={route}")
     case = synth_case(C, N, P, Hk, Hv, d, d, seed=11, slots=[2, -1, 3, 5, 5, 8])
     case["parents"][2, 3] = 3  # not before its child
-    g, ref, _ = _run_case(sh, case)
+    g, ref, _ = _run_case(sh, case, route=route)
     want = gdn.STATUS_PARENT | gdn.STATUS_SLOT_DUP | gdn.STATUS_SLOT_RANGE
     assert int(g.status.item()) == want == ref["status"]
     assert g.guards_intact()
@@ -339,3 +347,26 @@ def test_commit_layers_all_or_nothing(bad):
     assert int(status.item()) & want
     for g, (s0, h0) in zip(rounds, before):
         assert torch.equal(g.state, s0) and torch.equal(g.conv_hist, h0)
+
+
+def test_fused_matches_split_route():
+    """The fused call and the two separate calls on the same inputs: commit windows
+    bit-identical, out and replay log within the recurrence bar of each other, and the
+    commits that follow give the same pools within that bar."""
+    wl = WORKLOADS["tree-c4-n16"]
+    sh = gdn.Shape(**wl.shape_dict())
+    log("[fused-vs-split] tree-c4-n16")
+    case = dict(layer_params(wl, 0), **round_structure(wl, 0), **round_inputs(wl, 0, 0))
+    args = (sh, case["x"], case["ba"], case["conv_w"], case["conv_hist"], case["state"], case["dt_bias"], case["A"],
+            case["slot_ids"], case["parents"])
+    a, b = GpuRound(*args).verify(), GpuRound(*args, fused=True).verify()
+    torch.cuda.synchronize()
+    assert int(a.status.item()) == 0 and int(b.status.item()) == 0
+    assert torch.equal(a.commit_win.t, b.commit_win.t)
+    assert err_metric(b.out.np(), a.out.np()) <= REC_TOL
+    assert err_metric(b.replay_log.np(), a.replay_log.np()) <= REC_TOL
+    a.commit(case["accept_node"])
+    b.commit(case["accept_node"])
+    torch.cuda.synchronize()
+    assert err_metric(b.state.cpu().numpy(), a.state.cpu().numpy()) <= REC_TOL
+    assert torch.equal(a.conv_hist, b.conv_hist)
