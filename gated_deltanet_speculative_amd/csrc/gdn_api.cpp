@@ -48,7 +48,8 @@ int check_shape(const gdn_shape *sh, gdn::Dims *d) {
         sh->n_seqs > GDN_MAX_SEQS)
         return GDN_ERR_UNSUPPORTED;
     const int64_t ch = 2ll * sh->n_k_heads * sh->d_k + (int64_t)sh->n_v_heads * sh->d_v;
-    if (ch > (1 << 24) || (int64_t)sh->n_slots * sh->n_v_heads > (1 << 24)) return GDN_ERR_UNSUPPORTED;
+    if (ch > (1 << 24) || (int64_t)sh->n_slots * sh->n_v_heads > (1 << 24) || (int64_t)sh->n_nodes * ch * 12 > (1 << 30))
+        return GDN_ERR_UNSUPPORTED;
     *d = gdn::Dims{sh->n_seqs, sh->n_nodes, sh->n_slots, sh->n_k_heads, sh->n_v_heads, sh->d_k, sh->d_v, (int)ch};
     return GDN_OK;
 }

@@ -9,29 +9,36 @@
 //
 // Formulation.  Unrolling the recurrence along a node's root path, with G_i the product
 // of the decays on path(i), gives S_i = G_i S0 + sum_{a on path(i)} (G_i/G_a) k^_a d_a^T.
-// For value column j this yields a triangular system over the tree
-//   d_i = beta_i (v_i - G_i k^_i.S0 - sum_{a strict ancestor} (G_i/G_a)(k^_a.k^_i) d_a)
-//   o_i = (G_i q^_i.S0 + sum_{a on path(i)} (G_i/G_a)(k^_a.q^_i) d_a) / sqrt(d_k).
-// With Ck[a][i] = (G_i/G_a) k^_a.k^_i on strict ancestors, Cq[a][i] = (G_i/G_a) k^_a.q^_i
-// on the path, T = (I + diag(beta) Ck^T)^-1, M1 = T diag(beta):
-//   d = M1 V - K' S0,                 K' = T diag(beta G) K^
-//   o = (Q' S0 + W V) / sqrt(d_k),    Q' = diag(G) Q^ - Cq^T K',  W = Cq^T M1.
-// Everything but the slot's state S0 is known before S0 arrives, so a workgroup first
-// builds the (2N) x (d_k + N) matrix A = [[-K', M1], [Q'/sqrt(d_k), W/sqrt(d_k)]] from
-// q, k, gates and the tree while its S0 block is in flight, then one MFMA product
-// A x [S0; V] yields the delta rows (replay log) and output rows directly from the
-// accumulators.  Per-node states are never formed and S0 is read once.  q and k are
-// never normalised explicitly: their norms come from the diagonal of the Gram product
-// and fold into the coefficients.  Decay ratios are exp(L_i - L_a) of cumulative
-// log-decays, which cannot overflow.
+// For the raw (un-normalised) q and k rows, with rk_i = 1/|k_i|, rq_i = 1/|q_i| and the
+// products KS = K S0, QS = Q S0 of the raw rows with the slot's state:
+//   (I + Lm) D = rhs,  rhs_i = beta_i (v_i - G_i rk_i KS_i),
+//   Lm[i][a] = beta_i (G_i/G_a) rk_i rk_a (k_i . k_a)   for a a strict ancestor of i,
+//   O_i = G_i rq_i QS_i / sqrt(d_k) + sum_{a on path(i)} Cq[i][a] D_a,
+//   Cq[i][a] = (G_i/G_a) rq_i rk_a (q_i . k_a) / sqrt(d_k),
+// where D holds the delta rows (replay log) and O the output rows.  The tree algebra
+// (norms, Gram products, Lm, Cq and T = (I + Lm)^-1, all N x N) needs only q, k, the
+// gates and the tree, so it runs while the state block is still arriving; the state
+// enters through one dense product [K; Q] x S0, after which D = T rhs and O are two
+// small products on the accumulators.  Per-node states are never formed and S0 is read
+// once.  Decay ratios are exp(L_i - L_a) of cumulative log-decays, which cannot
+// overflow.
 //
-// Mapping: one workgroup (4 waves) per (lane, value head, block of 32 value columns);
-// products run on v_mfma_f32_16x16x4_f32 from LDS.  N is padded to NP (16 or 32) with
-// zero rows.  Barriers wait only for LDS traffic, so the state block requested at the
-// start stays in flight through the whole tree phase.  Workgroup ids are ordered so that
-// the workgroups sharing one (lane, q/k head) are congruent modulo the number of such
-// groups: with round-robin dispatch over the 8 XCDs they land on one XCD and read the
-// shared q/k rows through its L2.
+// Mapping: one workgroup (4 waves) per (lane, value head, block of 32 value columns).
+// Products run on v_mfma_f32_16x16x4_f32.  Within a 16-wide chunk of a contraction,
+// lane group g = lane/16 supplies index 4g + s in MFMA step s (a permutation shared by
+// both operands), so a tile's accumulators (lane holds rows 4g..4g+3 of column lane%16)
+// are directly the right operand of the next product, and the state block is loaded
+// from memory straight into that operand layout: no LDS copy, no transpose.  The
+// contraction over d_k is split by 16-row chunks across the waves (chunk q on wave
+// q mod 4) and the partial tiles are summed through LDS.  N is padded to NP (16 or 32)
+// with zero rows.  Barriers wait only for LDS traffic, so global loads stay in flight
+// across them.  Workgroup ids are ordered so that the workgroups sharing one (lane, q/k
+// head) are congruent modulo the number of such groups: with round-robin dispatch over
+// the 8 XCDs they land on one XCD and read the shared q/k rows through its L2.
+//
+// Load order.  Every load that does not depend on the slot (tree, gates, token rows,
+// taps) is issued before the slot id is consumed; the slot-mapped history and state are
+// requested under a uniform branch right after, so their latency overlaps the token rows.
 //
 // Fused route (conv + verify, "perf(qwen35): fuse the DFlash2 concurrent verify Gated
 // DeltaNet route", Optimizations): the workgroup reads the raw projected tokens x of its
@@ -60,63 +67,62 @@ __device__ inline void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Raw buffer resources: word 3 of the descriptor for the gfx9 family (32-bit data,
+// unswizzled); a load whose byte offset lies outside [0, num_records) returns zero and
+// makes no memory access.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kOutOfRange = 0x40000000;  // past every buffer range used here (at most 1 GiB)
+
+__device__ inline float load1(__amdgpu_buffer_rsrc_t r, int byte_offset) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_offset, 0, 0));
+}
+
+__device__ inline v4f load4(__amdgpu_buffer_rsrc_t r, int byte_offset) {
+    return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
+}
+
 template <int DK, int DV, int NP, bool FUSED>
 struct VerifyLayout {
     static constexpr int JB = DV < 32 ? DV : 32;  // value columns per workgroup
     static constexpr int NB = DV / JB;            // column blocks per head
+    static constexpr int CT = JB / 16;            // 16-column tiles of the block
+    static constexpr int NT = NP / 16;            // 16-row tiles of K (and of Q)
+    static constexpr int RT = 2 * NT;             // row tiles of [K; Q]
+    static constexpr int KC = DK / 16;            // 16-wide chunks of the d_k contraction
+    static constexpr int LC = (KC + kWaves - 1) / kWaves;  // chunks per wave
     static constexpr int R = 1 + DK + DV;         // replay-log row
-    static constexpr int KA = DK + NP;            // contraction length of the main product
+    static constexpr int G = DK / 2;              // 4-channel groups of one node's q|k slab
+    static constexpr int Q4 = JB / 4;             // 4-channel groups of one node's value block
+    static constexpr int NPART = DK / 4 > 16 ? 2 : 1;  // 16-lane partial sums per |row|^2
     // row strides (floats) are 4 mod 8 so 16 rows read with ds_read_b128 hit distinct banks
-    static constexpr int SA = (KA + 7) / 8 * 8 + 4;  // A: [2NP][SA]
-    static constexpr int SBT = SA;                   // [S0; V] transposed: [JB][SBT]
-    static constexpr int SG = NP + 4;                // small matrices
-    static constexpr int OFF_CQ = 2 * NP * SA;       // Cq^T [NP][SG] (own region)
-    static constexpr int OFF_X = OFF_CQ + NP * SG;   // late: [S0; V]^T; early aliases:
-    static constexpr int OFF_G = OFF_X;              //   Gram [2NP][SG]
-    static constexpr int OFF_CK = OFF_G + 2 * NP * SG;  // Ck^T [NP][SG]
-    static constexpr int OFF_MK = OFF_CK + NP * SG;     // -T diag(beta G / |k|) [NP][SG]
-    static constexpr int X_FLOATS = (JB * SBT > 4 * NP * SG) ? JB * SBT : 4 * NP * SG;
-    // fused route: raw token rows [NP][SX] (q|k slab, then the value block) staged over
-    // the Cq / late region, which is free until the coefficients are formed
-    static constexpr int SX = 2 * DK + JB;
-    static constexpr int OFF_STG = OFF_CQ;
-    static constexpr int STAGE = FUSED ? NP * SX : 0;
-    static constexpr int TAIL = NP * SG + X_FLOATS;
-    static constexpr int LDS_FLOATS = OFF_CQ + (TAIL > STAGE ? TAIL : STAGE);
+    static constexpr int SX = DK + 4;   // [K; Q] raw rows [2NP][SX]
+    static constexpr int SV = JB + 4;   // value rows [NP][SV]
+    static constexpr int SG = NP + 4;   // N x N matrices
+    static constexpr int SXS = 2 * DK + JB;  // fused: staged rows [NP + 3][SXS] of the block's channels
+    static constexpr int OFF_XQK = 0;
+    static constexpr int OFF_V = OFF_XQK + 2 * NP * SX;
+    static constexpr int OFF_LM = (OFF_V + NP * SV + 3) / 4 * 4;
+    static constexpr int OFF_CQ = OFF_LM + NP * SG;
+    static constexpr int OFF_T = OFF_CQ + NP * SG;
+    static constexpr int NG = G + Q4;             // channel groups of the block (q/k slab, then values)
+    static constexpr int OFF_TAP = OFF_T + NP * SG;                   // fused: taps [NG][4] of v4f
+    static constexpr int OFF_SCR = OFF_TAP + (FUSED ? NG * 16 : 0);
+    // scratch, reused phase by phase: staged tokens (until the conv), Gram partials (until
+    // the coefficients), partial state products (until the epilogue)
+    static constexpr int GRAM_TILES = RT * NT;
+    static constexpr int PROD_TILES = RT * CT;
+    static constexpr int STAGE = FUSED ? (NP + 3) * SXS : 0;  // node rows, then history columns 0..2
+    static constexpr int GPART = kWaves * GRAM_TILES * 256;
+    static constexpr int PPART = kWaves * PROD_TILES * 256;
+    static constexpr int SCR = STAGE > GPART ? (STAGE > PPART ? STAGE : PPART) : (GPART > PPART ? GPART : PPART);
+    static constexpr int LDS_FLOATS = OFF_SCR + SCR;
 };
 
-// One 16x16 tile of A[m0.., 0:K] x B[0:K, n0..] with both operands k-contiguous:
-// A(m, k) = A[m*AM + k], B(k, n) = B[n*BN + k].  Each 16-wide k chunk is read with one
-// ds_read_b128 per operand; lane group g = l/16 supplies k = k0 + 4g + s in MFMA step s,
-// a permutation of the contraction index shared by both operands.  Lane l receives
-// rows 4*(l/16) + v (v = 0..3) of column l % 16.
-template <int K, int AM, int BN>
-__device__ inline v4f mma_kc(const float *A, const float *B) {
-    const int l = threadIdx.x & 63;
-    const float *a = A + (l & 15) * AM + 4 * (l >> 4);
-    const float *b = B + (l & 15) * BN + 4 * (l >> 4);
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 16) {
-        const v4f av = *reinterpret_cast<const v4f *>(a + k0);
-        const v4f bv = *reinterpret_cast<const v4f *>(b + k0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[0], bv[0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[1], bv[1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[2], bv[2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[3], bv[3], acc, 0, 0, 0);
-    }
-    return acc;
-}
-
-// Same tile with A k-contiguous and B row-major in k: B(k, n) = B[k*BK + n].
-template <int K, int AM, int BK>
-__device__ inline v4f mma_kr(const float *A, const float *B) {
-    const int l = threadIdx.x & 63;
-    const float *a = A + (l & 15) * AM + (l >> 4);
-    const float *b = B + (l >> 4) * BK + (l & 15);
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[k0], b[k0 * BK], acc, 0, 0, 0);
+__device__ inline v4f mfma4(v4f a, v4f b, v4f acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
     return acc;
 }
 
@@ -130,26 +136,35 @@ __device__ inline float fast_softplus(float x) {
 __device__ inline float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + fast_exp(-x)); }
 __device__ inline float fast_silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + fast_exp(-z)); }
 
-// Tree conv + SiLU of 4 channels at one node.  xi: the node's own tokens; X(n): tokens of
-// node n from the staged rows; hc[j]: history column j (2 = newest); w[e]: the 4 taps of
-// channel e (tap 0 = oldest).  n1..n3 are the node's parent, grandparent and
-// great-grandparent (-1 past the root).  Returns silu(conv) and the 3 newest sources
-// (t1, t2, t3 = the node itself), which form the node's commit window.
-__device__ inline v4f conv_node(v4f xi, const float *stg, int sx, int n1, int n2, int n3, const v4f hc[3],
-                                const v4f w[4], v4f &t1, v4f &t2) {
-    const v4f x1 = *reinterpret_cast<const v4f *>(stg + (n1 > 0 ? n1 : 0) * sx);
-    const v4f x2 = *reinterpret_cast<const v4f *>(stg + (n2 > 0 ? n2 : 0) * sx);
-    const v4f x3 = *reinterpret_cast<const v4f *>(stg + (n3 > 0 ? n3 : 0) * sx);
-    t2 = n1 >= 0 ? x1 : hc[2];
-    t1 = n1 >= 0 ? (n2 >= 0 ? x2 : hc[2]) : hc[1];
-    const v4f t0 = n1 >= 0 ? (n2 >= 0 ? (n3 >= 0 ? x3 : hc[2]) : hc[1]) : hc[0];
+// x[lane] + x[lane - SH] within each row of 16 lanes (0 past the row start): DPP row_shr
+template <int SH>
+__device__ inline float add_row_shr(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + SH, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of W consecutive lanes (W = 4, 8 or 16; W = 16 is a DPP row),
+// left in the last lane of each group.
+template <int W>
+__device__ inline float group_sum_last(float x) {
+    x = add_row_shr<1>(x);
+    x = add_row_shr<2>(x);
+    if constexpr (W >= 8) x = add_row_shr<4>(x);
+    if constexpr (W >= 16) x = add_row_shr<8>(x);
+    return x;
+}
+
+// Tree conv + SiLU of 4 channels at one node from its sources, oldest first (x3 = the
+// node's own tokens); w[e] holds the 4 taps of channel e (tap 0 = oldest), summed from
+// the oldest source.
+__device__ inline v4f conv_silu(v4f x0, v4f x1, v4f x2, v4f x3, const v4f w[4]) {
     v4f y;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        float z = t0[e] * w[e][0];  // taps summed from the oldest column
-        z = fmaf(t1[e], w[e][1], z);
-        z = fmaf(t2[e], w[e][2], z);
-        z = fmaf(xi[e], w[e][3], z);
+        const v4f we = w[e];
+        float z = x0[e] * we[0];
+        z = fmaf(x1[e], we[1], z);
+        z = fmaf(x2[e], we[2], z);
+        z = fmaf(x3[e], we[3], z);
         y[e] = fast_silu(z);
     }
     return y;
@@ -164,9 +179,8 @@ __device__ inline void store_window(float *dst, v4f t1, v4f t2, v4f t3) {
 }
 
 // history columns of 4 channels from their 12 consecutive floats
-__device__ inline void hist_columns(const float *src, v4f hc[3]) {
-    const v4f *p = reinterpret_cast<const v4f *>(src);
-    const v4f a = p[0], b = p[1], e = p[2];  // ch0: a.x a.y a.z | ch1: a.w b.x b.y | ch2: b.z b.w e.x | ch3: e.y e.z e.w
+__device__ inline void hist_columns(const v4f raw[3], v4f hc[3]) {
+    const v4f a = raw[0], b = raw[1], e = raw[2];  // ch0: a.x a.y a.z | ch1: a.w b.x b.y | ch2: b.z b.w e.x | ch3: e.y e.z e.w
     hc[0] = v4f{a.x, a.w, b.z, e.y};
     hc[1] = v4f{a.y, b.x, b.w, e.z};
     hc[2] = v4f{a.z, b.y, e.x, e.w};
@@ -175,24 +189,28 @@ __device__ inline void hist_columns(const float *src, v4f hc[3]) {
 template <int DK, int DV, int NP, bool FUSED>
 __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     using Ly = VerifyLayout<DK, DV, NP, FUSED>;
-    constexpr int JB = Ly::JB, NB = Ly::NB, R = Ly::R, KA = Ly::KA, SA = Ly::SA, SBT = Ly::SBT, SG = Ly::SG;
-    constexpr int Q4 = JB / 4;  // 4-float groups per block row
+    constexpr int JB = Ly::JB, NB = Ly::NB, CT = Ly::CT, NT = Ly::NT, RT = Ly::RT, KC = Ly::KC, LC = Ly::LC;
+    constexpr int R = Ly::R, G = Ly::G, Q4 = Ly::Q4, SX = Ly::SX, SV = Ly::SV, SG = Ly::SG, SXS = Ly::SXS;
+    static_assert(kThreads % G == 0 && kThreads % Q4 == 0 && 64 % G == 0, "channel groups must tile a wave");
     extern __shared__ float lds[];
-    float *Am = lds;                // A: rows 0..NP-1 delta rows, NP..2NP-1 output rows
-    float *CqT = lds + Ly::OFF_CQ;  // Cq^T[i][a]
-    float *BmT = lds + Ly::OFF_X;   // [S0 block; V block]^T, written last
-    float *Gm = lds + Ly::OFF_G;    // early aliases of the [S0; V] region
-    float *CkT = lds + Ly::OFF_CK;
-    float *Mk = lds + Ly::OFF_MK;
+    float *XQK = lds + Ly::OFF_XQK;  // raw conv rows: k of node i at row i, q of node i at row NP + i
+    float *Vl = lds + Ly::OFF_V;     // conv value rows of the block
+    float *Lm = lds + Ly::OFF_LM;    // strictly lower solve matrix
+    float *Cq = lds + Ly::OFF_CQ;    // output coefficients (1/sqrt(d_k) folded in)
+    float *Tm = lds + Ly::OFF_T;     // T = (I + Lm)^-1
+    float *scr = lds + Ly::OFF_SCR;
     __shared__ int s_wbits[kWaves];
-    __shared__ float s_beta[NP], s_g[NP], s_L[NP], s_G[NP], s_rk[NP], s_rq[NP], s_gq[NP];
+    __shared__ float s_beta[NP], s_g[NP], s_L[NP], s_G[NP], s_gk[NP], s_gq[NP], s_r[2 * NP];
+    __shared__ float s_ssq[2 * NP][Ly::NPART];
     __shared__ unsigned int s_anc[NP];
+    // conv sources of node i, oldest first, as staged rows (node rows, or NP + j for
+    // history column j): s0 | s1 << 8 | s2 << 16; the node itself is the newest source
+    __shared__ int s_src[NP];
 
     const Dims d = args.d;
-    const float *__restrict__ state_pool = args.state_pool;
-    const int32_t *__restrict__ slot_ids = args.slot_ids;
-    float *__restrict__ out = args.out;
-    float *__restrict__ replay_log = args.replay_log;
+    // every kernel argument used for an address, read in the first batch of scalar loads
+    asm volatile("" ::"s"(d.C), "s"(d.N), "s"(d.P), "s"(d.Hk), "s"(d.Hv), "s"(d.Ch), "s"(FUSED ? args.x : args.qkv),
+                 "s"(args.conv_w), "s"(args.conv_hist), "s"(args.state_pool), "s"(args.slot_ids), "s"(args.parents));
     const int N = d.N, Hv = d.Hv;
     // workgroup -> (lane c, q/k head kh, share index ws); ws -> (value head h, column block jb)
     const int n_groups = d.C * d.Hk;
@@ -200,91 +218,121 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     const int c = grp / d.Hk, kh = grp - c * d.Hk;
     const int jb = ws % NB, h = kh + d.Hk * (ws / NB);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int g4 = lane >> 4, l16 = lane & 15;
     const int j0 = jb * JB;
 
-    // ---- loads, in the order they are consumed (global loads complete in order): tree
-    //      and gates, duplicate-slot check, q/k (raw tokens when fused), the V block, then
-    //      the state block.  Indices are clamped and out-of-range values selected to zero,
-    //      so every load is unconditional and all of them are in flight together.
+    // ---- loads, all issued before any of them is consumed.  Token rows, history and
+    //      state go through range-checked buffer loads: rows past N, and everything of a
+    //      padding or invalid lane, fall outside the range and read as zero without a
+    //      memory access, so no load sits behind a branch or a select.
+    // the slot id goes through a vector load: a scalar load would share its wait counter
+    // with the kernel-argument loads and hold up every load issued after it
+    // (it stays in a vector register until every load that does not need it is issued)
+    const int s_v = __builtin_bit_cast(
+        int, __builtin_amdgcn_raw_buffer_load_b32(
+                 __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(args.slot_ids), 0, 4 * d.C, kRsrcWord3), 4 * c, 0,
+                 0));
     const int par = args.parents[(int64_t)c * N + (lane < N ? lane : 0)];  // lane i of every wave: parent of node i
     const int tn = tid < N ? tid : 0;
     const int64_t trow = (int64_t)c * N + tn;
     const float braw = args.beta_logits[trow * args.gate_stride + h];
     const float araw = args.alpha_logits[trow * args.gate_stride + h] + args.dt_bias[h];
     const float Ah = args.A[h];
-    const int so = slot_ids[tid < d.C ? tid : 0];  // this thread's share of the duplicate check
-    const int s = slot_ids[c];
+    constexpr int DUP = (GDN_MAX_SEQS + kThreads - 1) / kThreads;
+    int so[DUP];  // slots of lanes tid, tid + 256, ... (duplicate check)
+#pragma unroll
+    for (int k = 0; k < DUP; ++k) so[k] = args.slot_ids[min(tid + kThreads * k, d.C - 1)];
 
-    // separate route: conv output rows; fused route: raw token rows of the same channels
-    constexpr int G = DK / 2;  // 4-channel groups of one head's q|k slab (kThreads % G == 0)
-    constexpr int QI = (G * NP + kThreads - 1) / kThreads;
-    constexpr int QF4 = 2 * NP * (DK / 4), QPT = FUSED ? QI : (QF4 + kThreads - 1) / kThreads;
+    // q|k slab (raw tokens when fused, conv rows otherwise): item u of a thread is group
+    // gq = tid % G of node (tid / G) * QPT + u; groups 0..DK/4-1 are q channels, the rest k
+    constexpr int QPT = (G * NP + kThreads - 1) / kThreads;
     const int gq = tid % G;
     const int chq = gq < DK / 4 ? kh * DK + 4 * gq : d.Hk * DK + kh * DK + 4 * (gq - DK / 4);
-    v4f qreg[QPT];  // separate: row r < NP k of node r, NP + i q of node i; fused: x of (node, gq)
+    const float *src = FUSED ? args.x : args.qkv;
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(src + (int64_t)c * N * d.Ch), 0,
+                                          (int)(4u * (unsigned)N * (unsigned)d.Ch), kRsrcWord3);
+    v4f qreg[QPT];
 #pragma unroll
     for (int u = 0; u < QPT; ++u) {
-        if constexpr (FUSED) {
-            const int i = min((tid + kThreads * u) / G, NP - 1);
-            const v4f x = reinterpret_cast<const v4f *>(args.x + ((int64_t)c * N + (i < N ? i : 0)) * d.Ch + chq)[0];
-            qreg[u] = i < N ? x : v4f{0.f, 0.f, 0.f, 0.f};
-        } else {
-            const int f = min(tid + kThreads * u, QF4 - 1), r = f / (DK / 4), q = f - r * (DK / 4);
-            const int i = r < NP ? r : r - NP;
-            const float *src =
-                args.qkv + ((int64_t)c * N + (i < N ? i : 0)) * d.Ch + (r < NP ? d.Hk * DK : 0) + kh * DK;
-            const v4f x = reinterpret_cast<const v4f *>(src)[q];
-            qreg[u] = i < N ? x : v4f{0.f, 0.f, 0.f, 0.f};
-        }
+        const int i = min((tid / G) * QPT + u, NP - 1);
+        qreg[u] = load4(xr, (i * d.Ch + chq) * 4);
     }
-    // V block: this thread's 4-column group gv is fixed (kThreads % Q4 == 0); surplus
-    // items are clamped to the last row, so their duplicate writes carry the same value
-    constexpr int VF4 = NP * Q4, VPT = (VF4 + kThreads - 1) / kThreads;
+    // value block: item u of a thread is group gv = tid % Q4 of node (tid / Q4) * VPT + u
+    constexpr int VPT = (Q4 * NP + kThreads - 1) / kThreads;
     const int gv = tid % Q4;
     const int chv = 2 * d.Hk * DK + h * DV + j0 + 4 * gv;
-    const float *vsrc = FUSED ? args.x : args.qkv;
     v4f vreg[VPT];
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-        const int i = min((tid + kThreads * u) / Q4, NP - 1);
-        const v4f x = reinterpret_cast<const v4f *>(vsrc + ((int64_t)c * N + (i < N ? i : 0)) * d.Ch + chv)[0];
-        vreg[u] = i < N ? x : v4f{0.f, 0.f, 0.f, 0.f};
+        const int i = min((tid / Q4) * VPT + u, NP - 1);
+        vreg[u] = load4(xr, (i * d.Ch + chv) * 4);
     }
-    // fused: the taps of this thread's q/k and value channel groups
-    v4f wq[4], wv[4];
+    // fused: the taps and history of the block's channel groups are loaded once per
+    // workgroup (4 + 3 float4 per group, spread over the threads) and staged in LDS
+    constexpr int NG = Ly::NG, TPT = (NG * 4 + kThreads - 1) / kThreads;
+    static_assert(NG <= kThreads, "one history group per thread");
+    auto group_channel = [&](int g) {
+        return g < G ? (g < DK / 4 ? kh * DK + 4 * g : d.Hk * DK + kh * DK + 4 * (g - DK / 4))
+                     : 2 * d.Hk * DK + h * DV + j0 + 4 * (g - G);
+    };
+    v4f treg[TPT];
     if constexpr (FUSED) {
-        const v4f *w4 = reinterpret_cast<const v4f *>(args.conv_w);
+        const __amdgpu_buffer_rsrc_t wr4 =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(args.conv_w), 0, d.Ch * 16, kRsrcWord3);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            wq[e] = w4[chq + e];
-            wv[e] = w4[chv + e];
+        for (int u = 0; u < TPT; ++u) {
+            const int f = tid + kThreads * u;
+            treg[u] = load4(wr4, f < NG * 4 ? (group_channel(f >> 2) + (f & 3)) * 16 : kOutOfRange);
         }
     }
-    if (s == -1) return;  // padding lane
+    // loads complete in issue order: keep everything the conv needs ahead of the state
+    __builtin_amdgcn_sched_barrier(0);
+    const int s = __builtin_amdgcn_readfirstlane(s_v);
+    // slot-mapped: the 12 history floats of each channel group (fused), and this wave's
+    // chunks of the state block in the right-operand layout,
+    // sreg[lc][ct][e] = S0[16q + 4*g4 + e][j0 + 16ct + l16] for chunk q = wave + 4*lc
     const bool s_ok = s >= 0 && s < d.P;
     const int sc = s_ok ? s : 0;
-    v4f hq[3], hv[3];  // fused: history columns of the two channel groups
+    v4f hreg[3];  // fused: the 12 history floats of channel group tid (if tid < NG)
     if constexpr (FUSED) {
-        hist_columns(args.conv_hist + ((int64_t)sc * d.Ch + chq) * 3, hq);
-        hist_columns(args.conv_hist + ((int64_t)sc * d.Ch + chv) * 3, hv);
-    }
-    constexpr int SF4 = DK * Q4, SPT = (SF4 + kThreads - 1) / kThreads;
-    v4f sreg[SPT];
-    {
-        const float *Sg = state_pool + ((int64_t)sc * Hv + h) * DK * DV + j0;
+        const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(args.conv_hist + (int64_t)sc * d.Ch * 3), 0, s_ok ? d.Ch * 12 : 0, kRsrcWord3);
+        const int hb = tid < NG ? group_channel(tid) * 12 : kOutOfRange;
 #pragma unroll
-        for (int u = 0; u < SPT; ++u) {
-            const int f = min(tid + kThreads * u, SF4 - 1), r = f / Q4, q = f - r * Q4;
-            sreg[u] = reinterpret_cast<const v4f *>(Sg + (int64_t)r * DV)[q];
+        for (int e = 0; e < 3; ++e) hreg[e] = load4(hr, hb + 16 * e);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int wv_u = __builtin_amdgcn_readfirstlane(wave);
+    float sreg[LC][CT][4];
+    {
+        const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(args.state_pool + ((int64_t)sc * Hv + h) * DK * DV), 0, s_ok ? DK * DV * 4 : 0,
+            kRsrcWord3);
+#pragma unroll
+        for (int lc = 0; lc < LC; ++lc) {
+            const int q = wv_u + kWaves * lc;
+            const int base = q < KC ? ((16 * q + 4 * g4) * DV + j0 + l16) * 4 : kOutOfRange;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    sreg[lc][ct][e] = load1(sr, base + (e * DV + 16 * ct) * 4);
         }
     }
 
-    // ---- lane validity (slot range, duplicate slot, parents); nothing is written for a bad lane
-    int bits = s_ok ? 0 : GDN_STATUS_SLOT_RANGE;
-    if (tid < d.C && tid != c && so == s) bits |= GDN_STATUS_SLOT_DUP;
-    for (int o = tid + kThreads; o < d.C; o += kThreads)  // lanes beyond the first 256
-        if (o != c && slot_ids[o] == s) bits |= GDN_STATUS_SLOT_DUP;
-    if (tid < N && (par < -1 || par >= tid)) bits |= GDN_STATUS_PARENT;
+    // ---- lane validity (slot range, duplicate slot, parents); nothing is written for a bad
+    //      lane and a padding lane (slot -1) is skipped without a status bit
+    int bits = 0;
+    if (s != -1) {
+        if (!s_ok) bits |= GDN_STATUS_SLOT_RANGE;
+#pragma unroll
+        for (int k = 0; k < DUP; ++k) {
+            const int o = tid + kThreads * k;
+            if (o < d.C && o != c && so[k] == s) bits |= GDN_STATUS_SLOT_DUP;
+        }
+        if (tid < N && (par < -1 || par >= tid)) bits |= GDN_STATUS_PARENT;
+    }
     {
         int wb = 0;
 #pragma unroll
@@ -292,52 +340,28 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
             if (__builtin_amdgcn_ballot_w64((bits >> b) & 1)) wb |= 1 << b;
         if (lane == 0) s_wbits[wave] = wb;
     }
-    float *stg = lds + Ly::OFF_STG;  // fused: staged token rows [NP][SX]
-    if constexpr (FUSED) {
-#pragma unroll
-        for (int u = 0; u < QPT; ++u) {
-            const int f = tid + kThreads * u;
-            if (f < G * NP) *reinterpret_cast<v4f *>(stg + (f / G) * Ly::SX + 4 * gq) = qreg[u];
-        }
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            const int f = tid + kThreads * u;
-            if (f < VF4) *reinterpret_cast<v4f *>(stg + (f / Q4) * Ly::SX + 2 * DK + 4 * gv) = vreg[u];
-        }
-    } else {
-        // conv rows into A (k rows 0..NP-1, q rows NP..2NP-1)
-#pragma unroll
-        for (int u = 0; u < QPT; ++u) {
-            const int f = min(tid + kThreads * u, QF4 - 1), r = f / (DK / 4), q = f - r * (DK / 4);
-            *reinterpret_cast<v4f *>(Am + r * SA + 4 * q) = qreg[u];
-        }
-    }
-    lds_barrier();
-    {
-        int all = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) all |= s_wbits[w];
-        if (all) {
-            if (ws == 0 && tid == 0 && args.status) atomicOr(args.status, all);
-            return;
-        }
-    }
 
-    // ---- tree, wave 0: cumulative log-decay L_i and ancestor set by pointer jumping
-    //      (log2(NP) rounds of lane shuffles, independent of the tree depth)
+    // ---- tree, wave 0: cumulative log-decay L_i, ancestor set (pointer jumping over
+    //      log2(NP) rounds of lane shuffles, independent of the tree depth), and the three
+    //      nearest ancestors of every node for the conv
     if (wave == 0) {
         const bool real = lane < N;
-        int jump = real ? par : -1;
+        const int a1 = real ? par : -1;
+        int jump = a1;
         float L = 0.f;
         if (real) L = fast_softplus(araw) * Ah;  // log g = softplus(a + dt_bias) * A
-        if (lane < NP) s_g[lane] = fast_exp(L);
+        if (lane < NP) s_g[lane] = real ? fast_exp(L) : 0.f;
         unsigned int anc = real ? 1u << lane : 0u;
+        const int a2s = __shfl(a1, a1 >= 0 ? a1 : 0);
+        const int a2 = a1 >= 0 ? a2s : -1;
+        const int a3s = __shfl(a2, a1 >= 0 ? a1 : 0);
+        const int a3 = a1 >= 0 ? a3s : -1;
 #pragma unroll
         for (int r = 1; r < NP; r <<= 1) {
-            const int src = jump < 0 ? lane : jump;
-            const float Lj = __shfl(L, src);
-            const unsigned int aj = __shfl(anc, src);
-            const int jj = __shfl(jump, src);
+            const int srcl = jump < 0 ? lane : jump;
+            const float Lj = __shfl(L, srcl);
+            const unsigned int aj = __shfl(anc, srcl);
+            const int jj = __shfl(jump, srcl);
             if (jump >= 0) {
                 L += Lj;
                 anc |= aj;
@@ -349,108 +373,210 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
             s_G[lane] = real ? fast_exp(L) : 0.f;
             s_anc[lane] = anc;
             s_beta[lane] = real ? fast_sigmoid(braw) : 0.f;
+            const int r2 = a1 >= 0 ? a1 : NP + 2;
+            const int r1 = a1 >= 0 ? (a2 >= 0 ? a2 : NP + 2) : NP + 1;
+            const int r0 = a1 >= 0 ? (a2 >= 0 ? (a3 >= 0 ? a3 : NP + 2) : NP + 1) : NP;
+            s_src[lane] = r0 | r1 << 8 | r2 << 16;
         }
     }
-    // ---- fused: tree conv + SiLU of the block's channels from the staged rows, into the
-    //      q/k rows of A and the V registers; commit windows of the owned channels
+    // fused: stage the raw token rows for the tree conv
+    float *stg = scr;
     if constexpr (FUSED) {
-        // lane i of every wave: parent, grandparent and great-grandparent of node i
-        const int a1 = lane < N ? par : -1;
-        const int a2s = __shfl(a1, a1 >= 0 ? a1 : 0);
-        const int a2 = a1 >= 0 ? a2s : -1;
-        const int a3s = __shfl(a2, a1 >= 0 ? a1 : 0);
-        const int a3 = a1 >= 0 ? a3s : -1;
-        const int n_share = NB * (Hv / d.Hk);
-        const bool own_q = (gq * n_share) / G == ws;  // the q/k windows of group gq are written here
-        float *win = args.commit_win + (int64_t)c * N * d.Ch * 3;
-        const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < QPT; ++u) {
-            const int f = tid + kThreads * u, i = min(f / G, NP - 1);
-            const int n1 = __shfl(a1, i), n2 = __shfl(a2, i), n3 = __shfl(a3, i);
-            v4f t1, t2;
-            const v4f y = conv_node(qreg[u], stg + 4 * gq, Ly::SX, n1, n2, n3, hq, wq, t1, t2);
-            if (f < G * NP) {
-                const int row = gq < DK / 4 ? NP + i : i, col = 4 * (gq < DK / 4 ? gq : gq - DK / 4);
-                *reinterpret_cast<v4f *>(Am + row * SA + col) = i < N ? y : zero;
-                if (own_q && i < N) store_window(win + ((int64_t)i * d.Ch + chq) * 3, t1, t2, qreg[u]);
+            const int f = tid + kThreads * u;
+            const int i = (tid / G) * QPT + u;
+            if (i < NP) *reinterpret_cast<v4f *>(stg + i * SXS + 4 * gq) = qreg[u];
+        }
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int f = tid + kThreads * u;
+            const int i = (tid / Q4) * VPT + u;
+            if (i < NP) *reinterpret_cast<v4f *>(stg + i * SXS + 2 * DK + 4 * gv) = vreg[u];
+        }
+#pragma unroll
+        for (int u = 0; u < TPT; ++u) {
+            const int f = tid + kThreads * u;
+            if (f < NG * 4) *reinterpret_cast<v4f *>(lds + Ly::OFF_TAP + 4 * f) = treg[u];
+        }
+        if (tid < NG) {  // history columns of group tid as staged rows NP..NP+2
+            v4f hc[3];
+            hist_columns(hreg, hc);
+            const int col = tid < G ? 4 * tid : 2 * DK + 4 * (tid - G);
+#pragma unroll
+            for (int e = 0; e < 3; ++e) *reinterpret_cast<v4f *>(stg + (NP + e) * SXS + col) = hc[e];
+        }
+    }
+    lds_barrier();
+    if (s == -1) return;  // padding lane
+    {
+        int all = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) all |= s_wbits[w];
+        if (all) {
+            if (ws == 0 && tid == 0 && args.status) atomicOr(args.status, all);
+            return;
+        }
+    }
+
+    // ---- conv + SiLU (fused) of the block's channels, or the loaded conv rows as they are:
+    //      raw q/k rows into XQK with their squared norms, value rows into Vl; fused: the
+    //      commit windows of the owned channels.  No global load is waited for here or in
+    //      the next two phases, so the window stores (masked per lane) hold nothing up.
+    {
+        const int n_share = NB * (Hv / d.Hk);
+        const bool own_q = (gq * n_share) / G == ws;  // the q/k windows of group gq are written here
+        float *win = FUSED ? args.commit_win + (int64_t)c * N * d.Ch * 3 : nullptr;
+        const v4f zero = {0.f, 0.f, 0.f, 0.f};
+        const v4f *tap = reinterpret_cast<const v4f *>(lds + Ly::OFF_TAP);
+        // every LDS read of the phase is issued before its first LDS write (the compiler
+        // cannot reorder them across writes to the same array), then compute, then write
+        v4f yq[QPT], yv[VPT], xq[QPT][3], xv[VPT][3], wq[4], wv[4];
+        if constexpr (FUSED) {
+            int sq[QPT], sv[VPT];
+#pragma unroll
+            for (int u = 0; u < QPT; ++u) sq[u] = s_src[min((tid / G) * QPT + u, NP - 1)];
+#pragma unroll
+            for (int u = 0; u < VPT; ++u) sv[u] = s_src[min((tid / Q4) * VPT + u, NP - 1)];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                wq[e] = tap[4 * gq + e];
+                wv[e] = tap[4 * (G + gv) + e];
+            }
+#pragma unroll
+            for (int u = 0; u < QPT; ++u)
+#pragma unroll
+                for (int e = 0; e < 3; ++e)
+                    xq[u][e] = *reinterpret_cast<const v4f *>(stg + ((sq[u] >> (8 * e)) & 255) * SXS + 4 * gq);
+#pragma unroll
+            for (int u = 0; u < VPT; ++u)
+#pragma unroll
+                for (int e = 0; e < 3; ++e)
+                    xv[u][e] = *reinterpret_cast<const v4f *>(stg + ((sv[u] >> (8 * e)) & 255) * SXS + 2 * DK + 4 * gv);
+        }
+#pragma unroll
+        for (int u = 0; u < QPT; ++u) {
+            const int i = (tid / G) * QPT + u;
+            yq[u] = qreg[u];
+            if constexpr (FUSED) yq[u] = conv_silu(xq[u][0], xq[u][1], xq[u][2], qreg[u], wq);
+            yq[u] = i < N ? yq[u] : zero;
+        }
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int i = (tid / Q4) * VPT + u;
+            yv[u] = vreg[u];
+            if constexpr (FUSED) yv[u] = conv_silu(xv[u][0], xv[u][1], xv[u][2], vreg[u], wv);
+            yv[u] = i < N ? yv[u] : zero;
+        }
+        const bool isq = gq < DK / 4;
+        const int cg = isq ? gq : gq - DK / 4;  // group within the q or k row
+#pragma unroll
+        for (int u = 0; u < QPT; ++u) {
+            const int i = (tid / G) * QPT + u;
+            float ss = yq[u].x * yq[u].x + yq[u].y * yq[u].y + yq[u].z * yq[u].z + yq[u].w * yq[u].w;
+            ss = group_sum_last<(DK / 4 < 16 ? DK / 4 : 16)>(ss);
+            if (i < NP) {
+                const int row = isq ? NP + i : i;
+                *reinterpret_cast<v4f *>(XQK + row * SX + 4 * cg) = yq[u];
+                if ((cg & 15) == (DK / 4 < 16 ? DK / 4 : 16) - 1) s_ssq[row][cg >> 4] = ss;
             }
         }
 #pragma unroll
         for (int u = 0; u < VPT; ++u) {
-            const int f = tid + kThreads * u, i = min(f / Q4, NP - 1);
-            const int n1 = __shfl(a1, i), n2 = __shfl(a2, i), n3 = __shfl(a3, i);
-            v4f t1, t2;
-            const v4f y = conv_node(vreg[u], stg + 2 * DK + 4 * gv, Ly::SX, n1, n2, n3, hv, wv, t1, t2);
-            if (f < VF4 && i < N) store_window(win + ((int64_t)i * d.Ch + chv) * 3, t1, t2, vreg[u]);
-            vreg[u] = i < N ? y : zero;
+            const int i = (tid / Q4) * VPT + u;
+            if (i < NP) *reinterpret_cast<v4f *>(Vl + i * SV + 4 * gv) = yv[u];
         }
-        lds_barrier();
-    }
-
-    // ---- Gram of the raw vectors: Gm[r][a] = (row r of A) . k_a; the diagonal tiles of
-    //      Q Q^T give |q_i|^2
-    {
-        constexpr int NT = NP / 16, TG = 2 * NP / 16 * NT, TQ = NP / 16;
-        for (int t = wave; t < TG + TQ; t += kWaves) {
-            if (t < TG) {
-                const int mt = t / NT, nt = t - mt * NT;
-                const v4f acc = mma_kc<DK, SA, SA>(Am + mt * 16 * SA, Am + nt * 16 * SA);
+        if constexpr (FUSED) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    Gm[(mt * 16 + 4 * (lane >> 4) + v) * SG + nt * 16 + (lane & 15)] = acc[v];
-                    if (mt == nt && 4 * (lane >> 4) + v == (lane & 15)) s_rk[mt * 16 + (lane & 15)] = inv_norm(acc[v]);
-                }
-            } else {
-                const int qt = t - TG;
-                const float *Qb = Am + (NP + qt * 16) * SA;
-                const v4f acc = mma_kc<DK, SA, SA>(Qb, Qb);
+            for (int u = 0; u < QPT; ++u) {
+                const int i = (tid / G) * QPT + u;
+                if (own_q && i < N) store_window(win + ((int64_t)i * d.Ch + chq) * 3, xq[u][1], xq[u][2], qreg[u]);
+            }
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    if (4 * (lane >> 4) + v == (lane & 15)) s_rq[qt * 16 + (lane & 15)] = inv_norm(acc[v]);
+            for (int u = 0; u < VPT; ++u) {
+                const int i = (tid / Q4) * VPT + u;
+                if (i < N) store_window(win + ((int64_t)i * d.Ch + chv) * 3, xv[u][1], xv[u][2], vreg[u]);
             }
         }
     }
     lds_barrier();
 
-    // ---- decayed, ancestor-masked, norm-scaled coefficients (stored transposed) and the
-    //      replay-log header (g, k^) of every node, once per (lane, head)
-    //      (CkT[i][a] carries beta_i: it is the strictly lower matrix of the solve below)
-    for (int p = tid; p < NP * NP; p += kThreads) {
-        const int i = p / NP, a = p - i * NP;
-        const bool on = (s_anc[i] >> a) & 1u;
-        const float r = on ? fast_exp(s_L[i] - s_L[a]) * s_rk[a] : 0.f;
-        CkT[i * SG + a] = (on && a < i) ? r * Gm[a * SG + i] * (s_rk[i] * s_beta[i]) : 0.f;
-        CqT[i * SG + a] = on ? r * Gm[(NP + i) * SG + a] * s_rq[i] : 0.f;
-    }
-    if (tid < NP) s_gq[tid] = s_G[tid] * s_rq[tid];
-    if (jb == 0) {
-        float *logc = replay_log + ((int64_t)c * N * Hv + h) * R;
-        for (int f = tid; f < N * DK; f += kThreads) {
-            const int i = f / DK, e = f - i * DK;
-            float *lrow = logc + (int64_t)i * Hv * R;
-            lrow[1 + e] = Am[i * SA + e] * s_rk[i];
-            if (e == 0) lrow[0] = s_g[i];
+    // ---- Gram products of the raw rows, split over the waves by 16-wide chunks of d_k:
+    //      tile (rt, at) = rows 16rt.. of [K; Q] against k rows 16at..  Partial tiles go to
+    //      LDS in accumulator order.  Meanwhile the row norms.
+    {
+        v4f acc[RT][NT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int at = 0; at < NT; ++at) acc[rt][at] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int lc = 0; lc < LC; ++lc) {
+            const int q = wv_u + kWaves * lc;
+            if (q < KC) {
+                v4f av[RT];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    av[rt] = *reinterpret_cast<const v4f *>(XQK + (16 * rt + l16) * SX + 16 * q + 4 * g4);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int at = 0; at < NT; ++at) acc[rt][at] = mfma4(av[rt], av[at], acc[rt][at]);
+            }
+        }
+        float *gp = scr + wave * Ly::GRAM_TILES * 256;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int at = 0; at < NT; ++at) *reinterpret_cast<v4f *>(gp + ((rt * NT + at) * 64 + lane) * 4) = acc[rt][at];
+        if (tid < 2 * NP) {
+            float sq = s_ssq[tid][0];
+            if constexpr (Ly::NPART > 1) sq += s_ssq[tid][1];
+            s_r[tid] = inv_norm(sq);
         }
     }
     lds_barrier();
 
-    // ---- T = (I + diag(beta) Ck^T)^-1 by forward substitution, one column per thread;
-    //      M1 = T diag(beta) goes into A (rows 0..NP-1, columns DK..),
-    //      Mk = -T diag(beta G / |k|) multiplies the raw k rows
+    // ---- decayed, ancestor-masked, norm-scaled coefficients, per-node scales, and the
+    //      replay-log header (g, k^) of every node (once per lane and value head)
+    const float isd = 1.0f / sqrtf((float)DK);
+    for (int p = tid; p < NP * NP; p += kThreads) {
+        const int i = p / NP, a = p - i * NP;
+        const bool on = (s_anc[i] >> a) & 1u;
+        const int ln = ((i & 15) >> 2) * 16 + (a & 15), v = i & 3;
+        const float *gk = scr + ((((i >> 4) * NT + (a >> 4)) * 64 + ln) * 4 + v);         // k_i . k_a
+        const float *gqk = scr + (((((NT + (i >> 4)) * NT) + (a >> 4)) * 64 + ln) * 4 + v);  // q_i . k_a
+        float skk = 0.f, sqk = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            skk += gk[w * Ly::GRAM_TILES * 256];
+            sqk += gqk[w * Ly::GRAM_TILES * 256];
+        }
+        const float r = on ? fast_exp(s_L[i] - s_L[a]) * s_r[a] : 0.f;
+        Lm[i * SG + a] = (on && a != i) ? r * skk * (s_r[i] * s_beta[i]) : 0.f;
+        Cq[i * SG + a] = r * sqk * (s_r[NP + i] * isd);
+    }
     if (tid < NP) {
-        const int a = tid;
+        s_gk[tid] = s_G[tid] * s_r[tid];
+        s_gq[tid] = s_G[tid] * s_r[NP + tid] * isd;
+    }
+    lds_barrier();
+
+    // ---- wave 0: T = (I + Lm)^-1 by forward substitution, one column per lane.  Every
+    //      wave: its chunks of [K; Q] x S0 (the state block arrives here at the latest).
+    if (wave == 0 && lane < NP) {
+        const int a = lane;
         float t[NP];
-        // row i of the solve matrix is read (i / 4 + 1 four-float groups) while row i - 1
-        // is being solved, so each row costs its FMA chain rather than an LDS round trip
+        // row i of Lm is read (i / 4 + 1 four-float groups) while row i - 1 is being
+        // solved, so each row costs its FMA chain rather than an LDS round trip
         v4f cur[NP / 4], nxt[NP / 4];
-        cur[0] = *reinterpret_cast<const v4f *>(CkT);
+        cur[0] = *reinterpret_cast<const v4f *>(Lm);
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
             if (i + 1 < NP)
 #pragma unroll
                 for (int m4 = 0; m4 <= (i + 1) / 4; ++m4)
-                    nxt[m4] = *reinterpret_cast<const v4f *>(CkT + (i + 1) * SG + 4 * m4);
+                    nxt[m4] = *reinterpret_cast<const v4f *>(Lm + (i + 1) * SG + 4 * m4);
             float s0 = 0.f, s1 = 0.f;
 #pragma unroll
             for (int m = 0; m < i; ++m) {
@@ -461,97 +587,95 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
 #pragma unroll
             for (int m4 = 0; m4 < NP / 4; ++m4) cur[m4] = nxt[m4];
         }
-        const float ba = s_beta[a], ga = ba * s_G[a] * s_rk[a];
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            Am[i * SA + DK + a] = t[i] * ba;
-            Mk[i * SG + a] = -t[i] * ga;
+        for (int i = 0; i < NP; ++i) Tm[i * SG + a] = t[i];
+    }
+    {
+        v4f acc[RT][CT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int lc = 0; lc < LC; ++lc) {
+            const int q = wv_u + kWaves * lc;
+            if (q < KC) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const v4f av = *reinterpret_cast<const v4f *>(XQK + (16 * rt + l16) * SX + 16 * q + 4 * g4);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) {
+                        const v4f bv = {sreg[lc][ct][0], sreg[lc][ct][1], sreg[lc][ct][2], sreg[lc][ct][3]};
+                        acc[rt][ct] = mfma4(av, bv, acc[rt][ct]);
+                    }
+                }
+            }
+        }
+        float *pp = scr + wave * Ly::PROD_TILES * 256;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) *reinterpret_cast<v4f *>(pp + ((rt * CT + ct) * 64 + lane) * 4) = acc[rt][ct];
+    }
+    // replay-log header (g, k^) of every node, once per lane and value head; written after
+    // the last wait for the state so that these stores never hold it up
+    if (jb == 0) {
+        float *logc = args.replay_log + ((int64_t)c * N * Hv + h) * R;
+        for (int f = tid; f < N * DK; f += kThreads) {
+            const int i = f / DK, e = f - i * DK;
+            float *lrow = logc + (int64_t)i * Hv * R;
+            lrow[1 + e] = XQK[i * SX + e] * s_r[i];
+            if (e == 0) lrow[0] = s_g[i];
         }
     }
     lds_barrier();
 
-    const float isd = 1.0f / sqrtf((float)DK);
-    // ---- -K' = Mk K (in place over the k rows once every tile has read them) and
-    //      W / sqrt(d_k) = Cq^T M1 / sqrt(d_k) (rows NP.., columns DK.. of A)
-    {
-        constexpr int NTK = DK / 16, TK = NP / 16 * NTK, TKW = (TK + kWaves - 1) / kWaves;
-        v4f kacc[TKW];
+    // ---- epilogue, wave nt < CT owns value columns j0 + 16nt..: KS and QS tiles from the
+    //      partials, rhs, D = T rhs (delta rows, replay log), O = diag(gq) QS + Cq D (output)
+    if (wave < CT) {
+        const int nt = wave, jj = 16 * nt + l16;
+        v4f rhs[NT], qs[NT];
 #pragma unroll
-        for (int u = 0; u < TKW; ++u) {
-            const int t = wave + kWaves * u;
-            if (t < TK) {
-                const int mt = t / NTK, nt = t - mt * NTK;
-                kacc[u] = mma_kr<NP, SG, SA>(Mk + mt * 16 * SG, Am + nt * 16);
+        for (int mt = 0; mt < NT; ++mt) {
+            v4f ks = {0.f, 0.f, 0.f, 0.f};
+            qs[mt] = ks;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float *pp = scr + (w * Ly::PROD_TILES * 64 + lane) * 4;
+                ks += *reinterpret_cast<const v4f *>(pp + (mt * CT + nt) * 256);
+                qs[mt] += *reinterpret_cast<const v4f *>(pp + ((NT + mt) * CT + nt) * 256);
             }
-        }
-        constexpr int NTW = NP / 16;
-        for (int t = wave; t < NTW * NTW; t += kWaves) {
-            const int mt = t / NTW, nt = t - mt * NTW;
-            const v4f acc = mma_kr<NP, SG, SA>(CqT + mt * 16 * SG, Am + DK + nt * 16);
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                Am[(NP + mt * 16 + 4 * (lane >> 4) + v) * SA + DK + nt * 16 + (lane & 15)] = acc[v] * isd;
-        }
-        lds_barrier();
-#pragma unroll
-        for (int u = 0; u < TKW; ++u) {
-            const int t = wave + kWaves * u;
-            if (t < TK) {
-                const int mt = t / NTK, nt = t - mt * NTK;
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    Am[(mt * 16 + 4 * (lane >> 4) + v) * SA + nt * 16 + (lane & 15)] = kacc[u][v];
-            }
-        }
-    }
-    lds_barrier();
-
-    // ---- Q' / sqrt(d_k) = (diag(G / |q|) Q + Cq^T (-K')) / sqrt(d_k) in place over the
-    //      q rows; meanwhile the state and V blocks become the transposed right operand
-    {
-        constexpr int NTK = DK / 16, TQ = NP / 16 * NTK;
-        for (int t = wave; t < TQ; t += kWaves) {
-            const int mt = t / NTK, nt = t - mt * NTK;
-            const v4f acc = mma_kr<NP, SG, SA>(CqT + mt * 16 * SG, Am + nt * 16);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int i = mt * 16 + 4 * (lane >> 4) + v;
-                float *q = Am + (NP + i) * SA + nt * 16 + (lane & 15);
-                *q = fmaf(s_gq[i], *q, acc[v]) * isd;
+                const int i = 16 * mt + 4 * g4 + v;
+                rhs[mt][v] = s_beta[i] * (Vl[i * SV + jj] - s_gk[i] * ks[v]);
             }
         }
-    }
-    // (indices clamped as at load time: surplus threads rewrite the last element with the
-    // value they loaded for it, so the stores need no condition)
+        v4f dl[NT];
 #pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-        const int f = min(tid + kThreads * u, SF4 - 1), r = f / Q4, q = f - r * Q4;
+        for (int mt = 0; mt < NT; ++mt) {
+            dl[mt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) BmT[(4 * q + e) * SBT + r] = sreg[u][e];
-    }
+            for (int kt = 0; kt < NT; ++kt)
+                dl[mt] = mfma4(*reinterpret_cast<const v4f *>(Tm + (16 * mt + l16) * SG + 16 * kt + 4 * g4), rhs[kt],
+                               dl[mt]);
+        }
+        float *logc = args.replay_log + ((int64_t)c * N * Hv + h) * R + 1 + DK + j0 + jj;
+        float *outc = args.out + ((int64_t)c * N * Hv + h) * DV + j0 + jj;
 #pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-        const int i = min((tid + kThreads * u) / Q4, NP - 1);
+        for (int mt = 0; mt < NT; ++mt) {
+            v4f o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) BmT[(4 * gv + e) * SBT + DK + i] = vreg[u][e];
-    }
-    lds_barrier();
-
-    // ---- [delta; o] = A x [S0; V]
-    {
-        constexpr int NTJ = JB / 16, TM = 2 * NP / 16 * NTJ;
-        float *logc = replay_log + ((int64_t)c * N * Hv + h) * R;
-        for (int t = wave; t < TM; t += kWaves) {
-            const int mt = t / NTJ, nt = t - mt * NTJ;
-            const v4f acc = mma_kc<KA, SA, SBT>(Am + mt * 16 * SA, BmT + nt * 16 * SBT);
-            const int col = j0 + nt * 16 + (lane & 15);
+            for (int v = 0; v < 4; ++v) o[v] = s_gq[16 * mt + 4 * g4 + v] * qs[mt][v];
+#pragma unroll
+            for (int kt = 0; kt < NT; ++kt)
+                o = mfma4(*reinterpret_cast<const v4f *>(Cq + (16 * mt + l16) * SG + 16 * kt + 4 * g4), dl[kt], o);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int row = mt * 16 + 4 * (lane >> 4) + v;
-                if (row < NP) {
-                    if (row < N) logc[(int64_t)row * Hv * R + 1 + DK + col] = acc[v];
-                } else if (row - NP < N) {
-                    out[(((int64_t)c * N + row - NP) * Hv + h) * DV + col] = acc[v];
+                const int i = 16 * mt + 4 * g4 + v;
+                if (i < N) {
+                    logc[(int64_t)i * Hv * R] = dl[mt][v];
+                    outc[(int64_t)i * Hv * DV] = o[v];
                 }
             }
         }

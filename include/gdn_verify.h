@@ -72,7 +72,8 @@ extern "C" {
 #define GDN_ERR_NULL 1        /* a required pointer is NULL                                  */
 #define GDN_ERR_SHAPE 2       /* non-positive dimension, H_v % H_k != 0, gate_stride < H_v   */
 #define GDN_ERR_UNSUPPORTED 3 /* d_conv != 4, d_k/d_v not in {16,32,64,128}, N > 32, C > 1024,
-                                 n_layers outside 1..GDN_MAX_LAYERS                           */
+                                 n_layers outside 1..GDN_MAX_LAYERS, Ch > 2^24, P*H_v > 2^24,
+                                 or one lane's commit windows above 1 GiB (N*Ch*12 bytes)     */
 #define GDN_ERR_ALIAS 4       /* an output byte range overlaps an input or another output    */
 #define GDN_ERR_HIP 5         /* a kernel launch failed                                      */
 #define GDN_ERR_ALIGN 6       /* a dense float buffer is not 16-byte aligned, or an int32 /

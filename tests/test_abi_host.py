@@ -87,6 +87,8 @@ def test_null_shape_and_pointers():
     (dict(d_v=256), _lib.GDN_ERR_UNSUPPORTED),
     (dict(n_nodes=33), _lib.GDN_ERR_UNSUPPORTED),
     (dict(n_seqs=1025), _lib.GDN_ERR_UNSUPPORTED),
+    (dict(n_k_heads=65536, n_v_heads=65536, d_k=128, d_v=16), _lib.GDN_ERR_UNSUPPORTED),  # Ch > 2^24
+    (dict(n_nodes=32, n_k_heads=8192, n_v_heads=8192, d_k=128, d_v=128), _lib.GDN_ERR_UNSUPPORTED),  # windows > 1 GiB
 ])
 def test_shape_rejections(kw, code):
     assert _conv(_shape(**kw), _ptrs(7)) == code
