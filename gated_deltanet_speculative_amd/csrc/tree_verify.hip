@@ -48,12 +48,14 @@
 // product operands; the conv output never goes to memory.  The commit windows are
 // written once: value channels by their owning workgroup, the q/k channels split evenly
 // over the workgroups that share them.
+#include <utility>
+
 #include "gdn_internal.h"
 
 namespace gdn {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -83,13 +85,16 @@ __device__ inline v4f load4(__amdgpu_buffer_rsrc_t r, int byte_offset) {
 
 template <int DK, int DV, int NP, bool FUSED>
 struct VerifyLayout {
-    static constexpr int JB = DV < 32 ? DV : 32;  // value columns per workgroup
+    static constexpr int JB = DV < 64 ? DV : 64;  // value columns per workgroup
     static constexpr int NB = DV / JB;            // column blocks per head
     static constexpr int CT = JB / 16;            // 16-column tiles of the block
     static constexpr int NT = NP / 16;            // 16-row tiles of K (and of Q)
     static constexpr int RT = 2 * NT;             // row tiles of [K; Q]
     static constexpr int KC = DK / 16;            // 16-wide chunks of the d_k contraction
-    static constexpr int LC = (KC + kWaves - 1) / kWaves;  // chunks per wave
+    static constexpr int GW = 4;                            // Gram: waves 0..3, chunk q on wave q % 4
+    static constexpr int LCG = (KC + GW - 1) / GW;          // Gram: chunks per wave
+    static constexpr int KP = kWaves / CT;                  // state product: waves per column tile
+    static constexpr int LCQ = (KC + KP - 1) / KP;          // state product: chunks per wave
     static constexpr int R = 1 + DK + DV;         // replay-log row
     static constexpr int G = DK / 2;              // 4-channel groups of one node's q|k slab
     static constexpr int Q4 = JB / 4;             // 4-channel groups of one node's value block
@@ -107,14 +112,19 @@ struct VerifyLayout {
     static constexpr int NG = G + Q4;             // channel groups of the block (q/k slab, then values)
     static constexpr int OFF_TAP = OFF_T + NP * SG;                   // fused: taps [NG][4] of v4f
     static constexpr int OFF_SCR = OFF_TAP + (FUSED ? NG * 16 : 0);
-    // scratch, reused phase by phase: staged tokens (until the conv), Gram partials (until
-    // the coefficients), partial state products (until the epilogue)
+    static constexpr int OFF_STG = OFF_SCR;  // fused: staged rows, dead once the conv is done
+    // scratch, reused: staged rows (until the conv), Gram partials (until the
+    // coefficients), partial state products
     static constexpr int GRAM_TILES = RT * NT;
-    static constexpr int PROD_TILES = RT * CT;
-    static constexpr int STAGE = FUSED ? (NP + 3) * SXS : 0;  // node rows, then history columns 0..2
-    static constexpr int GPART = kWaves * GRAM_TILES * 256;
-    static constexpr int PPART = kWaves * PROD_TILES * 256;
-    static constexpr int SCR = STAGE > GPART ? (STAGE > PPART ? STAGE : PPART) : (GPART > PPART ? GPART : PPART);
+    static constexpr int GPART = GW * GRAM_TILES * 256;
+    // state-product partials: unit u = wave u covers column tile u % CT and k part u / CT;
+    // units 4..7 (computed while waves 0..3 form the Gram) get their own region, units
+    // 0..3 (computed after the coefficients) reuse the Gram partials
+    static constexpr int UNIT = RT * 256;
+    static_assert(GPART >= 4 * UNIT, "units 0..3 fit in the Gram partials");
+    static constexpr int OFF_UHI = GPART;
+    static constexpr int STAGE = FUSED ? (NP + 3) * SXS : 0;
+    static constexpr int SCR = STAGE > GPART + 4 * UNIT ? STAGE : GPART + 4 * UNIT;
     static constexpr int LDS_FLOATS = OFF_SCR + SCR;
 };
 
@@ -140,6 +150,28 @@ __device__ inline float fast_silu(float z) { return z * __builtin_amdgcn_rcpf(1.
 template <int SH>
 __device__ inline float add_row_shr(float x) {
     return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + SH, 0xF, 0xF, true));
+}
+
+// value of the lane whose index differs in bit log2(X) within each quad (DPP quad_perm)
+template <int X>
+__device__ inline float quad_xor(float x) {
+    constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false));
+}
+
+// value of lane K of each row of 16 lanes, in every lane of the row (DPP row_newbcast)
+template <int K>
+__device__ inline float row_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + K, 0xF, 0xF, false));
+}
+
+// Forward substitution of one column of (I + L) t = e_a over a row of 16 lanes, lane i
+// holding t_i (initially [i == a]) and row i of the strictly lower L: at step k, t_k is
+// final and is broadcast to the row; rows above k are unchanged since L[i][k] = 0 there.
+template <int... K>
+__device__ inline float bcast_solve(float t, const v4f *Lr, std::integer_sequence<int, K...>) {
+    ((t = fmaf(-Lr[K / 4][K % 4], row_bcast<K>(t), t)), ...);
+    return t;
 }
 
 // Sum over aligned groups of W consecutive lanes (W = 4, 8 or 16; W = 16 is a DPP row),
@@ -189,7 +221,7 @@ __device__ inline void hist_columns(const v4f raw[3], v4f hc[3]) {
 template <int DK, int DV, int NP, bool FUSED>
 __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     using Ly = VerifyLayout<DK, DV, NP, FUSED>;
-    constexpr int JB = Ly::JB, NB = Ly::NB, CT = Ly::CT, NT = Ly::NT, RT = Ly::RT, KC = Ly::KC, LC = Ly::LC;
+    constexpr int JB = Ly::JB, NB = Ly::NB, CT = Ly::CT, NT = Ly::NT, RT = Ly::RT, KC = Ly::KC, LCG = Ly::LCG, KP = Ly::KP, LCQ = Ly::LCQ;
     constexpr int R = Ly::R, G = Ly::G, Q4 = Ly::Q4, SX = Ly::SX, SV = Ly::SV, SG = Ly::SG, SXS = Ly::SXS;
     static_assert(kThreads % G == 0 && kThreads % Q4 == 0 && 64 % G == 0, "channel groups must tile a wave");
     extern __shared__ float lds[];
@@ -289,9 +321,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     // loads complete in issue order: keep everything the conv needs ahead of the state
     __builtin_amdgcn_sched_barrier(0);
     const int s = __builtin_amdgcn_readfirstlane(s_v);
-    // slot-mapped: the 12 history floats of each channel group (fused), and this wave's
-    // chunks of the state block in the right-operand layout,
-    // sreg[lc][ct][e] = S0[16q + 4*g4 + e][j0 + 16ct + l16] for chunk q = wave + 4*lc
+    // slot-mapped: the 12 history floats of each channel group (fused)
     const bool s_ok = s >= 0 && s < d.P;
     const int sc = s_ok ? s : 0;
     v4f hreg[3];  // fused: the 12 history floats of channel group tid (if tid < NG)
@@ -304,22 +334,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     }
     __builtin_amdgcn_sched_barrier(0);
     const int wv_u = __builtin_amdgcn_readfirstlane(wave);
-    float sreg[LC][CT][4];
-    {
-        const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float *>(args.state_pool + ((int64_t)sc * Hv + h) * DK * DV), 0, s_ok ? DK * DV * 4 : 0,
-            kRsrcWord3);
-#pragma unroll
-        for (int lc = 0; lc < LC; ++lc) {
-            const int q = wv_u + kWaves * lc;
-            const int base = q < KC ? ((16 * q + 4 * g4) * DV + j0 + l16) * 4 : kOutOfRange;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-                    sreg[lc][ct][e] = load1(sr, base + (e * DV + 16 * ct) * 4);
-        }
-    }
+    const int pct = wv_u % CT, pkp = wv_u / CT;  // state product: column tile and k part of this wave
 
     // ---- lane validity (slot range, duplicate slot, parents); nothing is written for a bad
     //      lane and a padding lane (slot -1) is skipped without a status bit
@@ -380,7 +395,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
         }
     }
     // fused: stage the raw token rows for the tree conv
-    float *stg = scr;
+    float *stg = lds + Ly::OFF_STG;  // node rows 0..NP-1, then history columns 0..2
     if constexpr (FUSED) {
 #pragma unroll
         for (int u = 0; u < QPT; ++u) {
@@ -419,40 +434,59 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
         }
     }
 
-    // ---- conv + SiLU (fused) of the block's channels, or the loaded conv rows as they are:
-    //      raw q/k rows into XQK with their squared norms, value rows into Vl; fused: the
-    //      commit windows of the owned channels.  No global load is waited for here or in
-    //      the next two phases, so the window stores (masked per lane) hold nothing up.
+    // ---- this wave's chunks of the state block, in the right-operand layout
+    //      sreg[lc][e] = S0[16q + 4*g4 + e][j0 + 16*pct + l16], chunks q = pkp + KP*lc.  They
+    //      are requested only now, once the token rows have arrived, so that the rows the
+    //      conv and the tree algebra need first do not queue behind the state in HBM; the
+    //      state is first needed after the conv.
+    float sreg[LCQ][4];
     {
-        const int n_share = NB * (Hv / d.Hk);
-        const bool own_q = (gq * n_share) / G == ws;  // the q/k windows of group gq are written here
-        float *win = FUSED ? args.commit_win + (int64_t)c * N * d.Ch * 3 : nullptr;
+        const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(args.state_pool + ((int64_t)sc * Hv + h) * DK * DV), 0, s_ok ? DK * DV * 4 : 0,
+            kRsrcWord3);
+#pragma unroll
+        for (int lc = 0; lc < LCQ; ++lc) {
+            const int q = pkp + KP * lc;
+            const int base = (KC % KP == 0 || q < KC) ? ((16 * q + 4 * g4) * DV + j0 + 16 * pct + l16) * 4 : kOutOfRange;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sreg[lc][e] = load1(sr, base + e * DV * 4);
+        }
+    }
+
+    // ---- conv + SiLU (fused) of the block's channels, or the loaded conv rows as they are:
+    //      raw q/k rows into XQK with their squared norms, value rows into Vl
+    {
         const v4f zero = {0.f, 0.f, 0.f, 0.f};
         const v4f *tap = reinterpret_cast<const v4f *>(lds + Ly::OFF_TAP);
         // every LDS read of the phase is issued before its first LDS write (the compiler
         // cannot reorder them across writes to the same array), then compute, then write
+        // waves whose value items all lie past the padded node count skip the value part
+        const bool has_v = ((64 * wv_u) / Q4) * VPT < NP;
         v4f yq[QPT], yv[VPT], xq[QPT][3], xv[VPT][3], wq[4], wv[4];
         if constexpr (FUSED) {
-            int sq[QPT], sv[VPT];
+            int sq[QPT];
 #pragma unroll
             for (int u = 0; u < QPT; ++u) sq[u] = s_src[min((tid / G) * QPT + u, NP - 1)];
 #pragma unroll
-            for (int u = 0; u < VPT; ++u) sv[u] = s_src[min((tid / Q4) * VPT + u, NP - 1)];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                wq[e] = tap[4 * gq + e];
-                wv[e] = tap[4 * (G + gv) + e];
-            }
+            for (int e = 0; e < 4; ++e) wq[e] = tap[4 * gq + e];
 #pragma unroll
             for (int u = 0; u < QPT; ++u)
 #pragma unroll
                 for (int e = 0; e < 3; ++e)
                     xq[u][e] = *reinterpret_cast<const v4f *>(stg + ((sq[u] >> (8 * e)) & 255) * SXS + 4 * gq);
+            if (has_v) {
+                int sv[VPT];
 #pragma unroll
-            for (int u = 0; u < VPT; ++u)
+                for (int u = 0; u < VPT; ++u) sv[u] = s_src[min((tid / Q4) * VPT + u, NP - 1)];
 #pragma unroll
-                for (int e = 0; e < 3; ++e)
-                    xv[u][e] = *reinterpret_cast<const v4f *>(stg + ((sv[u] >> (8 * e)) & 255) * SXS + 2 * DK + 4 * gv);
+                for (int e = 0; e < 4; ++e) wv[e] = tap[4 * (G + gv) + e];
+#pragma unroll
+                for (int u = 0; u < VPT; ++u)
+#pragma unroll
+                    for (int e = 0; e < 3; ++e)
+                        xv[u][e] =
+                            *reinterpret_cast<const v4f *>(stg + ((sv[u] >> (8 * e)) & 255) * SXS + 2 * DK + 4 * gv);
+            }
         }
 #pragma unroll
         for (int u = 0; u < QPT; ++u) {
@@ -461,12 +495,14 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
             if constexpr (FUSED) yq[u] = conv_silu(xq[u][0], xq[u][1], xq[u][2], qreg[u], wq);
             yq[u] = i < N ? yq[u] : zero;
         }
+        if (has_v) {
 #pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            const int i = (tid / Q4) * VPT + u;
-            yv[u] = vreg[u];
-            if constexpr (FUSED) yv[u] = conv_silu(xv[u][0], xv[u][1], xv[u][2], vreg[u], wv);
-            yv[u] = i < N ? yv[u] : zero;
+            for (int u = 0; u < VPT; ++u) {
+                const int i = (tid / Q4) * VPT + u;
+                yv[u] = vreg[u];
+                if constexpr (FUSED) yv[u] = conv_silu(xv[u][0], xv[u][1], xv[u][2], vreg[u], wv);
+                yv[u] = i < N ? yv[u] : zero;
+            }
         }
         const bool isq = gq < DK / 4;
         const int cg = isq ? gq : gq - DK / 4;  // group within the q or k row
@@ -481,38 +517,51 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
                 if ((cg & 15) == (DK / 4 < 16 ? DK / 4 : 16) - 1) s_ssq[row][cg >> 4] = ss;
             }
         }
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            const int i = (tid / Q4) * VPT + u;
-            if (i < NP) *reinterpret_cast<v4f *>(Vl + i * SV + 4 * gv) = yv[u];
-        }
-        if constexpr (FUSED) {
-#pragma unroll
-            for (int u = 0; u < QPT; ++u) {
-                const int i = (tid / G) * QPT + u;
-                if (own_q && i < N) store_window(win + ((int64_t)i * d.Ch + chq) * 3, xq[u][1], xq[u][2], qreg[u]);
-            }
+        if (has_v) {
 #pragma unroll
             for (int u = 0; u < VPT; ++u) {
                 const int i = (tid / Q4) * VPT + u;
-                if (i < N) store_window(win + ((int64_t)i * d.Ch + chv) * 3, xv[u][1], xv[u][2], vreg[u]);
+                if (i < NP) *reinterpret_cast<v4f *>(Vl + i * SV + 4 * gv) = yv[u];
             }
         }
     }
     lds_barrier();
 
-    // ---- Gram products of the raw rows, split over the waves by 16-wide chunks of d_k:
-    //      tile (rt, at) = rows 16rt.. of [K; Q] against k rows 16at..  Partial tiles go to
-    //      LDS in accumulator order.  Meanwhile the row norms.
-    {
+    // ---- [K; Q] x S0 for this wave's unit (column tile pct, chunks q = pkp + KP*lc) into
+    //      LDS partial tiles in accumulator order
+    auto state_product = [&]() {
+        v4f acc[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int lc = 0; lc < LCQ; ++lc) {
+            const int q = pkp + KP * lc;
+            if (KC % KP == 0 || q < KC) {
+                const v4f bv = {sreg[lc][0], sreg[lc][1], sreg[lc][2], sreg[lc][3]};
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    acc[rt] = mfma4(*reinterpret_cast<const v4f *>(XQK + (16 * rt + l16) * SX + 16 * q + 4 * g4), bv,
+                                    acc[rt]);
+            }
+        }
+        float *pp = scr + (wv_u < 4 ? wv_u * Ly::UNIT : Ly::OFF_UHI + (wv_u - 4) * Ly::UNIT) + lane * 4;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) *reinterpret_cast<v4f *>(pp + rt * 256) = acc[rt];
+    };
+
+    // ---- waves 0..3: Gram products of the raw rows, split by 16-wide chunks of d_k:
+    //      tile (rt, at) = rows 16rt.. of [K; Q] against k rows 16at..; partial tiles go to
+    //      LDS in accumulator order; the row norms.
+    //      waves 4..7: their units of the state product.
+    if (wv_u < Ly::GW) {
         v4f acc[RT][NT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int at = 0; at < NT; ++at) acc[rt][at] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int lc = 0; lc < LC; ++lc) {
-            const int q = wv_u + kWaves * lc;
+        for (int lc = 0; lc < LCG; ++lc) {
+            const int q = wv_u + Ly::GW * lc;
             if (q < KC) {
                 v4f av[RT];
 #pragma unroll
@@ -534,11 +583,12 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
             if constexpr (Ly::NPART > 1) sq += s_ssq[tid][1];
             s_r[tid] = inv_norm(sq);
         }
+    } else {
+        state_product();
     }
     lds_barrier();
 
-    // ---- decayed, ancestor-masked, norm-scaled coefficients, per-node scales, and the
-    //      replay-log header (g, k^) of every node (once per lane and value head)
+    // ---- decayed, ancestor-masked, norm-scaled coefficients and per-node scales
     const float isd = 1.0f / sqrtf((float)DK);
     for (int p = tid; p < NP * NP; p += kThreads) {
         const int i = p / NP, a = p - i * NP;
@@ -548,7 +598,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
         const float *gqk = scr + (((((NT + (i >> 4)) * NT) + (a >> 4)) * 64 + ln) * 4 + v);  // q_i . k_a
         float skk = 0.f, sqk = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < Ly::GW; ++w) {
             skk += gk[w * Ly::GRAM_TILES * 256];
             sqk += gqk[w * Ly::GRAM_TILES * 256];
         }
@@ -562,76 +612,66 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     }
     lds_barrier();
 
-    // ---- wave 0: T = (I + Lm)^-1 by forward substitution, one column per lane.  Every
-    //      wave: its chunks of [K; Q] x S0 (the state block arrives here at the latest).
-    if (wave == 0 && lane < NP) {
-        const int a = lane;
-        float t[NP];
-        // row i of Lm is read (i / 4 + 1 four-float groups) while row i - 1 is being
-        // solved, so each row costs its FMA chain rather than an LDS round trip
-        v4f cur[NP / 4], nxt[NP / 4];
-        cur[0] = *reinterpret_cast<const v4f *>(Lm);
+    // ---- waves 0..3: their units of the state product.  Waves 4..7 (on the same SIMDs, so
+    //      the solve overlaps the products): T = (I + Lm)^-1 by forward substitution.
+    if (wv_u < 4) {
+        state_product();
+    } else if constexpr (NP == 16) {
+        // waves 4..7, four columns each: lane = (column a, row i) over rows of 16 lanes
+        const int a = 4 * (wv_u - 4) + (lane >> 4), i = lane & 15;
+        v4f Lr[4];
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            if (i + 1 < NP)
+        for (int k4 = 0; k4 < 4; ++k4) Lr[k4] = *reinterpret_cast<const v4f *>(Lm + i * SG + 4 * k4);
+        Tm[i * SG + a] = bcast_solve(i == a ? 1.f : 0.f, Lr, std::make_integer_sequence<int, 16>());
+    } else if (wv_u == 4) {
+        if (lane < NP) {
+            // one column per lane; row i + 1 of Lm is read while row i is being solved
+            const int a = lane;
+            float t[NP];
+            v4f cur[NP / 4], nxt[NP / 4];
+            cur[0] = *reinterpret_cast<const v4f *>(Lm);
 #pragma unroll
-                for (int m4 = 0; m4 <= (i + 1) / 4; ++m4)
-                    nxt[m4] = *reinterpret_cast<const v4f *>(Lm + (i + 1) * SG + 4 * m4);
-            float s0 = 0.f, s1 = 0.f;
+            for (int i = 0; i < NP; ++i) {
+                if (i + 1 < NP)
 #pragma unroll
-            for (int m = 0; m < i; ++m) {
-                if (m & 1) s1 = fmaf(cur[m / 4][m % 4], t[m], s1);
-                else s0 = fmaf(cur[m / 4][m % 4], t[m], s0);
-            }
-            t[i] = i < a ? 0.f : (i == a ? 1.f : -(s0 + s1));
+                    for (int m4 = 0; m4 <= (i + 1) / 4; ++m4)
+                        nxt[m4] = *reinterpret_cast<const v4f *>(Lm + (i + 1) * SG + 4 * m4);
+                float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-            for (int m4 = 0; m4 < NP / 4; ++m4) cur[m4] = nxt[m4];
-        }
-#pragma unroll
-        for (int i = 0; i < NP; ++i) Tm[i * SG + a] = t[i];
-    }
-    {
-        v4f acc[RT][CT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int lc = 0; lc < LC; ++lc) {
-            const int q = wv_u + kWaves * lc;
-            if (q < KC) {
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const v4f av = *reinterpret_cast<const v4f *>(XQK + (16 * rt + l16) * SX + 16 * q + 4 * g4);
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) {
-                        const v4f bv = {sreg[lc][ct][0], sreg[lc][ct][1], sreg[lc][ct][2], sreg[lc][ct][3]};
-                        acc[rt][ct] = mfma4(av, bv, acc[rt][ct]);
-                    }
+                for (int m = 0; m < i; ++m) {
+                    if (m & 1) s1 = fmaf(cur[m / 4][m % 4], t[m], s1);
+                    else s0 = fmaf(cur[m / 4][m % 4], t[m], s0);
                 }
+                t[i] = i < a ? 0.f : (i == a ? 1.f : -(s0 + s1));
+#pragma unroll
+                for (int m4 = 0; m4 < NP / 4; ++m4) cur[m4] = nxt[m4];
             }
-        }
-        float *pp = scr + wave * Ly::PROD_TILES * 256;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) *reinterpret_cast<v4f *>(pp + ((rt * CT + ct) * 64 + lane) * 4) = acc[rt][ct];
-    }
-    // replay-log header (g, k^) of every node, once per lane and value head; written after
-    // the last wait for the state so that these stores never hold it up
-    if (jb == 0) {
-        float *logc = args.replay_log + ((int64_t)c * N * Hv + h) * R;
-        for (int f = tid; f < N * DK; f += kThreads) {
-            const int i = f / DK, e = f - i * DK;
-            float *lrow = logc + (int64_t)i * Hv * R;
-            lrow[1 + e] = XQK[i * SX + e] * s_r[i];
-            if (e == 0) lrow[0] = s_g[i];
+            for (int i = 0; i < NP; ++i) Tm[i * SG + a] = t[i];
         }
     }
     lds_barrier();
 
-    // ---- epilogue, wave nt < CT owns value columns j0 + 16nt..: KS and QS tiles from the
-    //      partials, rhs, D = T rhs (delta rows, replay log), O = diag(gq) QS + Cq D (output)
+    // ---- epilogue: wave nt < CT owns value columns j0 + 16nt..: KS and QS tiles from the
+    //      partials, rhs, D = T rhs (delta rows, replay log), O = diag(gq) QS + Cq D (output).
+    //      Waves 4..7, once per lane and value head: the replay-log header (g, k^) of every
+    //      node (its stores go out beside the epilogue's).
+    static_assert(CT <= 4, "epilogue waves");
+    if (wv_u >= 4) {
+        const int t4 = tid - 256;
+        constexpr int T4 = kThreads - 256;
+        if (jb == 0) {
+            float *logc = args.replay_log + ((int64_t)c * N * Hv + h) * R;
+            for (int f = t4; f < N * DK; f += T4) {
+                const int i = f / DK, e = f - i * DK;
+                float sq = s_ssq[i][0];
+                if constexpr (Ly::NPART > 1) sq += s_ssq[i][1];
+                float *lrow = logc + (int64_t)i * Hv * R;
+                lrow[1 + e] = XQK[i * SX + e] * inv_norm(sq);
+                if (e == 0) lrow[0] = s_g[i];
+            }
+        }
+    }
     if (wave < CT) {
         const int nt = wave, jj = 16 * nt + l16;
         v4f rhs[NT], qs[NT];
@@ -640,10 +680,11 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
             v4f ks = {0.f, 0.f, 0.f, 0.f};
             qs[mt] = ks;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float *pp = scr + (w * Ly::PROD_TILES * 64 + lane) * 4;
-                ks += *reinterpret_cast<const v4f *>(pp + (mt * CT + nt) * 256);
-                qs[mt] += *reinterpret_cast<const v4f *>(pp + ((NT + mt) * CT + nt) * 256);
+            for (int kp = 0; kp < KP; ++kp) {
+                const int u = kp * CT + nt;
+                const float *pp = scr + (u < 4 ? u * Ly::UNIT : Ly::OFF_UHI + (u - 4) * Ly::UNIT) + lane * 4;
+                ks += *reinterpret_cast<const v4f *>(pp + mt * 256);
+                qs[mt] += *reinterpret_cast<const v4f *>(pp + (NT + mt) * 256);
             }
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -687,9 +728,60 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs 
     verify_body<DK, DV, NP, false>(args);
 }
 
+// Commit windows of the fused route, written by workgroups of their own that run beside
+// the verify workgroups of the same launch, so that these stores drain while the verify
+// workgroups compute.  Workgroup b covers lane b / blocks_per_lane and a block of
+// 4 * (kThreads / NP) channels; thread t covers node t / (kThreads / NP) and one 4-channel
+// group.  The window of node i is the last 3 sources of its extended sequence, oldest
+// first: the tokens of its parent and grandparent, or the slot's newest history columns
+// in their place past the root, then the node's own tokens ("perf(qwen35): fuse the
+// DFlash2 concurrent verify Gated DeltaNet route", Optimizations, first bullet).
+// Nothing is written for a padding or invalid lane (the verify workgroups report it).
+template <int NP>
+__device__ __forceinline__ void window_body(const VerifyArgs &args, int b) {
+    constexpr int GPB = kThreads / NP;  // 4-channel groups per workgroup
+    const Dims d = args.d;
+    const int N = d.N;
+    const int bpl = (d.Ch + 4 * GPB - 1) / (4 * GPB);
+    const int c = b / bpl, ch0 = (b - c * bpl) * 4 * GPB;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int i = tid / GPB, ch = ch0 + 4 * (tid % GPB);
+    const int s = args.slot_ids[c];
+    const int par = args.parents[(int64_t)c * N + (lane < N ? lane : 0)];  // lane j: parent of node j
+    // the lane's validity, as the verify workgroups decide it
+    int bad = (s < -1 || s >= d.P) ? 1 : 0;
+    for (int o = lane; o < d.C; o += 64)
+        if (o != c && args.slot_ids[o] == s) bad = 1;
+    if (lane < N && (par < -1 || par >= lane)) bad = 1;
+    if (s == -1 || __builtin_amdgcn_ballot_w64(bad)) return;  // uniform over the wave
+    const int ic = i < N ? i : 0;
+    const int a1 = __shfl(par, ic);
+    const int a2s = __shfl(par, a1 >= 0 ? a1 : 0);
+    const int a2 = a1 >= 0 ? a2s : -1;
+    if (i >= N || ch >= d.Ch) return;
+    const float *xr = args.x + (int64_t)c * N * d.Ch + ch;
+    const float *hr = args.conv_hist + ((int64_t)s * d.Ch + ch) * 3;
+    const v4f t3 = *reinterpret_cast<const v4f *>(xr + (int64_t)i * d.Ch);
+    v4f hraw[3];
+#pragma unroll
+    for (int e = 0; e < 3; ++e) hraw[e] = reinterpret_cast<const v4f *>(hr)[e];
+    v4f hc[3];
+    hist_columns(hraw, hc);
+    const v4f x1 = *reinterpret_cast<const v4f *>(xr + (int64_t)(a1 >= 0 ? a1 : 0) * d.Ch);
+    const v4f x2 = *reinterpret_cast<const v4f *>(xr + (int64_t)(a2 >= 0 ? a2 : 0) * d.Ch);
+    const v4f t2 = a1 >= 0 ? x1 : hc[2];
+    const v4f t1 = a1 >= 0 ? (a2 >= 0 ? x2 : hc[2]) : hc[1];
+    store_window(args.commit_win + (((int64_t)c * N + i) * d.Ch + ch) * 3, t1, t2, t3);
+}
+
 template <int DK, int DV, int NP>
 __global__ __launch_bounds__(kThreads) void conv_tree_verify_kernel(const VerifyArgs args) {
-    verify_body<DK, DV, NP, true>(args);
+    constexpr int NB = VerifyLayout<DK, DV, NP, true>::NB;
+    const int n_verify = NB * args.d.Hv * args.d.C;
+    if ((int)blockIdx.x < n_verify)
+        verify_body<DK, DV, NP, true>(args);
+    else
+        window_body<NP>(args, blockIdx.x - n_verify);
 }
 
 template <int DK, int DV, int NP, bool FUSED>
@@ -701,7 +793,9 @@ hipError_t launch(const VerifyArgs &a, hipStream_t stream) {
                                : reinterpret_cast<const void *>(&tree_verify_kernel<DK, DV, NP>);
     static const hipError_t attr = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
-    const int grid = Ly::NB * a.d.Hv * a.d.C;
+    // fused: the window workgroups follow the verify workgroups
+    const int grid = Ly::NB * a.d.Hv * a.d.C +
+                     (FUSED ? a.d.C * ((a.d.Ch + 4 * (kThreads / NP) - 1) / (4 * (kThreads / NP))) : 0);
     if constexpr (FUSED)
         hipLaunchKernelGGL((conv_tree_verify_kernel<DK, DV, NP>), dim3(grid), dim3(kThreads), lds, stream, a);
     else
