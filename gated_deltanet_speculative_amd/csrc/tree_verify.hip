@@ -205,9 +205,9 @@ __device__ inline v4f conv_silu(v4f x0, v4f x1, v4f x2, v4f x3, const v4f w[4]) 
 // window of 4 channels in the history layout [ch][3]: 12 consecutive floats
 __device__ inline void store_window(float *dst, v4f t1, v4f t2, v4f t3) {
     v4f *w = reinterpret_cast<v4f *>(dst);
-    w[0] = v4f{t1.x, t2.x, t3.x, t1.y};
-    w[1] = v4f{t2.y, t3.y, t1.z, t2.z};
-    w[2] = v4f{t3.z, t1.w, t2.w, t3.w};
+    __builtin_nontemporal_store(v4f{t1.x, t2.x, t3.x, t1.y}, w);
+    __builtin_nontemporal_store(v4f{t2.y, t3.y, t1.z, t2.z}, w + 1);
+    __builtin_nontemporal_store(v4f{t3.z, t1.w, t2.w, t3.w}, w + 2);
 }
 
 // history columns of 4 channels from their 12 consecutive floats
@@ -667,8 +667,8 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
                 float sq = s_ssq[i][0];
                 if constexpr (Ly::NPART > 1) sq += s_ssq[i][1];
                 float *lrow = logc + (int64_t)i * Hv * R;
-                lrow[1 + e] = XQK[i * SX + e] * inv_norm(sq);
-                if (e == 0) lrow[0] = s_g[i];
+                __builtin_nontemporal_store(XQK[i * SX + e] * inv_norm(sq), lrow + 1 + e);
+                if (e == 0) __builtin_nontemporal_store(s_g[i], lrow);
             }
         }
     }
@@ -715,8 +715,8 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
             for (int v = 0; v < 4; ++v) {
                 const int i = 16 * mt + 4 * g4 + v;
                 if (i < N) {
-                    logc[(int64_t)i * Hv * R] = dl[mt][v];
-                    outc[(int64_t)i * Hv * DV] = o[v];
+                    __builtin_nontemporal_store(dl[mt][v], logc + (int64_t)i * Hv * R);
+                    __builtin_nontemporal_store(o[v], outc + (int64_t)i * Hv * DV);
                 }
             }
         }
