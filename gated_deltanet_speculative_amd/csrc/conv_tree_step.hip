@@ -139,9 +139,10 @@ __global__ __launch_bounds__(kThreads) void conv_tree_step_kernel(
         *reinterpret_cast<v4f *>(conv_out + row * Ch + ch) = v4f{silu(za), silu(zb), silu(zc), silu(zd)};
         // commit window = taps 1..3 of each channel, [ch][3] layout: 12 floats for 4 channels
         v4f *wdst = reinterpret_cast<v4f *>(commit_win + (row * Ch + ch) * 3);
-        wdst[0] = v4f{t1.x, t2.x, t3.x, t1.y};
-        wdst[1] = v4f{t2.y, t3.y, t1.z, t2.z};
-        wdst[2] = v4f{t3.z, t1.w, t2.w, t3.w};
+        // (non-temporal: the windows are read again only by the commit, after the round)
+        __builtin_nontemporal_store(v4f{t1.x, t2.x, t3.x, t1.y}, wdst);
+        __builtin_nontemporal_store(v4f{t2.y, t3.y, t1.z, t2.z}, wdst + 1);
+        __builtin_nontemporal_store(v4f{t3.z, t1.w, t2.w, t3.w}, wdst + 2);
     }
 }
 

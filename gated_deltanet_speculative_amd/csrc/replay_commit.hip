@@ -212,18 +212,20 @@ __global__ __launch_bounds__(kThreads) void replay_commit_kernel(
         const int n4 = d.Ch * 3 / 4;
         const v4f *src = reinterpret_cast<const v4f *>(lp.commit_win[layer] + ((int64_t)c * N + e) * d.Ch * 3);
         v4f *dst = reinterpret_cast<v4f *>(lp.conv_hist[layer] + (int64_t)s * d.Ch * 3);
-        for (int idx = rb * kThreads + tid; idx < n4; idx += Cfg::NB * kThreads) dst[idx] = src[idx];
+        for (int idx = rb * kThreads + tid; idx < n4; idx += Cfg::NB * kThreads) __builtin_nontemporal_store(src[idx], dst + idx);
         return;
     }
 
-    // ---- S = G S0 + A, written back
+    // ---- S = G S0 + A, written back (non-temporal: the slot's state is read again only by
+    // a later round's verify)
     // (indices clamped as at load time: surplus threads recompute the last group from
     // the same loaded values and store the identical result)
 #pragma unroll
     for (int u = 0; u < FPT; ++u) {
         const v4f v = sv[u];
-        S4[min(tid + kThreads * u, F4 - 1)] =
-            v4f{fmaf(G, v.x, acc[u].x), fmaf(G, v.y, acc[u].y), fmaf(G, v.z, acc[u].z), fmaf(G, v.w, acc[u].w)};
+        __builtin_nontemporal_store(
+            v4f{fmaf(G, v.x, acc[u].x), fmaf(G, v.y, acc[u].y), fmaf(G, v.z, acc[u].z), fmaf(G, v.w, acc[u].w)},
+            S4 + min(tid + kThreads * u, F4 - 1));
     }
 }
 
