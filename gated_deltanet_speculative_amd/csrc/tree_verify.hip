@@ -117,14 +117,11 @@ struct VerifyLayout {
     // coefficients), partial state products
     static constexpr int GRAM_TILES = RT * NT;
     static constexpr int GPART = GW * GRAM_TILES * 256;
-    // state-product partials: unit u = wave u covers column tile u % CT and k part u / CT;
-    // units 4..7 (computed while waves 0..3 form the Gram) get their own region, units
-    // 0..3 (computed after the coefficients) reuse the Gram partials
+    // state-product partials: unit u = wave u covers column tile u % CT and k part u / CT
     static constexpr int UNIT = RT * 256;
-    static_assert(GPART >= 4 * UNIT, "units 0..3 fit in the Gram partials");
-    static constexpr int OFF_UHI = GPART;
+    static constexpr int OFF_UNIT = GPART;
     static constexpr int STAGE = FUSED ? (NP + 3) * SXS : 0;
-    static constexpr int SCR = STAGE > GPART + 4 * UNIT ? STAGE : GPART + 4 * UNIT;
+    static constexpr int SCR = STAGE > GPART + 8 * UNIT ? STAGE : GPART + 8 * UNIT;
     static constexpr int LDS_FLOATS = OFF_SCR + SCR;
 };
 
@@ -544,7 +541,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
                                     acc[rt]);
             }
         }
-        float *pp = scr + (wv_u < 4 ? wv_u * Ly::UNIT : Ly::OFF_UHI + (wv_u - 4) * Ly::UNIT) + lane * 4;
+        float *pp = scr + Ly::OFF_UNIT + wv_u * Ly::UNIT + lane * 4;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) *reinterpret_cast<v4f *>(pp + rt * 256) = acc[rt];
     };
@@ -552,7 +549,8 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     // ---- waves 0..3: Gram products of the raw rows, split by 16-wide chunks of d_k:
     //      tile (rt, at) = rows 16rt.. of [K; Q] against k rows 16at..; partial tiles go to
     //      LDS in accumulator order; the row norms.
-    //      waves 4..7: their units of the state product.
+    //      Every wave: its unit of the state product (the MFMA work of the round is kept in
+    //      this phase: fp32 MFMA and VALU from waves sharing a SIMD barely overlap).
     if (wv_u < Ly::GW) {
         v4f acc[RT][NT];
 #pragma unroll
@@ -583,9 +581,8 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
             if constexpr (Ly::NPART > 1) sq += s_ssq[tid][1];
             s_r[tid] = inv_norm(sq);
         }
-    } else {
-        state_product();
     }
+    state_product();
     lds_barrier();
 
     // ---- decayed, ancestor-masked, norm-scaled coefficients and per-node scales
@@ -612,10 +609,29 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     }
     lds_barrier();
 
-    // ---- waves 0..3: their units of the state product.  Waves 4..7 (on the same SIMDs, so
-    //      the solve overlaps the products): T = (I + Lm)^-1 by forward substitution.
+    // ---- waves 4..7: T = (I + Lm)^-1 by forward substitution.  Waves nt < CT: the KS and
+    //      QS tiles of value columns j0 + 16nt.. from the unit partials, and rhs.
+    v4f rhs[NT], qs[NT];
     if (wv_u < 4) {
-        state_product();
+        if (wave < CT) {
+            const int nt = wave, jj = 16 * nt + l16;
+#pragma unroll
+            for (int mt = 0; mt < NT; ++mt) {
+                v4f ks = {0.f, 0.f, 0.f, 0.f};
+                qs[mt] = ks;
+#pragma unroll
+                for (int kp = 0; kp < KP; ++kp) {
+                    const float *pp = scr + Ly::OFF_UNIT + (kp * CT + nt) * Ly::UNIT + lane * 4;
+                    ks += *reinterpret_cast<const v4f *>(pp + mt * 256);
+                    qs[mt] += *reinterpret_cast<const v4f *>(pp + (NT + mt) * 256);
+                }
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int i = 16 * mt + 4 * g4 + v;
+                    rhs[mt][v] = s_beta[i] * (Vl[i * SV + jj] - s_gk[i] * ks[v]);
+                }
+            }
+        }
     } else if constexpr (NP == 16) {
         // waves 4..7, four columns each: lane = (column a, row i) over rows of 16 lanes
         const int a = 4 * (wv_u - 4) + (lane >> 4), i = lane & 15;
@@ -652,8 +668,8 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     }
     lds_barrier();
 
-    // ---- epilogue: wave nt < CT owns value columns j0 + 16nt..: KS and QS tiles from the
-    //      partials, rhs, D = T rhs (delta rows, replay log), O = diag(gq) QS + Cq D (output).
+    // ---- epilogue: wave nt < CT owns value columns j0 + 16nt..: D = T rhs (delta rows,
+    //      replay log), O = diag(gq) QS + Cq D (output).
     //      Waves 4..7, once per lane and value head: the replay-log header (g, k^) of every
     //      node (its stores go out beside the epilogue's).
     static_assert(CT <= 4, "epilogue waves");
@@ -674,24 +690,6 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     }
     if (wave < CT) {
         const int nt = wave, jj = 16 * nt + l16;
-        v4f rhs[NT], qs[NT];
-#pragma unroll
-        for (int mt = 0; mt < NT; ++mt) {
-            v4f ks = {0.f, 0.f, 0.f, 0.f};
-            qs[mt] = ks;
-#pragma unroll
-            for (int kp = 0; kp < KP; ++kp) {
-                const int u = kp * CT + nt;
-                const float *pp = scr + (u < 4 ? u * Ly::UNIT : Ly::OFF_UHI + (u - 4) * Ly::UNIT) + lane * 4;
-                ks += *reinterpret_cast<const v4f *>(pp + mt * 256);
-                qs[mt] += *reinterpret_cast<const v4f *>(pp + (NT + mt) * 256);
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int i = 16 * mt + 4 * g4 + v;
-                rhs[mt][v] = s_beta[i] * (Vl[i * SV + jj] - s_gk[i] * ks[v]);
-            }
-        }
         v4f dl[NT];
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt) {
