@@ -13,7 +13,7 @@
 // launch: every workgroup runs the preflight over all lanes itself (slot range,
 // duplicate slots, parents, accept node) and also honours bits already in *status, so
 // all workgroups take the same commit-or-abort decision without a second kernel.  A
-// workgroup owns (lane, value head, 32-row block of the state).  It issues every load
+// workgroup owns (lane, value head, 64-row block of the state).  It issues every load
 // that does not need the slot id first, then its state block; every wave finds the
 // accepted path by pointer jumping over lane shuffles, and each thread loads the logged
 // g, k^ and delta values of its own state elements for every path node straight into
@@ -30,13 +30,17 @@ constexpr int kThreads = 256;
 constexpr int kBitmapSlots = 65536;  // duplicate-slot check via an LDS bitmap up to this pool size
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+// Four consecutive floats at a 4-byte-aligned address: log rows are 1 + d_k + d_v floats
+// long, so their k^ and delta slices carry no 16-byte alignment.  One dwordx4 load
+// (the HSA runtime runs in unaligned access mode).
+typedef float v4u __attribute__((ext_vector_type(4), aligned(4)));
 
 template <int DK, int DV>
 struct CommitCfg {
-    static constexpr int RB = DK < 32 ? DK : 32;  // state rows per workgroup
+    static constexpr int RB = DK < 64 ? DK : 64;  // state rows per workgroup
     static constexpr int NB = DK / RB;
     static constexpr int F4 = RB * DV / 4;        // 4-float groups per block
-    static constexpr int FPT = (F4 + kThreads - 1) / kThreads;
+    static constexpr int FPT = (F4 + kThreads - 1) / kThreads;  // state rows per thread
 };
 
 // Workgroup barrier for LDS communication only: waits for this wave's LDS operations,
@@ -78,6 +82,12 @@ __global__ __launch_bounds__(kThreads) void replay_commit_kernel(
     constexpr int RB = Cfg::RB, F4 = Cfg::F4, FPT = Cfg::FPT, R = 1 + DK + DV;
     constexpr int Q4 = DV / 4;
     static_assert(kThreads % Q4 == 0, "a thread keeps one 4-column group across its rows");
+    // Thread (w, q) = (tid / Q4, tid % Q4) owns the 4-column group q of the FPT consecutive
+    // rows w*FPT .. w*FPT+FPT-1 of the block (clamped to the last row where the block has
+    // fewer: surplus threads recompute and store identical values).  One load instruction
+    // u still covers whole rows, and the logged k^ values a thread needs are contiguous.
+    const int q = threadIdx.x % Q4, w = threadIdx.x / Q4;
+    auto row_of = [&](int u) { return min(w * FPT + u, RB - 1); };
     __shared__ unsigned int s_bitmap[kBitmapSlots / 32];
     __shared__ int s_wbits[kThreads / 64];
 
@@ -111,22 +121,21 @@ __global__ __launch_bounds__(kThreads) void replay_commit_kernel(
     v4f *S4 = reinterpret_cast<v4f *>(state_pool + (((int64_t)(s_ok ? s : 0) * Hv + h) * DK + r0) * DV);
     v4f sv[FPT];
 #pragma unroll
-    for (int u = 0; u < FPT; ++u) sv[u] = S4[min(tid + kThreads * u, F4 - 1)];
+    for (int u = 0; u < FPT; ++u) sv[u] = S4[row_of(u) * Q4 + q];
 
     // ---- accepted path (every wave computes it) and the replay of its logged rows.
     //      The transitions are linear, so S_final = G S0 + A with G the product of the
     //      path's g and A the same replay started from a zero state; A needs only the
     //      logged rows, so it is accumulated while the state block streams in.  Path nodes
-    //      are taken 8 at a time with all their loads issued together.
+    //      are taken 4 at a time with all their loads issued together (more would cost occupancy).
     const unsigned int pm = path_mask(par, lane, N, e);
-    const int q = tid % Q4;  // this thread's 4-column group (fixed across its rows)
     const float *logc = replay_log + ((int64_t)c * N * Hv + h) * R;
     v4f acc[FPT];
 #pragma unroll
     for (int u = 0; u < FPT; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
     float G = 1.0f;
     for (unsigned int bm = hist_copy ? 0u : pm; bm;) {
-        constexpr int kChunk = 8;
+        constexpr int kChunk = 4;
         float cg[kChunk], ck[kChunk][FPT];
         v4f cd[kChunk];
 #pragma unroll
@@ -136,14 +145,24 @@ __global__ __launch_bounds__(kThreads) void replay_commit_kernel(
             bm = has ? bm & (bm - 1u) : 0u;
             const float *lrow = logc + (int64_t)t * Hv * R;
             const float g = lrow[0];
-            const float d0 = lrow[1 + DK + 4 * q], d1 = lrow[2 + DK + 4 * q];
-            const float d2 = lrow[3 + DK + 4 * q], d3 = lrow[4 + DK + 4 * q];
+            const v4f dv4 = *reinterpret_cast<const v4u *>(lrow + 1 + DK + 4 * q);
             cg[j] = has ? g : 1.0f;
-            cd[j] = has ? v4f{d0, d1, d2, d3} : v4f{0.f, 0.f, 0.f, 0.f};
+            cd[j] = has ? dv4 : v4f{0.f, 0.f, 0.f, 0.f};
+            if constexpr (FPT % 4 == 0 && (kThreads / Q4) * FPT == RB) {  // no clamped rows: k^ as float4s
 #pragma unroll
-            for (int u = 0; u < FPT; ++u) {
-                const float kv = lrow[1 + r0 + min(tid + kThreads * u, F4 - 1) / Q4];
-                ck[j][u] = has ? kv : 0.f;
+                for (int u = 0; u < FPT; u += 4) {
+                    const v4f kv = *reinterpret_cast<const v4u *>(lrow + 1 + r0 + w * FPT + u);
+                    ck[j][u] = has ? kv.x : 0.f;
+                    ck[j][u + 1] = has ? kv.y : 0.f;
+                    ck[j][u + 2] = has ? kv.z : 0.f;
+                    ck[j][u + 3] = has ? kv.w : 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < FPT; ++u) {
+                    const float kv = lrow[1 + r0 + row_of(u)];
+                    ck[j][u] = has ? kv : 0.f;
+                }
             }
         }
 #pragma unroll
@@ -218,14 +237,12 @@ __global__ __launch_bounds__(kThreads) void replay_commit_kernel(
 
     // ---- S = G S0 + A, written back (non-temporal: the slot's state is read again only by
     // a later round's verify)
-    // (indices clamped as at load time: surplus threads recompute the last group from
-    // the same loaded values and store the identical result)
 #pragma unroll
     for (int u = 0; u < FPT; ++u) {
         const v4f v = sv[u];
         __builtin_nontemporal_store(
             v4f{fmaf(G, v.x, acc[u].x), fmaf(G, v.y, acc[u].y), fmaf(G, v.z, acc[u].z), fmaf(G, v.w, acc[u].w)},
-            S4 + min(tid + kThreads * u, F4 - 1));
+            S4 + row_of(u) * Q4 + q);
     }
 }
 
