@@ -23,22 +23,25 @@
 // once.  Decay ratios are exp(L_i - L_a) of cumulative log-decays, which cannot
 // overflow.
 //
-// Mapping: one workgroup (4 waves) per (lane, value head, block of 32 value columns).
+// Mapping: one workgroup (8 waves) per (lane, value head, block of 64 value columns).
 // Products run on v_mfma_f32_16x16x4_f32.  Within a 16-wide chunk of a contraction,
 // lane group g = lane/16 supplies index 4g + s in MFMA step s (a permutation shared by
 // both operands), so a tile's accumulators (lane holds rows 4g..4g+3 of column lane%16)
 // are directly the right operand of the next product, and the state block is loaded
 // from memory straight into that operand layout: no LDS copy, no transpose.  The
-// contraction over d_k is split by 16-row chunks across the waves (chunk q on wave
-// q mod 4) and the partial tiles are summed through LDS.  N is padded to NP (16 or 32)
-// with zero rows.  Barriers wait only for LDS traffic, so global loads stay in flight
-// across them.  Workgroup ids are ordered so that the workgroups sharing one (lane, q/k
-// head) are congruent modulo the number of such groups: with round-robin dispatch over
-// the 8 XCDs they land on one XCD and read the shared q/k rows through its L2.
+// contractions over d_k are split by 16-row chunks: the Gram products over waves 0..3
+// (chunk q on wave q mod 4), the state product over all 8 waves (wave w takes one
+// 16-column tile and every (8 / tiles)-th chunk), and the partial tiles are summed
+// through LDS.  N is padded to NP (16 or 32) with zero rows.  Barriers wait only for
+// LDS traffic, so global loads stay in flight across them.  Workgroup ids are ordered
+// so that the workgroups sharing one (lane, q/k head) are congruent modulo the number
+// of such groups: with round-robin dispatch over the 8 XCDs they land on one XCD and
+// read the shared q/k rows through its L2.
 //
 // Load order.  Every load that does not depend on the slot (tree, gates, token rows,
-// taps) is issued before the slot id is consumed; the slot-mapped history and state are
-// requested under a uniform branch right after, so their latency overlaps the token rows.
+// taps) is issued before the slot id is consumed and the slot-mapped history right
+// after it; the state block is requested only once the token rows are staged, so that
+// the rows the conv needs first do not queue behind it, and it arrives during the conv.
 //
 // Fused route (conv + verify, "perf(qwen35): fuse the DFlash2 concurrent verify Gated
 // DeltaNet route", Optimizations): the workgroup reads the raw projected tokens x of its
@@ -46,8 +49,8 @@
 // channels in registers (sources of node i, oldest first: the tokens of i's nearest
 // ancestors, then the slot's history columns), writing the results straight into the
 // product operands; the conv output never goes to memory.  The commit windows are
-// written once: value channels by their owning workgroup, the q/k channels split evenly
-// over the workgroups that share them.
+// written once, by copy-only workgroups appended to the same launch (one per lane and
+// block of channels), which run beside the verify workgroups.
 #include <utility>
 
 #include "gdn_internal.h"
