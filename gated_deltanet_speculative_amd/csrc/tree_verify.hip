@@ -202,14 +202,6 @@ __device__ inline v4f conv_silu(v4f x0, v4f x1, v4f x2, v4f x3, const v4f w[4]) 
     return y;
 }
 
-// window of 4 channels in the history layout [ch][3]: 12 consecutive floats
-__device__ inline void store_window(float *dst, v4f t1, v4f t2, v4f t3) {
-    v4f *w = reinterpret_cast<v4f *>(dst);
-    __builtin_nontemporal_store(v4f{t1.x, t2.x, t3.x, t1.y}, w);
-    __builtin_nontemporal_store(v4f{t2.y, t3.y, t1.z, t2.z}, w + 1);
-    __builtin_nontemporal_store(v4f{t3.z, t1.w, t2.w, t3.w}, w + 2);
-}
-
 // history columns of 4 channels from their 12 consecutive floats
 __device__ inline void hist_columns(const v4f raw[3], v4f hc[3]) {
     const v4f a = raw[0], b = raw[1], e = raw[2];  // ch0: a.x a.y a.z | ch1: a.w b.x b.y | ch2: b.z b.w e.x | ch3: e.y e.z e.w
@@ -737,7 +729,11 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs 
 // first: the tokens of its parent and grandparent, or the slot's newest history columns
 // in their place past the root, then the node's own tokens ("perf(qwen35): fuse the
 // DFlash2 concurrent verify Gated DeltaNet route", Optimizations, first bullet).
-// Nothing is written for a padding or invalid lane (the verify workgroups report it).
+// A node's windows are 3 * (kThreads / NP) consecutive 16-byte chunks; they go through a
+// wave-private transpose in LDS so that each store instruction writes consecutive chunks
+// from consecutive lanes (whole lines), which drains faster than 16-byte pieces at a
+// 48-byte lane stride.  Nothing is written for a padding or invalid lane (the verify
+// workgroups report it).
 template <int NP>
 __device__ __forceinline__ void window_body(const VerifyArgs &args, int b) {
     constexpr int GPB = kThreads / NP;  // 4-channel groups per workgroup
@@ -759,10 +755,11 @@ __device__ __forceinline__ void window_body(const VerifyArgs &args, int b) {
     const int a1 = __shfl(par, ic);
     const int a2s = __shfl(par, a1 >= 0 ? a1 : 0);
     const int a2 = a1 >= 0 ? a2s : -1;
-    if (i >= N || ch >= d.Ch) return;
-    const float *xr = args.x + (int64_t)c * N * d.Ch + ch;
-    const float *hr = args.conv_hist + ((int64_t)s * d.Ch + ch) * 3;
-    const v4f t3 = *reinterpret_cast<const v4f *>(xr + (int64_t)i * d.Ch);
+    // threads past the node count or the channel count load in-range rows and store nothing
+    const int chc = ch < d.Ch ? ch : 0;
+    const float *xr = args.x + (int64_t)c * N * d.Ch + chc;
+    const float *hr = args.conv_hist + ((int64_t)s * d.Ch + chc) * 3;
+    const v4f t3 = *reinterpret_cast<const v4f *>(xr + (int64_t)ic * d.Ch);
     v4f hraw[3];
 #pragma unroll
     for (int e = 0; e < 3; ++e) hraw[e] = reinterpret_cast<const v4f *>(hr)[e];
@@ -772,12 +769,30 @@ __device__ __forceinline__ void window_body(const VerifyArgs &args, int b) {
     const v4f x2 = *reinterpret_cast<const v4f *>(xr + (int64_t)(a2 >= 0 ? a2 : 0) * d.Ch);
     const v4f t2 = a1 >= 0 ? x1 : hc[2];
     const v4f t1 = a1 >= 0 ? (a2 >= 0 ? x2 : hc[2]) : hc[1];
-    store_window(args.commit_win + (((int64_t)c * N + i) * d.Ch + ch) * 3, t1, t2, t3);
+    // this thread's 12 window floats in the history layout [ch][3], as 3 chunks in LDS; the
+    // GPB threads of node i (within one wave) then store the node's 3 * GPB chunks in order
+    extern __shared__ float lds[];
+    v4f *chunks = reinterpret_cast<v4f *>(lds);
+    chunks[3 * tid] = v4f{t1.x, t2.x, t3.x, t1.y};
+    chunks[3 * tid + 1] = v4f{t2.y, t3.y, t1.z, t2.z};
+    chunks[3 * tid + 2] = v4f{t3.z, t1.w, t2.w, t3.w};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int gi = tid % GPB;
+    v4f *dst = reinterpret_cast<v4f *>(args.commit_win + (((int64_t)c * N + ic) * d.Ch + ch0) * 3);
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+        const int j = GPB * u + gi;  // chunk j holds part j % 3 of channel group j / 3
+        const v4f v = chunks[3 * (tid - gi) + j];
+        if (i < N && ch0 + 4 * (j / 3) < d.Ch) __builtin_nontemporal_store(v, dst + j);
+    }
 }
 
 template <int DK, int DV, int NP>
 __global__ __launch_bounds__(kThreads) void conv_tree_verify_kernel(const VerifyArgs args) {
     constexpr int NB = VerifyLayout<DK, DV, NP, true>::NB;
+    static_assert(kThreads * 12 <= VerifyLayout<DK, DV, NP, true>::LDS_FLOATS, "window chunks fit the LDS");
     const int n_verify = NB * args.d.Hv * args.d.C;
     if ((int)blockIdx.x < n_verify)
         verify_body<DK, DV, NP, true>(args);
