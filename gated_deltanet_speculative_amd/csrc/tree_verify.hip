@@ -62,6 +62,9 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+// four consecutive floats at a 4-byte-aligned address (one dwordx4 access: the HSA runtime
+// runs in unaligned access mode): replay-log rows are 1 + d_k + d_v floats long
+typedef float v4u __attribute__((ext_vector_type(4), aligned(4)));
 
 // Workgroup barrier for LDS communication only: waits for this wave's LDS operations,
 // not for its outstanding global loads, so prefetched data keeps streaming in.
@@ -668,21 +671,8 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     //      Waves 4..7, once per lane and value head: the replay-log header (g, k^) of every
     //      node (its stores go out beside the epilogue's).
     static_assert(CT <= 4, "epilogue waves");
-    if (wv_u >= 4) {
-        const int t4 = tid - 256;
-        constexpr int T4 = kThreads - 256;
-        if (jb == 0) {
-            float *logc = args.replay_log + ((int64_t)c * N * Hv + h) * R;
-            for (int f = t4; f < N * DK; f += T4) {
-                const int i = f / DK, e = f - i * DK;
-                float sq = s_ssq[i][0];
-                if constexpr (Ly::NPART > 1) sq += s_ssq[i][1];
-                float *lrow = logc + (int64_t)i * Hv * R;
-                __builtin_nontemporal_store(XQK[i * SX + e] * inv_norm(sq), lrow + 1 + e);
-                if (e == 0) __builtin_nontemporal_store(s_g[i], lrow);
-            }
-        }
-    }
+    static_assert(2 * NP * SV <= Ly::SCR, "output tiles fit the scratch");
+    float *Ot = scr, *Dt = scr + NP * SV;  // output and delta rows of the block, [NP][SV] each
     if (wave < CT) {
         const int nt = wave, jj = 16 * nt + l16;
         v4f dl[NT];
@@ -694,8 +684,6 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
                 dl[mt] = mfma4(*reinterpret_cast<const v4f *>(Tm + (16 * mt + l16) * SG + 16 * kt + 4 * g4), rhs[kt],
                                dl[mt]);
         }
-        float *logc = args.replay_log + ((int64_t)c * N * Hv + h) * R + 1 + DK + j0 + jj;
-        float *outc = args.out + ((int64_t)c * N * Hv + h) * DV + j0 + jj;
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt) {
             v4f o;
@@ -707,12 +695,39 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int i = 16 * mt + 4 * g4 + v;
-                if (i < N) {
-                    __builtin_nontemporal_store(dl[mt][v], logc + (int64_t)i * Hv * R);
-                    __builtin_nontemporal_store(o[v], outc + (int64_t)i * Hv * DV);
-                }
+                Ot[i * SV + jj] = o[v];
+                Dt[i * SV + jj] = dl[mt][v];
             }
         }
+    }
+    // waves 4..7, once per lane and value head: the replay-log header (g, k^) of every node
+    if (wv_u >= 4 && jb == 0) {
+        float *logc = args.replay_log + ((int64_t)c * N * Hv + h) * R;
+        for (int f = tid - 256; f < N * (DK / 4); f += kThreads - 256) {
+            const int i = f / (DK / 4), e4 = f - i * (DK / 4);
+            float sq = s_ssq[i][0];
+            if constexpr (Ly::NPART > 1) sq += s_ssq[i][1];
+            float *lrow = logc + (int64_t)i * Hv * R;
+            __builtin_nontemporal_store(*reinterpret_cast<const v4f *>(XQK + i * SX + 4 * e4) * inv_norm(sq),
+                                        reinterpret_cast<v4u *>(lrow + 1 + 4 * e4));
+            if (e4 == 0) __builtin_nontemporal_store(s_g[i], lrow);
+        }
+    }
+    lds_barrier();
+    // output rows and the log's delta rows of the block, in 16-byte chunks from consecutive
+    // lanes (whole lines per store instruction; a log row is 1 + d_k + d_v floats, so its
+    // chunks are only 4-byte aligned)
+    for (int f = tid; f < 2 * N * Q4; f += kThreads) {
+        const bool is_out = f < N * Q4;
+        const int ff = is_out ? f : f - N * Q4;
+        const int i = ff / Q4, q4 = ff - i * Q4;
+        const int64_t row = ((int64_t)c * N + i) * Hv + h;
+        if (is_out)
+            __builtin_nontemporal_store(*reinterpret_cast<const v4f *>(Ot + i * SV + 4 * q4),
+                                        reinterpret_cast<v4f *>(args.out + row * DV + j0 + 4 * q4));
+        else
+            __builtin_nontemporal_store(*reinterpret_cast<const v4f *>(Dt + i * SV + 4 * q4),
+                                        reinterpret_cast<v4u *>(args.replay_log + row * R + 1 + DK + j0 + 4 * q4));
     }
 }
 
