@@ -12,8 +12,13 @@ Sources (page title, then section):
          recurrence writing output + replay log; gates applied in-kernel),
          closing paragraph (tap/accumulation order kept; persistent state
          read-only during verification; replay-log commit advances it).
+  [P2] "Feature/support dflash2"
+       - deferred-state commit message: a step the drafter did not draft for commits
+         its post-step state to the slot immediately (the plain decode step).
   [P3] "qwen35: DSpark speculative decoding (Qwen3.8-27B drafters)"
        - raw-gate commit message: beta = sigmoid(b), gate = softplus(a + dt_bias) * A;
+       - DeltaNet-block commit message: one causal-conv step kernel (history window,
+         silu(conv), in-place history write-back) and the gated delta rule in place;
        - stacked-projection commit message: ssm_beta|ssm_alpha back to back,
          one l2_norm over the q|k slab, q/k heads broadcast (no repeat).
   [P4] "perf(qwen38): various DFlash2 optimizations concurrency C1-C5"
@@ -41,7 +46,10 @@ Readings where the pages are silent (each listed in the design notes):
   * lane validity: slot outside [-1, P), a slot used by two lanes, a parent
     outside [-1, i-1] or (commit only) an accept node outside [-1, N) sets a
     status bit; conv and verify then write nothing for that lane, and the
-    commit mutates nothing at all (all-or-nothing transaction).
+    commit mutates nothing at all (all-or-nothing transaction);
+  * the plain decode step (conv_step + decode_step) mutates the pools directly,
+    so it is a transaction like the commit: a bad slot anywhere, or a non-zero
+    incoming status, and nothing is written.
 
 Every function below is pinned by tests/test_oracle_pins.py against closed
 forms, library routines and brute force.
@@ -257,6 +265,82 @@ def replay_commit(replay_log, commit_win, slot_ids, parents, accept_node, state_
                 S = row[0] * S + np.outer(row[1:1 + d_k], row[1 + d_k:])
             state_pool[s, h] = S
         conv_hist[s] = commit_win[c, e]
+    return 0
+
+
+# ---------------------------------------------------------------- plain decode step
+def slot_preflight(slot_ids, n_slots, status_in=0):
+    """Status bits of a call that mutates the pools directly: slot range and duplicate
+    slots over every non-padding lane, OR-ed with status_in."""
+    bits = int(status_in)
+    C = len(slot_ids)
+    for c in range(C):
+        s = int(slot_ids[c])
+        if s == -1:
+            continue
+        if s < -1 or s >= n_slots:
+            bits |= STATUS_SLOT_RANGE
+        if any(int(slot_ids[o]) == s for o in range(C) if o != c):
+            bits |= STATUS_SLOT_DUP
+    return bits
+
+
+def conv_step(x, conv_w, conv_hist, slot_ids, conv_out, status_in=0):
+    """[P3] DeltaNet-block commit message: the causal-conv step of a decode or chain
+    verify (history window, silu(conv), in-place history write-back); [P5] ssm-conv.cu hunk.
+
+    x[c] holds a chain of N tokens for lane c (slot s).  With E the slot's history
+    columns followed by x[c, 0..N-1], conv_out[c, t] = silu(sum_j w[:, j] * E[t + j])
+    (the window ending at token t), and afterwards conv_hist[s] holds the last 3
+    columns of E.  If the preflight (slot range, duplicate slots, status_in) is not
+    clean nothing is written at all.  Mutates conv_hist / conv_out in place; returns
+    the status word.
+    """
+    x = np.asarray(x)
+    C, N, Ch = x.shape
+    W = D_CONV - 1
+    bits = slot_preflight(slot_ids, conv_hist.shape[0], status_in)
+    if bits:
+        return bits
+    for c in range(C):
+        s = int(slot_ids[c])
+        if s == -1:
+            continue
+        cols = [conv_hist[s][:, j].astype(np.float64) for j in range(W)]
+        cols += [x[c, t].astype(np.float64) for t in range(N)]
+        for t in range(N):
+            acc = np.zeros(Ch, dtype=np.float64)
+            for j in range(D_CONV):
+                acc = acc + conv_w[:, j].astype(np.float64) * cols[t + j]
+            conv_out[c, t] = silu(acc)
+        conv_hist[s] = np.stack(cols[-W:], axis=-1)
+    return 0
+
+
+def decode_step(qkv, beta_logits, alpha_logits, dt_bias, A, state_pool, slot_ids, n_k_heads, out, status_in=0):
+    """[P2] deferred-state commit message (a step without a draft commits its state at
+    once); [P3] raw-gate gated delta rule applied in place, no state copy.
+
+    One token per lane: qkv[c] is lane c's conv output row, beta_logits / alpha_logits
+    are [C, H_v].  For every non-padding lane (slot s) and value head h, token_step on
+    state_pool[s, h] replaces it in place and out[c, h] = o.  If the preflight (slot
+    range, duplicate slots, status_in) is not clean nothing is written at all.
+    Returns the status word.
+    """
+    P, H_v, d_k, d_v = state_pool.shape
+    bits = slot_preflight(slot_ids, P, status_in)
+    if bits:
+        return bits
+    for c in range(len(slot_ids)):
+        s = int(slot_ids[c])
+        if s == -1:
+            continue
+        for h in range(H_v):
+            q, k, v = split_qkv(np.asarray(qkv[c], np.float64), n_k_heads, H_v, d_k, d_v, h)
+            S_new, o, _, _, _ = token_step(state_pool[s, h].astype(np.float64), q, k, v, beta_logits[c, h],
+                                           alpha_logits[c, h], dt_bias[h], A[h])
+            state_pool[s, h] = S_new
+            out[c, h] = o
     return 0
 
 

@@ -430,3 +430,136 @@ def test_slot_permutation_equivariance():
     r2 = _round(case, pi[slots], parents, Hk, pool=pool2, hist=hist2)
     for name in ("conv_out", "commit_win", "out", "replay_log"):
         np.testing.assert_array_equal(r1[name], r2[name])
+
+
+# ------------------------------------------------------------------ plain decode step
+def _decode_case(rng, C, N, P, Hk, Hv, dk, dv):
+    case = _full_case(rng, C, N, P, Hk, Hv, dk, dv)
+    case["qkv"] = rng.standard_normal((C, case["x"].shape[2])).astype(np.float32)
+    return case
+
+
+@pytest.mark.parametrize("n", [1, 5])
+def test_conv_step_is_textbook_conv_with_history_shift(n):
+    """The chain conv step equals numpy.correlate over [history; tokens] followed by
+    SiLU, and leaves the slot holding the last 3 columns of that sequence."""
+    rng = np.random.default_rng(20 + n)
+    C, Ch, P = 3, 12, 4
+    x, w, hist, out, _ = _conv_case(rng, C, n, Ch, P, None)
+    slots = np.array([3, -1, 0], np.int32)
+    hist64 = hist.astype(np.float64)
+    assert O.conv_step(x, w, hist64, slots, out) == 0
+    for c in (0, 2):
+        s = slots[c]
+        for ch in range(Ch):
+            seq = np.concatenate([hist[s, ch].astype(np.float64), x[c, :, ch].astype(np.float64)])
+            z = np.correlate(seq, w[ch].astype(np.float64), mode="valid")
+            np.testing.assert_allclose(out[c, :, ch], z * special.expit(z), rtol=1e-13, atol=1e-14)
+            np.testing.assert_array_equal(hist64[s, ch], seq[-3:])
+    assert np.isnan(out[1]).all()  # padding lane
+    for s in (1, 2):  # unused slots keep their history
+        assert hist64[s].tobytes() == hist[s].astype(np.float64).tobytes()
+
+
+def test_conv_step_equals_tree_conv_of_a_chain():
+    """conv_step on a chain gives the tree conv's outputs, and the history it leaves is
+    the tree conv's commit window of the last token."""
+    rng = np.random.default_rng(26)
+    C, N, Ch, P = 2, 4, 10, 3
+    parents = np.tile(np.arange(-1, N - 1, dtype=np.int32), (C, 1))
+    x, w, hist, out, win = _conv_case(rng, C, N, Ch, P, parents)
+    slots = np.array([2, 1], np.int32)
+    assert O.conv_tree_step(x, w, hist, slots, parents, out, win) == 0
+    out2 = np.full_like(out, np.nan)
+    hist64 = hist.astype(np.float64)
+    assert O.conv_step(x, w, hist64, slots, out2) == 0
+    np.testing.assert_allclose(out2, out, rtol=1e-15, atol=0)
+    for c in range(C):
+        np.testing.assert_array_equal(hist64[slots[c]], win[c, N - 1])
+
+
+@pytest.mark.parametrize("bad,bit", [("slot_range", O.STATUS_SLOT_RANGE), ("slot_dup", O.STATUS_SLOT_DUP),
+                                     ("status_in", 0x100)])
+def test_plain_step_is_all_or_nothing(bad, bit):
+    rng = np.random.default_rng(27)
+    C, P, Hk, Hv, dk, dv = 3, 4, 1, 2, 8, 8
+    case = _decode_case(rng, C, 2, P, Hk, Hv, dk, dv)
+    slots = {"slot_range": [0, 4, 2], "slot_dup": [0, 2, 2], "status_in": [0, 1, 2]}[bad]
+    slots = np.array(slots, np.int32)
+    status_in = bit if bad == "status_in" else 0
+    hist = case["hist"].astype(np.float64)
+    out = np.full(case["x"].shape, np.nan)
+    assert O.conv_step(case["x"], case["conv_w"], hist, slots, out, status_in) & bit
+    assert np.isnan(out).all() and hist.tobytes() == case["hist"].astype(np.float64).tobytes()
+    pool = case["pool"].astype(np.float64)
+    o = np.full((C, Hv, dv), np.nan)
+    st = O.decode_step(case["qkv"], case["ba"][:, 0, :Hv], case["ba"][:, 0, Hv:], case["dt"], case["A"], pool, slots,
+                       Hk, o, status_in)
+    assert st & bit
+    assert np.isnan(o).all() and pool.tobytes() == case["pool"].astype(np.float64).tobytes()
+
+
+def test_decode_step_zero_beta_is_pure_decay():
+    """beta = 0 (b -> -inf): the state only decays, S' = g S, and the output reads it."""
+    rng = np.random.default_rng(28)
+    C, P, Hk, Hv, dk, dv = 1, 2, 1, 2, 8, 4
+    case = _decode_case(rng, C, 1, P, Hk, Hv, dk, dv)
+    b = np.full((C, Hv), -1e4)
+    a = case["ba"][:, 0, Hv:].astype(np.float64)
+    pool = case["pool"].astype(np.float64)
+    out = np.full((C, Hv, dv), np.nan)
+    with np.errstate(over="ignore"):  # sigmoid(-1e4) = 1 / (1 + inf) = 0 exactly
+        assert O.decode_step(case["qkv"], b, a, case["dt"], case["A"], pool, np.array([1], np.int32), Hk, out) == 0
+    for h in range(Hv):
+        g = np.exp(np.log1p(np.exp(a[0, h] + np.float64(case["dt"][h]))) * np.float64(case["A"][h]))
+        S0 = case["pool"][1, h].astype(np.float64)
+        np.testing.assert_allclose(pool[1, h], g * S0, rtol=1e-14)
+        q = case["qkv"][0, :dk].astype(np.float64)
+        np.testing.assert_allclose(out[0, h], g * S0.T @ (q / np.linalg.norm(q)) / np.sqrt(dk), rtol=1e-12)
+    assert pool[0].tobytes() == case["pool"][0].astype(np.float64).tobytes()
+
+
+def test_decode_step_stores_and_retrieves_one_association():
+    """Empty state, beta = 1 (b -> +inf) and q = k: the step writes k^ v^T and reads
+    back exactly v / sqrt(d_k), whatever the decay."""
+    rng = np.random.default_rng(29)
+    Hk, Hv, dk, dv = 1, 1, 16, 8
+    case = _decode_case(rng, 1, 1, 1, Hk, Hv, dk, dv)
+    qkv = case["qkv"].astype(np.float64)
+    qkv[0, :dk] = qkv[0, dk:2 * dk]  # q = k
+    pool = np.zeros((1, Hv, dk, dv))
+    out = np.full((1, Hv, dv), np.nan)
+    assert O.decode_step(qkv, np.full((1, Hv), 1e4), case["ba"][:, 0, Hv:], case["dt"], case["A"], pool,
+                         np.array([0], np.int32), Hk, out) == 0
+    k = qkv[0, dk:2 * dk]
+    v = qkv[0, 2 * dk:]
+    np.testing.assert_allclose(pool[0, 0], np.outer(k / np.linalg.norm(k), v), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(out[0, 0], v / np.sqrt(dk), rtol=1e-13)
+
+
+def test_decode_steps_equal_chain_verify_then_commit():
+    """k plain steps (conv step + decode step, one token at a time) leave the pools and
+    produce the outputs of a k-token chain verify followed by the commit of all k tokens."""
+    rng = np.random.default_rng(30)
+    C, N, P, Hk, Hv, dk, dv = 3, 4, 4, 2, 4, 8, 8
+    case = _full_case(rng, C, N, P, Hk, Hv, dk, dv)
+    slots = np.array([3, -1, 0], np.int32)
+    parents = np.tile(np.arange(-1, N - 1, dtype=np.int32), (C, 1))
+    r = _round(case, slots, parents, Hk)
+    assert r["status"] == 0
+    pool_v, hist_v = case["pool"].astype(np.float64), case["hist"].astype(np.float64)
+    assert O.replay_commit(r["replay_log"], r["commit_win"], slots, parents, np.array([N - 1, -1, N - 1], np.int32),
+                           pool_v, hist_v) == 0
+    pool_d, hist_d = case["pool"].astype(np.float64), case["hist"].astype(np.float64)
+    for t in range(N):
+        qkv = np.full((C, 1, case["x"].shape[2]), np.nan)
+        assert O.conv_step(case["x"][:, t:t + 1], case["conv_w"], hist_d, slots, qkv) == 0
+        out = np.full((C, Hv, dv), np.nan)
+        assert O.decode_step(qkv[:, 0], case["ba"][:, t, :Hv], case["ba"][:, t, Hv:], case["dt"], case["A"], pool_d,
+                             slots, Hk, out) == 0
+        for c in (0, 2):
+            np.testing.assert_allclose(qkv[c, 0], r["conv_out"][c, t], rtol=1e-14, atol=1e-15)
+            np.testing.assert_allclose(out[c], r["out"][c, t], rtol=1e-11, atol=1e-12)
+        assert np.isnan(out[1]).all()
+    np.testing.assert_allclose(pool_d, pool_v, rtol=1e-11, atol=1e-12)
+    np.testing.assert_array_equal(hist_d, hist_v)
