@@ -52,6 +52,9 @@ def parse():
                     help="one multi-layer commit launch per round, or one commit launch per instance")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, launch 4 plain device copies of this many MiB (counter calibration)")
+    ap.add_argument("--mode", choices=("verify", "decode"), default="verify",
+                    help="the speculative round (headline metric), or the plain decode step of a lane "
+                         "without a draft: conv step + one-token recurrence per instance, state in place")
     return ap.parse_args()
 
 
@@ -64,6 +67,32 @@ def algorithmic_bytes(wl, accept_depths):
     commit = sum(4 * (2 * Hv * dk * dv + 2 * W * Ch) + a * 4 * Hv * R for a in accept_depths if a > 0)
     # fused: the conv output is neither written nor read back
     return dict(conv=conv, verify=verify, conv_verify=conv + verify - 2 * 4 * C * N * Ch, commit=commit)
+
+
+def calibrate_copy(mib, dev):
+    """Four plain device copies of `mib` MiB: the counter-calibration reference of a
+    rocprofv3 --pmc run (no-op for 0)."""
+    if not mib:
+        return
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device=dev)
+    dst = torch.empty(n, device=dev)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def decode_bytes(wl):
+    """Algorithmic bytes of the plain decode step (one token per lane), every input read
+    once and every output written once: conv step = history read + written, token,
+    conv output, taps; recurrence = state read + written, conv row, gates, dt/A, output."""
+    C, Ch, Hv, dk, dv = wl.n_seqs, wl.channels, wl.n_v_heads, wl.d_k, wl.d_v
+    W = wl.d_conv - 1
+    conv = 4 * Ch * (C * (W + 1 + 1 + W) + wl.d_conv)
+    decode = 4 * (2 * C * Hv * dk * dv + C * Ch + 2 * C * Hv + 2 * Hv + C * Hv * dv)
+    return dict(conv_step=conv, decode_step=decode)
 
 
 def measured_traffic(workload, kernel):
@@ -106,12 +135,123 @@ def cpu_baseline(wl, seconds, seed):
                        f"{t_used:.1f} s")
 
 
+def decode_main(args):
+    """The plain decode step at the workload's head shape: one token per lane, for every
+    layer instance the conv step (history written in place) and the one-token recurrence
+    (state updated in place).  value = C * L / step time."""
+    import torch
+
+    import gated_deltanet_speculative_amd as gdn
+    from workloads import WORKLOADS, layer_params, round_inputs, round_structure
+
+    wl = WORKLOADS[args.workload]
+    sh = gdn.Shape(**dict(wl.shape_dict(), n_nodes=1))
+    C, P, Ch, Hv, dk, dv = sh.n_seqs, sh.n_slots, sh.channels, sh.n_v_heads, sh.d_k, sh.d_v
+    L = args.instances
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t_gen = time.time()
+    slot_ids = d(round_structure(wl, 0, args.seed)["slot_ids"])
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    inst = []
+    for l in range(L):
+        lp, ri = layer_params(wl, l, args.seed), round_inputs(wl, l, 0, args.seed)
+        ba = d(ri["ba"][:, 0])
+        inst.append(dict(x=d(ri["x"][:, :1]), beta=ba[:, :Hv], alpha=ba[:, Hv:], conv_w=d(lp["conv_w"]),
+                         conv_hist=d(lp["conv_hist"]), state=d(lp["state"]), dt_bias=d(lp["dt_bias"]), A=d(lp["A"]),
+                         qkv=torch.empty((C, 1, Ch), device=dev), out=torch.empty((C, Hv, dv), device=dev)))
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+
+    def conv(b):
+        gdn.conv_step(sh, b["x"], b["conv_w"], b["conv_hist"], slot_ids, status, conv_out=b["qkv"])
+
+    def rec(b):
+        gdn.decode_step(sh, b["qkv"][:, 0], b["beta"], b["alpha"], b["dt_bias"], b["A"], b["state"], slot_ids,
+                        status, out=b["out"])
+
+    def step():
+        for b in inst:
+            conv(b)
+            rec(b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "device status bits set"
+
+    def timed_graph(fn, reps):
+        run = fn
+        if not args.eager:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            run = g.replay
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps  # ms per replay
+
+    ms_step = timed_graph(step, args.steps)
+    kern = {}
+    if not args.profile_only:
+        kern["conv_step"] = timed_graph(lambda: [conv(b) for b in inst], args.kernel_reps) * 1e3 / L
+        kern["decode_step"] = timed_graph(lambda: [rec(b) for b in inst], args.kernel_reps) * 1e3 / L
+    assert int(status.item()) == 0, "device status bits set"
+    calibrate_copy(args.calibrate_copy, dev)
+    kb = decode_bytes(wl)
+    roofline = None
+    if kern:
+        dom = max(kern, key=lambda k: kern[k])
+        achieved = kb[dom] / (kern[dom] * 1e-6) / 1e9
+        roofline = dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(wl.name + "-decode", dom),
+                        bytes_per_launch=int(kb[dom]), us_per_launch=round(kern[dom], 3))
+    line = {
+        "metric": "GDN plain decode tokens/s (one token per lane, state committed in place)",
+        "value": round(C * L / (ms_step * 1e-3), 1),
+        "unit": "decode tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "timing": ("eager launches" if args.eager else "HIP graph replay of the whole step")
+                  + "; inputs resident in HBM",
+        "config": {"workload": wl.name + "-decode", "lanes": C, "tokens_per_lane": 1, "slots": P,
+                   "k_heads": wl.n_k_heads, "v_heads": Hv, "d_k": dk, "d_v": dv, "conv_channels": Ch,
+                   "layer_instances": L, "step": "conv step + one-token recurrence per instance"},
+        "step_gbs": round(L * (kb["conv_step"] + kb["decode_step"]) / (ms_step * 1e-3) / 1e9, 1),
+        "kernel_us": {k: round(v, 3) for k, v in kern.items()},
+        "kernel_gbs": {k: round(kb[k] / (kern[k] * 1e-6) / 1e9, 1) for k in kern},
+        "roofline": roofline,
+        "setup_s": round(t_gen, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the route needs no collective, "
               "so multi-GPU throughput is the per-GPU figure times the lane-sharded GPU count.", file=sys.stderr)
         sys.exit(2)
+    if args.mode == "decode":
+        decode_main(args)
+        return
 
     import torch
 
@@ -241,13 +381,7 @@ def main():
             torch.cuda.synchronize()
             kern[name] = ev0.elapsed_time(ev1) * 1e3 / (args.kernel_reps * L)  # us per layer instance
 
-    if args.calibrate_copy:
-        n = args.calibrate_copy * (1 << 20) // 4
-        src = torch.ones(n, device=dev)
-        dst = torch.empty(n, device=dev)
-        for _ in range(4):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+    calibrate_copy(args.calibrate_copy, dev)
 
     mean_depths = np.mean([np.mean(dd) for dd in depths]) if depths else 0.0
     ab = algorithmic_bytes(wl, [int(round(mean_depths))] * C)

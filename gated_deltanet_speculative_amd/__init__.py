@@ -9,6 +9,12 @@ include/gdn_verify.h (libgdnverify.so, hand-written gfx950 HIP kernels):
     replay_commit   -> advances state_pool / conv_hist of accepting slots
     replay_commit_layers -> the same for every layer of a round, one launch
 
+and, for a step without a draft (plain decode), two calls that advance the slots
+directly:
+
+    conv_step       -> conv_out; writes each slot's conv history in place
+    decode_step     -> out; applies one token to each slot's state in place
+
 The library is loaded on first use and must have been built
 (`python -m gated_deltanet_speculative_amd.build`); there is no fallback path.
 """
@@ -23,8 +29,10 @@ from ._lib import (  # noqa: F401
     STATUS_PARENT,
     STATUS_SLOT_DUP,
     STATUS_SLOT_RANGE,
+    conv_step,
     conv_tree_step,
     conv_tree_verify,
+    decode_step,
     load_library,
     replay_commit,
     replay_commit_layers,

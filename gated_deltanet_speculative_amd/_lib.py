@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libgdnverify.so")
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP, GDN_ERR_ALIGN = range(7)
 STATUS_SLOT_RANGE, STATUS_SLOT_DUP, STATUS_PARENT, STATUS_ACCEPT = 1, 2, 4, 8
 EXPORTED = ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_conv_tree_verify", "gdn_replay_commit",
-            "gdn_replay_commit_layers", "gdn_strerror")
+            "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step", "gdn_strerror")
 MAX_LAYERS = 64
 
 
@@ -77,8 +77,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdn_conv_tree_verify.argtypes = [sp, vp, vp, vp, vp, vp, i64] + [vp] * 10
     lib.gdn_replay_commit.argtypes = [sp] + [vp] * 9
     lib.gdn_replay_commit_layers.argtypes = [sp, i32] + [vp] * 9
+    lib.gdn_conv_step.argtypes = [sp] + [vp] * 7
+    lib.gdn_decode_step.argtypes = [sp, vp, vp, vp, i64] + [vp] * 7
     for f in ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_conv_tree_verify", "gdn_replay_commit",
-              "gdn_replay_commit_layers"):
+              "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step"):
         getattr(lib, f).restype = i32
     lib.gdn_strerror.argtypes = [ctypes.c_int]
     lib.gdn_strerror.restype = ctypes.c_char_p
@@ -295,3 +297,68 @@ def replay_commit_layers(sh: Shape, replay_logs, commit_wins, slot_ids, parents,
     _check(load_library().gdn_replay_commit_layers(ctypes.byref(cs), ctypes.c_int32(L), *args),
            "gdn_replay_commit_layers")
     return status
+
+
+# ---------------------------------------------------------------- plain decode step
+def _row_gate_view(t: torch.Tensor, name: str, sh: Shape) -> tuple:
+    """A [C, H_v] float32 view whose lane rows are `gate_stride` floats apart (e.g. one half
+    of the stacked beta|alpha projection of a one-token step).  Returns (pointer, stride)."""
+    if t.dtype != torch.float32 or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a float32 device tensor")
+    C, Hv = sh.n_seqs, sh.n_v_heads
+    if tuple(t.shape) != (C, Hv):
+        raise ValueError(f"{name}: expected shape {(C, Hv)}, got {tuple(t.shape)}")
+    s0, s1 = t.stride()
+    if s1 != 1:
+        raise ValueError(f"{name}: heads of one lane must be contiguous")
+    return t.data_ptr(), int(s0 if C > 1 else Hv)
+
+
+def conv_step(sh: Shape, x, conv_w, conv_hist, slot_ids, status, conv_out=None):
+    """Causal conv + SiLU over a chain of n_nodes tokens per lane, writing each slot's new
+    history into conv_hist in place (a transaction on the status word).  Returns conv_out."""
+    C, N, P, Ch = sh.n_seqs, sh.n_nodes, sh.n_slots, sh.channels
+    if status is None:
+        raise ValueError("conv_step needs a status word (it mutates the history pool)")
+    if conv_out is None:
+        conv_out = torch.empty((C, N, Ch), dtype=torch.float32, device=x.device)
+    args = [
+        _dev(x, "x", torch.float32, (C, N, Ch)),
+        _dev(conv_w, "conv_w", torch.float32, (Ch, sh.d_conv)),
+        _dev(conv_hist, "conv_hist", torch.float32, (P, Ch, sh.d_conv - 1)),
+        _dev(slot_ids, "slot_ids", torch.int32, (C,)),
+        _dev(conv_out, "conv_out", torch.float32, (C, N, Ch)),
+        _dev(status, "status", torch.int32, (1,)),
+        _stream(x),
+    ]
+    cs = sh.c_struct()
+    _check(load_library().gdn_conv_step(ctypes.byref(cs), *args), "gdn_conv_step")
+    return conv_out
+
+
+def decode_step(sh: Shape, qkv, beta_logits, alpha_logits, dt_bias, A, state_pool, slot_ids, status, out=None):
+    """One token of the recurrence per lane applied to the slots' states in place (n_nodes
+    must be 1).  qkv is [C, Ch]; beta/alpha logits are [C, H_v] views sharing one row
+    stride.  A transaction on the status word.  Returns out [C, H_v, d_v]."""
+    C, P, Hv, dk, dv = sh.n_seqs, sh.n_slots, sh.n_v_heads, sh.d_k, sh.d_v
+    if status is None:
+        raise ValueError("decode_step needs a status word (it mutates the state pool)")
+    if out is None:
+        out = torch.empty((C, Hv, dv), dtype=torch.float32, device=qkv.device)
+    bp, bs = _row_gate_view(beta_logits, "beta_logits", sh)
+    ap, as_ = _row_gate_view(alpha_logits, "alpha_logits", sh)
+    if bs != as_:
+        raise ValueError("beta_logits and alpha_logits must share one row stride")
+    args = [
+        _dev(qkv, "qkv", torch.float32, (C, sh.channels)), bp, ap, bs,
+        _dev(dt_bias, "dt_bias", torch.float32, (Hv,)),
+        _dev(A, "A", torch.float32, (Hv,)),
+        _dev(state_pool, "state_pool", torch.float32, (P, Hv, dk, dv)),
+        _dev(slot_ids, "slot_ids", torch.int32, (C,)),
+        _dev(out, "out", torch.float32, (C, Hv, dv)),
+        _dev(status, "status", torch.int32, (1,)),
+        _stream(qkv),
+    ]
+    cs = sh.c_struct()
+    _check(load_library().gdn_decode_step(ctypes.byref(cs), *args), "gdn_decode_step")
+    return out

@@ -14,6 +14,7 @@
 // issued together up front; tree ancestors are found with lane shuffles.  conv_out rows go out as
 // coalesced 16-byte stores; the commit window of 4 channels is 12 consecutive floats,
 // written as three 16-byte stores.
+#include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -24,18 +25,7 @@ constexpr int kChBlock = 64;           // channels per workgroup
 constexpr int kGroups = kChBlock / 4;  // 4-float channel groups per LDS row
 constexpr int kRowsPerPass = kThreads / kGroups;
 
-typedef float v4f __attribute__((ext_vector_type(4)));
-
 __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
-
-// Workgroup barrier for LDS communication only: waits for this wave's LDS operations,
-// not for its outstanding global loads.
-__device__ inline void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt left open
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 __global__ __launch_bounds__(kThreads) void conv_tree_step_kernel(
     Dims d, const float *__restrict__ x, const float *__restrict__ conv_w, const float *__restrict__ conv_hist,

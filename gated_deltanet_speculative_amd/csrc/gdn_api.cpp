@@ -221,6 +221,44 @@ int gdn_replay_commit(const gdn_shape *sh, const float *replay_log, const float 
                                     &conv_hist, status, stream);
 }
 
+int gdn_conv_step(const gdn_shape *sh, const float *x, const float *conv_w, float *conv_hist,
+                  const int32_t *slot_ids, float *conv_out, int32_t *status, hipStream_t stream) {
+    gdn::Dims d;
+    if (int r = check_shape(sh, &d)) return r;
+    if (!x || !conv_w || !conv_hist || !slot_ids || !conv_out || !status) return GDN_ERR_NULL;
+    if (!aligned({x, conv_w, conv_hist, conv_out}, 16) || !aligned({slot_ids, status}, 4)) return GDN_ERR_ALIGN;
+    const size_t cnc = (size_t)d.C * d.N * d.Ch;
+    if (any_alias({{conv_hist, (size_t)d.P * d.Ch * 3 * F}, {conv_out, cnc * F}, {status, I}},
+                  {{x, cnc * F}, {conv_w, (size_t)d.Ch * 4 * F}, {slot_ids, (size_t)d.C * I}}))
+        return GDN_ERR_ALIAS;
+    return gdn::launch_conv_step(d, x, conv_w, conv_hist, slot_ids, conv_out, status, stream) == hipSuccess
+               ? GDN_OK
+               : GDN_ERR_HIP;
+}
+
+int gdn_decode_step(const gdn_shape *sh, const float *qkv, const float *beta_logits, const float *alpha_logits,
+                    int64_t gate_stride, const float *dt_bias, const float *A, float *state_pool,
+                    const int32_t *slot_ids, float *out, int32_t *status, hipStream_t stream) {
+    gdn::Dims d;
+    if (int r = check_shape(sh, &d)) return r;
+    if (d.N != 1) return GDN_ERR_UNSUPPORTED;
+    if (!qkv || !beta_logits || !alpha_logits || !dt_bias || !A || !state_pool || !slot_ids || !out || !status)
+        return GDN_ERR_NULL;
+    if (gate_stride < d.Hv) return GDN_ERR_SHAPE;
+    if (!aligned({qkv, state_pool, out}, 16) || !aligned({beta_logits, alpha_logits, dt_bias, A, slot_ids, status}, 4))
+        return GDN_ERR_ALIGN;
+    const size_t gate_bytes = ((size_t)(d.C - 1) * (size_t)gate_stride + d.Hv) * F;
+    if (any_alias({{state_pool, (size_t)d.P * d.Hv * d.dk * d.dv * F}, {out, (size_t)d.C * d.Hv * d.dv * F},
+                   {status, I}},
+                  {{qkv, (size_t)d.C * d.Ch * F}, {beta_logits, gate_bytes}, {alpha_logits, gate_bytes},
+                   {dt_bias, (size_t)d.Hv * F}, {A, (size_t)d.Hv * F}, {slot_ids, (size_t)d.C * I}}))
+        return GDN_ERR_ALIAS;
+    return gdn::launch_decode_step(d, qkv, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids,
+                                   out, status, stream) == hipSuccess
+               ? GDN_OK
+               : GDN_ERR_HIP;
+}
+
 const char *gdn_strerror(int code) {
     switch (code) {
         case GDN_OK: return "success";

@@ -68,4 +68,12 @@ hipError_t launch_replay_commit(const Dims &d, int n_layers, const LayerPtrs &lp
                                 const int32_t *parents, const int32_t *accept_node, int32_t *status,
                                 hipStream_t stream);
 
+// Plain decode step: chain conv with in-place history write-back, then one token of the
+// recurrence applied to the slot's state in place.
+hipError_t launch_conv_step(const Dims &d, const float *x, const float *conv_w, float *conv_hist,
+                            const int32_t *slot_ids, float *conv_out, int32_t *status, hipStream_t stream);
+hipError_t launch_decode_step(const Dims &d, const float *qkv, const float *beta_logits, const float *alpha_logits,
+                              int64_t gate_stride, const float *dt_bias, const float *A, float *state_pool,
+                              const int32_t *slot_ids, float *out, int32_t *status, hipStream_t stream);
+
 }  // namespace gdn

@@ -21,6 +21,7 @@
 // state (the transitions are linear: S_final = G S0 + A).  After the preflight (barriers
 // wait for LDS traffic only) it writes G S0 + A back.
 // One extra workgroup row per lane copies the commit window into the history pool.
+#include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -29,12 +30,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBitmapSlots = 65536;  // duplicate-slot check via an LDS bitmap up to this pool size
 
-typedef float v4f __attribute__((ext_vector_type(4)));
-// Four consecutive floats at a 4-byte-aligned address: log rows are 1 + d_k + d_v floats
-// long, so their k^ and delta slices carry no 16-byte alignment.  One dwordx4 load
-// (the HSA runtime runs in unaligned access mode).
-typedef float v4u __attribute__((ext_vector_type(4), aligned(4)));
-
 template <int DK, int DV>
 struct CommitCfg {
     static constexpr int RB = DK < 64 ? DK : 64;  // state rows per workgroup
@@ -42,15 +37,6 @@ struct CommitCfg {
     static constexpr int F4 = RB * DV / 4;        // 4-float groups per block
     static constexpr int FPT = (F4 + kThreads - 1) / kThreads;  // state rows per thread
 };
-
-// Workgroup barrier for LDS communication only: waits for this wave's LDS operations,
-// not for its outstanding global loads, so requested state keeps streaming in.
-__device__ inline void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt left open
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 constexpr int kPreRows = 4;  // lanes' parent entries checked per thread in the first pass
 

@@ -53,6 +53,7 @@
 // block of channels), which run beside the verify workgroups.
 #include <utility>
 
+#include "gdn_device.h"
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -60,20 +61,6 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-
-typedef float v4f __attribute__((ext_vector_type(4)));
-// four consecutive floats at a 4-byte-aligned address (one dwordx4 access: the HSA runtime
-// runs in unaligned access mode): replay-log rows are 1 + d_k + d_v floats long
-typedef float v4u __attribute__((ext_vector_type(4), aligned(4)));
-
-// Workgroup barrier for LDS communication only: waits for this wave's LDS operations,
-// not for its outstanding global loads, so prefetched data keeps streaming in.
-__device__ inline void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt left open
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
 // Raw buffer resources: word 3 of the descriptor for the gfx9 family (32-bit data,
 // unswizzled); a load whose byte offset lies outside [0, num_records) returns zero and
@@ -138,16 +125,6 @@ __device__ inline v4f mfma4(v4f a, v4f b, v4f acc) {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
     return acc;
 }
-
-// 1 / max(|x|, 1e-6) from |x|^2, and the gate nonlinearities, on the hardware
-// transcendental units (about 1 ulp each; the outputs carry a 2e-4 tolerance)
-__device__ inline float inv_norm(float sq) { return fminf(__builtin_amdgcn_rsqf(sq), 1e6f); }
-__device__ inline float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
-__device__ inline float fast_softplus(float x) {
-    return fmaxf(x, 0.f) + 0.6931471805599453f * __builtin_amdgcn_logf(1.0f + fast_exp(-fabsf(x)));
-}
-__device__ inline float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + fast_exp(-x)); }
-__device__ inline float fast_silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + fast_exp(-z)); }
 
 // x[lane] + x[lane - SH] within each row of 16 lanes (0 past the row start): DPP row_shr
 template <int SH>

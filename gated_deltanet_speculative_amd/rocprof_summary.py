@@ -29,6 +29,8 @@ KERNEL_SOURCES = {  # (matched in this order: conv_tree_verify before tree_verif
     "conv_tree_step": "csrc/conv_tree_step.hip",
     "tree_verify": "csrc/tree_verify.hip",
     "replay_commit": "csrc/replay_commit.hip",
+    "decode_step": "csrc/decode_step.hip",
+    "conv_step": "csrc/decode_step.hip",
 }
 
 

@@ -16,6 +16,13 @@
  *   gdn_conv_tree_verify      the first two calls fused (conv output kept on chip);
  *   gdn_replay_commit_layers  the commit of every layer of a round in one launch.
  *
+ * A step without a draft (plain decode) skips verify and commit and advances the slots
+ * directly, also on one stream:
+ *   gdn_conv_step    causal conv + SiLU over a chain of tokens per lane, writing each
+ *                    slot's new conv history in place;
+ *   gdn_decode_step  one token of the gated delta rule applied to each slot's state in
+ *                    place, with the output row.
+ *
  * Sources (page title, then section):
  *   "perf(qwen35): fuse the DFlash2 concurrent verify Gated DeltaNet route",
  *       Summary and Optimizations (the three operations and their inputs/outputs),
@@ -41,15 +48,16 @@
  *     `stream` and returns without synchronising.  Verify and commit of a round
  *     must be issued on the same stream (or the caller orders them).
  *   - Output buffers must not overlap any input or each other (checked on byte
- *     ranges, GDN_ERR_ALIAS); the commit's two in-place pools must not overlap its
- *     inputs or each other.
+ *     ranges, GDN_ERR_ALIAS); the pools updated in place (by the commit and the plain
+ *     decode step) must not overlap their inputs or each other.
  *   - Dense float buffers (x, conv_w, conv_hist, conv_out, commit_win, qkv, state_pool,
  *     out) must be 16-byte aligned; every other buffer 4-byte aligned (GDN_ERR_ALIGN).
  *   - Host errors are returned synchronously and nothing is enqueued.
  *   - Lane errors found on the device are OR-ed into *status as GDN_STATUS_* bits
  *     (caller zeroes *status before the round).  Conv and verify write nothing for
- *     an offending lane; the commit mutates nothing at all if *status is non-zero
- *     after its preflight, including bits left there by the round's conv/verify.
+ *     an offending lane; the commit and the plain decode step mutate nothing at all
+ *     if *status is non-zero after their preflight, including bits left there by an
+ *     earlier call of the round.
  *   - A lane whose slot id is -1 is a padding lane: nothing is read or written for it.
  *
  * Notation: C = n_seqs lanes, N = n_nodes draft nodes per lane, P = n_slots pool
@@ -73,7 +81,8 @@ extern "C" {
 #define GDN_ERR_SHAPE 2       /* non-positive dimension, H_v % H_k != 0, gate_stride < H_v   */
 #define GDN_ERR_UNSUPPORTED 3 /* d_conv != 4, d_k/d_v not in {16,32,64,128}, N > 32, C > 1024,
                                  n_layers outside 1..GDN_MAX_LAYERS, Ch > 2^24, P*H_v > 2^24,
-                                 or one lane's commit windows above 1 GiB (N*Ch*12 bytes)     */
+                                 one lane's commit windows above 1 GiB (N*Ch*12 bytes), or
+                                 N != 1 for gdn_decode_step                                  */
 #define GDN_ERR_ALIAS 4       /* an output byte range overlaps an input or another output    */
 #define GDN_ERR_HIP 5         /* a kernel launch failed                                      */
 #define GDN_ERR_ALIGN 6       /* a dense float buffer is not 16-byte aligned, or an int32 /
@@ -223,6 +232,60 @@ int gdn_replay_commit_layers(const gdn_shape *sh, int32_t n_layers, const float 
                              const float *const *commit_wins, const int32_t *slot_ids, const int32_t *parents,
                              const int32_t *accept_node, float *const *state_pools, float *const *conv_hists,
                              int32_t *status, hipStream_t stream);
+
+/*
+ * Plain decode step, conv part ("qwen35: DSpark speculative decoding (Qwen3.8-27B
+ * drafters)", DeltaNet-block commit message: one causal-conv step kernel with history
+ * window, silu(conv) and in-place history write-back; tap order from
+ * "llama-cpp-bonsai-gdn-conv.patch", ssm-conv.cu hunk).
+ *
+ * x[c] is a chain of N = n_nodes tokens for lane c (slot s).  With E the slot's history
+ * columns conv_hist[s][:, 0..2] (oldest first) followed by x[c][0..N-1]:
+ *   conv_out[c][t][ch] = silu( sum_{j=0..3} conv_w[ch][j] * E[t + j][ch] )
+ * and afterwards conv_hist[s][ch][j] = E[N + j][ch], j = 0..2 (the last 3 columns,
+ * bit-exact copies).  A transaction: every non-padding lane's slot must lie in [0, P)
+ * and be used by no other lane, and *status must be zero on entry; otherwise the
+ * offending bits are OR-ed into *status and nothing is written at all.
+ *
+ *   x          [C][N][Ch]     tokens                                (read)
+ *   conv_w     [Ch][4]        depthwise taps                        (read)
+ *   conv_hist  [P][Ch][3]     persistent history pool, updated in place
+ *   slot_ids   [C]            int32, -1 = padding lane              (read)
+ *   conv_out   [C][N][Ch]     written for non-padding lanes
+ *   status     int32*, REQUIRED (GDN_ERR_NULL otherwise)
+ */
+int gdn_conv_step(const gdn_shape *sh, const float *x, const float *conv_w, float *conv_hist,
+                  const int32_t *slot_ids, float *conv_out, int32_t *status, hipStream_t stream);
+
+/*
+ * Plain decode step, recurrence part ("Feature/support dflash2", deferred-state commit
+ * message: a step the drafter did not draft for commits its post-step state to the slot
+ * immediately; "qwen35: DSpark speculative decoding", DeltaNet-block and raw-gate commit
+ * messages: the gated delta rule in place with the gates applied in-kernel).
+ *
+ * One token per lane (n_nodes must be 1, GDN_ERR_UNSUPPORTED otherwise).  For lane c
+ * (slot s) and value head h (q/k head kh = h % H_k), with q, k, v the head's slices of
+ * qkv[c], b = beta_logits[c*gate_stride + h], a = alpha_logits[c*gate_stride + h]:
+ *   q^ = q/|q|, k^ = k/|k|;  beta = sigmoid(b);  g = exp(softplus(a + dt_bias[h]) * A[h])
+ *   S' = g * state_pool[s][h];  delta = beta * (v - S'^T k^)
+ *   state_pool[s][h] = S' + k^ delta^T           (in place)
+ *   out[c][h] = state_pool[s][h]^T q^ / sqrt(d_k)
+ * A transaction with the same preflight as gdn_conv_step, so a step whose conv part
+ * failed leaves the state untouched too.
+ *
+ *   qkv            [C][Ch]             conv output row of each lane's token  (read)
+ *   beta_logits    element (c,h) at beta_logits[c*gate_stride + h]          (read)
+ *   alpha_logits   element (c,h) at alpha_logits[c*gate_stride + h]         (read)
+ *   gate_stride    >= H_v (2*H_v for the stacked b|a projection)
+ *   dt_bias, A     [H_v]                                                    (read)
+ *   state_pool     [P][H_v][d_k][d_v]  updated in place
+ *   slot_ids       [C]                 int32, -1 = padding lane             (read)
+ *   out            [C][H_v][d_v]       written for non-padding lanes
+ *   status         int32*, REQUIRED (GDN_ERR_NULL otherwise)
+ */
+int gdn_decode_step(const gdn_shape *sh, const float *qkv, const float *beta_logits, const float *alpha_logits,
+                    int64_t gate_stride, const float *dt_bias, const float *A, float *state_pool,
+                    const int32_t *slot_ids, float *out, int32_t *status, hipStream_t stream);
 
 /* Static description of a GDN_OK / GDN_ERR_* code. */
 const char *gdn_strerror(int code);

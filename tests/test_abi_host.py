@@ -209,3 +209,42 @@ def test_fused_rejections():
     assert _fused(sh, p, 8) == _lib.GDN_ERR_ALIAS
     p = _ptrs(13)
     assert _fused(sh, p, 8, status=p[2] + 4) == _lib.GDN_ERR_ALIAS  # status inside the history pool
+
+
+def _conv_step(sh, ptrs, status):
+    """ptrs: x, conv_w, conv_hist, slot_ids, conv_out"""
+    lib = gdn.load_library()
+    cs = sh.c_struct()
+    return lib.gdn_conv_step(ctypes.byref(cs), *ptrs, status, None)
+
+
+def _decode_step(sh, ptrs, gate_stride, status):
+    """ptrs: qkv, beta, alpha, dt_bias, A, state_pool, slot_ids, out"""
+    lib = gdn.load_library()
+    cs = sh.c_struct()
+    p = list(ptrs)
+    return lib.gdn_decode_step(ctypes.byref(cs), p[0], p[1], p[2], gate_stride, *p[3:], status, None)
+
+
+def test_plain_step_rejections():
+    st = FAKE + (1 << 40)
+    one = _shape(n_nodes=1)
+    assert _conv_step(_shape(), _ptrs(5), None) == _lib.GDN_ERR_NULL  # status is required
+    assert _decode_step(one, _ptrs(8), 8, None) == _lib.GDN_ERR_NULL
+    assert _decode_step(_shape(n_nodes=2), _ptrs(8), 8, st) == _lib.GDN_ERR_UNSUPPORTED  # one token only
+    assert _decode_step(one, _ptrs(8), 3, st) == _lib.GDN_ERR_SHAPE  # gate stride below H_v
+    assert _conv_step(_shape(d_conv=5), _ptrs(5), st) == _lib.GDN_ERR_UNSUPPORTED
+    p = _ptrs(5)
+    p[2] += 8  # history pool not 16-byte aligned
+    assert _conv_step(_shape(), p, st) == _lib.GDN_ERR_ALIGN
+    p = _ptrs(8)
+    p[5] += 4  # state pool not 16-byte aligned
+    assert _decode_step(one, p, 8, st) == _lib.GDN_ERR_ALIGN
+    p = _ptrs(5)
+    p[2] = p[0] + 64  # history pool (written in place) inside x
+    assert _conv_step(_shape(), p, st) == _lib.GDN_ERR_ALIAS
+    p = _ptrs(8)
+    p[5] = p[0] + 16  # state pool (written in place) over qkv
+    assert _decode_step(one, p, 8, st) == _lib.GDN_ERR_ALIAS
+    p = _ptrs(8)
+    assert _decode_step(one, p, 8, p[7] + 4) == _lib.GDN_ERR_ALIAS  # status inside out
