@@ -30,21 +30,34 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBitmapSlots = 65536;  // duplicate-slot check via an LDS bitmap up to this pool size
 constexpr int kTokChunk = 8;         // conv step: tokens loaded together
+constexpr int kLanesPerThread = (GDN_MAX_SEQS + kThreads - 1) / kThreads;
+
+// The slot ids of lanes tid, tid + kThreads, ... (for slot_preflight), loaded ahead of
+// the bulk loads so the preflight does not wait for them.
+struct LaneSlots {
+    int v[kLanesPerThread];
+    __device__ LaneSlots(const int32_t *__restrict__ slot_ids, int C) {
+#pragma unroll
+        for (int k = 0; k < kLanesPerThread; ++k) v[k] = slot_ids[min((int)threadIdx.x + kThreads * k, C - 1)];
+    }
+};
 
 // Slot preflight of a call that mutates the pools: GDN_STATUS_SLOT_RANGE /
 // GDN_STATUS_SLOT_DUP over every non-padding lane.  Every thread of the workgroup must
 // call it (it contains barriers); all threads receive the same bits.
-__device__ int slot_preflight(const int32_t *__restrict__ slot_ids, const Dims &d, unsigned int *bitmap,
-                              int *word) {
+__device__ int slot_preflight(const LaneSlots &ls, const int32_t *__restrict__ slot_ids, const Dims &d,
+                              unsigned int *bitmap, int *word) {
     const bool use_bitmap = d.P <= kBitmapSlots;
     if (use_bitmap)
         for (int w = threadIdx.x; w < (d.P + 31) / 32; w += kThreads) bitmap[w] = 0u;
     if (threadIdx.x == 0) *word = 0;
     lds_barrier();
     int bits = 0;
-    for (int t = threadIdx.x; t < d.C; t += kThreads) {
-        const int st = slot_ids[t];
-        if (st == -1) continue;
+#pragma unroll
+    for (int k = 0; k < kLanesPerThread; ++k) {
+        const int t = threadIdx.x + kThreads * k;
+        const int st = ls.v[k];
+        if (t >= d.C || st == -1) continue;
         if (st < -1 || st >= d.P) {
             bits |= GDN_STATUS_SLOT_RANGE;
         } else if (use_bitmap) {
@@ -60,6 +73,25 @@ __device__ int slot_preflight(const int32_t *__restrict__ slot_ids, const Dims &
     return *word;
 }
 
+// Sum over the lanes of a wave that share lane % Q (Q = 4 or 8): rotations within each
+// row of 16 lanes, then the row pairs and wave halves exchanged by permlane swaps (with
+// both operands equal, the two results of a swap add up to the pairwise sum).
+template <int M>
+__device__ inline float row_ror(float x) {  // lane (i - M) mod 16 of each row of 16 lanes (DPP row_ror)
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + M, 0xF, 0xF, false));
+}
+
+template <int Q>
+__device__ inline float sum_lanes_sharing(float x) {
+    static_assert(Q == 4 || Q == 8, "column groups per wave row");
+    if constexpr (Q == 4) x += row_ror<4>(x);
+    x += row_ror<8>(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // ---- conv step: thread = (lane c = blockIdx.y, 4-channel group g); the window slides
 //      over the chain in registers, oldest column first (tap 0 multiplies it).
 __global__ __launch_bounds__(kThreads) void conv_step_kernel(Dims d, const float *__restrict__ x,
@@ -71,6 +103,7 @@ __global__ __launch_bounds__(kThreads) void conv_step_kernel(Dims d, const float
     __shared__ int s_word;
     const int c = blockIdx.y, G4 = d.Ch / 4;
     const int g = blockIdx.x * kThreads + threadIdx.x, gc = g < G4 ? g : G4 - 1;
+    const LaneSlots lanes(slot_ids, d.C);
     const int s = slot_ids[c];
     const int st_in = *status;
     const bool s_ok = s >= 0 && s < d.P;
@@ -85,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void conv_step_kernel(Dims d, const float
 #pragma unroll
     for (int t = 0; t < kTokChunk; ++t) xt[t] = xr[(int64_t)min(t, d.N - 1) * G4];
 
-    const int bits = slot_preflight(slot_ids, d, s_bitmap, &s_word);
+    const int bits = slot_preflight(lanes, slot_ids, d, s_bitmap, &s_word);
     if (bits || st_in) {
         if (bits && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) atomicOr(status, bits);
         return;
@@ -155,14 +188,15 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     const int kh = h % d.Hk;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int q = tid % Q4, r = tid / Q4;
-    const int s = slot_ids[c];
+    // loads in the order they are needed, all issued before any is consumed: this lane's
+    // slot id (a vector load, so that its wait does not hold up the loads behind it),
+    // the preflight's slot ids, q / k rows, value columns and gates, then the state block
+    const int s_v = __builtin_bit_cast(
+        int, __builtin_amdgcn_raw_buffer_load_b32(
+                 __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(slot_ids), 0, 4 * d.C, 0x00020000), 4 * c, 0,
+                 0));
+    const LaneSlots lanes(slot_ids, d.C);
     const int st_in = *status;
-    const bool s_ok = s >= 0 && s < d.P;
-    // loads first: the state block (slot clamped into range), q / k rows, value columns, gates
-    v4f *S4 = reinterpret_cast<v4f *>(state_pool + ((int64_t)(s_ok ? s : 0) * d.Hv + h) * DK * DV + j0) + q;
-    v4f sv[RPT];
-#pragma unroll
-    for (int k = 0; k < RPT; ++k) sv[k] = S4[min(r + RG * k, DK - 1) * (DV / 4)];
     const float *row = qkv + (int64_t)c * d.Ch;
     v4f qk4 = {0.f, 0.f, 0.f, 0.f};
     if (wave < 2 && lane < DK / 4)  // wave 0: q row, wave 1: k row of q/k head kh
@@ -171,9 +205,16 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     const float braw = beta_logits[(int64_t)c * gate_stride + h];
     const float araw = alpha_logits[(int64_t)c * gate_stride + h] + dt_bias[h];
     const float Ah = A[h];
+    __builtin_amdgcn_sched_barrier(0);
+    const int s = __builtin_amdgcn_readfirstlane(s_v);
+    const bool s_ok = s >= 0 && s < d.P;
+    v4f *S4 = reinterpret_cast<v4f *>(state_pool + ((int64_t)(s_ok ? s : 0) * d.Hv + h) * DK * DV + j0) + q;
+    v4f sv[RPT];  // the state block (slot clamped into range; written back only if the step commits)
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) sv[k] = S4[min(r + RG * k, DK - 1) * (DV / 4)];
 
     if (wave < 2 && lane < DK / 4) reinterpret_cast<v4f *>(wave == 0 ? s_q : s_k)[lane] = qk4;
-    const int bits = slot_preflight(slot_ids, d, s_bitmap, &s_word);  // its barriers also publish s_q / s_k
+    const int bits = slot_preflight(lanes, slot_ids, d, s_bitmap, &s_word);  // its barriers also publish s_q / s_k
     if (bits || st_in) {
         if (bits && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) atomicOr(status, bits);
         return;
@@ -206,12 +247,9 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
         }
     }
 #pragma unroll
-    for (int m = Q4; m < 64; m <<= 1) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            pu[e] += __shfl_xor(pu[e], m);
-            pw[e] += __shfl_xor(pw[e], m);
-        }
+    for (int e = 0; e < 4; ++e) {
+        pu[e] = sum_lanes_sharing<Q4>(pu[e]);
+        pw[e] = sum_lanes_sharing<Q4>(pw[e]);
     }
     if (lane < Q4) {
         s_part[wave][0][q] = pu;
