@@ -17,6 +17,8 @@ Sources (page title, then section):
          its post-step state to the slot immediately (the plain decode step).
   [P3] "qwen35: DSpark speculative decoding (Qwen3.8-27B drafters)"
        - raw-gate commit message: beta = sigmoid(b), gate = softplus(a + dt_bias) * A;
+       - v_len commit message: verify and accept run over each lane's drafted length,
+         not the buffer-sizing length;
        - DeltaNet-block commit message: one causal-conv step kernel (history window,
          silu(conv), in-place history write-back) and the gated delta rule in place;
        - stacked-projection commit message: ssm_beta|ssm_alpha back to back,
@@ -43,9 +45,14 @@ Readings where the pages are silent (each listed in the design notes):
   * replay-log row = (g, k_hat[d_k], delta[d_v]): 1 + d_k + d_v floats (257 at 128);
   * accept_node[c] = deepest accepted node (-1 = nothing); the accepted path is
     that node's root path; a lane with slot -1 is padding and is never touched;
-  * lane validity: slot outside [-1, P), a slot used by two lanes, a parent
-    outside [-1, i-1] or (commit only) an accept node outside [-1, N) sets a
-    status bit; conv and verify then write nothing for that lane, and the
+  * ragged lanes: lane c may draft fewer than N nodes (lane_nodes[c], default
+    N); nodes i >= lane_nodes[c] are absent: never read, written or validated.
+    Parents precede children, so an absent node is never an ancestor of a
+    present one and the present nodes compute exactly what a lane_nodes[c]-node
+    batch would;
+  * lane validity: slot outside [-1, P), a slot used by two lanes, a node count
+    outside [0, N], a present node's parent outside [-1, i-1] or (commit only)
+    an accept node outside [-1, lane_nodes[c]) sets a status bit; conv and verify then write nothing for that lane, and the
     commit mutates nothing at all (all-or-nothing transaction);
   * the plain decode step (conv_step + decode_step) mutates the pools directly,
     so it is a transaction like the commit: a bad slot anywhere, or a non-zero
@@ -63,6 +70,7 @@ STATUS_SLOT_RANGE = 1
 STATUS_SLOT_DUP = 2
 STATUS_PARENT = 4
 STATUS_ACCEPT = 8
+STATUS_NODES = 16
 
 D_CONV = 4
 
@@ -107,10 +115,17 @@ def root_path(parents_row, node):
     return path[::-1]
 
 
-def lane_status(slot_ids, parents, n_slots):
-    """Per-lane status bits for conv and verify (padding lanes get 0 and are skipped)."""
+def lane_counts(lane_nodes, C, N):
+    """Nodes present in each lane: lane_nodes[c] (the lane's own draft length), or all N."""
+    return [N] * C if lane_nodes is None else [int(v) for v in lane_nodes]
+
+
+def lane_status(slot_ids, parents, n_slots, lane_nodes=None):
+    """Per-lane status bits for conv and verify (padding lanes get 0 and are skipped).
+    Only the present nodes' parents are checked; a node count outside [0, N] is an error."""
     slot_ids = np.asarray(slot_ids)
     C, N = np.asarray(parents).shape
+    counts = lane_counts(lane_nodes, C, N)
     bits = np.zeros(C, dtype=np.int64)
     for c in range(C):
         s = int(slot_ids[c])
@@ -120,7 +135,10 @@ def lane_status(slot_ids, parents, n_slots):
             bits[c] |= STATUS_SLOT_RANGE
         if any(int(slot_ids[o]) == s for o in range(C) if o != c):
             bits[c] |= STATUS_SLOT_DUP
-        for i in range(N):
+        if not 0 <= counts[c] <= N:
+            bits[c] |= STATUS_NODES
+            continue
+        for i in range(counts[c]):
             p = int(parents[c][i])
             if p < -1 or p >= i:
                 bits[c] |= STATUS_PARENT
@@ -128,27 +146,30 @@ def lane_status(slot_ids, parents, n_slots):
 
 
 # ---------------------------------------------------------------- conv tree step
-def conv_tree_step(x, conv_w, conv_hist, slot_ids, parents, conv_out, commit_win):
+def conv_tree_step(x, conv_w, conv_hist, slot_ids, parents, conv_out, commit_win, lane_nodes=None):
     """[P1] Optimizations, first bullet; [P5] ssm-conv.cu hunk.
 
     For lane c with slot s and node i, the extended sequence is the slot's
     history columns (oldest first) followed by the tokens on i's root path.
     conv_out[c,i,ch] = silu(sum_{j=0..3} w[ch,j] * E[-4+j][ch]) and
     commit_win[c,i,ch,:] = E[-3:][ch] (the history the slot would hold if i
-    were the last accepted node).  Writes only valid, non-padding lanes;
+    were the last accepted node).  Writes only valid, non-padding lanes and,
+    with lane_nodes, only their present nodes i < lane_nodes[c] ([P3] v_len
+    commit message: verify runs over the drafted length, not the buffer size);
     returns the OR of the lane status bits.
     """
     x = np.asarray(x)
     C, N, Ch = x.shape
     P = conv_hist.shape[0]
     W = D_CONV - 1
-    bits = lane_status(slot_ids, parents, P)
+    bits = lane_status(slot_ids, parents, P, lane_nodes)
+    counts = lane_counts(lane_nodes, C, N)
     for c in range(C):
         s = int(slot_ids[c])
         if s == -1 or bits[c]:
             continue
         hist_cols = [conv_hist[s][:, j].astype(np.float64) for j in range(W)]
-        for i in range(N):
+        for i in range(counts[c]):
             ext = hist_cols + [x[c, a].astype(np.float64) for a in root_path(parents[c], i)]
             win = ext[-D_CONV:]
             acc = np.zeros(Ch, dtype=np.float64)
@@ -190,7 +211,7 @@ def split_qkv(row, n_k_heads, n_v_heads, d_k, d_v, h):
 
 
 def tree_verify(qkv, beta_logits, alpha_logits, dt_bias, A, state_pool, slot_ids, parents,
-                n_k_heads, out, replay_log):
+                n_k_heads, out, replay_log, lane_nodes=None):
     """[P1] Optimizations, second and third bullets.
 
     Per valid lane c (slot s) and value head h, nodes in index order: the
@@ -198,18 +219,20 @@ def tree_verify(qkv, beta_logits, alpha_logits, dt_bias, A, state_pool, slot_ids
     parent node's state; apply token_step.  out[c,i,h] = o,
     replay_log[c,i,h] = (g, k_hat, delta).  state_pool is only read.
     beta_logits / alpha_logits are [C, N, H_v] arrays (the stacked projection's
-    two halves).  Returns the OR of the lane status bits.
+    two halves).  With lane_nodes only the present nodes i < lane_nodes[c] are
+    run and written.  Returns the OR of the lane status bits.
     """
     C, N, _ = qkv.shape
     P, H_v, d_k, d_v = state_pool.shape
-    bits = lane_status(slot_ids, parents, P)
+    bits = lane_status(slot_ids, parents, P, lane_nodes)
+    counts = lane_counts(lane_nodes, C, N)
     for c in range(C):
         s = int(slot_ids[c])
         if s == -1 or bits[c]:
             continue
         for h in range(H_v):
             states = {}
-            for i in range(N):
+            for i in range(counts[c]):
                 p = int(parents[c][i])
                 S_par = state_pool[s, h].astype(np.float64) if p == -1 else states[p]
                 q, k, v = split_qkv(qkv[c, i].astype(np.float64), n_k_heads, H_v, d_k, d_v, h)
@@ -224,23 +247,25 @@ def tree_verify(qkv, beta_logits, alpha_logits, dt_bias, A, state_pool, slot_ids
 
 
 # ---------------------------------------------------------------- commit
-def commit_preflight(slot_ids, parents, accept_node, n_slots, status_in=0):
-    """[P4] transaction preflight: status bits over all non-padding lanes, OR-ed with status_in."""
+def commit_preflight(slot_ids, parents, accept_node, n_slots, status_in=0, lane_nodes=None):
+    """[P4] transaction preflight: status bits over all non-padding lanes, OR-ed with status_in.
+    The accept node must be a present node of its lane (or -1)."""
     C, N = np.asarray(parents).shape
     bits = int(status_in)
-    lb = lane_status(slot_ids, parents, n_slots)
+    lb = lane_status(slot_ids, parents, n_slots, lane_nodes)
+    counts = lane_counts(lane_nodes, C, N)
     for c in range(C):
         if int(slot_ids[c]) == -1:
             continue
         bits |= int(lb[c])
         e = int(accept_node[c])
-        if e < -1 or e >= N:
+        if e < -1 or e >= min(max(counts[c], 0), N):
             bits |= STATUS_ACCEPT
     return bits
 
 
 def replay_commit(replay_log, commit_win, slot_ids, parents, accept_node, state_pool, conv_hist,
-                  status_in=0):
+                  status_in=0, lane_nodes=None):
     """[P1] closing paragraph; [P4] mechanism 3 and transaction preflight.
 
     If the preflight (including any bit already in status_in) is clean, every
@@ -250,7 +275,7 @@ def replay_commit(replay_log, commit_win, slot_ids, parents, accept_node, state_
     Mutates state_pool / conv_hist in place; returns the status word.
     """
     P, H_v, d_k, d_v = state_pool.shape
-    bits = commit_preflight(slot_ids, parents, accept_node, P, status_in)
+    bits = commit_preflight(slot_ids, parents, accept_node, P, status_in, lane_nodes)
     if bits:
         return bits
     for c in range(len(slot_ids)):
@@ -355,13 +380,14 @@ def new_outputs(C, N, Ch, H_v, d_k, d_v, fill=np.nan):
     )
 
 
-def verify_round(x, ba, conv_w, conv_hist, state_pool, dt_bias, A, slot_ids, parents, n_k_heads):
+def verify_round(x, ba, conv_w, conv_hist, state_pool, dt_bias, A, slot_ids, parents, n_k_heads,
+                 lane_nodes=None):
     """Conv then verify for one layer of one round; returns the float64 outputs and status."""
     C, N, Ch = x.shape
     P, H_v, d_k, d_v = state_pool.shape
     o = new_outputs(C, N, Ch, H_v, d_k, d_v)
-    st = conv_tree_step(x, conv_w, conv_hist, slot_ids, parents, o["conv_out"], o["commit_win"])
+    st = conv_tree_step(x, conv_w, conv_hist, slot_ids, parents, o["conv_out"], o["commit_win"], lane_nodes)
     st |= tree_verify(o["conv_out"], ba[:, :, :H_v], ba[:, :, H_v:], dt_bias, A, state_pool,
-                      slot_ids, parents, n_k_heads, o["out"], o["replay_log"])
+                      slot_ids, parents, n_k_heads, o["out"], o["replay_log"], lane_nodes)
     o["status"] = st
     return o

@@ -563,3 +563,70 @@ def test_decode_steps_equal_chain_verify_then_commit():
         assert np.isnan(out[1]).all()
     np.testing.assert_allclose(pool_d, pool_v, rtol=1e-11, atol=1e-12)
     np.testing.assert_array_equal(hist_d, hist_v)
+
+
+# ------------------------------------------------------------------ ragged lanes
+def _ragged_case():
+    rng = np.random.default_rng(90)
+    C, N, P, Hk, Hv, dk, dv = 4, 6, 6, 1, 2, 8, 8
+    case = _full_case(rng, C, N, P, Hk, Hv, dk, dv)
+    parents = np.array([[-1, 0, 1, 1, 3, 0], [-1, -1, 0, 2, 2, 4], [-1, 0, 0, 1, 2, 3], [-1, 0, 1, 2, 3, 4]],
+                       np.int32)
+    return case, parents, np.array([5, 0, 3, 2], np.int32), np.array([6, 2, 0, 3], np.int32), Hk
+
+
+def test_ragged_lane_equals_a_batch_of_its_own_length():
+    """A lane with v present nodes gives exactly the outputs of that lane run alone as a
+    v-node batch; absent nodes are never written, and garbage in their parents is ignored."""
+    case, parents, slots, counts, Hk = _ragged_case()
+    garbage = parents.copy()
+    for c in range(len(slots)):
+        garbage[c, counts[c]:] = 99  # absent nodes: not validated
+    r = O.verify_round(case["x"], case["ba"], case["conv_w"], case["hist"], case["pool"], case["dt"], case["A"],
+                       slots, garbage, Hk, lane_nodes=counts)
+    assert r["status"] == 0
+    for c in range(len(slots)):
+        v = int(counts[c])
+        for name in ("conv_out", "commit_win", "out", "replay_log"):
+            assert np.isnan(r[name][c, v:]).all()
+        if v == 0:
+            continue
+        alone = O.verify_round(case["x"][c:c + 1, :v], case["ba"][c:c + 1, :v], case["conv_w"], case["hist"],
+                               case["pool"], case["dt"], case["A"], slots[c:c + 1], parents[c:c + 1, :v], Hk)
+        assert alone["status"] == 0
+        for name in ("conv_out", "commit_win", "out", "replay_log"):
+            np.testing.assert_array_equal(r[name][c, :v], alone[name][0])
+
+
+@pytest.mark.parametrize("bad", [-1, 7])
+def test_ragged_lane_count_out_of_range(bad):
+    case, parents, slots, counts, Hk = _ragged_case()
+    counts = counts.copy()
+    counts[2] = bad
+    r = O.verify_round(case["x"], case["ba"], case["conv_w"], case["hist"], case["pool"], case["dt"], case["A"],
+                       slots, parents, Hk, lane_nodes=counts)
+    assert r["status"] == O.STATUS_NODES
+    assert np.isnan(r["out"][2]).all() and not np.isnan(r["out"][0]).any()
+
+
+def test_ragged_commit_accepts_only_present_nodes():
+    case, parents, slots, counts, Hk = _ragged_case()
+    r = O.verify_round(case["x"], case["ba"], case["conv_w"], case["hist"], case["pool"], case["dt"], case["A"],
+                       slots, parents, Hk, lane_nodes=counts)
+    pool, hist = case["pool"].astype(np.float64), case["hist"].astype(np.float64)
+    accept = np.array([5, 1, -1, 2], np.int32)  # the last present node of lanes 0, 1, 3; lane 2 has none
+    assert O.replay_commit(r["replay_log"], r["commit_win"], slots, parents, accept, pool, hist,
+                           lane_nodes=counts) == 0
+    for c, e in ((0, 5), (1, 1), (3, 2)):
+        S = case["pool"][slots[c]].astype(np.float64)
+        for t in O.root_path(parents[c], e):
+            for h in range(S.shape[0]):
+                row = r["replay_log"][c, t, h]
+                S[h] = row[0] * S[h] + np.outer(row[1:9], row[9:])
+        np.testing.assert_allclose(pool[slots[c]], S, rtol=1e-13)
+    assert pool[slots[2]].tobytes() == case["pool"][slots[2]].astype(np.float64).tobytes()
+    pool2, hist2 = case["pool"].astype(np.float64), case["hist"].astype(np.float64)
+    st = O.replay_commit(r["replay_log"], r["commit_win"], slots, parents, np.array([5, 2, -1, 2], np.int32), pool2,
+                         hist2, lane_nodes=counts)  # node 2 of lane 1 is absent
+    assert st == O.STATUS_ACCEPT
+    assert pool2.tobytes() == case["pool"].astype(np.float64).tobytes()
