@@ -52,21 +52,26 @@ def parse():
                     help="one multi-layer commit launch per round, or one commit launch per instance")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the run, launch 4 plain device copies of this many MiB (counter calibration)")
+    ap.add_argument("--ragged", action="store_true",
+                    help="verify mode: each round draws every lane's node count uniformly from 1..N (seeded) and "
+                         "accepts the lane's last node; throughput counts the present nodes")
     ap.add_argument("--mode", choices=("verify", "decode"), default="verify",
                     help="the speculative round (headline metric), or the plain decode step of a lane "
                          "without a draft: conv step + one-token recurrence per instance, state in place")
     return ap.parse_args()
 
 
-def algorithmic_bytes(wl, accept_depths):
-    """Every input read once and every output written once, at the library's layouts (fp32)."""
+def algorithmic_bytes(wl, accept_depths, lane_counts=None):
+    """Every input read once and every output written once, at the library's layouts (fp32).
+    lane_counts: nodes present per lane (ragged lanes; default N each)."""
     C, N, Ch, Hv, dk, dv = wl.n_seqs, wl.n_nodes, wl.channels, wl.n_v_heads, wl.d_k, wl.d_v
     W, R = wl.d_conv - 1, wl.log_row
-    conv = 4 * Ch * (C * (W + N + N + N * W) + wl.d_conv)
-    verify = 4 * (C * Hv * dk * dv + C * N * Ch + 2 * C * N * Hv + 2 * Hv + C * N * Hv * dv + C * N * Hv * R)
+    n = C * N if lane_counts is None else int(np.sum(lane_counts))  # present nodes of the round
+    conv = 4 * Ch * (C * W + n * (1 + 1 + W) + wl.d_conv)
+    verify = 4 * (C * Hv * dk * dv + n * Ch + 2 * n * Hv + 2 * Hv + n * Hv * dv + n * Hv * R)
     commit = sum(4 * (2 * Hv * dk * dv + 2 * W * Ch) + a * 4 * Hv * R for a in accept_depths if a > 0)
     # fused: the conv output is neither written nor read back
-    return dict(conv=conv, verify=verify, conv_verify=conv + verify - 2 * 4 * C * N * Ch, commit=commit)
+    return dict(conv=conv, verify=verify, conv_verify=conv + verify - 2 * 4 * n * Ch, commit=commit)
 
 
 def calibrate_copy(mib, dev):
@@ -271,8 +276,13 @@ def main():
     t_gen = time.time()
     rounds = [round_structure(wl, r, args.seed) for r in range(args.rounds)]
     slot_ids = d(rounds[0]["slot_ids"])
+    if args.ragged:  # per-lane node counts, and each lane accepts its last present node
+        for r, rd in enumerate(rounds):
+            rd["lane_nodes"] = np.random.default_rng([args.seed, 77, r]).integers(1, N + 1, size=C).astype(np.int32)
+            rd["accept_node"] = rd["lane_nodes"] - 1
     parents = [d(r["parents"]) for r in rounds]
     accepts = [d(r["accept_node"]) for r in rounds]
+    counts = [d(r["lane_nodes"]) if args.ragged else None for r in rounds]
     depths = [[len(path_to_root(r["parents"][c], int(e))) if e >= 0 else 0 for c, e in enumerate(r["accept_node"])]
               for r in rounds]
     status = torch.zeros(1, dtype=torch.int32, device=dev)  # the round's status word, shared by every layer
@@ -291,20 +301,20 @@ def main():
 
     def conv(b, r):
         gdn.conv_tree_step(sh, b["x"], b["conv_w"], b["conv_hist"], slot_ids, parents[r], conv_out=b["conv_out"],
-                           commit_win=b["commit_win"], status=status)
+                           commit_win=b["commit_win"], status=status, lane_nodes=counts[r])
 
     def verify(b, r):
         gdn.tree_verify(sh, b["conv_out"], b["beta"], b["alpha"], b["dt_bias"], b["A"], b["state"], slot_ids,
-                        parents[r], out=b["out"], replay_log=b["log"], status=status)
+                        parents[r], out=b["out"], replay_log=b["log"], status=status, lane_nodes=counts[r])
 
     def conv_verify(b, r):
         gdn.conv_tree_verify(sh, b["x"], b["conv_w"], b["conv_hist"], b["beta"], b["alpha"], b["dt_bias"], b["A"],
                              b["state"], slot_ids, parents[r], out=b["out"], replay_log=b["log"],
-                             commit_win=b["commit_win"], status=status)
+                             commit_win=b["commit_win"], status=status, lane_nodes=counts[r])
 
     def commit(b, r):
         gdn.replay_commit(sh, b["log"], b["commit_win"], slot_ids, parents[r], accepts[r], b["state"], b["conv_hist"],
-                          status)
+                          status, lane_nodes=counts[r])
 
     if L > gdn.MAX_LAYERS and args.commit == "layers":
         raise SystemExit(f"--instances {L} exceeds the {gdn.MAX_LAYERS} layers of one multi-layer commit")
@@ -312,7 +322,7 @@ def main():
 
     def commit_layers(r):
         gdn.replay_commit_layers(sh, layer_bufs["log"], layer_bufs["commit_win"], slot_ids, parents[r], accepts[r],
-                                 layer_bufs["state"], layer_bufs["conv_hist"], status)
+                                 layer_bufs["state"], layer_bufs["conv_hist"], status, lane_nodes=counts[r])
 
     def step(r):
         for b in inst:
@@ -384,8 +394,9 @@ def main():
     calibrate_copy(args.calibrate_copy, dev)
 
     mean_depths = np.mean([np.mean(dd) for dd in depths]) if depths else 0.0
-    ab = algorithmic_bytes(wl, [int(round(mean_depths))] * C)
-    ab_rounds = [algorithmic_bytes(wl, dd) for dd in depths]
+    # per-kernel times are taken on round 0: with ragged lanes its node counts set the bytes
+    ab = algorithmic_bytes(wl, [int(round(mean_depths))] * C, rounds[0].get("lane_nodes"))
+    ab_rounds = [algorithmic_bytes(wl, dd, rd.get("lane_nodes")) for dd, rd in zip(depths, rounds)]
     commit_bytes = float(np.mean([a["commit"] for a in ab_rounds]))
     kernel_bytes = {"conv_tree_step": ab["conv"], "tree_verify": ab["verify"], "conv_tree_verify": ab["conv_verify"],
                     "replay_commit": commit_bytes}
@@ -405,8 +416,10 @@ def main():
     if not args.no_cpu_baseline and not args.profile_only:
         cpu = cpu_baseline(wl, args.cpu_seconds, args.seed)
 
-    tokens = C * N * L
-    step_bytes = L * (ab["conv_verify"] if args.route == "fused" else ab["conv"] + ab["verify"]) + L * commit_bytes
+    present = [int(np.sum(rd["lane_nodes"])) if args.ragged else C * N for rd in rounds]
+    tokens = float(np.mean(present)) * L  # verified tokens per step (rounds cycle over the steps)
+    kv = [(a["conv_verify"] if args.route == "fused" else a["conv"] + a["verify"]) for a in ab_rounds]
+    step_bytes = L * float(np.mean(kv)) + L * commit_bytes
     line = {
         "metric": "GDN verify tokens/s (C=4, 16-node trees, d=128); achieved HBM GB/s vs peak",
         "value": round(tokens / (ms_step * 1e-3), 1),
@@ -425,12 +438,14 @@ def main():
                    "v_heads": Hv, "d_k": dk, "d_v": dv, "conv_channels": Ch, "layer_instances": L,
                    "step": ("fused conv+verify" if args.route == "fused" else "conv step + verify")
                            + " per instance, then " + ("one multi-layer commit" if args.commit == "layers"
-                                                      else "commit per instance")},
+                                                      else "commit per instance"),
+                   **({"ragged": "lane node counts uniform in 1..N, mean "
+                                 + f"{np.mean(present) / C:.2f} per lane"} if args.ragged else {})},
         "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "kernel_us": {k: round(v, 3) for k, v in kern.items()},
         "kernel_gbs": {k: round(kernel_bytes[k] / (kern[k] * 1e-6) / 1e9, 1) for k in kern},
-        "verify_only_tokens_per_s": (round(C * N / (sum(v for k, v in kern.items() if k != "replay_commit") * 1e-6), 1)
-                                     if kern else None),
+        "verify_only_tokens_per_s": (round(present[0] / (sum(v for k, v in kern.items() if k != "replay_commit")
+                                                         * 1e-6), 1) if kern else None),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "setup_s": round(t_gen, 1),

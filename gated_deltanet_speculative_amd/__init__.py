@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     MAX_LAYERS,
     Shape,
     STATUS_ACCEPT,
+    STATUS_NODES,
     STATUS_PARENT,
     STATUS_SLOT_DUP,
     STATUS_SLOT_RANGE,

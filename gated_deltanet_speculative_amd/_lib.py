@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdnverify.so")
 
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP, GDN_ERR_ALIGN = range(7)
-STATUS_SLOT_RANGE, STATUS_SLOT_DUP, STATUS_PARENT, STATUS_ACCEPT = 1, 2, 4, 8
+STATUS_SLOT_RANGE, STATUS_SLOT_DUP, STATUS_PARENT, STATUS_ACCEPT, STATUS_NODES = 1, 2, 4, 8, 16
 EXPORTED = ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_conv_tree_verify", "gdn_replay_commit",
             "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step", "gdn_strerror")
 MAX_LAYERS = 64
@@ -72,11 +72,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib = ctypes.CDLL(p)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     sp = ctypes.POINTER(_CShape)
-    lib.gdn_conv_tree_step.argtypes = [sp] + [vp] * 9
-    lib.gdn_tree_verify.argtypes = [sp, vp, vp, vp, i64] + [vp] * 9
-    lib.gdn_conv_tree_verify.argtypes = [sp, vp, vp, vp, vp, vp, i64] + [vp] * 10
-    lib.gdn_replay_commit.argtypes = [sp] + [vp] * 9
-    lib.gdn_replay_commit_layers.argtypes = [sp, i32] + [vp] * 9
+    lib.gdn_conv_tree_step.argtypes = [sp] + [vp] * 10
+    lib.gdn_tree_verify.argtypes = [sp, vp, vp, vp, i64] + [vp] * 10
+    lib.gdn_conv_tree_verify.argtypes = [sp, vp, vp, vp, vp, vp, i64] + [vp] * 11
+    lib.gdn_replay_commit.argtypes = [sp] + [vp] * 10
+    lib.gdn_replay_commit_layers.argtypes = [sp, i32] + [vp] * 10
     lib.gdn_conv_step.argtypes = [sp] + [vp] * 7
     lib.gdn_decode_step.argtypes = [sp, vp, vp, vp, i64] + [vp] * 7
     for f in ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_conv_tree_verify", "gdn_replay_commit",
@@ -130,6 +130,11 @@ def _gate_view(t: torch.Tensor, name: str, sh: Shape) -> tuple:
     return t.data_ptr(), int(stride)
 
 
+def _counts(lane_nodes, sh: Shape):
+    """Pointer to the per-lane node counts ([C] int32 device tensor), or None (every lane has N nodes)."""
+    return None if lane_nodes is None else _dev(lane_nodes, "lane_nodes", torch.int32, (sh.n_seqs,))
+
+
 def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
@@ -148,8 +153,9 @@ def _status(status: Optional[torch.Tensor], like: torch.Tensor) -> torch.Tensor:
 
 # ---------------------------------------------------------------- the three calls
 def conv_tree_step(sh: Shape, x, conv_w, conv_hist, slot_ids, parents, conv_out=None, commit_win=None,
-                   status=None):
-    """Tree conv + SiLU and commit windows; returns (conv_out, commit_win, status)."""
+                   status=None, lane_nodes=None):
+    """Tree conv + SiLU and commit windows; returns (conv_out, commit_win, status).
+    lane_nodes ([C] int32, optional): nodes present per lane (ragged lanes)."""
     C, N, P, Ch = sh.n_seqs, sh.n_nodes, sh.n_slots, sh.channels
     if conv_out is None:
         conv_out = torch.empty((C, N, Ch), dtype=torch.float32, device=x.device)
@@ -162,6 +168,7 @@ def conv_tree_step(sh: Shape, x, conv_w, conv_hist, slot_ids, parents, conv_out=
         _dev(conv_hist, "conv_hist", torch.float32, (P, Ch, sh.d_conv - 1)),
         _dev(slot_ids, "slot_ids", torch.int32, (C,)),
         _dev(parents, "parents", torch.int32, (C, N)),
+        _counts(lane_nodes, sh),
         _dev(conv_out, "conv_out", torch.float32, (C, N, Ch)),
         _dev(commit_win, "commit_win", torch.float32, (C, N, Ch, sh.d_conv - 1)),
         status.data_ptr(),
@@ -173,7 +180,7 @@ def conv_tree_step(sh: Shape, x, conv_w, conv_hist, slot_ids, parents, conv_out=
 
 
 def tree_verify(sh: Shape, qkv, beta_logits, alpha_logits, dt_bias, A, state_pool, slot_ids, parents, out=None,
-                replay_log=None, status=None):
+                replay_log=None, status=None, lane_nodes=None):
     """Read-only tree verify; beta/alpha logits are [C, N, H_v] views sharing one row stride
     (e.g. ba[..., :H_v] and ba[..., H_v:] of the stacked projection).  Returns (out, replay_log, status)."""
     C, N, P, Hv, dk, dv = sh.n_seqs, sh.n_nodes, sh.n_slots, sh.n_v_heads, sh.d_k, sh.d_v
@@ -193,6 +200,7 @@ def tree_verify(sh: Shape, qkv, beta_logits, alpha_logits, dt_bias, A, state_poo
         _dev(state_pool, "state_pool", torch.float32, (P, Hv, dk, dv)),
         _dev(slot_ids, "slot_ids", torch.int32, (C,)),
         _dev(parents, "parents", torch.int32, (C, N)),
+        _counts(lane_nodes, sh),
         _dev(out, "out", torch.float32, (C, N, Hv, dv)),
         _dev(replay_log, "replay_log", torch.float32, (C, N, Hv, sh.log_row)),
         status.data_ptr(),
@@ -204,7 +212,7 @@ def tree_verify(sh: Shape, qkv, beta_logits, alpha_logits, dt_bias, A, state_poo
 
 
 def conv_tree_verify(sh: Shape, x, conv_w, conv_hist, beta_logits, alpha_logits, dt_bias, A, state_pool, slot_ids,
-                     parents, out=None, replay_log=None, commit_win=None, status=None):
+                     parents, out=None, replay_log=None, commit_win=None, status=None, lane_nodes=None):
     """Fused tree conv + verify (the conv output stays on chip).  Returns
     (out, replay_log, commit_win, status)."""
     C, N, P, Hv, dk, dv, Ch = sh.n_seqs, sh.n_nodes, sh.n_slots, sh.n_v_heads, sh.d_k, sh.d_v, sh.channels
@@ -229,6 +237,7 @@ def conv_tree_verify(sh: Shape, x, conv_w, conv_hist, beta_logits, alpha_logits,
         _dev(state_pool, "state_pool", torch.float32, (P, Hv, dk, dv)),
         _dev(slot_ids, "slot_ids", torch.int32, (C,)),
         _dev(parents, "parents", torch.int32, (C, N)),
+        _counts(lane_nodes, sh),
         _dev(out, "out", torch.float32, (C, N, Hv, dv)),
         _dev(replay_log, "replay_log", torch.float32, (C, N, Hv, sh.log_row)),
         _dev(commit_win, "commit_win", torch.float32, (C, N, Ch, sh.d_conv - 1)),
@@ -241,7 +250,7 @@ def conv_tree_verify(sh: Shape, x, conv_w, conv_hist, beta_logits, alpha_logits,
 
 
 def replay_commit(sh: Shape, replay_log, commit_win, slot_ids, parents, accept_node, state_pool, conv_hist,
-                  status):
+                  status, lane_nodes=None):
     """Preflight + replay commit in place on state_pool / conv_hist; returns status."""
     C, N, P, Hv, dk, dv, Ch = sh.n_seqs, sh.n_nodes, sh.n_slots, sh.n_v_heads, sh.d_k, sh.d_v, sh.channels
     if status is None:
@@ -251,6 +260,7 @@ def replay_commit(sh: Shape, replay_log, commit_win, slot_ids, parents, accept_n
         _dev(commit_win, "commit_win", torch.float32, (C, N, Ch, sh.d_conv - 1)),
         _dev(slot_ids, "slot_ids", torch.int32, (C,)),
         _dev(parents, "parents", torch.int32, (C, N)),
+        _counts(lane_nodes, sh),
         _dev(accept_node, "accept_node", torch.int32, (C,)),
         _dev(state_pool, "state_pool", torch.float32, (P, Hv, dk, dv)),
         _dev(conv_hist, "conv_hist", torch.float32, (P, Ch, sh.d_conv - 1)),
@@ -263,7 +273,7 @@ def replay_commit(sh: Shape, replay_log, commit_win, slot_ids, parents, accept_n
 
 
 def replay_commit_layers(sh: Shape, replay_logs, commit_wins, slot_ids, parents, accept_node, state_pools,
-                         conv_hists, status):
+                         conv_hists, status, lane_nodes=None):
     """Preflight + replay commit of every layer of the round in one launch.
 
     replay_logs, commit_wins, state_pools and conv_hists are equal-length sequences
@@ -288,6 +298,7 @@ def replay_commit_layers(sh: Shape, replay_logs, commit_wins, slot_ids, parents,
         ctypes.cast(logs, ctypes.c_void_p), ctypes.cast(wins, ctypes.c_void_p),
         _dev(slot_ids, "slot_ids", torch.int32, (C,)),
         _dev(parents, "parents", torch.int32, (C, N)),
+        _counts(lane_nodes, sh),
         _dev(accept_node, "accept_node", torch.int32, (C,)),
         ctypes.cast(pools, ctypes.c_void_p), ctypes.cast(hists, ctypes.c_void_p),
         _dev(status, "status", torch.int32, (1,)),

@@ -29,8 +29,8 @@ __device__ inline float silu(float z) { return z / (1.0f + expf(-z)); }
 
 __global__ __launch_bounds__(kThreads) void conv_tree_step_kernel(
     Dims d, const float *__restrict__ x, const float *__restrict__ conv_w, const float *__restrict__ conv_hist,
-    const int32_t *__restrict__ slot_ids, const int32_t *__restrict__ parents, float *__restrict__ conv_out,
-    float *__restrict__ commit_win, int32_t *__restrict__ status) {
+    const int32_t *__restrict__ slot_ids, const int32_t *__restrict__ parents, const int32_t *__restrict__ lane_nodes,
+    float *__restrict__ conv_out, float *__restrict__ commit_win, int32_t *__restrict__ status) {
     extern __shared__ v4f rows4[];  // [3 + N][kGroups]: history columns 0..2, then token rows
     __shared__ int s_wbits[kThreads / 64];
 
@@ -44,6 +44,7 @@ __global__ __launch_bounds__(kThreads) void conv_tree_step_kernel(
     //      rows of the block (into LDS), the 4 taps of this thread's channel group
     const int lane = tid & 63;
     const int par = parents[(int64_t)c * N + (lane < N ? lane : 0)];  // lane i of every wave holds parent i
+    const int nv = lane_node_count(lane_nodes, d, c);                   // nodes present in this lane
     const int so = slot_ids[tid < d.C ? tid : 0];
     const v4f *x4 = reinterpret_cast<const v4f *>(x + ((int64_t)c * N) * Ch + ch0);
     const int q = tid % kGroups;  // this thread's channel group (fixed: 256 % 16 == 0)
@@ -63,16 +64,18 @@ __global__ __launch_bounds__(kThreads) void conv_tree_step_kernel(
     // ---- history block [ch][3] (contiguous), this thread's float of it
     const int hn = ng * 12;
     const float hv = conv_hist[((int64_t)(s_ok ? s : 0) * Ch + ch0) * 3 + (tid < hn ? tid : 0)];
-    // ---- lane validity (slot range, duplicate slot, parents); nothing is written for a bad lane
+    // ---- lane validity (slot range, duplicate slot, node count, present nodes' parents);
+    //      nothing is written for a bad lane
     int bits = s_ok ? 0 : GDN_STATUS_SLOT_RANGE;
     if (tid < d.C && tid != c && so == s) bits |= GDN_STATUS_SLOT_DUP;
     for (int o = tid + kThreads; o < d.C; o += kThreads)
         if (o != c && slot_ids[o] == s) bits |= GDN_STATUS_SLOT_DUP;
-    if (tid < N && (par < -1 || par >= tid)) bits |= GDN_STATUS_PARENT;
+    if (nv < 0 || nv > N) bits |= GDN_STATUS_NODES;
+    if (tid < nv && tid < N && (par < -1 || par >= tid)) bits |= GDN_STATUS_PARENT;
     {
         int wb = 0;
 #pragma unroll
-        for (int b = 0; b < 3; ++b)
+        for (int b = 0; b < 5; ++b)
             if (__builtin_amdgcn_ballot_w64((bits >> b) & 1)) wb |= 1 << b;
         if ((tid & 63) == 0) s_wbits[tid >> 6] = wb;
     }
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void conv_tree_step_kernel(
         const int n2 = n1 >= 0 ? n2s : -1;
         const int n3s = __shfl(par, n2 >= 0 ? n2 : 0);
         const int n3 = n2 >= 0 ? n3s : -1;
-        if (i >= N || q >= ng) continue;
+        if (i >= nv || q >= ng) continue;  // absent node (nv <= N: a bad count returned above)
         const int cnt = 1 + (n1 >= 0) + (n2 >= 0) + (n3 >= 0);
         const int nn[4] = {n0, n1, n2, n3};
         int src[4];
@@ -139,12 +142,12 @@ __global__ __launch_bounds__(kThreads) void conv_tree_step_kernel(
 }  // namespace
 
 hipError_t launch_conv_tree_step(const Dims &d, const float *x, const float *conv_w, const float *conv_hist,
-                                 const int32_t *slot_ids, const int32_t *parents, float *conv_out,
-                                 float *commit_win, int32_t *status, hipStream_t stream) {
+                                 const int32_t *slot_ids, const int32_t *parents, const int32_t *lane_nodes,
+                                 float *conv_out, float *commit_win, int32_t *status, hipStream_t stream) {
     const dim3 grid((d.Ch + kChBlock - 1) / kChBlock, d.C);
     const size_t lds = sizeof(v4f) * (3 + d.N) * kGroups;
     hipLaunchKernelGGL(conv_tree_step_kernel, grid, dim3(kThreads), lds, stream, d, x, conv_w, conv_hist, slot_ids,
-                       parents, conv_out, commit_win, status);
+                       parents, lane_nodes, conv_out, commit_win, status);
     return hipGetLastError();
 }
 

@@ -61,28 +61,28 @@ constexpr size_t F = sizeof(float), I = sizeof(int32_t);
 extern "C" {
 
 int gdn_conv_tree_step(const gdn_shape *sh, const float *x, const float *conv_w, const float *conv_hist,
-                       const int32_t *slot_ids, const int32_t *parents, float *conv_out, float *commit_win,
-                       int32_t *status, hipStream_t stream) {
+                       const int32_t *slot_ids, const int32_t *parents, const int32_t *lane_nodes, float *conv_out,
+                       float *commit_win, int32_t *status, hipStream_t stream) {
     gdn::Dims d;
     if (int r = check_shape(sh, &d)) return r;
     if (!x || !conv_w || !conv_hist || !slot_ids || !parents || !conv_out || !commit_win) return GDN_ERR_NULL;
-    if (!aligned({x, conv_w, conv_hist, conv_out, commit_win}, 16) || !aligned({slot_ids, parents, status}, 4))
+    if (!aligned({x, conv_w, conv_hist, conv_out, commit_win}, 16) || !aligned({slot_ids, parents, lane_nodes, status}, 4))
         return GDN_ERR_ALIGN;
     const size_t cnc = (size_t)d.C * d.N * d.Ch;
     if (any_alias({{conv_out, cnc * F}, {commit_win, cnc * 3 * F}, {status, I}},
                   {{x, cnc * F}, {conv_w, (size_t)d.Ch * 4 * F}, {conv_hist, (size_t)d.P * d.Ch * 3 * F},
-                   {slot_ids, (size_t)d.C * I}, {parents, (size_t)d.C * d.N * I}}))
+                   {slot_ids, (size_t)d.C * I}, {parents, (size_t)d.C * d.N * I}, {lane_nodes, (size_t)d.C * I}}))
         return GDN_ERR_ALIAS;
-    return gdn::launch_conv_tree_step(d, x, conv_w, conv_hist, slot_ids, parents, conv_out, commit_win, status,
-                                      stream) == hipSuccess
+    return gdn::launch_conv_tree_step(d, x, conv_w, conv_hist, slot_ids, parents, lane_nodes, conv_out, commit_win,
+                                      status, stream) == hipSuccess
                ? GDN_OK
                : GDN_ERR_HIP;
 }
 
 int gdn_tree_verify(const gdn_shape *sh, const float *qkv, const float *beta_logits, const float *alpha_logits,
                     int64_t gate_stride, const float *dt_bias, const float *A, const float *state_pool,
-                    const int32_t *slot_ids, const int32_t *parents, float *out, float *replay_log,
-                    int32_t *status, hipStream_t stream) {
+                    const int32_t *slot_ids, const int32_t *parents, const int32_t *lane_nodes, float *out,
+                    float *replay_log, int32_t *status, hipStream_t stream) {
     gdn::Dims d;
     if (int r = check_shape(sh, &d)) return r;
     if (!qkv || !beta_logits || !alpha_logits || !dt_bias || !A || !state_pool || !slot_ids || !parents || !out ||
@@ -90,7 +90,7 @@ int gdn_tree_verify(const gdn_shape *sh, const float *qkv, const float *beta_log
         return GDN_ERR_NULL;
     if (gate_stride < d.Hv) return GDN_ERR_SHAPE;
     if (!aligned({qkv, state_pool, out}, 16) ||
-        !aligned({beta_logits, alpha_logits, dt_bias, A, slot_ids, parents, replay_log, status}, 4))
+        !aligned({beta_logits, alpha_logits, dt_bias, A, slot_ids, parents, lane_nodes, replay_log, status}, 4))
         return GDN_ERR_ALIGN;
     const size_t rows = (size_t)d.C * d.N;
     const size_t gate_bytes = ((rows - 1) * (size_t)gate_stride + d.Hv) * F;
@@ -99,7 +99,7 @@ int gdn_tree_verify(const gdn_shape *sh, const float *qkv, const float *beta_log
                   {{qkv, rows * d.Ch * F}, {beta_logits, gate_bytes}, {alpha_logits, gate_bytes},
                    {dt_bias, (size_t)d.Hv * F}, {A, (size_t)d.Hv * F},
                    {state_pool, (size_t)d.P * d.Hv * d.dk * d.dv * F}, {slot_ids, (size_t)d.C * I},
-                   {parents, rows * I}}))
+                   {parents, rows * I}, {lane_nodes, (size_t)d.C * I}}))
         return GDN_ERR_ALIAS;
     gdn::VerifyArgs a{};
     a.d = d;
@@ -112,6 +112,7 @@ int gdn_tree_verify(const gdn_shape *sh, const float *qkv, const float *beta_log
     a.state_pool = state_pool;
     a.slot_ids = slot_ids;
     a.parents = parents;
+    a.lane_nodes = lane_nodes;
     a.out = out;
     a.replay_log = replay_log;
     a.status = status;
@@ -121,8 +122,8 @@ int gdn_tree_verify(const gdn_shape *sh, const float *qkv, const float *beta_log
 int gdn_conv_tree_verify(const gdn_shape *sh, const float *x, const float *conv_w, const float *conv_hist,
                          const float *beta_logits, const float *alpha_logits, int64_t gate_stride,
                          const float *dt_bias, const float *A, const float *state_pool, const int32_t *slot_ids,
-                         const int32_t *parents, float *out, float *replay_log, float *commit_win, int32_t *status,
-                         hipStream_t stream) {
+                         const int32_t *parents, const int32_t *lane_nodes, float *out, float *replay_log,
+                         float *commit_win, int32_t *status, hipStream_t stream) {
     gdn::Dims d;
     if (int r = check_shape(sh, &d)) return r;
     if (!x || !conv_w || !conv_hist || !beta_logits || !alpha_logits || !dt_bias || !A || !state_pool ||
@@ -130,7 +131,7 @@ int gdn_conv_tree_verify(const gdn_shape *sh, const float *x, const float *conv_
         return GDN_ERR_NULL;
     if (gate_stride < d.Hv) return GDN_ERR_SHAPE;
     if (!aligned({x, conv_w, conv_hist, state_pool, out, commit_win}, 16) ||
-        !aligned({beta_logits, alpha_logits, dt_bias, A, slot_ids, parents, replay_log, status}, 4))
+        !aligned({beta_logits, alpha_logits, dt_bias, A, slot_ids, parents, lane_nodes, replay_log, status}, 4))
         return GDN_ERR_ALIGN;
     const size_t rows = (size_t)d.C * d.N;
     const size_t gate_bytes = ((rows - 1) * (size_t)gate_stride + d.Hv) * F;
@@ -140,7 +141,7 @@ int gdn_conv_tree_verify(const gdn_shape *sh, const float *x, const float *conv_
                   {{x, rows * d.Ch * F}, {conv_w, (size_t)d.Ch * 4 * F}, {conv_hist, (size_t)d.P * d.Ch * 3 * F},
                    {beta_logits, gate_bytes}, {alpha_logits, gate_bytes}, {dt_bias, (size_t)d.Hv * F},
                    {A, (size_t)d.Hv * F}, {state_pool, (size_t)d.P * d.Hv * d.dk * d.dv * F},
-                   {slot_ids, (size_t)d.C * I}, {parents, rows * I}}))
+                   {slot_ids, (size_t)d.C * I}, {parents, rows * I}, {lane_nodes, (size_t)d.C * I}}))
         return GDN_ERR_ALIAS;
     gdn::VerifyArgs a{};
     a.d = d;
@@ -156,6 +157,7 @@ int gdn_conv_tree_verify(const gdn_shape *sh, const float *x, const float *conv_
     a.state_pool = state_pool;
     a.slot_ids = slot_ids;
     a.parents = parents;
+    a.lane_nodes = lane_nodes;
     a.out = out;
     a.replay_log = replay_log;
     a.status = status;
@@ -164,8 +166,8 @@ int gdn_conv_tree_verify(const gdn_shape *sh, const float *x, const float *conv_
 
 int gdn_replay_commit_layers(const gdn_shape *sh, int32_t n_layers, const float *const *replay_logs,
                              const float *const *commit_wins, const int32_t *slot_ids, const int32_t *parents,
-                             const int32_t *accept_node, float *const *state_pools, float *const *conv_hists,
-                             int32_t *status, hipStream_t stream) {
+                             const int32_t *lane_nodes, const int32_t *accept_node, float *const *state_pools,
+                             float *const *conv_hists, int32_t *status, hipStream_t stream) {
     gdn::Dims d;
     if (int r = check_shape(sh, &d)) return r;
     if (n_layers < 1 || n_layers > GDN_MAX_LAYERS) return GDN_ERR_UNSUPPORTED;
@@ -186,13 +188,13 @@ int gdn_replay_commit_layers(const gdn_shape *sh, int32_t n_layers, const float 
         lp.state_pool[l] = state_pools[l];
         lp.conv_hist[l] = conv_hists[l];
     }
-    if (!aligned({slot_ids, parents, accept_node, status}, 4)) return GDN_ERR_ALIGN;
+    if (!aligned({slot_ids, parents, lane_nodes, accept_node, status}, 4)) return GDN_ERR_ALIGN;
     // every layer's pools against every input, the status word and every other layer's pools
     for (int l = 0; l < n_layers; ++l) {
         const Range outs[2] = {{state_pools[l], pool_b}, {conv_hists[l], hist_b}};
         for (const Range &o : outs) {
             if (any_alias({o, {status, I}}, {{slot_ids, (size_t)d.C * I}, {parents, rows * I},
-                                              {accept_node, (size_t)d.C * I}}))
+                                              {lane_nodes, (size_t)d.C * I}, {accept_node, (size_t)d.C * I}}))
                 return GDN_ERR_ALIAS;
             for (int m = 0; m < n_layers; ++m) {
                 if (overlap(o, {replay_logs[m], log_b}) || overlap(o, {commit_wins[m], win_b})) return GDN_ERR_ALIAS;
@@ -204,21 +206,23 @@ int gdn_replay_commit_layers(const gdn_shape *sh, int32_t n_layers, const float 
             }
         }
     }
-    return gdn::launch_replay_commit(d, n_layers, lp, slot_ids, parents, accept_node, status, stream) == hipSuccess
+    return gdn::launch_replay_commit(d, n_layers, lp, slot_ids, parents, lane_nodes, accept_node, status, stream) ==
+                   hipSuccess
                ? GDN_OK
                : GDN_ERR_HIP;
 }
 
 int gdn_replay_commit(const gdn_shape *sh, const float *replay_log, const float *commit_win,
-                      const int32_t *slot_ids, const int32_t *parents, const int32_t *accept_node,
-                      float *state_pool, float *conv_hist, int32_t *status, hipStream_t stream) {
+                      const int32_t *slot_ids, const int32_t *parents, const int32_t *lane_nodes,
+                      const int32_t *accept_node, float *state_pool, float *conv_hist, int32_t *status,
+                      hipStream_t stream) {
     if (!replay_log || !commit_win || !state_pool || !conv_hist) {
         gdn::Dims d;
         if (int r = check_shape(sh, &d)) return r;
         return GDN_ERR_NULL;
     }
-    return gdn_replay_commit_layers(sh, 1, &replay_log, &commit_win, slot_ids, parents, accept_node, &state_pool,
-                                    &conv_hist, status, stream);
+    return gdn_replay_commit_layers(sh, 1, &replay_log, &commit_win, slot_ids, parents, lane_nodes, accept_node,
+                                    &state_pool, &conv_hist, status, stream);
 }
 
 int gdn_conv_step(const gdn_shape *sh, const float *x, const float *conv_w, float *conv_hist,

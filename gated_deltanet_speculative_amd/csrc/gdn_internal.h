@@ -12,30 +12,15 @@ struct Dims {
     int C, N, P, Hk, Hv, dk, dv, Ch;
 };
 
-// Per-lane validity on the device, evaluated cooperatively by every thread of a
-// workgroup.  Returns the lane's GDN_STATUS_* bits (0 = lane is valid); `s` is the
-// lane's slot id and must not be -1.  Uses one LDS word; contains barriers, so
-// every thread of the workgroup must call it.
-__device__ inline int lane_status_bits(const int32_t *__restrict__ slot_ids, const int32_t *__restrict__ parents,
-                                       const Dims &d, int c, int s, int *lds_word) {
-    int bits = 0;
-    if (s < -1 || s >= d.P) bits |= GDN_STATUS_SLOT_RANGE;
-    for (int o = threadIdx.x; o < d.C; o += blockDim.x)
-        if (o != c && slot_ids[o] == s) bits |= GDN_STATUS_SLOT_DUP;
-    for (int i = threadIdx.x; i < d.N; i += blockDim.x) {
-        const int p = parents[(int64_t)c * d.N + i];
-        if (p < -1 || p >= i) bits |= GDN_STATUS_PARENT;
-    }
-    if (threadIdx.x == 0) *lds_word = 0;
-    __syncthreads();
-    if (bits) atomicOr(lds_word, bits);
-    __syncthreads();
-    return *lds_word;
+// Nodes present in lane c: lane_nodes[c] (the lane's drafted length) or all N when the
+// caller passes no counts.  A count outside [0, N] is reported as GDN_STATUS_NODES.
+__device__ inline int lane_node_count(const int32_t *__restrict__ lane_nodes, const Dims &d, int c) {
+    return lane_nodes ? lane_nodes[c] : d.N;
 }
 
 hipError_t launch_conv_tree_step(const Dims &d, const float *x, const float *conv_w, const float *conv_hist,
-                                 const int32_t *slot_ids, const int32_t *parents, float *conv_out,
-                                 float *commit_win, int32_t *status, hipStream_t stream);
+                                 const int32_t *slot_ids, const int32_t *parents, const int32_t *lane_nodes,
+                                 float *conv_out, float *commit_win, int32_t *status, hipStream_t stream);
 
 // Arguments of the tree verify kernels, passed by value.  The separate route reads the
 // conv output `qkv`; the fused route reads x, conv_w and conv_hist, computes the conv
@@ -50,6 +35,7 @@ struct VerifyArgs {
     const float *dt_bias, *A;
     const float *state_pool;
     const int32_t *slot_ids, *parents;
+    const int32_t *lane_nodes;  // may be null: every lane has N nodes
     float *out, *replay_log;
     int32_t *status;
 };
@@ -65,8 +51,8 @@ struct LayerPtrs {
 };
 
 hipError_t launch_replay_commit(const Dims &d, int n_layers, const LayerPtrs &lp, const int32_t *slot_ids,
-                                const int32_t *parents, const int32_t *accept_node, int32_t *status,
-                                hipStream_t stream);
+                                const int32_t *parents, const int32_t *lane_nodes, const int32_t *accept_node,
+                                int32_t *status, hipStream_t stream);
 
 // Plain decode step: chain conv with in-place history write-back, then one token of the
 // recurrence applied to the slot's state in place.

@@ -63,7 +63,7 @@ __device__ inline unsigned int path_mask(int par, int lane, int N, int e) {
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void replay_commit_kernel(
     Dims d, const LayerPtrs lp, const int32_t *__restrict__ slot_ids, const int32_t *__restrict__ parents,
-    const int32_t *__restrict__ accept_node, int32_t *__restrict__ status) {
+    const int32_t *__restrict__ lane_nodes, const int32_t *__restrict__ accept_node, int32_t *__restrict__ status) {
     using Cfg = CommitCfg<DK, DV>;
     constexpr int RB = Cfg::RB, F4 = Cfg::F4, FPT = Cfg::FPT, R = 1 + DK + DV;
     constexpr int Q4 = DV / 4;
@@ -88,17 +88,18 @@ __global__ __launch_bounds__(kThreads) void replay_commit_kernel(
 
     // ---- every load that does not need the slot id, issued first: the lane's parents
     //      (lane i of every wave holds parents[i]) and this thread's share of the
-    //      preflight (one lane's slot and accept node, kPreRows parent entries with the
-    //      slot of their lane)
+    //      preflight (one lane's slot, accept node and node count, kPreRows parent entries
+    //      with the slot and node count of their lane)
     const int par = parents[(int64_t)c * N + (lane < N ? lane : 0)];
     const int tl = tid < C ? tid : 0;
-    const int so = slot_ids[tl], eo = accept_node[tl];
-    int pp[kPreRows], ps[kPreRows];
+    const int so = slot_ids[tl], eo = accept_node[tl], no = lane_node_count(lane_nodes, d, tl);
+    int pp[kPreRows], ps[kPreRows], pn[kPreRows];
 #pragma unroll
     for (int u = 0; u < kPreRows; ++u) {
         const int idx = min(tid + kThreads * u, C * N - 1);
         pp[u] = parents[idx];
         ps[u] = slot_ids[idx / N];
+        pn[u] = lane_node_count(lane_nodes, d, idx / N);
     }
     const int s = slot_ids[c], e = accept_node[c];
     const int st_in = *status;
@@ -165,7 +166,8 @@ __global__ __launch_bounds__(kThreads) void replay_commit_kernel(
     }
 
     // ---- preflight over every lane (slot range, duplicate slots via an LDS bitmap or a
-    //      scan, parents, accept node); every workgroup reaches the same verdict
+    //      scan, node count, present nodes' parents, accept node); every workgroup reaches
+    //      the same verdict
     const bool use_bitmap = d.P <= kBitmapSlots;
     if (use_bitmap)
         for (int w = tid; w < (d.P + 31) / 32; w += kThreads) s_bitmap[w] = 0u;
@@ -175,7 +177,9 @@ __global__ __launch_bounds__(kThreads) void replay_commit_kernel(
         const int st = t == tid ? so : slot_ids[t];
         if (st == -1) continue;
         const int et = t == tid ? eo : accept_node[t];
-        if (et < -1 || et >= N) bits |= GDN_STATUS_ACCEPT;
+        const int nt = t == tid ? no : lane_node_count(lane_nodes, d, t);
+        if (nt < 0 || nt > N) bits |= GDN_STATUS_NODES;
+        if (et < -1 || et >= min(max(nt, 0), N)) bits |= GDN_STATUS_ACCEPT;  // a present node or -1
         if (st < -1 || st >= d.P) {
             bits |= GDN_STATUS_SLOT_RANGE;
         } else if (use_bitmap) {
@@ -188,16 +192,18 @@ __global__ __launch_bounds__(kThreads) void replay_commit_kernel(
 #pragma unroll
     for (int u = 0; u < kPreRows; ++u) {
         const int idx = tid + kThreads * u;
-        if (idx < C * N && ps[u] != -1 && (pp[u] < -1 || pp[u] >= idx % N)) bits |= GDN_STATUS_PARENT;
+        if (idx < C * N && ps[u] != -1 && idx % N < pn[u] && (pp[u] < -1 || pp[u] >= idx % N))
+            bits |= GDN_STATUS_PARENT;
     }
     for (int idx = tid + kThreads * kPreRows; idx < C * N; idx += kThreads) {  // beyond the first pass
         const int p = parents[idx];
-        if (slot_ids[idx / N] != -1 && (p < -1 || p >= idx % N)) bits |= GDN_STATUS_PARENT;
+        if (slot_ids[idx / N] != -1 && idx % N < lane_node_count(lane_nodes, d, idx / N) && (p < -1 || p >= idx % N))
+            bits |= GDN_STATUS_PARENT;
     }
     {
         int wb = 0;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < 5; ++b)
             if (__builtin_amdgcn_ballot_w64((bits >> b) & 1)) wb |= 1 << b;
         if (lane == 0) s_wbits[wave] = wb;
     }
@@ -234,19 +240,20 @@ __global__ __launch_bounds__(kThreads) void replay_commit_kernel(
 
 template <int DK, int DV>
 hipError_t launch(const Dims &d, int n_layers, const LayerPtrs &lp, const int32_t *slots, const int32_t *parents,
-                  const int32_t *accept, int32_t *status, hipStream_t stream) {
+                  const int32_t *lane_nodes, const int32_t *accept, int32_t *status, hipStream_t stream) {
     hipLaunchKernelGGL((replay_commit_kernel<DK, DV>), dim3(CommitCfg<DK, DV>::NB * n_layers, d.Hv + 1, d.C),
-                       dim3(kThreads), 0, stream, d, lp, slots, parents, accept, status);
+                       dim3(kThreads), 0, stream, d, lp, slots, parents, lane_nodes, accept, status);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_replay_commit(const Dims &d, int n_layers, const LayerPtrs &lp, const int32_t *slot_ids,
-                                const int32_t *parents, const int32_t *accept_node, int32_t *status,
-                                hipStream_t stream) {
-#define GDN_COMMIT_CASE(K, V) \
-    if (d.dk == K && d.dv == V) return launch<K, V>(d, n_layers, lp, slot_ids, parents, accept_node, status, stream);
+                                const int32_t *parents, const int32_t *lane_nodes, const int32_t *accept_node,
+                                int32_t *status, hipStream_t stream) {
+#define GDN_COMMIT_CASE(K, V)                                                                               \
+    if (d.dk == K && d.dv == V)                                                                             \
+        return launch<K, V>(d, n_layers, lp, slot_ids, parents, lane_nodes, accept_node, status, stream);
 #define GDN_COMMIT_ROW(K) GDN_COMMIT_CASE(K, 16) GDN_COMMIT_CASE(K, 32) GDN_COMMIT_CASE(K, 64) GDN_COMMIT_CASE(K, 128)
     GDN_COMMIT_ROW(16) GDN_COMMIT_ROW(32) GDN_COMMIT_ROW(64) GDN_COMMIT_ROW(128)
 #undef GDN_COMMIT_ROW

@@ -190,7 +190,9 @@ __device__ inline void hist_columns(const v4f raw[3], v4f hc[3]) {
     hc[2] = v4f{a.z, b.y, e.x, e.w};
 }
 
-template <int DK, int DV, int NP, bool FUSED>
+// RAGGED: the caller passed per-lane node counts (without them every lane has N nodes and
+// the count costs nothing)
+template <int DK, int DV, int NP, bool FUSED, bool RAGGED>
 __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     using Ly = VerifyLayout<DK, DV, NP, FUSED>;
     constexpr int JB = Ly::JB, NB = Ly::NB, CT = Ly::CT, NT = Ly::NT, RT = Ly::RT, KC = Ly::KC, LCG = Ly::LCG, KP = Ly::KP, LCQ = Ly::LCQ;
@@ -236,6 +238,13 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
         int, __builtin_amdgcn_raw_buffer_load_b32(
                  __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(args.slot_ids), 0, 4 * d.C, kRsrcWord3), 4 * c, 0,
                  0));
+    // ragged lanes: the lane's node count the same way
+    int nv_v = 0;
+    if constexpr (RAGGED)
+        nv_v = __builtin_bit_cast(
+            int, __builtin_amdgcn_raw_buffer_load_b32(
+                     __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(args.lane_nodes), 0, 4 * d.C, kRsrcWord3),
+                     4 * c, 0, 0));
     const int par = args.parents[(int64_t)c * N + (lane < N ? lane : 0)];  // lane i of every wave: parent of node i
     const int tn = tid < N ? tid : 0;
     const int64_t trow = (int64_t)c * N + tn;
@@ -307,9 +316,13 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     __builtin_amdgcn_sched_barrier(0);
     const int wv_u = __builtin_amdgcn_readfirstlane(wave);
     const int pct = wv_u % CT, pkp = wv_u / CT;  // state product: column tile and k part of this wave
+    // nodes present in this lane (nodes past them are absent: zero rows, nothing written)
+    const int nv = RAGGED ? __builtin_amdgcn_readfirstlane(nv_v) : N;
+    const int nvc = min(max(nv, 0), N);
 
-    // ---- lane validity (slot range, duplicate slot, parents); nothing is written for a bad
-    //      lane and a padding lane (slot -1) is skipped without a status bit
+    // ---- lane validity (slot range, duplicate slot, node count, present nodes' parents);
+    //      nothing is written for a bad lane and a padding lane (slot -1) is skipped
+    //      without a status bit
     int bits = 0;
     if (s != -1) {
         if (!s_ok) bits |= GDN_STATUS_SLOT_RANGE;
@@ -318,12 +331,13 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
             const int o = tid + kThreads * k;
             if (o < d.C && o != c && so[k] == s) bits |= GDN_STATUS_SLOT_DUP;
         }
-        if (tid < N && (par < -1 || par >= tid)) bits |= GDN_STATUS_PARENT;
+        if (nv != nvc) bits |= GDN_STATUS_NODES;
+        if (tid < nvc && (par < -1 || par >= tid)) bits |= GDN_STATUS_PARENT;
     }
     {
         int wb = 0;
 #pragma unroll
-        for (int b = 0; b < 3; ++b)
+        for (int b = 0; b < 5; ++b)
             if (__builtin_amdgcn_ballot_w64((bits >> b) & 1)) wb |= 1 << b;
         if (lane == 0) s_wbits[wave] = wb;
     }
@@ -332,7 +346,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     //      log2(NP) rounds of lane shuffles, independent of the tree depth), and the three
     //      nearest ancestors of every node for the conv
     if (wave == 0) {
-        const bool real = lane < N;
+        const bool real = lane < nvc;
         const int a1 = real ? par : -1;
         int jump = a1;
         float L = 0.f;
@@ -465,7 +479,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
             const int i = (tid / G) * QPT + u;
             yq[u] = qreg[u];
             if constexpr (FUSED) yq[u] = conv_silu(xq[u][0], xq[u][1], xq[u][2], qreg[u], wq);
-            yq[u] = i < N ? yq[u] : zero;
+            yq[u] = i < nvc ? yq[u] : zero;
         }
         if (has_v) {
 #pragma unroll
@@ -473,7 +487,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
                 const int i = (tid / Q4) * VPT + u;
                 yv[u] = vreg[u];
                 if constexpr (FUSED) yv[u] = conv_silu(xv[u][0], xv[u][1], xv[u][2], vreg[u], wv);
-                yv[u] = i < N ? yv[u] : zero;
+                yv[u] = i < nvc ? yv[u] : zero;
             }
         }
         const bool isq = gq < DK / 4;
@@ -680,7 +694,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     // waves 4..7, once per lane and value head: the replay-log header (g, k^) of every node
     if (wv_u >= 4 && jb == 0) {
         float *logc = args.replay_log + ((int64_t)c * N * Hv + h) * R;
-        for (int f = tid - 256; f < N * (DK / 4); f += kThreads - 256) {
+        for (int f = tid - 256; f < nvc * (DK / 4); f += kThreads - 256) {
             const int i = f / (DK / 4), e4 = f - i * (DK / 4);
             float sq = s_ssq[i][0];
             if constexpr (Ly::NPART > 1) sq += s_ssq[i][1];
@@ -694,9 +708,9 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     // output rows and the log's delta rows of the block, in 16-byte chunks from consecutive
     // lanes (whole lines per store instruction; a log row is 1 + d_k + d_v floats, so its
     // chunks are only 4-byte aligned)
-    for (int f = tid; f < 2 * N * Q4; f += kThreads) {
-        const bool is_out = f < N * Q4;
-        const int ff = is_out ? f : f - N * Q4;
+    for (int f = tid; f < 2 * nvc * Q4; f += kThreads) {
+        const bool is_out = f < nvc * Q4;
+        const int ff = is_out ? f : f - nvc * Q4;
         const int i = ff / Q4, q4 = ff - i * Q4;
         const int64_t row = ((int64_t)c * N + i) * Hv + h;
         if (is_out)
@@ -708,9 +722,9 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     }
 }
 
-template <int DK, int DV, int NP>
+template <int DK, int DV, int NP, bool RAGGED>
 __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs args) {
-    verify_body<DK, DV, NP, false>(args);
+    verify_body<DK, DV, NP, false, RAGGED>(args);
 }
 
 // Commit windows of the fused route, written by workgroups of their own that run beside
@@ -726,7 +740,7 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs 
 // from consecutive lanes (whole lines), which drains faster than 16-byte pieces at a
 // 48-byte lane stride.  Nothing is written for a padding or invalid lane (the verify
 // workgroups report it).
-template <int NP>
+template <int NP, bool RAGGED>
 __device__ __forceinline__ void window_body(const VerifyArgs &args, int b) {
     constexpr int GPB = kThreads / NP;  // 4-channel groups per workgroup
     const Dims d = args.d;
@@ -737,15 +751,19 @@ __device__ __forceinline__ void window_body(const VerifyArgs &args, int b) {
     const int i = tid / GPB, ch = ch0 + 4 * (tid % GPB);
     const int s = args.slot_ids[c];
     const int par = args.parents[(int64_t)c * N + (lane < N ? lane : 0)];  // lane j: parent of node j
+    const int nv = RAGGED ? args.lane_nodes[c] : N;
     // the lane's validity, as the verify workgroups decide it
-    int bad = (s < -1 || s >= d.P) ? 1 : 0;
+    int bad = (s < -1 || s >= d.P || nv < 0 || nv > N) ? 1 : 0;
     for (int o = lane; o < d.C; o += 64)
         if (o != c && args.slot_ids[o] == s) bad = 1;
-    if (lane < N && (par < -1 || par >= lane)) bad = 1;
+    if (lane < nv && lane < N && (par < -1 || par >= lane)) bad = 1;
     if (s == -1 || __builtin_amdgcn_ballot_w64(bad)) return;  // uniform over the wave
+    // absent nodes' parents are not checked: treat those nodes as root children so that no
+    // address is formed from them (present nodes' ancestors are present)
+    const int parv = lane < nv ? par : -1;
     const int ic = i < N ? i : 0;
-    const int a1 = __shfl(par, ic);
-    const int a2s = __shfl(par, a1 >= 0 ? a1 : 0);
+    const int a1 = __shfl(parv, ic);
+    const int a2s = __shfl(parv, a1 >= 0 ? a1 : 0);
     const int a2 = a1 >= 0 ? a2s : -1;
     // threads past the node count or the channel count load in-range rows and store nothing
     const int chc = ch < d.Ch ? ch : 0;
@@ -777,45 +795,49 @@ __device__ __forceinline__ void window_body(const VerifyArgs &args, int b) {
     for (int u = 0; u < 3; ++u) {
         const int j = GPB * u + gi;  // chunk j holds part j % 3 of channel group j / 3
         const v4f v = chunks[3 * (tid - gi) + j];
-        if (i < N && ch0 + 4 * (j / 3) < d.Ch) __builtin_nontemporal_store(v, dst + j);
+        if (i < nv && ch0 + 4 * (j / 3) < d.Ch) __builtin_nontemporal_store(v, dst + j);
     }
 }
 
-template <int DK, int DV, int NP>
+template <int DK, int DV, int NP, bool RAGGED>
 __global__ __launch_bounds__(kThreads) void conv_tree_verify_kernel(const VerifyArgs args) {
     constexpr int NB = VerifyLayout<DK, DV, NP, true>::NB;
     static_assert(kThreads * 12 <= VerifyLayout<DK, DV, NP, true>::LDS_FLOATS, "window chunks fit the LDS");
     const int n_verify = NB * args.d.Hv * args.d.C;
     if ((int)blockIdx.x < n_verify)
-        verify_body<DK, DV, NP, true>(args);
+        verify_body<DK, DV, NP, true, RAGGED>(args);
     else
-        window_body<NP>(args, blockIdx.x - n_verify);
+        window_body<NP, RAGGED>(args, blockIdx.x - n_verify);
 }
 
-template <int DK, int DV, int NP, bool FUSED>
+template <int DK, int DV, int NP, bool FUSED, bool RAGGED>
 hipError_t launch(const VerifyArgs &a, hipStream_t stream) {
     using Ly = VerifyLayout<DK, DV, NP, FUSED>;
     const size_t lds = sizeof(float) * Ly::LDS_FLOATS;
     // the LDS limit is a property of the kernel, set once (also keeps stream capture clean)
-    const void *kernel = FUSED ? reinterpret_cast<const void *>(&conv_tree_verify_kernel<DK, DV, NP>)
-                               : reinterpret_cast<const void *>(&tree_verify_kernel<DK, DV, NP>);
+    const void *kernel = FUSED ? reinterpret_cast<const void *>(&conv_tree_verify_kernel<DK, DV, NP, RAGGED>)
+                               : reinterpret_cast<const void *>(&tree_verify_kernel<DK, DV, NP, RAGGED>);
     static const hipError_t attr = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
     // fused: the window workgroups follow the verify workgroups
     const int grid = Ly::NB * a.d.Hv * a.d.C +
                      (FUSED ? a.d.C * ((a.d.Ch + 4 * (kThreads / NP) - 1) / (4 * (kThreads / NP))) : 0);
     if constexpr (FUSED)
-        hipLaunchKernelGGL((conv_tree_verify_kernel<DK, DV, NP>), dim3(grid), dim3(kThreads), lds, stream, a);
+        hipLaunchKernelGGL((conv_tree_verify_kernel<DK, DV, NP, RAGGED>), dim3(grid), dim3(kThreads), lds, stream, a);
     else
-        hipLaunchKernelGGL((tree_verify_kernel<DK, DV, NP>), dim3(grid), dim3(kThreads), lds, stream, a);
+        hipLaunchKernelGGL((tree_verify_kernel<DK, DV, NP, RAGGED>), dim3(grid), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
 }
 
 template <int DK, int DV>
 hipError_t launch_np(const VerifyArgs &a, hipStream_t stream) {
     const bool fused = a.x != nullptr;
-    if (a.d.N <= 16) return fused ? launch<DK, DV, 16, true>(a, stream) : launch<DK, DV, 16, false>(a, stream);
-    return fused ? launch<DK, DV, 32, true>(a, stream) : launch<DK, DV, 32, false>(a, stream);
+    const bool ragged = a.lane_nodes != nullptr;
+    if (a.d.N <= 16)
+        return fused ? (ragged ? launch<DK, DV, 16, true, true>(a, stream) : launch<DK, DV, 16, true, false>(a, stream))
+                     : (ragged ? launch<DK, DV, 16, false, true>(a, stream) : launch<DK, DV, 16, false, false>(a, stream));
+    return fused ? (ragged ? launch<DK, DV, 32, true, true>(a, stream) : launch<DK, DV, 32, true, false>(a, stream))
+                 : (ragged ? launch<DK, DV, 32, false, true>(a, stream) : launch<DK, DV, 32, false, false>(a, stream));
 }
 
 }  // namespace

@@ -59,6 +59,13 @@
  *     if *status is non-zero after their preflight, including bits left there by an
  *     earlier call of the round.
  *   - A lane whose slot id is -1 is a padding lane: nothing is read or written for it.
+ *   - Ragged lanes: the tree calls and the commit take an optional lane_nodes [C] (int32,
+ *     device; NULL = every lane has N nodes).  Lane c then has N_c = lane_nodes[c] nodes
+ *     0..N_c-1 (its drafted length; "qwen35: DSpark speculative decoding", v_len commit
+ *     message); nodes i >= N_c are absent: their inputs are not used, their outputs are
+ *     not written and their parents are not checked, and the commit accepts only present
+ *     nodes.  Parents precede children, so the present nodes compute exactly what a batch
+ *     of N_c nodes would.  N_c outside [0, N] sets GDN_STATUS_NODES.
  *
  * Notation: C = n_seqs lanes, N = n_nodes draft nodes per lane, P = n_slots pool
  * slots, H_k q/k heads, H_v value heads (H_v % H_k == 0; value head h uses q/k head
@@ -92,7 +99,8 @@ extern "C" {
 #define GDN_STATUS_SLOT_RANGE 1 /* slot id outside [-1, P)                                   */
 #define GDN_STATUS_SLOT_DUP 2   /* the same non-negative slot id used by two lanes           */
 #define GDN_STATUS_PARENT 4     /* parents[c][i] outside [-1, i-1]                           */
-#define GDN_STATUS_ACCEPT 8     /* accept_node[c] outside [-1, N) (commit only)              */
+#define GDN_STATUS_ACCEPT 8     /* accept_node[c] outside [-1, N_c) (commit only)            */
+#define GDN_STATUS_NODES 16     /* lane_nodes[c] outside [0, N]                              */
 
 #define GDN_MAX_NODES 32
 #define GDN_MAX_SEQS 1024
@@ -127,13 +135,14 @@ typedef struct gdn_shape {
  *   conv_hist  [P][Ch][3]     persistent history pool, READ-ONLY here
  *   slot_ids   [C]            int32, -1 = padding lane               (read)
  *   parents    [C][N]         int32 draft-tree parents               (read)
- *   conv_out   [C][N][Ch]     written for valid lanes
- *   commit_win [C][N][Ch][3]  written for valid lanes
- *   status     int32*         may be NULL; SLOT_RANGE / SLOT_DUP / PARENT bits
+ *   lane_nodes [C]            int32 nodes per lane, or NULL (= N)    (read)
+ *   conv_out   [C][N][Ch]     written for valid lanes' present nodes
+ *   commit_win [C][N][Ch][3]  written for valid lanes' present nodes
+ *   status     int32*         may be NULL; SLOT_RANGE / SLOT_DUP / PARENT / NODES bits
  */
 int gdn_conv_tree_step(const gdn_shape *sh, const float *x, const float *conv_w, const float *conv_hist,
-                       const int32_t *slot_ids, const int32_t *parents, float *conv_out, float *commit_win,
-                       int32_t *status, hipStream_t stream);
+                       const int32_t *slot_ids, const int32_t *parents, const int32_t *lane_nodes, float *conv_out,
+                       float *commit_win, int32_t *status, hipStream_t stream);
 
 /*
  * Read-only slot-mapped tree verify ("perf(qwen35): fuse the DFlash2 concurrent
@@ -157,23 +166,23 @@ int gdn_conv_tree_step(const gdn_shape *sh, const float *x, const float *conv_w,
  *   gate_stride    floats between consecutive tokens' gate rows, >= H_v
  *   dt_bias, A     [H_v]               (A negative, e.g. -exp(A_log))
  *   state_pool     [P][H_v][d_k][d_v]  persistent, READ-ONLY here
- *   slot_ids, parents                  as above
- *   out            [C][N][H_v][d_v]    written for valid lanes
- *   replay_log     [C][N][H_v][R]      written for valid lanes
+ *   slot_ids, parents, lane_nodes      as above
+ *   out            [C][N][H_v][d_v]    written for valid lanes' present nodes
+ *   replay_log     [C][N][H_v][R]      written for valid lanes' present nodes
  *   status         int32*              may be NULL
  */
 int gdn_tree_verify(const gdn_shape *sh, const float *qkv, const float *beta_logits, const float *alpha_logits,
                     int64_t gate_stride, const float *dt_bias, const float *A, const float *state_pool,
-                    const int32_t *slot_ids, const int32_t *parents, float *out, float *replay_log,
-                    int32_t *status, hipStream_t stream);
+                    const int32_t *slot_ids, const int32_t *parents, const int32_t *lane_nodes, float *out,
+                    float *replay_log, int32_t *status, hipStream_t stream);
 
 /*
  * Replay-log commit ("perf(qwen35): fuse the DFlash2 concurrent verify Gated DeltaNet
  * route", closing paragraph of Optimizations; "perf(qwen38): various DFlash2
  * optimizations concurrency C1-C5", Summary item 3 and the transaction preflight).
  *
- * Preflight over every non-padding lane: slot range, duplicate slots, parents and
- * accept_node[c] in [-1, N).  If *status is then non-zero nothing is written.
+ * Preflight over every non-padding lane: slot range, duplicate slots, node counts,
+ * parents and accept_node[c] in [-1, N_c).  If *status is then non-zero nothing is written.
  * Otherwise every non-padding lane with e = accept_node[c] >= 0 replays the logged
  * transitions of e's root path, in path order, into its slot:
  *   S <- g_t * S + k^_t delta_t^T    for state_pool[s][h], every h,
@@ -182,13 +191,15 @@ int gdn_tree_verify(const gdn_shape *sh, const float *qkv, const float *beta_log
  *
  *   replay_log, commit_win   outputs of this round's verify / conv    (read)
  *   slot_ids, parents        the round's mapping and trees            (read)
+ *   lane_nodes [C]           int32 nodes per lane, or NULL (= N)      (read)
  *   accept_node [C]          int32 deepest accepted node, -1 = none   (read)
  *   state_pool, conv_hist    updated in place
  *   status                   int32*, REQUIRED (GDN_ERR_NULL otherwise)
  */
 int gdn_replay_commit(const gdn_shape *sh, const float *replay_log, const float *commit_win,
-                      const int32_t *slot_ids, const int32_t *parents, const int32_t *accept_node,
-                      float *state_pool, float *conv_hist, int32_t *status, hipStream_t stream);
+                      const int32_t *slot_ids, const int32_t *parents, const int32_t *lane_nodes,
+                      const int32_t *accept_node, float *state_pool, float *conv_hist, int32_t *status,
+                      hipStream_t stream);
 
 /*
  * Fused tree conv + verify: gdn_conv_tree_step followed by gdn_tree_verify on its
@@ -200,7 +211,7 @@ int gdn_replay_commit(const gdn_shape *sh, const float *replay_log, const float 
  *
  *   x, conv_w, conv_hist          as in gdn_conv_tree_step (conv_hist READ-ONLY)
  *   beta_logits .. state_pool     as in gdn_tree_verify (state_pool READ-ONLY)
- *   slot_ids, parents             as above
+ *   slot_ids, parents, lane_nodes as above
  *   out, replay_log               as in gdn_tree_verify
  *   commit_win                    as in gdn_conv_tree_step
  *   status                        may be NULL
@@ -210,8 +221,8 @@ int gdn_replay_commit(const gdn_shape *sh, const float *replay_log, const float 
 int gdn_conv_tree_verify(const gdn_shape *sh, const float *x, const float *conv_w, const float *conv_hist,
                          const float *beta_logits, const float *alpha_logits, int64_t gate_stride,
                          const float *dt_bias, const float *A, const float *state_pool, const int32_t *slot_ids,
-                         const int32_t *parents, float *out, float *replay_log, float *commit_win, int32_t *status,
-                         hipStream_t stream);
+                         const int32_t *parents, const int32_t *lane_nodes, float *out, float *replay_log,
+                         float *commit_win, int32_t *status, hipStream_t stream);
 
 /*
  * Multi-layer replay-log commit: the commit above for every GDN layer of the round in
@@ -224,14 +235,14 @@ int gdn_conv_tree_verify(const gdn_shape *sh, const float *x, const float *conv_
  *   n_layers                 1..GDN_MAX_LAYERS
  *   replay_logs, commit_wins host arrays of n_layers device pointers (layouts as above)
  *   state_pools, conv_hists  host arrays of n_layers device pointers, updated in place
- *   slot_ids, parents, accept_node, status   as in gdn_replay_commit (status REQUIRED)
+ *   slot_ids, parents, lane_nodes, accept_node, status   as in gdn_replay_commit (status REQUIRED)
  * Every layer's pools must be disjoint from every input and from each other
  * (GDN_ERR_ALIAS).
  */
 int gdn_replay_commit_layers(const gdn_shape *sh, int32_t n_layers, const float *const *replay_logs,
                              const float *const *commit_wins, const int32_t *slot_ids, const int32_t *parents,
-                             const int32_t *accept_node, float *const *state_pools, float *const *conv_hists,
-                             int32_t *status, hipStream_t stream);
+                             const int32_t *lane_nodes, const int32_t *accept_node, float *const *state_pools,
+                             float *const *conv_hists, int32_t *status, hipStream_t stream);
 
 /*
  * Plain decode step, conv part ("qwen35: DSpark speculative decoding (Qwen3.8-27B

@@ -60,9 +60,11 @@ def shape_of(C, N, P, Hk, Hv, dk, dv) -> gdn.Shape:
 class GpuRound:
     """Device copies of one layer's inputs plus guarded outputs; runs conv, verify, commit."""
 
-    def __init__(self, sh: gdn.Shape, x, ba, conv_w, conv_hist, state, dt_bias, A, slot_ids, parents, fused=False):
+    def __init__(self, sh: gdn.Shape, x, ba, conv_w, conv_hist, state, dt_bias, A, slot_ids, parents, fused=False,
+                 lane_nodes=None):
         self.sh = sh
         self.fused = fused  # verify() runs the fused conv + verify call instead of the two separate calls
+        self.lane_nodes = None if lane_nodes is None else dev(np.asarray(lane_nodes, np.int32))
         C, N, Ch, Hv = sh.n_seqs, sh.n_nodes, sh.channels, sh.n_v_heads
         self.x, self.ba, self.conv_w = dev(x), dev(ba), dev(conv_w)
         self.conv_hist, self.state = dev(conv_hist), dev(state)
@@ -80,34 +82,38 @@ class GpuRound:
         if self.fused:
             gdn.conv_tree_verify(sh, self.x, self.conv_w, self.conv_hist, self.ba[..., :Hv], self.ba[..., Hv:],
                                  self.dt_bias, self.A, self.state, self.slot_ids, self.parents, out=self.out.t,
-                                 replay_log=self.replay_log.t, commit_win=self.commit_win.t, status=self.status)
+                                 replay_log=self.replay_log.t, commit_win=self.commit_win.t, status=self.status,
+                                 lane_nodes=self.lane_nodes)
             return self
         gdn.conv_tree_step(sh, self.x, self.conv_w, self.conv_hist, self.slot_ids, self.parents,
-                           conv_out=self.conv_out.t, commit_win=self.commit_win.t, status=self.status)
+                           conv_out=self.conv_out.t, commit_win=self.commit_win.t, status=self.status,
+                           lane_nodes=self.lane_nodes)
         gdn.tree_verify(sh, self.conv_out.t, self.ba[..., :Hv], self.ba[..., Hv:], self.dt_bias, self.A,
                         self.state, self.slot_ids, self.parents, out=self.out.t, replay_log=self.replay_log.t,
-                        status=self.status)
+                        status=self.status, lane_nodes=self.lane_nodes)
         return self
 
     def commit(self, accept_node):
         gdn.replay_commit(self.sh, self.replay_log.t, self.commit_win.t, self.slot_ids, self.parents,
-                          dev(np.asarray(accept_node, np.int32)), self.state, self.conv_hist, self.status)
+                          dev(np.asarray(accept_node, np.int32)), self.state, self.conv_hist, self.status,
+                          lane_nodes=self.lane_nodes)
         return self
 
     def guards_intact(self) -> bool:
         return all(b.guards_intact() for b in (self.conv_out, self.commit_win, self.out, self.replay_log))
 
 
-def oracle_round(sh, x, ba, conv_w, conv_hist, state, dt_bias, A, slot_ids, parents):
+def oracle_round(sh, x, ba, conv_w, conv_hist, state, dt_bias, A, slot_ids, parents, lane_nodes=None):
     return O.verify_round(x, ba, conv_w, conv_hist, state, dt_bias, A, np.asarray(slot_ids, np.int32),
-                          np.asarray(parents, np.int32), sh.n_k_heads)
+                          np.asarray(parents, np.int32), sh.n_k_heads, lane_nodes)
 
 
-def oracle_commit(sh, ref, slot_ids, parents, accept, state, conv_hist, status_in=0):
+def oracle_commit(sh, ref, slot_ids, parents, accept, state, conv_hist, status_in=0, lane_nodes=None):
     pool = state.astype(np.float64)
     hist = conv_hist.astype(np.float64)
     st = O.replay_commit(ref["replay_log"], ref["commit_win"], np.asarray(slot_ids, np.int32),
-                         np.asarray(parents, np.int32), np.asarray(accept, np.int32), pool, hist, status_in)
+                         np.asarray(parents, np.int32), np.asarray(accept, np.int32), pool, hist, status_in,
+                         lane_nodes)
     return st, pool, hist
 
 

@@ -48,23 +48,31 @@ def _ptrs(n, stride=1 << 28):
     return [FAKE + k * stride for k in range(n)]
 
 
-def _conv(sh, ptrs, status=None):
+# The helpers below take the pointers of each call without its optional lane_nodes
+# argument and pass lane_nodes (default NULL: every lane has N nodes) in its place.
+def _conv(sh, ptrs, status=None, lane_nodes=None):
+    """ptrs: x, conv_w, conv_hist, slot_ids, parents, conv_out, commit_win"""
     lib = gdn.load_library()
     cs = sh.c_struct() if sh is not None else None
-    return lib.gdn_conv_tree_step(ctypes.byref(cs) if cs else None, *ptrs, status, None)
+    p = list(ptrs)
+    return lib.gdn_conv_tree_step(ctypes.byref(cs) if cs else None, *p[:5], lane_nodes, *p[5:], status, None)
 
 
-def _verify(sh, ptrs, gate_stride, status=None):
+def _verify(sh, ptrs, gate_stride, status=None, lane_nodes=None):
+    """ptrs: qkv, beta, alpha, dt_bias, A, state_pool, slot_ids, parents, out, replay_log"""
     lib = gdn.load_library()
     cs = sh.c_struct()
     p = list(ptrs)
-    return lib.gdn_tree_verify(ctypes.byref(cs), p[0], p[1], p[2], gate_stride, *p[3:], status, None)
+    return lib.gdn_tree_verify(ctypes.byref(cs), p[0], p[1], p[2], gate_stride, *p[3:8], lane_nodes, *p[8:], status,
+                               None)
 
 
-def _commit(sh, ptrs, status):
+def _commit(sh, ptrs, status, lane_nodes=None):
+    """ptrs: replay_log, commit_win, slot_ids, parents, accept_node, state_pool, conv_hist"""
     lib = gdn.load_library()
     cs = sh.c_struct()
-    return lib.gdn_replay_commit(ctypes.byref(cs), *ptrs, status, None)
+    p = list(ptrs)
+    return lib.gdn_replay_commit(ctypes.byref(cs), *p[:4], lane_nodes, *p[4:], status, None)
 
 
 def test_null_shape_and_pointers():
@@ -144,7 +152,8 @@ def _commit_layers(sh, L, per_layer, shared, status, n_layers=None):
     arrs = [(ctypes.c_void_p * L)(*v) for v in per_layer]
     cast = [ctypes.cast(a, ctypes.c_void_p) for a in arrs]
     return lib.gdn_replay_commit_layers(ctypes.byref(cs), ctypes.c_int32(L if n_layers is None else n_layers),
-                                        cast[0], cast[1], *shared, cast[2], cast[3], status, None)
+                                        cast[0], cast[1], shared[0], shared[1], None, shared[2], cast[2], cast[3],
+                                        status, None)
 
 
 def _layer_ptrs(L):
@@ -181,7 +190,7 @@ def _fused(sh, ptrs, gate_stride, status=None):
     lib = gdn.load_library()
     cs = sh.c_struct()
     p = list(ptrs)
-    return lib.gdn_conv_tree_verify(ctypes.byref(cs), *p[:5], gate_stride, *p[5:], status, None)
+    return lib.gdn_conv_tree_verify(ctypes.byref(cs), *p[:5], gate_stride, *p[5:10], None, *p[10:], status, None)
 
 
 def test_fused_rejections():
@@ -248,3 +257,15 @@ def test_plain_step_rejections():
     assert _decode_step(one, p, 8, st) == _lib.GDN_ERR_ALIAS
     p = _ptrs(8)
     assert _decode_step(one, p, 8, p[7] + 4) == _lib.GDN_ERR_ALIAS  # status inside out
+
+
+def test_lane_nodes_checked_like_any_input():
+    sh = _shape()
+    nodes = FAKE + (1 << 41)
+    assert _conv(sh, _ptrs(7), lane_nodes=nodes + 2) == _lib.GDN_ERR_ALIGN  # int32 counts need 4-byte alignment
+    p = _ptrs(7)
+    assert _conv(sh, p, lane_nodes=p[5] + 4) == _lib.GDN_ERR_ALIAS  # counts inside conv_out
+    p = _ptrs(10)
+    assert _verify(sh, p, 8, lane_nodes=p[9] + 8) == _lib.GDN_ERR_ALIAS  # counts inside the replay log
+    p = _ptrs(7)
+    assert _commit(sh, p, FAKE + (9 << 28), lane_nodes=p[5] + 16) == _lib.GDN_ERR_ALIAS  # counts inside the pool
