@@ -14,7 +14,9 @@ Sources (page title, then section):
          read-only during verification; replay-log commit advances it).
   [P2] "Feature/support dflash2"
        - deferred-state commit message: a step the drafter did not draft for commits
-         its post-step state to the slot immediately (the plain decode step).
+         its post-step state to the slot immediately (the plain decode step);
+       - first-version commit message: the recurrence of prefill runs on a chunked GDN
+         kernel that closes with a SiLU or, by gate_mode, a sigmoid output gate.
   [P3] "qwen35: DSpark speculative decoding (Qwen3.8-27B drafters)"
        - raw-gate commit message: beta = sigmoid(b), gate = softplus(a + dt_bias) * A;
        - v_len commit message: verify and accept run over each lane's drafted length,
@@ -54,9 +56,12 @@ Readings where the pages are silent (each listed in the design notes):
     outside [0, N], a present node's parent outside [-1, i-1] or (commit only)
     an accept node outside [-1, lane_nodes[c]) sets a status bit; conv and verify then write nothing for that lane, and the
     commit mutates nothing at all (all-or-nothing transaction);
-  * the plain decode step (conv_step + decode_step) mutates the pools directly,
-    so it is a transaction like the commit: a bad slot anywhere, or a non-zero
-    incoming status, and nothing is written.
+  * the plain decode step (conv_step + decode_step) and the prefill mutate the
+    pools directly, so they are transactions like the commit: a bad slot
+    anywhere, or a non-zero incoming status, and nothing is written;
+  * prefill: a chain of T tokens per lane, equal to T single-token steps (the
+    chunking is the kernel's business); its optional output gate is
+    o * silu(z) (gate_mode 0) or o * sigmoid(z) (gate_mode 1).
 
 Every function below is pinned by tests/test_oracle_pins.py against closed
 forms, library routines and brute force.
@@ -366,6 +371,45 @@ def decode_step(qkv, beta_logits, alpha_logits, dt_bias, A, state_pool, slot_ids
                                            alpha_logits[c, h], dt_bias[h], A[h])
             state_pool[s, h] = S_new
             out[c, h] = o
+    return 0
+
+
+# ---------------------------------------------------------------- prefill
+def output_gate(o, z, gate_mode):
+    """[P2] chunked-GDN commit message: the kernel closes with a SiLU (gate_mode 0) or a
+    sigmoid (gate_mode 1) gate on the output: o * silu(z) or o * sigmoid(z)."""
+    z = np.asarray(z, np.float64)
+    return o * (silu(z) if gate_mode == 0 else sigmoid(z))
+
+
+def prefill(qkv, beta_logits, alpha_logits, dt_bias, A, state_pool, slot_ids, n_k_heads, out, gate_z=None,
+            gate_mode=0, status_in=0):
+    """[P2] chunked-GDN commit message (the recurrence over a prompt's tokens, with an
+    optional closing output gate); [P3] raw-gate commit message.
+
+    qkv[c] holds the conv output rows of a chain of T tokens for lane c (slot s);
+    beta_logits / alpha_logits are [C, T, H_v].  For every non-padding lane and value
+    head h, token_step over the tokens in order, starting from and replacing
+    state_pool[s, h] in place; out[c, t, h] = o, times act(gate_z[c, t, h]) when a gate
+    is given (output_gate).  A transaction like decode_step: nothing is written unless
+    the slot preflight and status_in are clean.  Returns the status word.
+    """
+    P, H_v, d_k, d_v = state_pool.shape
+    bits = slot_preflight(slot_ids, P, status_in)
+    if bits:
+        return bits
+    C, T, _ = qkv.shape
+    for c in range(C):
+        s = int(slot_ids[c])
+        if s == -1:
+            continue
+        for h in range(H_v):
+            S = state_pool[s, h].astype(np.float64)
+            for t in range(T):
+                q, k, v = split_qkv(np.asarray(qkv[c, t], np.float64), n_k_heads, H_v, d_k, d_v, h)
+                S, o, _, _, _ = token_step(S, q, k, v, beta_logits[c, t, h], alpha_logits[c, t, h], dt_bias[h], A[h])
+                out[c, t, h] = o if gate_z is None else output_gate(o, gate_z[c, t, h], gate_mode)
+            state_pool[s, h] = S
     return 0
 
 

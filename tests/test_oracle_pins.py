@@ -630,3 +630,72 @@ def test_ragged_commit_accepts_only_present_nodes():
                          hist2, lane_nodes=counts)  # node 2 of lane 1 is absent
     assert st == O.STATUS_ACCEPT
     assert pool2.tobytes() == case["pool"].astype(np.float64).tobytes()
+
+
+# ------------------------------------------------------------------ prefill
+def _prefill_case(seed=110, C=3, T=9, P=4, Hk=2, Hv=4, dk=8, dv=8):
+    rng = np.random.default_rng(seed)
+    case = _full_case(rng, C, T, P, Hk, Hv, dk, dv)
+    case["qkv"] = rng.standard_normal((C, T, case["x"].shape[2])).astype(np.float32)
+    case["z"] = rng.standard_normal((C, T, Hv, dv)).astype(np.float32)
+    return case, Hk
+
+
+def _run_prefill(case, Hk, slots, gate=None, mode=0):
+    Hv = case["pool"].shape[1]
+    pool = case["pool"].astype(np.float64)
+    out = np.full(case["z"].shape, np.nan)
+    st = O.prefill(case["qkv"], case["ba"][..., :Hv], case["ba"][..., Hv:], case["dt"], case["A"], pool, slots, Hk,
+                   out, gate, mode)
+    return st, pool, out
+
+
+def test_prefill_equals_single_token_steps():
+    """The prefill over T tokens leaves the state and gives the outputs of T successive
+    plain decode steps."""
+    case, Hk = _prefill_case()
+    slots = np.array([2, -1, 0], np.int32)
+    st, pool, out = _run_prefill(case, Hk, slots)
+    assert st == 0
+    Hv = case["pool"].shape[1]
+    pool_d = case["pool"].astype(np.float64)
+    for t in range(case["qkv"].shape[1]):
+        o = np.full((3, Hv, case["z"].shape[3]), np.nan)
+        assert O.decode_step(case["qkv"][:, t], case["ba"][:, t, :Hv], case["ba"][:, t, Hv:], case["dt"], case["A"],
+                             pool_d, slots, Hk, o) == 0
+        np.testing.assert_allclose(out[:, t], o, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(pool, pool_d, rtol=1e-13, atol=1e-15)
+    assert np.isnan(out[1]).all()
+    for s in (1, 3):
+        assert pool[s].tobytes() == case["pool"][s].astype(np.float64).tobytes()
+
+
+def test_prefill_output_gates():
+    """gate_mode 1 multiplies by the logistic function (scipy's expit); gate_mode 0 by
+    silu(z) = z * expit(z), so the SiLU-gated output is the sigmoid-gated one times z."""
+    case, Hk = _prefill_case(seed=111)
+    slots = np.array([0, 1, 3], np.int32)
+    _, _, plain = _run_prefill(case, Hk, slots)
+    _, _, sig = _run_prefill(case, Hk, slots, case["z"], 1)
+    _, _, sil = _run_prefill(case, Hk, slots, case["z"], 0)
+    z = case["z"].astype(np.float64)
+    np.testing.assert_allclose(sig, plain * special.expit(z), rtol=1e-14, atol=1e-16)
+    np.testing.assert_allclose(sil, sig * z, rtol=1e-13, atol=1e-16)
+    zero = np.zeros_like(case["z"])
+    _, _, s0 = _run_prefill(case, Hk, slots, zero, 1)
+    _, _, l0 = _run_prefill(case, Hk, slots, zero, 0)
+    np.testing.assert_array_equal(s0, plain / 2)
+    assert (l0 == 0).all()
+
+
+@pytest.mark.parametrize("bad,bit", [("slot_dup", O.STATUS_SLOT_DUP), ("status_in", 0x100)])
+def test_prefill_is_all_or_nothing(bad, bit):
+    case, Hk = _prefill_case(seed=112)
+    slots = np.array([0, 2, 2] if bad == "slot_dup" else [0, 1, 2], np.int32)
+    Hv = case["pool"].shape[1]
+    pool = case["pool"].astype(np.float64)
+    out = np.full(case["z"].shape, np.nan)
+    st = O.prefill(case["qkv"], case["ba"][..., :Hv], case["ba"][..., Hv:], case["dt"], case["A"], pool, slots, Hk,
+                   out, status_in=bit if bad == "status_in" else 0)
+    assert st & bit
+    assert np.isnan(out).all() and pool.tobytes() == case["pool"].astype(np.float64).tobytes()
