@@ -30,6 +30,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+MFMA_FP32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, vendor figure
 
 
 def parse():
@@ -38,7 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="tree-c4-n16")
-    ap.add_argument("--instances", type=int, default=64)
+    ap.add_argument("--instances", type=int, default=None,
+                    help="independent layer instances per step (default 64; 8 for --mode prefill)")
     ap.add_argument("--rounds", type=int, default=4, help="distinct tree/acceptance draws cycled over steps")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--kernel-reps", type=int, default=20, help="repetitions of each per-kernel timing loop")
@@ -55,9 +57,11 @@ def parse():
     ap.add_argument("--ragged", action="store_true",
                     help="verify mode: each round draws every lane's node count uniformly from 1..N (seeded) and "
                          "accepts the lane's last node; throughput counts the present nodes")
-    ap.add_argument("--mode", choices=("verify", "decode"), default="verify",
-                    help="the speculative round (headline metric), or the plain decode step of a lane "
-                         "without a draft: conv step + one-token recurrence per instance, state in place")
+    ap.add_argument("--mode", choices=("verify", "decode", "prefill"), default="verify",
+                    help="the speculative round (headline metric); the plain decode step of a lane "
+                         "without a draft (conv step + one-token recurrence per instance, state in place); "
+                         "or a prompt filling the slots (conv step + chunked prefill per instance)")
+    ap.add_argument("--prompt", type=int, default=1024, help="--mode prefill: prompt tokens per lane")
     return ap.parse_args()
 
 
@@ -98,6 +102,19 @@ def decode_bytes(wl):
     conv = 4 * Ch * (C * (W + 1 + 1 + W) + wl.d_conv)
     decode = 4 * (2 * C * Hv * dk * dv + C * Ch + 2 * C * Hv + 2 * Hv + C * Hv * dv)
     return dict(conv_step=conv, decode_step=decode)
+
+
+def prefill_cost(wl, T, chunk=16):
+    """Algorithmic flops and bytes of the chunked prefill over T tokens per lane.  Flops: the
+    dense products of the chunked form per token and value head -- [K; Q] S0 (4 d_k d_v), the
+    state update K^T W D (2 d_k d_v), the Gram products (4 B d_k) and D = T rhs, Cq D
+    (4 B d_v) with B = 16-token chunks.  Bytes: the conv output rows, gates and outputs once,
+    the state read and written once."""
+    C, Ch, Hv, dk, dv = wl.n_seqs, wl.channels, wl.n_v_heads, wl.d_k, wl.d_v
+    flops = C * T * Hv * (6 * dk * dv + 4 * chunk * (dk + dv))
+    bytes_ = 4 * (C * T * Ch + 2 * C * T * Hv + C * T * Hv * dv + 2 * C * Hv * dk * dv + 2 * Hv)
+    conv = 4 * Ch * (2 * C * T + 2 * 3 * C + wl.d_conv)  # tokens in, conv out, history in + out, taps
+    return dict(flops=flops, bytes=bytes_, conv_bytes=conv)
 
 
 def measured_traffic(workload, kernel):
@@ -248,14 +265,130 @@ def decode_main(args):
     print(json.dumps(line), flush=True)
 
 
+def prefill_main(args):
+    """A prompt of T tokens per lane filling the slots at the workload's head shape: for every
+    layer instance the chain conv step over the prompt (history written in place), then the
+    chunked prefill (state updated in place).  value = C * T * L / step time."""
+    import torch
+
+    import gated_deltanet_speculative_amd as gdn
+    from workloads import WORKLOADS, layer_params, round_structure
+
+    wl = WORKLOADS[args.workload]
+    T, L = args.prompt, args.instances
+    sh = gdn.Shape(**dict(wl.shape_dict(), n_nodes=T))
+    C, P, Ch, Hv, dk, dv = sh.n_seqs, sh.n_slots, sh.channels, sh.n_v_heads, sh.d_k, sh.d_v
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t_gen = time.time()
+    gen = torch.Generator(device=dev)
+    slot_ids = d(round_structure(wl, 0, args.seed)["slot_ids"])
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    inst = []
+    for l in range(L):
+        lp = layer_params(wl, l, args.seed)
+        gen.manual_seed(args.seed * 1000003 + l)  # prompt tokens ~ N(0,1), b|a logits ~ N(0,1)
+        ba = torch.randn((C, T, 2 * Hv), generator=gen, device=dev)
+        inst.append(dict(x=torch.randn((C, T, Ch), generator=gen, device=dev), beta=ba[..., :Hv], alpha=ba[..., Hv:],
+                         conv_w=d(lp["conv_w"]), conv_hist=d(lp["conv_hist"]), state=d(lp["state"]),
+                         dt_bias=d(lp["dt_bias"]), A=d(lp["A"]), qkv=torch.empty((C, T, Ch), device=dev),
+                         out=torch.empty((C, T, Hv, dv), device=dev)))
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+
+    def conv(b):
+        gdn.conv_step(sh, b["x"], b["conv_w"], b["conv_hist"], slot_ids, status, conv_out=b["qkv"])
+
+    def rec(b):
+        gdn.prefill(sh, b["qkv"], b["beta"], b["alpha"], b["dt_bias"], b["A"], b["state"], slot_ids, status,
+                    out=b["out"])
+
+    def step():
+        for b in inst:
+            conv(b)
+            rec(b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "device status bits set"
+
+    def timed(fn, reps):
+        run = fn
+        if not args.eager:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            run = g.replay
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps  # ms per run
+
+    ms_step = timed(step, args.steps)
+    kern = {}
+    if not args.profile_only:
+        kern["conv_step"] = timed(lambda: [conv(b) for b in inst], args.kernel_reps) * 1e3 / L
+        kern["prefill"] = timed(lambda: [rec(b) for b in inst], args.kernel_reps) * 1e3 / L
+    assert int(status.item()) == 0, "device status bits set"
+    calibrate_copy(args.calibrate_copy, dev)
+    cost = prefill_cost(wl, T)
+    roofline = None
+    if kern:
+        tflops = cost["flops"] / (kern["prefill"] * 1e-6) / 1e12
+        roofline = dict(bound="mfma", kernel="prefill", achieved=round(tflops, 2), peak=MFMA_FP32_PEAK_TFLOPS,
+                        unit="TFLOP/s", frac=round(tflops / MFMA_FP32_PEAK_TFLOPS, 4),
+                        traffic=measured_traffic(wl.name + "-prefill", "prefill"), flops_per_launch=cost["flops"],
+                        us_per_launch=round(kern["prefill"], 3))
+    line = {
+        "metric": "GDN prefill tokens/s (prompt filling the slots)",
+        "value": round(C * T * L / (ms_step * 1e-3), 1),
+        "unit": "prompt tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "timing": ("eager launches" if args.eager else "HIP graph replay of the whole step")
+                  + "; inputs resident in HBM",
+        "config": {"workload": wl.name + "-prefill", "lanes": C, "prompt_tokens": T, "slots": P,
+                   "k_heads": wl.n_k_heads, "v_heads": Hv, "d_k": dk, "d_v": dv, "conv_channels": Ch,
+                   "layer_instances": L, "step": "conv step over the prompt + chunked prefill per instance"},
+        "kernel_us": {k: round(v, 3) for k, v in kern.items()},
+        "kernel_gbs": ({"conv_step": round(cost["conv_bytes"] / (kern["conv_step"] * 1e-6) / 1e9, 1),
+                        "prefill": round(cost["bytes"] / (kern["prefill"] * 1e-6) / 1e9, 1)} if kern else {}),
+        "roofline": roofline,
+        "setup_s": round(t_gen, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the route needs no collective, "
               "so multi-GPU throughput is the per-GPU figure times the lane-sharded GPU count.", file=sys.stderr)
         sys.exit(2)
+    if args.instances is None:
+        args.instances = 8 if args.mode == "prefill" else 64
     if args.mode == "decode":
         decode_main(args)
+        return
+    if args.mode == "prefill":
+        prefill_main(args)
         return
 
     import torch

@@ -15,6 +15,10 @@ directly:
     conv_step       -> conv_out; writes each slot's conv history in place
     decode_step     -> out; applies one token to each slot's state in place
 
+and a prompt fills a slot with conv_step over its tokens followed by
+
+    prefill         -> out; the recurrence over the prompt, each slot's state in place
+
 The library is loaded on first use and must have been built
 (`python -m gated_deltanet_speculative_amd.build`); there is no fallback path.
 """
@@ -23,6 +27,7 @@ from ._lib import (  # noqa: F401
     EXPORTED,
     GdnError,
     LIB_PATH,
+    MAX_CHAIN,
     MAX_LAYERS,
     Shape,
     STATUS_ACCEPT,
@@ -34,6 +39,7 @@ from ._lib import (  # noqa: F401
     conv_tree_step,
     conv_tree_verify,
     decode_step,
+    prefill,
     load_library,
     replay_commit,
     replay_commit_layers,

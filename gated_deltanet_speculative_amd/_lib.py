@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libgdnverify.so")
 GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP, GDN_ERR_ALIGN = range(7)
 STATUS_SLOT_RANGE, STATUS_SLOT_DUP, STATUS_PARENT, STATUS_ACCEPT, STATUS_NODES = 1, 2, 4, 8, 16
 EXPORTED = ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_conv_tree_verify", "gdn_replay_commit",
-            "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step", "gdn_strerror")
+            "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step", "gdn_prefill", "gdn_strerror")
+MAX_CHAIN = 65536
 MAX_LAYERS = 64
 
 
@@ -79,8 +80,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdn_replay_commit_layers.argtypes = [sp, i32] + [vp] * 10
     lib.gdn_conv_step.argtypes = [sp] + [vp] * 7
     lib.gdn_decode_step.argtypes = [sp, vp, vp, vp, i64] + [vp] * 7
+    lib.gdn_prefill.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, vp, vp, vp]
     for f in ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_conv_tree_verify", "gdn_replay_commit",
-              "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step"):
+              "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step", "gdn_prefill"):
         getattr(lib, f).restype = i32
     lib.gdn_strerror.argtypes = [ctypes.c_int]
     lib.gdn_strerror.restype = ctypes.c_char_p
@@ -372,4 +374,38 @@ def decode_step(sh: Shape, qkv, beta_logits, alpha_logits, dt_bias, A, state_poo
     ]
     cs = sh.c_struct()
     _check(load_library().gdn_decode_step(ctypes.byref(cs), *args), "gdn_decode_step")
+    return out
+
+
+# ---------------------------------------------------------------- prefill
+def prefill(sh: Shape, qkv, beta_logits, alpha_logits, dt_bias, A, state_pool, slot_ids, status, gate_z=None,
+            gate_mode=0, out=None):
+    """The recurrence over a chain of n_nodes tokens per lane (qkv [C, T, Ch] = the conv
+    output of the prompt), updating the slots' states in place; beta/alpha logits are
+    [C, T, H_v] views sharing one row stride.  With gate_z ([C, T, H_v, d_v]) the output is
+    gated by silu(z) (gate_mode 0) or sigmoid(z) (gate_mode 1).  A transaction on the
+    status word.  Returns out [C, T, H_v, d_v]."""
+    C, T, P, Hv, dk, dv = sh.n_seqs, sh.n_nodes, sh.n_slots, sh.n_v_heads, sh.d_k, sh.d_v
+    if status is None:
+        raise ValueError("prefill needs a status word (it mutates the state pool)")
+    if out is None:
+        out = torch.empty((C, T, Hv, dv), dtype=torch.float32, device=qkv.device)
+    bp, bs = _gate_view(beta_logits, "beta_logits", sh)
+    ap, as_ = _gate_view(alpha_logits, "alpha_logits", sh)
+    if bs != as_:
+        raise ValueError("beta_logits and alpha_logits must share one row stride")
+    args = [
+        _dev(qkv, "qkv", torch.float32, (C, T, sh.channels)), bp, ap, bs,
+        _dev(dt_bias, "dt_bias", torch.float32, (Hv,)),
+        _dev(A, "A", torch.float32, (Hv,)),
+        _dev(state_pool, "state_pool", torch.float32, (P, Hv, dk, dv)),
+        _dev(slot_ids, "slot_ids", torch.int32, (C,)),
+        None if gate_z is None else _dev(gate_z, "gate_z", torch.float32, (C, T, Hv, dv)),
+        ctypes.c_int32(int(gate_mode)),
+        _dev(out, "out", torch.float32, (C, T, Hv, dv)),
+        _dev(status, "status", torch.int32, (1,)),
+        _stream(qkv),
+    ]
+    cs = sh.c_struct()
+    _check(load_library().gdn_prefill(ctypes.byref(cs), *args), "gdn_prefill")
     return out

@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdnverify.so")
 ARCH = "gfx950"
 
-SOURCES = ["gdn_api.cpp", "conv_tree_step.hip", "tree_verify.hip", "replay_commit.hip", "decode_step.hip"]
+SOURCES = ["gdn_api.cpp", "conv_tree_step.hip", "tree_verify.hip", "replay_commit.hip", "decode_step.hip",
+           "prefill.hip"]
 
 # Packed-FP32 instructions are disabled: the compiler may otherwise fuse ordinary
 # float code into them.

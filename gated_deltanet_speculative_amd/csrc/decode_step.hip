@@ -28,59 +28,18 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBitmapSlots = 65536;  // duplicate-slot check via an LDS bitmap up to this pool size
-constexpr int kTokChunk = 8;         // conv step: tokens loaded together
-constexpr int kLanesPerThread = (GDN_MAX_SEQS + kThreads - 1) / kThreads;
+constexpr int kTokChunk = 8;  // conv step: tokens loaded together
+constexpr int kTokRun = 32;   // conv step: tokens per thread (runs of a long chain in parallel)
+using LaneSlots = LaneSlotsT<kThreads>;
 
-// The slot ids of lanes tid, tid + kThreads, ... (for slot_preflight), loaded ahead of
-// the bulk loads so the preflight does not wait for them.
-struct LaneSlots {
-    int v[kLanesPerThread];
-    __device__ LaneSlots(const int32_t *__restrict__ slot_ids, int C) {
-#pragma unroll
-        for (int k = 0; k < kLanesPerThread; ++k) v[k] = slot_ids[min((int)threadIdx.x + kThreads * k, C - 1)];
-    }
-};
-
-// Slot preflight of a call that mutates the pools: GDN_STATUS_SLOT_RANGE /
-// GDN_STATUS_SLOT_DUP over every non-padding lane.  Every thread of the workgroup must
-// call it (it contains barriers); all threads receive the same bits.
-__device__ int slot_preflight(const LaneSlots &ls, const int32_t *__restrict__ slot_ids, const Dims &d,
-                              unsigned int *bitmap, int *word) {
-    const bool use_bitmap = d.P <= kBitmapSlots;
-    if (use_bitmap)
-        for (int w = threadIdx.x; w < (d.P + 31) / 32; w += kThreads) bitmap[w] = 0u;
-    if (threadIdx.x == 0) *word = 0;
-    lds_barrier();
-    int bits = 0;
-#pragma unroll
-    for (int k = 0; k < kLanesPerThread; ++k) {
-        const int t = threadIdx.x + kThreads * k;
-        const int st = ls.v[k];
-        if (t >= d.C || st == -1) continue;
-        if (st < -1 || st >= d.P) {
-            bits |= GDN_STATUS_SLOT_RANGE;
-        } else if (use_bitmap) {
-            const unsigned int m = 1u << (st & 31);
-            if (atomicOr(&bitmap[st >> 5], m) & m) bits |= GDN_STATUS_SLOT_DUP;
-        } else {
-            for (int o = 0; o < d.C; ++o)
-                if (o != t && slot_ids[o] == st) bits |= GDN_STATUS_SLOT_DUP;
-        }
-    }
-    if (bits) atomicOr(word, bits);
-    lds_barrier();
-    return *word;
-}
-
-// Sum over the lanes of a wave that share lane % Q (Q = 4 or 8): rotations within each
-// row of 16 lanes, then the row pairs and wave halves exchanged by permlane swaps (with
-// both operands equal, the two results of a swap add up to the pairwise sum).
 template <int M>
 __device__ inline float row_ror(float x) {  // lane (i - M) mod 16 of each row of 16 lanes (DPP row_ror)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + M, 0xF, 0xF, false));
 }
 
+// Sum over the lanes of a wave that share lane % Q (Q = 4 or 8): rotations within each
+// row of 16 lanes, then the row pairs and wave halves exchanged by permlane swaps (with
+// both operands equal, the two results of a swap add up to the pairwise sum).
 template <int Q>
 __device__ inline float sum_lanes_sharing(float x) {
     static_assert(Q == 4 || Q == 8, "column groups per wave row");
@@ -92,8 +51,12 @@ __device__ inline float sum_lanes_sharing(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// ---- conv step: thread = (lane c = blockIdx.y, 4-channel group g); the window slides
-//      over the chain in registers, oldest column first (tap 0 multiplies it).
+// ---- conv step: thread = (lane c = blockIdx.y, 4-channel group g, run r = blockIdx.z of
+//      kTokRun consecutive tokens).  The window slides over the run in registers, oldest
+//      column first (tap 0 multiplies it); a run's first window is the 3 tokens before it,
+//      or the slot's history for run 0.  The thread of run 0 is the only one that reads the
+//      slot's history, and it alone writes the new one (the last 3 columns of history +
+//      chain, formed from the chain's last tokens), so the in-place update has no hazard.
 __global__ __launch_bounds__(kThreads) void conv_step_kernel(Dims d, const float *__restrict__ x,
                                                              const float *__restrict__ conv_w,
                                                              float *__restrict__ conv_hist,
@@ -101,41 +64,63 @@ __global__ __launch_bounds__(kThreads) void conv_step_kernel(Dims d, const float
                                                              float *__restrict__ conv_out, int32_t *__restrict__ status) {
     __shared__ unsigned int s_bitmap[kBitmapSlots / 32];
     __shared__ int s_word;
-    const int c = blockIdx.y, G4 = d.Ch / 4;
+    const int c = blockIdx.y, G4 = d.Ch / 4, N = d.N;
     const int g = blockIdx.x * kThreads + threadIdx.x, gc = g < G4 ? g : G4 - 1;
+    const int t0 = blockIdx.z * kTokRun, tn = min(kTokRun, N - t0);
+    const bool first = blockIdx.z == 0;
     const LaneSlots lanes(slot_ids, d.C);
     const int s = slot_ids[c];
     const int st_in = *status;
     const bool s_ok = s >= 0 && s < d.P;
-    // loads first: taps, the slot's history (slot clamped into range), the first tokens
+    // loads first: taps, the run's first window (history, or the 3 tokens before the run),
+    // the run's first tokens, and (run 0) the chain's last 3 tokens for the new history
     v4f w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) w[e] = reinterpret_cast<const v4f *>(conv_w)[4 * gc + e];
     v4f *hp = reinterpret_cast<v4f *>(conv_hist + ((int64_t)(s_ok ? s : 0) * d.Ch + 4 * gc) * 3);
-    const v4f h0 = hp[0], h1 = hp[1], h2 = hp[2];
-    const v4f *xr = reinterpret_cast<const v4f *>(x + (int64_t)c * d.N * d.Ch) + gc;
+    const v4f *xr = reinterpret_cast<const v4f *>(x + (int64_t)c * N * d.Ch) + gc;
+    v4f a, b, cc;  // window columns, oldest first
+    if (first) {
+        const v4f h0 = hp[0], h1 = hp[1], h2 = hp[2];  // layout [ch][3]: 12 consecutive floats
+        a = v4f{h0.x, h0.w, h1.z, h2.y};
+        b = v4f{h0.y, h1.x, h1.w, h2.z};
+        cc = v4f{h0.z, h1.y, h2.x, h2.w};
+    } else {
+        a = xr[(int64_t)(t0 - 3) * G4];
+        b = xr[(int64_t)(t0 - 2) * G4];
+        cc = xr[(int64_t)(t0 - 1) * G4];
+    }
     v4f xt[kTokChunk];
 #pragma unroll
-    for (int t = 0; t < kTokChunk; ++t) xt[t] = xr[(int64_t)min(t, d.N - 1) * G4];
+    for (int t = 0; t < kTokChunk; ++t) xt[t] = xr[(int64_t)min(t0 + t, N - 1) * G4];
+    v4f last[3];  // run 0: tokens N-3..N-1 (clamped; only those that exist are used)
+    if (first)
+#pragma unroll
+        for (int k = 0; k < 3; ++k) last[k] = xr[(int64_t)max(N - 3 + k, 0) * G4];
 
-    const int bits = slot_preflight(lanes, slot_ids, d, s_bitmap, &s_word);
+    const int bits = slot_preflight<kThreads>(lanes, slot_ids, d.C, d.P, s_bitmap, &s_word);
     if (bits || st_in) {
-        if (bits && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) atomicOr(status, bits);
+        if (bits && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) atomicOr(status, bits);
         return;
     }
     if (s < 0 || g >= G4) return;  // padding lane, or past the channels
 
-    // history columns of the 4 channels (layout [ch][3]: 12 consecutive floats)
-    v4f a = {h0.x, h0.w, h1.z, h2.y}, b = {h0.y, h1.x, h1.w, h2.z}, cc = {h0.z, h1.y, h2.x, h2.w};
-    v4f *orow = reinterpret_cast<v4f *>(conv_out + (int64_t)c * d.N * d.Ch) + g;
-    for (int t0 = 0; t0 < d.N; t0 += kTokChunk) {
-        if (t0 > 0) {
+    // the new history (run 0): the last 3 columns of [history; chain]
+    v4f nh[3];
+    if (first) {
+        const v4f old[3] = {a, b, cc};
 #pragma unroll
-            for (int t = 0; t < kTokChunk; ++t) xt[t] = xr[(int64_t)min(t0 + t, d.N - 1) * G4];
+        for (int k = 0; k < 3; ++k) nh[k] = N - 3 + k >= 0 ? last[k] : old[N + k];
+    }
+    v4f *orow = reinterpret_cast<v4f *>(conv_out + (int64_t)c * N * d.Ch) + g;
+    for (int u0 = 0; u0 < tn; u0 += kTokChunk) {
+        if (u0 > 0) {
+#pragma unroll
+            for (int t = 0; t < kTokChunk; ++t) xt[t] = xr[(int64_t)min(t0 + u0 + t, N - 1) * G4];
         }
 #pragma unroll
         for (int t = 0; t < kTokChunk; ++t) {
-            if (t0 + t >= d.N) break;
+            if (u0 + t >= tn) break;
             v4f y;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -145,17 +130,17 @@ __global__ __launch_bounds__(kThreads) void conv_step_kernel(Dims d, const float
                 z = fmaf(xt[t][e], w[e][3], z);
                 y[e] = z / (1.0f + expf(-z));
             }
-            orow[(int64_t)(t0 + t) * G4] = y;
+            orow[(int64_t)(t0 + u0 + t) * G4] = y;
             a = b;
             b = cc;
             cc = xt[t];
         }
     }
-    // the slot's new history: the last 3 columns, in place (only this thread reads or
-    // writes these 12 floats)
-    hp[0] = v4f{a.x, b.x, cc.x, a.y};
-    hp[1] = v4f{b.y, cc.y, a.z, b.z};
-    hp[2] = v4f{cc.z, a.w, b.w, cc.w};
+    if (first) {  // in place: only this thread reads or writes these 12 floats
+        hp[0] = v4f{nh[0].x, nh[1].x, nh[2].x, nh[0].y};
+        hp[1] = v4f{nh[1].y, nh[2].y, nh[0].z, nh[1].z};
+        hp[2] = v4f{nh[2].z, nh[0].w, nh[1].w, nh[2].w};
+    }
 }
 
 // ---- decode step: workgroup = (lane c = blockIdx.y, value head h, block of JB value
@@ -214,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     for (int k = 0; k < RPT; ++k) sv[k] = S4[min(r + RG * k, DK - 1) * (DV / 4)];
 
     if (wave < 2 && lane < DK / 4) reinterpret_cast<v4f *>(wave == 0 ? s_q : s_k)[lane] = qk4;
-    const int bits = slot_preflight(lanes, slot_ids, d, s_bitmap, &s_word);  // its barriers also publish s_q / s_k
+    const int bits = slot_preflight<kThreads>(lanes, slot_ids, d.C, d.P, s_bitmap, &s_word);  // its barriers also publish s_q / s_k
     if (bits || st_in) {
         if (bits && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) atomicOr(status, bits);
         return;
@@ -291,8 +276,9 @@ hipError_t launch_decode(const Dims &d, const float *qkv, const float *beta_logi
 hipError_t launch_conv_step(const Dims &d, const float *x, const float *conv_w, float *conv_hist,
                             const int32_t *slot_ids, float *conv_out, int32_t *status, hipStream_t stream) {
     const int groups = d.Ch / 4;
-    hipLaunchKernelGGL(conv_step_kernel, dim3((groups + kThreads - 1) / kThreads, d.C), dim3(kThreads), 0, stream, d,
-                       x, conv_w, conv_hist, slot_ids, conv_out, status);
+    const dim3 grid((groups + kThreads - 1) / kThreads, d.C, (d.N + kTokRun - 1) / kTokRun);
+    hipLaunchKernelGGL(conv_step_kernel, grid, dim3(kThreads), 0, stream, d, x, conv_w, conv_hist, slot_ids, conv_out,
+                       status);
     return hipGetLastError();
 }
 

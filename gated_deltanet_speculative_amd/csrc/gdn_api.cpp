@@ -38,17 +38,20 @@ bool aligned(std::initializer_list<const void *> ps, uintptr_t a) {
 
 bool pow2_width(int v) { return v == 16 || v == 32 || v == 64 || v == 128; }
 
-int check_shape(const gdn_shape *sh, gdn::Dims *d) {
+// chain = false: a draft tree (n_nodes <= GDN_MAX_NODES, commit windows of one lane below
+// 1 GiB); chain = true: a chain of up to GDN_MAX_CHAIN tokens (conv step, prefill)
+int check_shape(const gdn_shape *sh, gdn::Dims *d, bool chain = false) {
     if (!sh) return GDN_ERR_NULL;
     if (sh->n_seqs <= 0 || sh->n_nodes <= 0 || sh->n_slots <= 0 || sh->n_k_heads <= 0 || sh->n_v_heads <= 0 ||
         sh->d_k <= 0 || sh->d_v <= 0 || sh->d_conv <= 0)
         return GDN_ERR_SHAPE;
     if (sh->n_v_heads % sh->n_k_heads != 0) return GDN_ERR_SHAPE;
-    if (sh->d_conv != 4 || !pow2_width(sh->d_k) || !pow2_width(sh->d_v) || sh->n_nodes > GDN_MAX_NODES ||
-        sh->n_seqs > GDN_MAX_SEQS)
+    if (sh->d_conv != 4 || !pow2_width(sh->d_k) || !pow2_width(sh->d_v) ||
+        sh->n_nodes > (chain ? GDN_MAX_CHAIN : GDN_MAX_NODES) || sh->n_seqs > GDN_MAX_SEQS)
         return GDN_ERR_UNSUPPORTED;
     const int64_t ch = 2ll * sh->n_k_heads * sh->d_k + (int64_t)sh->n_v_heads * sh->d_v;
-    if (ch > (1 << 24) || (int64_t)sh->n_slots * sh->n_v_heads > (1 << 24) || (int64_t)sh->n_nodes * ch * 12 > (1 << 30))
+    if (ch > (1 << 24) || (int64_t)sh->n_slots * sh->n_v_heads > (1 << 24) ||
+        (!chain && (int64_t)sh->n_nodes * ch * 12 > (1 << 30)))
         return GDN_ERR_UNSUPPORTED;
     *d = gdn::Dims{sh->n_seqs, sh->n_nodes, sh->n_slots, sh->n_k_heads, sh->n_v_heads, sh->d_k, sh->d_v, (int)ch};
     return GDN_OK;
@@ -228,7 +231,7 @@ int gdn_replay_commit(const gdn_shape *sh, const float *replay_log, const float 
 int gdn_conv_step(const gdn_shape *sh, const float *x, const float *conv_w, float *conv_hist,
                   const int32_t *slot_ids, float *conv_out, int32_t *status, hipStream_t stream) {
     gdn::Dims d;
-    if (int r = check_shape(sh, &d)) return r;
+    if (int r = check_shape(sh, &d, true)) return r;
     if (!x || !conv_w || !conv_hist || !slot_ids || !conv_out || !status) return GDN_ERR_NULL;
     if (!aligned({x, conv_w, conv_hist, conv_out}, 16) || !aligned({slot_ids, status}, 4)) return GDN_ERR_ALIGN;
     const size_t cnc = (size_t)d.C * d.N * d.Ch;
@@ -259,6 +262,31 @@ int gdn_decode_step(const gdn_shape *sh, const float *qkv, const float *beta_log
         return GDN_ERR_ALIAS;
     return gdn::launch_decode_step(d, qkv, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids,
                                    out, status, stream) == hipSuccess
+               ? GDN_OK
+               : GDN_ERR_HIP;
+}
+
+int gdn_prefill(const gdn_shape *sh, const float *qkv, const float *beta_logits, const float *alpha_logits,
+                int64_t gate_stride, const float *dt_bias, const float *A, float *state_pool, const int32_t *slot_ids,
+                const float *gate_z, int32_t gate_mode, float *out, int32_t *status, hipStream_t stream) {
+    gdn::Dims d;
+    if (int r = check_shape(sh, &d, true)) return r;
+    if (!qkv || !beta_logits || !alpha_logits || !dt_bias || !A || !state_pool || !slot_ids || !out || !status)
+        return GDN_ERR_NULL;
+    if (gate_stride < d.Hv || (gate_mode != 0 && gate_mode != 1)) return GDN_ERR_SHAPE;
+    if (!aligned({qkv, state_pool, out, gate_z}, 16) ||
+        !aligned({beta_logits, alpha_logits, dt_bias, A, slot_ids, status}, 4))
+        return GDN_ERR_ALIGN;
+    const size_t rows = (size_t)d.C * d.N;
+    const size_t gate_bytes = ((rows - 1) * (size_t)gate_stride + d.Hv) * F;
+    const size_t out_b = rows * d.Hv * d.dv * F;
+    if (any_alias({{state_pool, (size_t)d.P * d.Hv * d.dk * d.dv * F}, {out, out_b}, {status, I}},
+                  {{qkv, rows * d.Ch * F}, {beta_logits, gate_bytes}, {alpha_logits, gate_bytes},
+                   {dt_bias, (size_t)d.Hv * F}, {A, (size_t)d.Hv * F}, {slot_ids, (size_t)d.C * I},
+                   {gate_z, out_b}}))
+        return GDN_ERR_ALIAS;
+    return gdn::launch_prefill(d, d.N, qkv, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids,
+                               gate_z, gate_mode, out, status, stream) == hipSuccess
                ? GDN_OK
                : GDN_ERR_HIP;
 }

@@ -4,6 +4,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <utility>
+
+#include "gdn_verify.h"
+
 namespace gdn {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -30,5 +34,99 @@ __device__ inline float fast_softplus(float x) {
 }
 __device__ inline float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + fast_exp(-x)); }
 __device__ inline float fast_silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + fast_exp(-z)); }
+
+// Four steps of v_mfma_f32_16x16x4_f32 over one 16-wide chunk of a contraction.  Within the
+// chunk, lane group g = lane / 16 supplies index 4g + s in step s (a permutation shared by
+// both operands), so a 16 x 16 accumulator tile -- lane holding rows 4g..4g+3 of column
+// lane % 16 -- is directly the right operand of a following product.
+__device__ inline v4f mfma4(v4f a, v4f b, v4f acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+    return acc;
+}
+
+// x[lane] + x[lane - SH] within each row of 16 lanes (0 past the row start): DPP row_shr
+template <int SH>
+__device__ inline float add_row_shr(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + SH, 0xF, 0xF, true));
+}
+
+// value of lane K of each row of 16 lanes, in every lane of the row (DPP row_newbcast)
+template <int K>
+__device__ inline float row_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + K, 0xF, 0xF, false));
+}
+
+// Forward substitution of one column of (I + L) t = e_a over a row of 16 lanes, lane i
+// holding t_i (initially [i == a]) and row i of the strictly lower L: at step k, t_k is
+// final and is broadcast to the row; rows above k are unchanged since L[i][k] = 0 there.
+template <int... K>
+__device__ inline float bcast_solve(float t, const v4f *Lr, std::integer_sequence<int, K...>) {
+    ((t = fmaf(-Lr[K / 4][K % 4], row_bcast<K>(t), t)), ...);
+    return t;
+}
+
+// Sum over aligned groups of W consecutive lanes (W = 4, 8 or 16; W = 16 is a DPP row),
+// left in the last lane of each group; with W = 16 also the inclusive prefix sum along
+// each row of 16 lanes.
+template <int W>
+__device__ inline float group_sum_last(float x) {
+    x = add_row_shr<1>(x);
+    x = add_row_shr<2>(x);
+    if constexpr (W >= 8) x = add_row_shr<4>(x);
+    if constexpr (W >= 16) x = add_row_shr<8>(x);
+    return x;
+}
+
+// ---- slot preflight of the calls that write the pools directly (plain decode step,
+//      prefill): slot range and duplicate slots over every non-padding lane
+
+constexpr int kBitmapSlots = 65536;  // duplicate-slot check via an LDS bitmap up to this pool size
+
+// The slot ids of lanes tid, tid + THREADS, ... (for slot_preflight), loaded ahead of the
+// bulk loads so the preflight does not wait behind them.
+template <int THREADS>
+struct LaneSlotsT {
+    static constexpr int kPerThread = (GDN_MAX_SEQS + THREADS - 1) / THREADS;
+    int v[kPerThread];
+    __device__ LaneSlotsT(const int32_t *__restrict__ slot_ids, int C) {
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) v[k] = slot_ids[min((int)threadIdx.x + THREADS * k, C - 1)];
+    }
+};
+
+// GDN_STATUS_SLOT_RANGE / GDN_STATUS_SLOT_DUP over every non-padding lane, with an LDS
+// bitmap of kBitmapSlots / 32 words (or a scan for larger pools) and one LDS word.  Every
+// thread of the workgroup must call it (it contains barriers); all receive the same bits.
+template <int THREADS>
+__device__ int slot_preflight(const LaneSlotsT<THREADS> &ls, const int32_t *__restrict__ slot_ids, int C, int P,
+                              unsigned int *bitmap, int *word) {
+    const bool use_bitmap = P <= kBitmapSlots;
+    if (use_bitmap)
+        for (int w = threadIdx.x; w < (P + 31) / 32; w += THREADS) bitmap[w] = 0u;
+    if (threadIdx.x == 0) *word = 0;
+    lds_barrier();
+    int bits = 0;
+#pragma unroll
+    for (int k = 0; k < LaneSlotsT<THREADS>::kPerThread; ++k) {
+        const int t = threadIdx.x + THREADS * k;
+        const int st = ls.v[k];
+        if (t >= C || st == -1) continue;
+        if (st < -1 || st >= P) {
+            bits |= GDN_STATUS_SLOT_RANGE;
+        } else if (use_bitmap) {
+            const unsigned int m = 1u << (st & 31);
+            if (atomicOr(&bitmap[st >> 5], m) & m) bits |= GDN_STATUS_SLOT_DUP;
+        } else {
+            for (int o = 0; o < C; ++o)
+                if (o != t && slot_ids[o] == st) bits |= GDN_STATUS_SLOT_DUP;
+        }
+    }
+    if (bits) atomicOr(word, bits);
+    lds_barrier();
+    return *word;
+}
 
 }  // namespace gdn

@@ -28,7 +28,6 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBitmapSlots = 65536;  // duplicate-slot check via an LDS bitmap up to this pool size
 
 template <int DK, int DV>
 struct CommitCfg {

@@ -51,8 +51,6 @@
 // product operands; the conv output never goes to memory.  The commit windows are
 // written once, by copy-only workgroups appended to the same launch (one per lane and
 // block of channels), which run beside the verify workgroups.
-#include <utility>
-
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -117,53 +115,6 @@ struct VerifyLayout {
     static constexpr int SCR = STAGE > GPART + 8 * UNIT ? STAGE : GPART + 8 * UNIT;
     static constexpr int LDS_FLOATS = OFF_SCR + SCR;
 };
-
-__device__ inline v4f mfma4(v4f a, v4f b, v4f acc) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
-    return acc;
-}
-
-// x[lane] + x[lane - SH] within each row of 16 lanes (0 past the row start): DPP row_shr
-template <int SH>
-__device__ inline float add_row_shr(float x) {
-    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + SH, 0xF, 0xF, true));
-}
-
-// value of the lane whose index differs in bit log2(X) within each quad (DPP quad_perm)
-template <int X>
-__device__ inline float quad_xor(float x) {
-    constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false));
-}
-
-// value of lane K of each row of 16 lanes, in every lane of the row (DPP row_newbcast)
-template <int K>
-__device__ inline float row_bcast(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + K, 0xF, 0xF, false));
-}
-
-// Forward substitution of one column of (I + L) t = e_a over a row of 16 lanes, lane i
-// holding t_i (initially [i == a]) and row i of the strictly lower L: at step k, t_k is
-// final and is broadcast to the row; rows above k are unchanged since L[i][k] = 0 there.
-template <int... K>
-__device__ inline float bcast_solve(float t, const v4f *Lr, std::integer_sequence<int, K...>) {
-    ((t = fmaf(-Lr[K / 4][K % 4], row_bcast<K>(t), t)), ...);
-    return t;
-}
-
-// Sum over aligned groups of W consecutive lanes (W = 4, 8 or 16; W = 16 is a DPP row),
-// left in the last lane of each group.
-template <int W>
-__device__ inline float group_sum_last(float x) {
-    x = add_row_shr<1>(x);
-    x = add_row_shr<2>(x);
-    if constexpr (W >= 8) x = add_row_shr<4>(x);
-    if constexpr (W >= 16) x = add_row_shr<8>(x);
-    return x;
-}
 
 // Tree conv + SiLU of 4 channels at one node from its sources, oldest first (x3 = the
 // node's own tokens); w[e] holds the 4 taps of channel e (tap 0 = oldest), summed from

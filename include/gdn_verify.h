@@ -23,6 +23,10 @@
  *   gdn_decode_step  one token of the gated delta rule applied to each slot's state in
  *                    place, with the output row.
  *
+ * A prompt fills a slot the same way, with gdn_conv_step over its tokens and then
+ *   gdn_prefill      the gated delta rule over a chain of tokens per lane, the slot's state
+ *                    updated in place, with an optional closing output gate.
+ *
  * Sources (page title, then section):
  *   "perf(qwen35): fuse the DFlash2 concurrent verify Gated DeltaNet route",
  *       Summary and Optimizations (the three operations and their inputs/outputs),
@@ -88,8 +92,9 @@ extern "C" {
 #define GDN_ERR_SHAPE 2       /* non-positive dimension, H_v % H_k != 0, gate_stride < H_v   */
 #define GDN_ERR_UNSUPPORTED 3 /* d_conv != 4, d_k/d_v not in {16,32,64,128}, N > 32, C > 1024,
                                  n_layers outside 1..GDN_MAX_LAYERS, Ch > 2^24, P*H_v > 2^24,
-                                 one lane's commit windows above 1 GiB (N*Ch*12 bytes), or
-                                 N != 1 for gdn_decode_step                                  */
+                                 one lane's commit windows above 1 GiB (N*Ch*12 bytes),
+                                 N != 1 for gdn_decode_step, or N > GDN_MAX_CHAIN for the
+                                 chain calls gdn_conv_step / gdn_prefill                     */
 #define GDN_ERR_ALIAS 4       /* an output byte range overlaps an input or another output    */
 #define GDN_ERR_HIP 5         /* a kernel launch failed                                      */
 #define GDN_ERR_ALIGN 6       /* a dense float buffer is not 16-byte aligned, or an int32 /
@@ -103,6 +108,7 @@ extern "C" {
 #define GDN_STATUS_NODES 16     /* lane_nodes[c] outside [0, N]                              */
 
 #define GDN_MAX_NODES 32
+#define GDN_MAX_CHAIN 65536 /* tokens per lane of gdn_conv_step and gdn_prefill */
 #define GDN_MAX_SEQS 1024
 #define GDN_MAX_LAYERS 64
 
@@ -250,7 +256,7 @@ int gdn_replay_commit_layers(const gdn_shape *sh, int32_t n_layers, const float 
  * window, silu(conv) and in-place history write-back; tap order from
  * "llama-cpp-bonsai-gdn-conv.patch", ssm-conv.cu hunk).
  *
- * x[c] is a chain of N = n_nodes tokens for lane c (slot s).  With E the slot's history
+ * x[c] is a chain of N = n_nodes tokens for lane c (slot s), 1..GDN_MAX_CHAIN.  With E the slot's history
  * columns conv_hist[s][:, 0..2] (oldest first) followed by x[c][0..N-1]:
  *   conv_out[c][t][ch] = silu( sum_{j=0..3} conv_w[ch][j] * E[t + j][ch] )
  * and afterwards conv_hist[s][ch][j] = E[N + j][ch], j = 0..2 (the last 3 columns,
@@ -297,6 +303,35 @@ int gdn_conv_step(const gdn_shape *sh, const float *x, const float *conv_w, floa
 int gdn_decode_step(const gdn_shape *sh, const float *qkv, const float *beta_logits, const float *alpha_logits,
                     int64_t gate_stride, const float *dt_bias, const float *A, float *state_pool,
                     const int32_t *slot_ids, float *out, int32_t *status, hipStream_t stream);
+
+/*
+ * Prefill ("Feature/support dflash2", first-version commit message: prefill's recurrence
+ * runs on a chunked GDN kernel that closes with a SiLU or, by gate_mode, a sigmoid output
+ * gate; gates as in gdn_tree_verify).
+ *
+ * n_nodes = T is the number of tokens per lane (1..GDN_MAX_CHAIN), a chain.  For lane c
+ * (slot s) and value head h, the tokens t = 0..T-1 in order apply the rule of
+ * gdn_decode_step to state_pool[s][h] (in place), and
+ *   out[c][t][h] = o_t                      without a gate (gate_z NULL),
+ *   out[c][t][h] = o_t * silu(z)            gate_mode 0,
+ *   out[c][t][h] = o_t * sigmoid(z)         gate_mode 1,   z = gate_z[c][t][h]
+ * (silu(z) = z * sigmoid(z)).  A transaction with the preflight of gdn_conv_step.
+ *
+ *   qkv            [C][T][Ch]          conv output rows of the tokens        (read)
+ *   beta_logits    element (c,t,h) at beta_logits[(c*T+t)*gate_stride + h] (read)
+ *   alpha_logits   element (c,t,h) at alpha_logits[(c*T+t)*gate_stride + h](read)
+ *   gate_stride    >= H_v
+ *   dt_bias, A     [H_v]                                                    (read)
+ *   state_pool     [P][H_v][d_k][d_v]  updated in place
+ *   slot_ids       [C]                 int32, -1 = padding lane             (read)
+ *   gate_z         [C][T][H_v][d_v]    output gate values, or NULL          (read)
+ *   gate_mode      0 (SiLU) or 1 (sigmoid); GDN_ERR_SHAPE otherwise
+ *   out            [C][T][H_v][d_v]    written for non-padding lanes
+ *   status         int32*, REQUIRED (GDN_ERR_NULL otherwise)
+ */
+int gdn_prefill(const gdn_shape *sh, const float *qkv, const float *beta_logits, const float *alpha_logits,
+                int64_t gate_stride, const float *dt_bias, const float *A, float *state_pool, const int32_t *slot_ids,
+                const float *gate_z, int32_t gate_mode, float *out, int32_t *status, hipStream_t stream);
 
 /* Static description of a GDN_OK / GDN_ERR_* code. */
 const char *gdn_strerror(int code);

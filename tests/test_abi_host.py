@@ -269,3 +269,35 @@ def test_lane_nodes_checked_like_any_input():
     assert _verify(sh, p, 8, lane_nodes=p[9] + 8) == _lib.GDN_ERR_ALIAS  # counts inside the replay log
     p = _ptrs(7)
     assert _commit(sh, p, FAKE + (9 << 28), lane_nodes=p[5] + 16) == _lib.GDN_ERR_ALIAS  # counts inside the pool
+
+
+def test_prefill_rejections():
+    lib = gdn.load_library()
+    st = FAKE + (1 << 40)
+
+    def call(sh, p, gate_stride=8, gate_mode=0, status=st):
+        cs = sh.c_struct()
+        return lib.gdn_prefill(ctypes.byref(cs), p[0], p[1], p[2], gate_stride, p[3], p[4], p[5], p[6], p[7],
+                               ctypes.c_int32(gate_mode), p[8], status, None)
+
+    p = _ptrs(9)  # qkv, beta, alpha, dt_bias, A, state_pool, slot_ids, gate_z, out
+    assert call(_shape(n_nodes=1000), p, status=None) == _lib.GDN_ERR_NULL
+    assert call(_shape(n_nodes=65537), p) == _lib.GDN_ERR_UNSUPPORTED  # longer than GDN_MAX_CHAIN
+    assert call(_shape(n_nodes=1000), p, gate_mode=2) == _lib.GDN_ERR_SHAPE
+    assert call(_shape(n_nodes=1000), p, gate_stride=3) == _lib.GDN_ERR_SHAPE
+    q = list(p)
+    q[7] += 4  # gate values not 16-byte aligned
+    assert call(_shape(n_nodes=1000), q) == _lib.GDN_ERR_ALIGN
+    q = list(p)
+    q[5] = q[0] + 64  # state pool (written in place) inside qkv
+    assert call(_shape(n_nodes=1000), q) == _lib.GDN_ERR_ALIAS
+    q = list(p)
+    q[8] = q[7] + 16  # out overlapping the gate values
+    assert call(_shape(n_nodes=1000), q) == _lib.GDN_ERR_ALIAS
+
+
+def test_conv_step_chain_limit():
+    """The chain conv step takes up to GDN_MAX_CHAIN tokens (it feeds the prefill); longer
+    chains are rejected before anything is enqueued."""
+    assert gdn.MAX_CHAIN == 65536
+    assert _conv_step(_shape(n_nodes=65537), _ptrs(5), FAKE + (1 << 40)) == _lib.GDN_ERR_UNSUPPORTED

@@ -99,11 +99,12 @@ def _compare_rows(gbuf, ref, slots, tol, label):
     return e
 
 
-@pytest.mark.parametrize("n", [1, 5, 19])
+@pytest.mark.parametrize("n", [1, 2, 5, 19, 70])
 def test_conv_step_parity(n):
-    """Chain conv step over n tokens (19 spans three 8-token chunks with a ragged tail)."""
+    """Chain conv step over n tokens: 2 leaves a history mixing old columns and tokens, 19
+    spans three 8-token loads with a ragged tail, 70 three 32-token runs of threads."""
     C, P, Hk, Hv, dk, dv = 3, 6, 2, 4, 32, 16
-    case = synth_case(C, 20, P, Hk, Hv, dk, dv, seed=40 + n, tree=False)
+    case = synth_case(C, max(n, 20), P, Hk, Hv, dk, dv, seed=40 + n, tree=False)
     slots = np.array([4, -1, 1], np.int32)
     log(f"[plain] conv_step n={n} C={C} Ch={case['x'].shape[2]} slots={slots.tolist()}")
     g, r = PlainStep(case, Hk, slots), OraclePlain(case, Hk, slots)
