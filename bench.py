@@ -288,6 +288,8 @@ def prefill_main(args):
     gen = torch.Generator(device=dev)
     slot_ids = d(round_structure(wl, 0, args.seed)["slot_ids"])
     status = torch.zeros(1, dtype=torch.int32, device=dev)
+    # one workspace for every instance: their prefills run one after another on the stream
+    workspace = torch.empty(gdn.prefill_workspace_size(sh) // 4, dtype=torch.float32, device=dev)
     inst = []
     for l in range(L):
         lp = layer_params(wl, l, args.seed)
@@ -305,7 +307,7 @@ def prefill_main(args):
 
     def rec(b):
         gdn.prefill(sh, b["qkv"], b["beta"], b["alpha"], b["dt_bias"], b["A"], b["state"], slot_ids, status,
-                    out=b["out"])
+                    out=b["out"], workspace=workspace)
 
     def step():
         for b in inst:
@@ -345,9 +347,11 @@ def prefill_main(args):
     roofline = None
     if kern:
         tflops = cost["flops"] / (kern["prefill"] * 1e-6) / 1e12
-        roofline = dict(bound="mfma", kernel="prefill", achieved=round(tflops, 2), peak=MFMA_FP32_PEAK_TFLOPS,
-                        unit="TFLOP/s", frac=round(tflops / MFMA_FP32_PEAK_TFLOPS, 4),
-                        traffic=measured_traffic(wl.name + "-prefill", "prefill"), flops_per_launch=cost["flops"],
+        parts = [measured_traffic(wl.name + "-prefill", k) for k in ("prefill_prep", "prefill_state")]
+        roofline = dict(bound="mfma", kernel="prefill (prefill_prep + prefill_state launches of one call)",
+                        achieved=round(tflops, 2), peak=MFMA_FP32_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=round(tflops / MFMA_FP32_PEAK_TFLOPS, 4),
+                        traffic=None if None in parts else sum(parts), flops_per_launch=cost["flops"],
                         us_per_launch=round(kern["prefill"], 3))
     line = {
         "metric": "GDN prefill tokens/s (prompt filling the slots)",

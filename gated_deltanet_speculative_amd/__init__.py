@@ -18,6 +18,7 @@ directly:
 and a prompt fills a slot with conv_step over its tokens followed by
 
     prefill         -> out; the recurrence over the prompt, each slot's state in place
+                       (prefill_workspace_size: the scratch bytes it needs)
 
 The library is loaded on first use and must have been built
 (`python -m gated_deltanet_speculative_amd.build`); there is no fallback path.
@@ -40,6 +41,7 @@ from ._lib import (  # noqa: F401
     conv_tree_verify,
     decode_step,
     prefill,
+    prefill_workspace_size,
     load_library,
     replay_commit,
     replay_commit_layers,

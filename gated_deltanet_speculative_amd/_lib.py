@@ -18,10 +18,12 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdnverify.so")
 
-GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP, GDN_ERR_ALIGN = range(7)
+(GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP, GDN_ERR_ALIGN,
+ GDN_ERR_WORKSPACE) = range(8)
 STATUS_SLOT_RANGE, STATUS_SLOT_DUP, STATUS_PARENT, STATUS_ACCEPT, STATUS_NODES = 1, 2, 4, 8, 16
 EXPORTED = ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_conv_tree_verify", "gdn_replay_commit",
-            "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step", "gdn_prefill", "gdn_strerror")
+            "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step", "gdn_prefill", "gdn_prefill_workspace_size",
+            "gdn_strerror")
 MAX_CHAIN = 65536
 MAX_LAYERS = 64
 
@@ -80,7 +82,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdn_replay_commit_layers.argtypes = [sp, i32] + [vp] * 10
     lib.gdn_conv_step.argtypes = [sp] + [vp] * 7
     lib.gdn_decode_step.argtypes = [sp, vp, vp, vp, i64] + [vp] * 7
-    lib.gdn_prefill.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, vp, vp, vp]
+    lib.gdn_prefill.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.gdn_prefill_workspace_size.argtypes = [sp]
+    lib.gdn_prefill_workspace_size.restype = ctypes.c_size_t
     for f in ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_conv_tree_verify", "gdn_replay_commit",
               "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step", "gdn_prefill"):
         getattr(lib, f).restype = i32
@@ -378,18 +382,32 @@ def decode_step(sh: Shape, qkv, beta_logits, alpha_logits, dt_bias, A, state_poo
 
 
 # ---------------------------------------------------------------- prefill
+def prefill_workspace_size(sh: Shape) -> int:
+    """Bytes of device workspace prefill needs for this shape (0 for an invalid shape)."""
+    cs = sh.c_struct()
+    return int(load_library().gdn_prefill_workspace_size(ctypes.byref(cs)))
+
+
 def prefill(sh: Shape, qkv, beta_logits, alpha_logits, dt_bias, A, state_pool, slot_ids, status, gate_z=None,
-            gate_mode=0, out=None):
+            gate_mode=0, out=None, workspace=None):
     """The recurrence over a chain of n_nodes tokens per lane (qkv [C, T, Ch] = the conv
     output of the prompt), updating the slots' states in place; beta/alpha logits are
     [C, T, H_v] views sharing one row stride.  With gate_z ([C, T, H_v, d_v]) the output is
     gated by silu(z) (gate_mode 0) or sigmoid(z) (gate_mode 1).  A transaction on the
-    status word.  Returns out [C, T, H_v, d_v]."""
+    status word.  `workspace` is a float32 device tensor of at least
+    prefill_workspace_size(sh) bytes (allocated per call when omitted).
+    Returns out [C, T, H_v, d_v]."""
     C, T, P, Hv, dk, dv = sh.n_seqs, sh.n_nodes, sh.n_slots, sh.n_v_heads, sh.d_k, sh.d_v
     if status is None:
         raise ValueError("prefill needs a status word (it mutates the state pool)")
     if out is None:
         out = torch.empty((C, T, Hv, dv), dtype=torch.float32, device=qkv.device)
+    ws_bytes = prefill_workspace_size(sh)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=qkv.device)
+    if not (isinstance(workspace, torch.Tensor) and workspace.dtype == torch.float32 and workspace.is_cuda
+            and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous float32 device tensor")
     bp, bs = _gate_view(beta_logits, "beta_logits", sh)
     ap, as_ = _gate_view(alpha_logits, "alpha_logits", sh)
     if bs != as_:
@@ -403,6 +421,7 @@ def prefill(sh: Shape, qkv, beta_logits, alpha_logits, dt_bias, A, state_pool, s
         None if gate_z is None else _dev(gate_z, "gate_z", torch.float32, (C, T, Hv, dv)),
         ctypes.c_int32(int(gate_mode)),
         _dev(out, "out", torch.float32, (C, T, Hv, dv)),
+        workspace.data_ptr(), ctypes.c_size_t(workspace.numel() * 4),
         _dev(status, "status", torch.int32, (1,)),
         _stream(qkv),
     ]

@@ -266,27 +266,37 @@ int gdn_decode_step(const gdn_shape *sh, const float *qkv, const float *beta_log
                : GDN_ERR_HIP;
 }
 
+size_t gdn_prefill_workspace_size(const gdn_shape *sh) {
+    gdn::Dims d;
+    if (check_shape(sh, &d, true)) return 0;
+    return gdn::prefill_workspace_floats(d) * F;
+}
+
 int gdn_prefill(const gdn_shape *sh, const float *qkv, const float *beta_logits, const float *alpha_logits,
                 int64_t gate_stride, const float *dt_bias, const float *A, float *state_pool, const int32_t *slot_ids,
-                const float *gate_z, int32_t gate_mode, float *out, int32_t *status, hipStream_t stream) {
+                const float *gate_z, int32_t gate_mode, float *out, float *workspace, size_t workspace_bytes,
+                int32_t *status, hipStream_t stream) {
     gdn::Dims d;
     if (int r = check_shape(sh, &d, true)) return r;
-    if (!qkv || !beta_logits || !alpha_logits || !dt_bias || !A || !state_pool || !slot_ids || !out || !status)
+    if (!qkv || !beta_logits || !alpha_logits || !dt_bias || !A || !state_pool || !slot_ids || !out || !workspace ||
+        !status)
         return GDN_ERR_NULL;
     if (gate_stride < d.Hv || (gate_mode != 0 && gate_mode != 1)) return GDN_ERR_SHAPE;
-    if (!aligned({qkv, state_pool, out, gate_z}, 16) ||
+    const size_t ws_b = gdn::prefill_workspace_floats(d) * F;
+    if (workspace_bytes < ws_b) return GDN_ERR_WORKSPACE;
+    if (!aligned({qkv, state_pool, out, gate_z, workspace}, 16) ||
         !aligned({beta_logits, alpha_logits, dt_bias, A, slot_ids, status}, 4))
         return GDN_ERR_ALIGN;
     const size_t rows = (size_t)d.C * d.N;
     const size_t gate_bytes = ((rows - 1) * (size_t)gate_stride + d.Hv) * F;
     const size_t out_b = rows * d.Hv * d.dv * F;
-    if (any_alias({{state_pool, (size_t)d.P * d.Hv * d.dk * d.dv * F}, {out, out_b}, {status, I}},
+    if (any_alias({{state_pool, (size_t)d.P * d.Hv * d.dk * d.dv * F}, {out, out_b}, {workspace, ws_b}, {status, I}},
                   {{qkv, rows * d.Ch * F}, {beta_logits, gate_bytes}, {alpha_logits, gate_bytes},
                    {dt_bias, (size_t)d.Hv * F}, {A, (size_t)d.Hv * F}, {slot_ids, (size_t)d.C * I},
                    {gate_z, out_b}}))
         return GDN_ERR_ALIAS;
     return gdn::launch_prefill(d, d.N, qkv, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids,
-                               gate_z, gate_mode, out, status, stream) == hipSuccess
+                               gate_z, gate_mode, out, workspace, status, stream) == hipSuccess
                ? GDN_OK
                : GDN_ERR_HIP;
 }
@@ -300,6 +310,7 @@ const char *gdn_strerror(int code) {
         case GDN_ERR_ALIAS: return "an output buffer overlaps an input or another output";
         case GDN_ERR_HIP: return "HIP kernel launch failed";
         case GDN_ERR_ALIGN: return "a buffer is misaligned (dense float buffers need 16 bytes, others 4)";
+        case GDN_ERR_WORKSPACE: return "the workspace is smaller than the size query returns for this shape";
         default: return "unknown error code";
     }
 }

@@ -63,10 +63,17 @@ hipError_t launch_decode_step(const Dims &d, const float *qkv, const float *beta
                               const int32_t *slot_ids, float *out, int32_t *status, hipStream_t stream);
 
 // Prefill: the recurrence over a chain of d.N tokens per lane, state updated in place,
-// optional output gate (gate_z may be null).
+// optional output gate (gate_z may be null).  Two launches: the chunk coefficients of
+// every (lane, value head, chunk of kPrefillChunk tokens) into `workspace`
+// (kPackFloats floats each), then the state recurrence over the chunks.
+constexpr int kPrefillChunk = 16;
+constexpr int kPackFloats = 580;
+inline size_t prefill_workspace_floats(const Dims &d) {
+    return (size_t)d.C * d.Hv * (size_t)((d.N + kPrefillChunk - 1) / kPrefillChunk) * kPackFloats;
+}
 hipError_t launch_prefill(const Dims &d, int n_tokens, const float *qkv, const float *beta_logits,
                           const float *alpha_logits, int64_t gate_stride, const float *dt_bias, const float *A,
                           float *state_pool, const int32_t *slot_ids, const float *gate_z, int gate_mode, float *out,
-                          int32_t *status, hipStream_t stream);
+                          float *workspace, int32_t *status, hipStream_t stream);
 
 }  // namespace gdn

@@ -8,26 +8,32 @@
 // ("qwen35: DSpark speculative decoding (Qwen3.8-27B drafters)", raw-gate commit message).
 //
 // Chunked form.  Within a chunk of B = 16 tokens, with cumulative log-decays L_t from the
-// chunk start (G_t = exp(L_t)), raw rows q_t, k_t, inverse norms rq_t, rk_t and the state
+// chunk start (G_t = exp(L_t)), raw rows q_t, k_t, inverse norms rk_t, rq_t and the state
 // S at the chunk start:
 //   (I + Lm) D = rhs,  rhs_t = beta_t (v_t - G_t rk_t (K S)_t),
 //   Lm[t][u] = beta_t exp(L_t - L_u) rk_t rk_u (k_t . k_u)                 (u < t)
 //   O_t = G_t rq_t (Q S)_t / sqrt(d_k) + sum_{u <= t} Cq[t][u] D_u,
 //   Cq[t][u] = exp(L_t - L_u) rq_t rk_u (q_t . k_u) / sqrt(d_k)            (u <= t)
 //   S <- G_B S + sum_u exp(L_B - L_u) rk_u k_u D_u^T
-// i.e. the tree verify's formulation on a chain, followed by the state update.  Every
-// product with d_k or d_v in it runs on v_mfma_f32_16x16x4_f32 with the operand
-// permutation of mfma4, so the state tile stays in registers across chunks in exactly the
-// layout in which the next chunk's products and the update consume and produce it.
+// i.e. the tree verify's formulation on a chain, followed by the state update.
 //
-// Mapping: one workgroup (4 waves) per (lane, value head, block of 64 value columns);
-// wave w owns the 16-column tile w of the state for the whole prompt.  Per chunk: stage
-// the chunk's rows in LDS (padding tokens of the last chunk as zero rows), issue the next
-// chunk's loads, then norms + gates, the Gram products (split over the waves by d_k
-// chunk) and each wave's [K; Q] S; coefficients; T = (I + Lm)^-1 by broadcast forward
-// substitution; D, O, the output gate and the state update per wave; outputs leave as
-// 16-byte chunks of whole rows.  The state is read once before the first chunk and
-// written once after the last.
+// Two launches.  Everything that does not involve the state -- norms, gates, the Gram
+// products, Lm, Cq and T = (I + Lm)^-1 -- depends on one chunk's tokens only, so the first
+// kernel computes it for every (lane, value head, chunk) at once, a workgroup per chunk,
+// into a package of kPackFloats floats in the caller's workspace.  The second kernel
+// carries the state through the chunks in order and does only what involves it: the
+// products [K; Q] S, D = T rhs, O = diag(c) QS + Cq D, the output gate and the update, all
+// on v_mfma_f32_16x16x4_f32 with the operand permutation of mfma4, so the state tile stays
+// in registers across chunks in exactly the layout in which the next chunk's products and
+// the update consume and produce it.
+//
+// Package of (lane c, value head h, chunk j), floats:
+//   [0, 256)    T[t][u] row-major                  [256, 512)  Cq[t][u] row-major
+//   [512, 528)  a_t = beta_t                       [528, 544)  b_t = G_t rk_t
+//   [544, 560)  c_t = G_t rq_t / sqrt(d_k)         [560, 576)  w_t = exp(L_B - L_t) rk_t
+//   [576, 580)  G_B, four copies (so that every lane's load of it is a vector load)
+// Padding tokens of the last chunk are zero rows: beta = 0 and no decay, so they write
+// nothing into D, O or the state.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -36,87 +42,272 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int BC = 16;  // tokens per chunk
+constexpr int BC = kPrefillChunk;  // tokens per chunk
+static_assert(BC == 16, "one 16 x 16 MFMA tile of tokens per chunk");
+constexpr int PK_T = 0, PK_CQ = 256, PK_A = 512, PK_B = 528, PK_C = 544, PK_W = 560, PK_GEND = 576;
+static_assert(PK_GEND + 4 == kPackFloats && kPackFloats % 4 == 0, "package layout");
 
 template <int DK, int DV>
 struct PrefillCfg {
-    static constexpr int JB = DV < 64 ? DV : 64;      // value columns per workgroup
+    static constexpr int JB = DV < 64 ? DV : 64;      // value columns per state workgroup
     static constexpr int NB = DV / JB;                // column blocks per head
     static constexpr int CT = JB / 16;                // 16-column tiles: wave w < CT owns tile w
     static constexpr int KC = DK / 16;                // 16-wide chunks of d_k
     static constexpr int SX = DK + 4;                 // raw q / k rows in LDS (4 mod 8 floats)
-    static constexpr int SV = JB + 4;                 // value, gate and output rows
     static constexpr int SG = BC + 4;                 // 16 x 16 matrices
     static constexpr int QK4 = BC * DK / 4;           // float4 groups of a chunk's q (or k) rows
     static constexpr int QPT = (2 * QK4 + kThreads - 1) / kThreads;
-    static constexpr int V4 = BC * JB / 4;            // float4 groups of a chunk's value block
-    static_assert(V4 <= kThreads, "one value group per thread");
 };
 
 // element (i, a) of a 16 x 16 accumulator tile stored lane-major (lane * 4 + component)
 __device__ inline int tile_index(int i, int a) { return (16 * (i >> 2) + a) * 4 + (i & 3); }
 
-template <int DK, int DV>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(
+// Raw buffer resources: word 3 of the descriptor for the gfx9 family (32-bit data,
+// unswizzled).  A load whose byte offset lies outside [0, num_records) returns zero and
+// a store there is dropped, without a memory access.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;  // cache-policy operand of the buffer stores: nt
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const float *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, bytes, kRsrcWord3);
+}
+__device__ inline float load1(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ inline v4f load4(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// The q and k rows of q/k head kh of one chunk, as float4 groups: item u of a thread is
+// group f = tid + kThreads * u of the q rows (f < QK4), then of the k rows.  `off` is the
+// group's byte offset from the chunk's first row; the chunk's resource ends after its last
+// real token, so the rows of padding tokens read as zero.
+template <int DK>
+struct ChunkRows {
+    using Cfg = PrefillCfg<DK, 16>;
+    int off[Cfg::QPT], lds[Cfg::QPT];  // byte offset in the chunk, float offset in [Q; K] LDS rows
+    v4f x[Cfg::QPT];
+    __device__ ChunkRows(int Ch, int Hk, int kh) {
+#pragma unroll
+        for (int u = 0; u < Cfg::QPT; ++u) {
+            const int f = min((int)threadIdx.x + kThreads * u, 2 * Cfg::QK4 - 1);
+            const int m = f / Cfg::QK4, r = f - m * Cfg::QK4, t = r / (DK / 4), grp = r - t * (DK / 4);
+            off[u] = (t * Ch + m * Hk * DK + kh * DK + 4 * grp) * 4;
+            lds[u] = (m * BC + t) * Cfg::SX + 4 * grp;
+        }
+    }
+    __device__ void load(__amdgpu_buffer_rsrc_t r) {
+#pragma unroll
+        for (int u = 0; u < Cfg::QPT; ++u) x[u] = load4(r, off[u]);
+    }
+    // into LDS: q rows at [0, BC), k rows at [BC, 2 BC) of rows of Cfg::SX floats
+    __device__ void stage(float *QK) const {
+#pragma unroll
+        for (int u = 0; u < Cfg::QPT; ++u)
+            if ((int)threadIdx.x + kThreads * u < 2 * Cfg::QK4) *reinterpret_cast<v4f *>(QK + lds[u]) = x[u];
+    }
+};
+
+// ---- kernel 1: the packages of one (lane, q/k head, chunk), for each value head that
+// shares the q/k head.  Grid (chunks * H_k, C).
+template <int DK>
+__global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     Dims d, int T, const float *__restrict__ qkv, const float *__restrict__ beta_logits,
     const float *__restrict__ alpha_logits, int64_t gate_stride, const float *__restrict__ dt_bias,
-    const float *__restrict__ A, float *__restrict__ state_pool, const int32_t *__restrict__ slot_ids,
-    const float *__restrict__ gate_z, int gate_mode, float *__restrict__ out, int32_t *__restrict__ status) {
+    const float *__restrict__ A, float *__restrict__ pack) {
+    using Cfg = PrefillCfg<DK, 16>;
+    constexpr int SX = Cfg::SX, SG = Cfg::SG, KC = Cfg::KC;
+    constexpr int HG = kThreads / BC;  // value heads whose gates are formed together
+    __shared__ __align__(16) float QK[2 * BC * SX];  // q rows, then k rows
+    __shared__ __align__(16) float s_gram[kWaves][2][256];
+    __shared__ __align__(16) float Lm[BC * SG], Tm[BC * BC];
+    __shared__ float s_rk[BC], s_rq[BC], s_kk[256], s_qk[256];
+    __shared__ float s_beta[HG][BC], s_L[HG][BC];
+    const float *Ql = QK, *Kl = QK + BC * SX;
+
+    const int nch = (T + BC - 1) / BC;
+    const int j = blockIdx.x % nch, kh = blockIdx.x / nch, c = blockIdx.y;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
+    const int k0 = j * BC, nc = min(BC, T - k0);
+    const int R = d.Hv / d.Hk;  // value heads h = kh + H_k m, m < R
+    // (a padding lane's packages are computed like any other and never read)
+
+    ChunkRows<DK> rows(d.Ch, d.Hk, kh);
+    rows.load(rsrc(qkv + ((int64_t)c * T + k0) * d.Ch, nc * d.Ch * 4));
+    rows.stage(QK);
+    lds_barrier();
+
+    // inverse norms of the 32 raw rows, 8 threads per row
+    {
+        const int r = tid >> 3, p = tid & 7;
+        const float *x = r < BC ? Kl + r * SX : Ql + (r - BC) * SX;
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < DK / 8; ++e) ss = fmaf(x[p + 8 * e], x[p + 8 * e], ss);
+        ss = group_sum_last<8>(ss);
+        if (p == 7) (r < BC ? s_rk[r] : s_rq[r - BC]) = inv_norm(ss);
+    }
+    // Gram partials K K^T and Q K^T, d_k chunk q on wave q % 4
+    {
+        v4f gkk = {0.f, 0.f, 0.f, 0.f}, gqk = gkk;
+#pragma unroll
+        for (int q = 0; q < KC; ++q) {
+            if (q % kWaves != wave) continue;
+            const v4f ak = *reinterpret_cast<const v4f *>(Kl + l16 * SX + 16 * q + 4 * g4);
+            const v4f aq = *reinterpret_cast<const v4f *>(Ql + l16 * SX + 16 * q + 4 * g4);
+            gkk = mfma4(ak, ak, gkk);
+            gqk = mfma4(aq, ak, gqk);
+        }
+        *reinterpret_cast<v4f *>(&s_gram[wave][0][lane * 4]) = gkk;
+        *reinterpret_cast<v4f *>(&s_gram[wave][1][lane * 4]) = gqk;
+    }
+    lds_barrier();
+    {  // thread (i, a): k_i . k_a and q_i . k_a
+        const int i = tid >> 4, a = tid & 15, idx = tile_index(i, a);
+        float kk = 0.f, qk = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            kk += s_gram[w][0][idx];
+            qk += s_gram[w][1][idx];
+        }
+        s_kk[tid] = kk;
+        s_qk[tid] = qk;
+    }
+
+    const float isd = 1.0f / sqrtf((float)DK);
+    for (int m0 = 0; m0 < R; m0 += HG) {
+        // gates of value heads m0 .. m0 + HG - 1: thread (m, t), a row of 16 lanes per head,
+        // and the inclusive prefix of the log-decays over the chunk
+        {
+            const int m = m0 + (tid >> 4), t = tid & 15;
+            const int h = kh + d.Hk * min(m, R - 1);
+            const int64_t trow = (int64_t)c * T + min(k0 + t, T - 1);
+            const float xb = beta_logits[trow * gate_stride + h];
+            const float xa = alpha_logits[trow * gate_stride + h] + dt_bias[h];
+            const bool real = t < nc;
+            const float ell = real ? fast_softplus(xa) * A[h] : 0.f;  // log g
+            const float L = group_sum_last<16>(ell);
+            s_beta[tid >> 4][t] = real ? fast_sigmoid(xb) : 0.f;
+            s_L[tid >> 4][t] = L;
+        }
+        for (int m = m0; m < min(R, m0 + HG); ++m) {
+            lds_barrier();  // gates formed; the previous head's Tm and Lm consumed
+            const int h = kh + d.Hk * m, mg = m - m0;
+            float *pk = pack + (((int64_t)c * d.Hv + h) * nch + j) * kPackFloats;
+            {
+                const int i = tid >> 4, a = tid & 15;
+                const float r = a <= i ? fast_exp(s_L[mg][i] - s_L[mg][a]) * s_rk[a] : 0.f;
+                Lm[i * SG + a] = a < i ? r * s_kk[tid] * (s_beta[mg][i] * s_rk[i]) : 0.f;
+                pk[PK_CQ + tid] = r * s_qk[tid] * (s_rq[i] * isd);
+            }
+            if (tid < BC) {
+                const float G = fast_exp(s_L[mg][tid]), Lend = s_L[mg][BC - 1];  // padding adds no decay
+                pk[PK_A + tid] = s_beta[mg][tid];
+                pk[PK_B + tid] = G * s_rk[tid];
+                pk[PK_C + tid] = G * s_rq[tid] * isd;
+                pk[PK_W + tid] = fast_exp(Lend - s_L[mg][tid]) * s_rk[tid];
+                if (tid < 4) pk[PK_GEND + tid] = fast_exp(Lend);
+            }
+            lds_barrier();
+            // T = (I + Lm)^-1: lane (column a, row i) over rows of 16 lanes
+            {
+                const int a = 4 * wave + (lane >> 4), i = lane & 15;
+                v4f Lr[4];
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4) Lr[k4] = *reinterpret_cast<const v4f *>(Lm + i * SG + 4 * k4);
+                Tm[i * BC + a] = bcast_solve(i == a ? 1.f : 0.f, Lr, std::make_integer_sequence<int, 16>());
+            }
+            lds_barrier();
+            if (tid < BC * BC / 4)
+                *reinterpret_cast<v4f *>(pk + PK_T + 4 * tid) = *reinterpret_cast<const v4f *>(Tm + 4 * tid);
+        }
+        lds_barrier();  // s_beta / s_L of this group consumed
+    }
+}
+
+// One chunk's package operands and value / gate values in the accumulator layout of lane
+// (g4, l16): rows 4 g4 .. 4 g4 + 3, value column jj.
+struct Frag {
+    v4f tf, cf, a, b, cc, w, v, z;
+    float gend;
+};
+
+// ---- kernel 2: the state through the chunks.  One workgroup (4 waves) per (lane, value
+// head, block of 64 value columns); wave w owns the 16-column tile w of the state for the
+// whole prompt.  Workgroup ids are ordered so that the workgroups sharing one (lane, q/k
+// head) are congruent modulo C * H_k and read the shared q/k rows through one L2.  One
+// barrier per chunk: the rows of chunk j are staged in LDS buffer j % 2, so staging chunk
+// j + 1 never overlaps a wave still reading chunk j - 1.  Every per-chunk buffer (rows,
+// values, gate values, outputs, package) is addressed by a per-lane offset that is the
+// same for every chunk and a chunk base that moves by a uniform step; its range ends at
+// the chunk's last real token.
+template <int DK, int DV, bool GATED>
+__global__ __launch_bounds__(kThreads) void prefill_state_kernel(
+    Dims d, int T, const float *__restrict__ qkv, const float *__restrict__ pack, float *__restrict__ state_pool,
+    const int32_t *__restrict__ slot_ids, const float *__restrict__ gate_z, int gate_mode, float *__restrict__ out,
+    int32_t *__restrict__ status) {
     using Cfg = PrefillCfg<DK, DV>;
-    constexpr int JB = Cfg::JB, NB = Cfg::NB, CT = Cfg::CT, KC = Cfg::KC, SX = Cfg::SX, SV = Cfg::SV;
-    constexpr int SG = Cfg::SG, QK4 = Cfg::QK4, QPT = Cfg::QPT, V4 = Cfg::V4;
+    constexpr int JB = Cfg::JB, NB = Cfg::NB, CT = Cfg::CT, KC = Cfg::KC, SX = Cfg::SX;
     __shared__ unsigned int s_bitmap[kBitmapSlots / 32];
     __shared__ int s_word;
-    __shared__ __align__(16) float Ql[BC * SX], Kl[BC * SX], Vl[BC * SV], Zl[BC * SV], Ot[BC * SV];
-    __shared__ __align__(16) float s_gram[kWaves][2][256];
-    __shared__ __align__(16) float Lm[BC * SG], Cq[BC * SG], Tm[BC * SG];
-    __shared__ float s_rk[BC], s_rq[BC], s_beta[BC], s_L[BC];
+    __shared__ __align__(16) float QK[2][2 * BC * SX];  // per buffer: q rows, then k rows
 
-    const int c = blockIdx.y, h = blockIdx.x / NB, jb = blockIdx.x - h * NB, j0 = jb * JB;
-    const int kh = h % d.Hk, Ch = d.Ch, Hv = d.Hv;
+    const int n_groups = d.C * d.Hk;
+    const int grp = blockIdx.x % n_groups, ws = blockIdx.x / n_groups;
+    const int c = grp / d.Hk, kh = grp - c * d.Hk;
+    const int jb = ws % NB, h = kh + d.Hk * (ws / NB), j0 = jb * JB;
+    const int Ch = d.Ch, HvDV = d.Hv * DV;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
-    const bool gated = gate_z != nullptr;
-    const float isd = 1.0f / sqrtf((float)DK);
+    const int cw = min(wave, CT - 1), jj = j0 + 16 * cw + l16;  // this lane's value column
+    const int nch = (T + BC - 1) / BC;
 
     // ---- loads that do not need the slot first (the slot id through a vector load, so
     //      its wait does not hold up the loads behind it), then the state tile
     const int s_v = __builtin_bit_cast(
         int, __builtin_amdgcn_raw_buffer_load_b32(
-                 __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(slot_ids), 0, 4 * d.C, 0x00020000), 4 * c, 0,
+                 __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(slot_ids), 0, 4 * d.C, kRsrcWord3), 4 * c, 0,
                  0));
     const LaneSlotsT<kThreads> lanes(slot_ids, d.C);
     const int st_in = *status;
-    const float dt = dt_bias[h], Ah = A[h];
 
-    // one chunk's loads: item u of a thread is float4 group f = tid + kThreads * u of the
-    // q rows (f < QK4) or k rows; the value / gate group tid (< V4); token tid's gates
-    v4f xq[QPT], xv, xz;
-    float xb, xa;
-    auto load_chunk = [&](int k0) {
-        const float *row0 = qkv + (int64_t)c * T * Ch;
+    // per-lane byte offsets within a chunk: value (and gate value / output) rows 4 g4 + v
+    int vo[4], zo[4];
 #pragma unroll
-        for (int u = 0; u < QPT; ++u) {
-            const int f = min(tid + kThreads * u, 2 * QK4 - 1);
-            const int m = f / QK4, r = f - m * QK4, t = r / (DK / 4), grp = r - t * (DK / 4);
-            const int tok = min(k0 + t, T - 1);
-            xq[u] = *reinterpret_cast<const v4f *>(row0 + (int64_t)tok * Ch + m * d.Hk * DK + kh * DK + 4 * grp);
+    for (int v = 0; v < 4; ++v) {
+        vo[v] = ((4 * g4 + v) * Ch + 2 * d.Hk * DK + h * DV + jj) * 4;
+        zo[v] = ((4 * g4 + v) * HvDV + h * DV + jj) * 4;
+    }
+    const float *pk0 = pack + ((int64_t)c * d.Hv + h) * nch * kPackFloats;
+    auto chunk_base = [&](const float *buf, int row_floats, int k0) { return buf + ((int64_t)c * T + k0) * row_floats; };
+    auto load_frag = [&](int jc, Frag &f) {
+        const int k0 = jc * BC, nc = min(BC, T - k0);
+        const __amdgpu_buffer_rsrc_t pr = rsrc(pk0 + (int64_t)jc * kPackFloats, kPackFloats * 4);
+        f.tf = load4(pr, (PK_T + 16 * l16 + 4 * g4) * 4);
+        f.cf = load4(pr, (PK_CQ + 16 * l16 + 4 * g4) * 4);
+        f.a = load4(pr, (PK_A + 4 * g4) * 4);
+        f.b = load4(pr, (PK_B + 4 * g4) * 4);
+        f.cc = load4(pr, (PK_C + 4 * g4) * 4);
+        f.w = load4(pr, (PK_W + 4 * g4) * 4);
+        f.gend = load1(pr, (PK_GEND + g4) * 4);
+        const __amdgpu_buffer_rsrc_t vr = rsrc(chunk_base(qkv, Ch, k0), nc * Ch * 4);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) f.v[v] = load1(vr, vo[v]);
+        if constexpr (GATED) {
+            const __amdgpu_buffer_rsrc_t zr = rsrc(chunk_base(gate_z, HvDV, k0), nc * HvDV * 4);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) f.z[v] = load1(zr, zo[v]);
         }
-        const int tv = min(tid, V4 - 1) / (JB / 4), cg = min(tid, V4 - 1) % (JB / 4);
-        const int tokv = min(k0 + tv, T - 1);
-        xv = *reinterpret_cast<const v4f *>(row0 + (int64_t)tokv * Ch + 2 * d.Hk * DK + h * DV + j0 + 4 * cg);
-        if (gated)
-            xz = *reinterpret_cast<const v4f *>(gate_z + (((int64_t)c * T + tokv) * Hv + h) * DV + j0 + 4 * cg);
-        const int tokg = min(k0 + min(tid, BC - 1), T - 1);
-        xb = beta_logits[((int64_t)c * T + tokg) * gate_stride + h];
-        xa = alpha_logits[((int64_t)c * T + tokg) * gate_stride + h];
     };
-    load_chunk(0);
+    ChunkRows<DK> rows(Ch, d.Hk, kh);
+    rows.load(rsrc(chunk_base(qkv, Ch, 0), min(BC, T) * Ch * 4));
+    Frag fn;
+    load_frag(0, fn);
     __builtin_amdgcn_sched_barrier(0);
     const int s = __builtin_amdgcn_readfirstlane(s_v);
     const bool s_ok = s >= 0 && s < d.P;
     // the state tile of this wave in the MFMA operand layout:
-    // sreg[q][e] = S[16q + 4*g4 + e][j0 + 16*wave + l16]   (waves w < CT)
-    float *Sp = state_pool + ((int64_t)(s_ok ? s : 0) * Hv + h) * DK * DV + j0 + 16 * min(wave, CT - 1) + l16;
+    // sreg[q][e] = S[16q + 4*g4 + e][jj]   (waves w < CT)
+    float *Sp = state_pool + ((int64_t)(s_ok ? s : 0) * d.Hv + h) * DK * DV + jj;
     v4f sreg[KC];
 #pragma unroll
     for (int q = 0; q < KC; ++q)
@@ -125,137 +316,63 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 
     const int bits = slot_preflight<kThreads>(lanes, slot_ids, d.C, d.P, s_bitmap, &s_word);
     if (bits || st_in) {
-        if (bits && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) atomicOr(status, bits);
+        if (bits && blockIdx.x == 0 && tid == 0) atomicOr(status, bits);
         return;
     }
     if (s < 0) return;  // padding lane (uniform over the workgroup)
 
-    for (int k0 = 0; k0 < T; k0 += BC) {
-        const int nc = min(BC, T - k0);  // tokens of this chunk (the rest are zero rows)
-        // ---- stage the chunk; wave 0 forms the gates and the cumulative log-decay
-#pragma unroll
-        for (int u = 0; u < QPT; ++u) {
-            const int f = tid + kThreads * u;
-            if (f < 2 * QK4) {
-                const int m = f / QK4, r = f - m * QK4, t = r / (DK / 4), grp = r - t * (DK / 4);
-                *reinterpret_cast<v4f *>((m ? Kl : Ql) + t * SX + 4 * grp) = t < nc ? xq[u] : v4f{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-        if (tid < V4) {
-            const int tv = tid / (JB / 4), cg = tid % (JB / 4);
-            *reinterpret_cast<v4f *>(Vl + tv * SV + 4 * cg) = tv < nc ? xv : v4f{0.f, 0.f, 0.f, 0.f};
-            if (gated) *reinterpret_cast<v4f *>(Zl + tv * SV + 4 * cg) = xz;
-        }
-        if (wave == 0) {
-            const bool real = lane < nc;
-            const float ell = real ? fast_softplus(xa + dt) * Ah : 0.f;  // log g
-            const float L = group_sum_last<16>(ell);                     // inclusive prefix over tokens
-            if (lane < BC) {
-                s_beta[lane] = real ? fast_sigmoid(xb) : 0.f;
-                s_L[lane] = L;
-            }
-        }
+    for (int jc = 0; jc < nch; ++jc) {
+        const int k0 = jc * BC, nc = min(BC, T - k0);
+        float *Qb = QK[jc & 1], *Kb = Qb + BC * SX;
+        rows.stage(Qb);
+        const Frag f = fn;
         lds_barrier();
-
-        // ---- the next chunk's loads go out now, under this chunk's arithmetic
-        if (k0 + BC < T) load_chunk(k0 + BC);
-
-        // ---- inverse norms of the 32 raw rows: 8 threads per row
-        {
-            const int r = tid >> 3, p = tid & 7;
-            const float *x = (r < BC ? Kl + r * SX : Ql + (r - BC) * SX);
-            float ss = 0.f;
-#pragma unroll
-            for (int e = p; e < DK; e += 8) ss = fmaf(x[e], x[e], ss);
-            ss = group_sum_last<8>(ss);
-            if (p == 7) (r < BC ? s_rk[r] : s_rq[r - BC]) = inv_norm(ss);
+        if (jc + 1 < nch) {  // the next chunk's loads go out now, under this chunk's products
+            rows.load(rsrc(chunk_base(qkv, Ch, k0 + BC), min(BC, T - k0 - BC) * Ch * 4));
+            load_frag(jc + 1, fn);
         }
-        // ---- Gram partials (d_k chunk q on wave q % 4) and this wave's [K; Q] S tile
-        v4f ks = {0.f, 0.f, 0.f, 0.f}, qs = ks, gkk = ks, gqk = ks;
+        if (wave < CT) {
+            // [K; Q] S
+            v4f ks = {0.f, 0.f, 0.f, 0.f}, qs = ks;
 #pragma unroll
-        for (int q = 0; q < KC; ++q) {
-            const v4f ak = *reinterpret_cast<const v4f *>(Kl + l16 * SX + 16 * q + 4 * g4);
-            const v4f aq = *reinterpret_cast<const v4f *>(Ql + l16 * SX + 16 * q + 4 * g4);
-            if (q % kWaves == wave) {
-                gkk = mfma4(ak, ak, gkk);
-                gqk = mfma4(aq, ak, gqk);
-            }
-            if (wave < CT) {
+            for (int q = 0; q < KC; ++q) {
+                const v4f ak = *reinterpret_cast<const v4f *>(Kb + l16 * SX + 16 * q + 4 * g4);
+                const v4f aq = *reinterpret_cast<const v4f *>(Qb + l16 * SX + 16 * q + 4 * g4);
                 ks = mfma4(ak, sreg[q], ks);
                 qs = mfma4(aq, sreg[q], qs);
             }
-        }
-        *reinterpret_cast<v4f *>(&s_gram[wave][0][lane * 4]) = gkk;
-        *reinterpret_cast<v4f *>(&s_gram[wave][1][lane * 4]) = gqk;
-        lds_barrier();
-
-        // ---- coefficients, thread (i, a)
-        {
-            const int i = tid >> 4, a = tid & 15, idx = tile_index(i, a);
-            float kk = 0.f, qk = 0.f;
+            // the update's left operand K^T (lane supplies K[token 4*g4 + s][16 rt + l16] in
+            // step s), read while the products run
+            v4f kt[KC];
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                kk += s_gram[w][0][idx];
-                qk += s_gram[w][1][idx];
-            }
-            const float r = a <= i ? fast_exp(s_L[i] - s_L[a]) * s_rk[a] : 0.f;
-            Lm[i * SG + a] = a < i ? r * kk * (s_beta[i] * s_rk[i]) : 0.f;
-            Cq[i * SG + a] = r * qk * (s_rq[i] * isd);
-        }
-        lds_barrier();
-
-        // ---- T = (I + Lm)^-1: lane (column a, row i) over rows of 16 lanes
-        {
-            const int a = 4 * wave + (lane >> 4), i = lane & 15;
-            v4f Lr[4];
+            for (int rt = 0; rt < KC; ++rt)
 #pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) Lr[k4] = *reinterpret_cast<const v4f *>(Lm + i * SG + 4 * k4);
-            Tm[i * SG + a] = bcast_solve(i == a ? 1.f : 0.f, Lr, std::make_integer_sequence<int, 16>());
-        }
-        lds_barrier();
-
-        // ---- per wave: D = T rhs, O = diag(gq) QS + Cq D, the gate, and the state update
-        if (wave < CT) {
-            const int jj = 16 * wave + l16;
-            const float Lend = s_L[BC - 1];  // padding tokens add no decay
+                for (int e = 0; e < 4; ++e) kt[rt][e] = Kb[(4 * g4 + e) * SX + 16 * rt + l16];
+            // D = T rhs, O = diag(c) QS + Cq D, the gate; outputs of padding tokens are dropped
             v4f rhs, o, bw;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int t = 4 * g4 + v;
-                const float G = fast_exp(s_L[t]);
-                rhs[v] = s_beta[t] * (Vl[t * SV + jj] - G * s_rk[t] * ks[v]);
-                o[v] = G * s_rq[t] * isd * qs[v];
+                rhs[v] = f.a[v] * (f.v[v] - f.b[v] * ks[v]);
+                o[v] = f.cc[v] * qs[v];
             }
-            const v4f dl = mfma4(*reinterpret_cast<const v4f *>(Tm + l16 * SG + 4 * g4), rhs, v4f{0.f, 0.f, 0.f, 0.f});
-            o = mfma4(*reinterpret_cast<const v4f *>(Cq + l16 * SG + 4 * g4), dl, o);
+            const v4f dl = mfma4(f.tf, rhs, v4f{0.f, 0.f, 0.f, 0.f});
+            o = mfma4(f.cf, dl, o);
+            const __amdgpu_buffer_rsrc_t orr = rsrc(chunk_base(out, HvDV, k0), nc * HvDV * 4);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int t = 4 * g4 + v;
-                if (gated) {
-                    const float z = Zl[t * SV + jj];
-                    o[v] *= gate_mode == 0 ? fast_silu(z) : fast_sigmoid(z);
+                if constexpr (GATED) {
+                    const float sg = fast_sigmoid(f.z[v]);
+                    o[v] *= gate_mode == 0 ? f.z[v] * sg : sg;  // silu(z) = z sigmoid(z)
                 }
-                Ot[t * SV + jj] = o[v];
-                bw[v] = fast_exp(Lend - s_L[t]) * s_rk[t] * dl[v];
+                // (the element goes through a scalar: this compiler's __builtin_bit_cast of a vector
+                // element lvalue reads element 0 whatever the index)
+                const float ov = o[v];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), orr, zo[v], 0, kNonTemporal);
+                bw[v] = f.w[v] * dl[v];
             }
-            // S <- G_end S + K^T diag(w) D, tile by tile of 16 d_k rows: the A operand is
-            // K^T (lane supplies K[token 4*g4 + s][16 rt + l16] in step s)
-            const float Gend = fast_exp(Lend);
+            // S <- G_B S + K^T diag(w) D, tile by tile of 16 d_k rows
 #pragma unroll
-            for (int rt = 0; rt < KC; ++rt) {
-                v4f a4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) a4[e] = Kl[(4 * g4 + e) * SX + 16 * rt + l16];
-                sreg[rt] = mfma4(a4, bw, Gend * sreg[rt]);
-            }
-        }
-        lds_barrier();
-
-        // ---- outputs of the chunk: 16-byte chunks of whole rows from consecutive lanes
-        for (int f = tid; f < nc * (JB / 4); f += kThreads) {
-            const int t = f / (JB / 4), cg = f - t * (JB / 4);
-            __builtin_nontemporal_store(*reinterpret_cast<const v4f *>(Ot + t * SV + 4 * cg),
-                                        reinterpret_cast<v4f *>(out + (((int64_t)c * T + k0 + t) * Hv + h) * DV + j0) + cg);
+            for (int rt = 0; rt < KC; ++rt) sreg[rt] = mfma4(kt[rt], bw, f.gend * sreg[rt]);
         }
     }
 
@@ -271,11 +388,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 template <int DK, int DV>
 hipError_t launch(const Dims &d, int T, const float *qkv, const float *beta_logits, const float *alpha_logits,
                   int64_t gate_stride, const float *dt_bias, const float *A, float *state_pool,
-                  const int32_t *slot_ids, const float *gate_z, int gate_mode, float *out, int32_t *status,
-                  hipStream_t stream) {
-    hipLaunchKernelGGL((prefill_kernel<DK, DV>), dim3(PrefillCfg<DK, DV>::NB * d.Hv, d.C), dim3(kThreads), 0, stream, d,
-                       T, qkv, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids, gate_z,
-                       gate_mode, out, status);
+                  const int32_t *slot_ids, const float *gate_z, int gate_mode, float *out, float *workspace,
+                  int32_t *status, hipStream_t stream) {
+    const int nch = (T + BC - 1) / BC;
+    hipLaunchKernelGGL((prefill_prep_kernel<DK>), dim3(nch * d.Hk, d.C), dim3(kThreads), 0, stream, d, T, qkv,
+                       beta_logits, alpha_logits, gate_stride, dt_bias, A, workspace);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    const dim3 grid(PrefillCfg<DK, DV>::NB * d.Hv * d.C);
+    if (gate_z)
+        hipLaunchKernelGGL((prefill_state_kernel<DK, DV, true>), grid, dim3(kThreads), 0, stream, d, T, qkv, workspace,
+                           state_pool, slot_ids, gate_z, gate_mode, out, status);
+    else
+        hipLaunchKernelGGL((prefill_state_kernel<DK, DV, false>), grid, dim3(kThreads), 0, stream, d, T, qkv,
+                           workspace, state_pool, slot_ids, gate_z, gate_mode, out, status);
     return hipGetLastError();
 }
 
@@ -284,11 +409,11 @@ hipError_t launch(const Dims &d, int T, const float *qkv, const float *beta_logi
 hipError_t launch_prefill(const Dims &d, int n_tokens, const float *qkv, const float *beta_logits,
                           const float *alpha_logits, int64_t gate_stride, const float *dt_bias, const float *A,
                           float *state_pool, const int32_t *slot_ids, const float *gate_z, int gate_mode, float *out,
-                          int32_t *status, hipStream_t stream) {
+                          float *workspace, int32_t *status, hipStream_t stream) {
 #define GDN_PREFILL_CASE(K, V)                                                                                  \
     if (d.dk == K && d.dv == V)                                                                                 \
         return launch<K, V>(d, n_tokens, qkv, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, \
-                            slot_ids, gate_z, gate_mode, out, status, stream);
+                            slot_ids, gate_z, gate_mode, out, workspace, status, stream);
 #define GDN_PREFILL_ROW(K) GDN_PREFILL_CASE(K, 16) GDN_PREFILL_CASE(K, 32) GDN_PREFILL_CASE(K, 64) GDN_PREFILL_CASE(K, 128)
     GDN_PREFILL_ROW(16) GDN_PREFILL_ROW(32) GDN_PREFILL_ROW(64) GDN_PREFILL_ROW(128)
 #undef GDN_PREFILL_ROW

@@ -30,7 +30,8 @@ KERNEL_SOURCES = {  # (matched in this order: conv_tree_verify before tree_verif
     "tree_verify": "csrc/tree_verify.hip",
     "replay_commit": "csrc/replay_commit.hip",
     "decode_step": "csrc/decode_step.hip",
-    "prefill": "csrc/prefill.hip",
+    "prefill_prep": "csrc/prefill.hip",
+    "prefill_state": "csrc/prefill.hip",
     "conv_step": "csrc/decode_step.hip",
 }
 

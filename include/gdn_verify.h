@@ -79,6 +79,7 @@
 #ifndef GDN_VERIFY_H
 #define GDN_VERIFY_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -99,6 +100,7 @@ extern "C" {
 #define GDN_ERR_HIP 5         /* a kernel launch failed                                      */
 #define GDN_ERR_ALIGN 6       /* a dense float buffer is not 16-byte aligned, or an int32 /
                                  gate buffer not 4-byte aligned                              */
+#define GDN_ERR_WORKSPACE 7   /* workspace_bytes below gdn_prefill_workspace_size()          */
 
 /* Device status bits (OR-ed into *status). */
 #define GDN_STATUS_SLOT_RANGE 1 /* slot id outside [-1, P)                                   */
@@ -327,11 +329,22 @@ int gdn_decode_step(const gdn_shape *sh, const float *qkv, const float *beta_log
  *   gate_z         [C][T][H_v][d_v]    output gate values, or NULL          (read)
  *   gate_mode      0 (SiLU) or 1 (sigmoid); GDN_ERR_SHAPE otherwise
  *   out            [C][T][H_v][d_v]    written for non-padding lanes
+ *   workspace      device scratch of at least gdn_prefill_workspace_size(sh) bytes,
+ *                  16-byte aligned, overlapping nothing else; its contents on entry do
+ *                  not matter and are undefined afterwards.  It holds the per-chunk
+ *                  coefficients of the chunked form (C * H_v * ceil(T / 16) * 2320 bytes)
+ *                  and must not be used by another call until this one has run.
+ *   workspace_bytes its size (GDN_ERR_WORKSPACE if too small)
  *   status         int32*, REQUIRED (GDN_ERR_NULL otherwise)
  */
 int gdn_prefill(const gdn_shape *sh, const float *qkv, const float *beta_logits, const float *alpha_logits,
                 int64_t gate_stride, const float *dt_bias, const float *A, float *state_pool, const int32_t *slot_ids,
-                const float *gate_z, int32_t gate_mode, float *out, int32_t *status, hipStream_t stream);
+                const float *gate_z, int32_t gate_mode, float *out, float *workspace, size_t workspace_bytes,
+                int32_t *status, hipStream_t stream);
+
+/* Bytes of workspace gdn_prefill needs for this shape (n_nodes = T tokens per lane); 0 if
+   the shape is invalid for gdn_prefill.  Host only, no device call. */
+size_t gdn_prefill_workspace_size(const gdn_shape *sh);
 
 /* Static description of a GDN_OK / GDN_ERR_* code. */
 const char *gdn_strerror(int code);

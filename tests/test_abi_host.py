@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libra
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|const char \*)\s*(gdn_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^(?:int|size_t|const char \*)\s*(gdn_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_exports_every_declared_function():
@@ -275,13 +275,26 @@ def test_prefill_rejections():
     lib = gdn.load_library()
     st = FAKE + (1 << 40)
 
-    def call(sh, p, gate_stride=8, gate_mode=0, status=st):
+    def call(sh, p, gate_stride=8, gate_mode=0, status=st, ws_bytes=None):
         cs = sh.c_struct()
+        if ws_bytes is None:
+            ws_bytes = lib.gdn_prefill_workspace_size(ctypes.byref(cs))
         return lib.gdn_prefill(ctypes.byref(cs), p[0], p[1], p[2], gate_stride, p[3], p[4], p[5], p[6], p[7],
-                               ctypes.c_int32(gate_mode), p[8], status, None)
+                               ctypes.c_int32(gate_mode), p[8], p[9], ctypes.c_size_t(ws_bytes), status, None)
 
-    p = _ptrs(9)  # qkv, beta, alpha, dt_bias, A, state_pool, slot_ids, gate_z, out
+    p = _ptrs(10)  # qkv, beta, alpha, dt_bias, A, state_pool, slot_ids, gate_z, out, workspace
     assert call(_shape(n_nodes=1000), p, status=None) == _lib.GDN_ERR_NULL
+    q = list(p)
+    q[9] = None  # no workspace
+    assert call(_shape(n_nodes=1000), q) == _lib.GDN_ERR_NULL
+    need = gdn.prefill_workspace_size(_shape(n_nodes=1000))
+    assert call(_shape(n_nodes=1000), p, ws_bytes=need - 1) == _lib.GDN_ERR_WORKSPACE
+    q = list(p)
+    q[9] = q[8] + 64  # workspace inside the output
+    assert call(_shape(n_nodes=1000), q) == _lib.GDN_ERR_ALIAS
+    q = list(p)
+    q[9] += 4  # workspace not 16-byte aligned
+    assert call(_shape(n_nodes=1000), q) == _lib.GDN_ERR_ALIGN
     assert call(_shape(n_nodes=65537), p) == _lib.GDN_ERR_UNSUPPORTED  # longer than GDN_MAX_CHAIN
     assert call(_shape(n_nodes=1000), p, gate_mode=2) == _lib.GDN_ERR_SHAPE
     assert call(_shape(n_nodes=1000), p, gate_stride=3) == _lib.GDN_ERR_SHAPE
@@ -294,6 +307,16 @@ def test_prefill_rejections():
     q = list(p)
     q[8] = q[7] + 16  # out overlapping the gate values
     assert call(_shape(n_nodes=1000), q) == _lib.GDN_ERR_ALIAS
+
+
+def test_prefill_workspace_size():
+    """One package of 580 floats per (lane, value head, chunk of 16 tokens); 0 for shapes the
+    prefill rejects."""
+    sh = _shape(n_nodes=37)
+    assert gdn.prefill_workspace_size(sh) == sh.n_seqs * sh.n_v_heads * 3 * 580 * 4
+    assert gdn.prefill_workspace_size(_shape(n_nodes=16)) == _shape().n_seqs * _shape().n_v_heads * 580 * 4
+    assert gdn.prefill_workspace_size(_shape(n_nodes=65537)) == 0
+    assert gdn.prefill_workspace_size(_shape(d_k=24)) == 0
 
 
 def test_conv_step_chain_limit():

@@ -29,7 +29,7 @@ def _inputs(C, T, P, Hk, Hv, dk, dv, seed, pad=None):
     return case
 
 
-def _gpu_prefill(case, Hk, qkv=None, gate=False, mode=0, status=None):
+def _gpu_prefill(case, Hk, qkv=None, gate=False, mode=0, status=None, workspace=None):
     C, T, Ch = case["x"].shape
     P, Hv, dk, dv = case["state"].shape
     sh = gdn.Shape(C, T, P, Hk, Hv, dk, dv)
@@ -39,7 +39,7 @@ def _gpu_prefill(case, Hk, qkv=None, gate=False, mode=0, status=None):
     status = torch.zeros(1, dtype=torch.int32, device="cuda") if status is None else status
     gdn.prefill(sh, dev(case["qkv"]) if qkv is None else qkv, ba[..., :Hv], ba[..., Hv:], dev(case["dt_bias"]),
                 dev(case["A"]), state, dev(case["slot_ids"]), status, gate_z=dev(case["z"]) if gate else None,
-                gate_mode=mode, out=out.t)
+                gate_mode=mode, out=out.t, workspace=workspace)
     return state, out, status
 
 
@@ -150,6 +150,21 @@ def test_prefill_equals_decode_steps_on_gpu():
     e_out = max(err_metric(out.np()[:, t], outs[t].cpu().numpy()) for t in range(T))
     assert e_state <= REC_TOL and e_out <= REC_TOL, (e_state, e_out)
     log(f"[prefill] vs decode steps: out {e_out:.2e} state {e_state:.2e}")
+
+
+def test_prefill_workspace_contents_do_not_matter():
+    """A workspace holding NaN (and larger than needed) gives the results of a fresh one,
+    bit for bit, on two calls in a row with different prompt lengths."""
+    for T in (53, 20):
+        case = _inputs(2, T, 4, 2, 4, 32, 32, seed=250 + T)
+        sh = gdn.Shape(2, T, 4, 2, 4, 32, 32)
+        log(f"[prefill] NaN workspace, T={T}")
+        ws = torch.full((gdn.prefill_workspace_size(sh) // 4 + 100,), float("nan"), device="cuda")
+        st_a, out_a, status_a = _gpu_prefill(case, 2, gate=True, workspace=ws)
+        st_b, out_b, status_b = _gpu_prefill(case, 2, gate=True)
+        torch.cuda.synchronize()
+        assert int(status_a.item()) == 0 and int(status_b.item()) == 0
+        assert torch.equal(st_a, st_b) and np.array_equal(out_a.np(), out_b.np())
 
 
 @pytest.mark.parametrize("bad", ["slot_dup", "status_in"])
