@@ -225,22 +225,26 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     }
 }
 
-// One chunk's package operands and value / gate values in the accumulator layout of lane
-// (g4, l16): rows 4 g4 .. 4 g4 + 3, value column jj.
-struct Frag {
-    v4f tf, cf, a, b, cc, w, v, z;
-    float gend;
-};
+// A chunk's package in LDS: T and Cq with rows of LP_S floats (so that 16 lanes reading a
+// 16-byte piece of one row each hit distinct banks), then the four per-token vectors and
+// G_B.  Thread t < kPkGroups stages float4 group t of the package.
+constexpr int LP_S = BC + 4, LP_T = 0, LP_CQ = BC * LP_S, LP_V = 2 * BC * LP_S, LP_G = LP_V + 4 * BC;
+constexpr int LP_FLOATS = LP_G + 4, kPkGroups = kPackFloats / 4;
+static_assert(kPkGroups <= kThreads, "one package group per thread");
+__device__ inline int package_lds_offset(int t) {  // float offset of package group t in LDS
+    return t < 64 ? LP_T + (t >> 2) * LP_S + 4 * (t & 3)
+                  : t < 128 ? LP_CQ + ((t - 64) >> 2) * LP_S + 4 * (t & 3) : LP_V + 4 * (t - 128);
+}
 
 // ---- kernel 2: the state through the chunks.  One workgroup (4 waves) per (lane, value
 // head, block of 64 value columns); wave w owns the 16-column tile w of the state for the
 // whole prompt.  Workgroup ids are ordered so that the workgroups sharing one (lane, q/k
 // head) are congruent modulo C * H_k and read the shared q/k rows through one L2.  One
-// barrier per chunk: the rows of chunk j are staged in LDS buffer j % 2, so staging chunk
-// j + 1 never overlaps a wave still reading chunk j - 1.  Every per-chunk buffer (rows,
-// values, gate values, outputs, package) is addressed by a per-lane offset that is the
-// same for every chunk and a chunk base that moves by a uniform step; its range ends at
-// the chunk's last real token.
+// barrier per chunk: the rows and the package of chunk j are staged in LDS buffer j % 2,
+// so staging chunk j + 1 never overlaps a wave still reading chunk j - 1.  Every per-chunk
+// buffer (rows, values, gate values, outputs, package) is addressed by a per-lane offset
+// that is the same for every chunk and a chunk base that moves by a uniform step; its
+// range ends at the chunk's last real token.
 template <int DK, int DV, bool GATED>
 __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     Dims d, int T, const float *__restrict__ qkv, const float *__restrict__ pack, float *__restrict__ state_pool,
@@ -251,6 +255,7 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     __shared__ unsigned int s_bitmap[kBitmapSlots / 32];
     __shared__ int s_word;
     __shared__ __align__(16) float QK[2][2 * BC * SX];  // per buffer: q rows, then k rows
+    __shared__ __align__(16) float PK[2][LP_FLOATS];
 
     const int n_groups = d.C * d.Hk;
     const int grp = blockIdx.x % n_groups, ws = blockIdx.x / n_groups;
@@ -270,38 +275,35 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     const LaneSlotsT<kThreads> lanes(slot_ids, d.C);
     const int st_in = *status;
 
-    // per-lane byte offsets within a chunk: value (and gate value / output) rows 4 g4 + v
+    // per-lane byte offsets within a chunk: value (and gate value / output) rows 4 g4 + v;
+    // this thread's package group
     int vo[4], zo[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         vo[v] = ((4 * g4 + v) * Ch + 2 * d.Hk * DK + h * DV + jj) * 4;
         zo[v] = ((4 * g4 + v) * HvDV + h * DV + jj) * 4;
     }
+    const int pk_off = tid < kPkGroups ? 16 * tid : kPackFloats * 4;  // past the range: reads zero
+    const int pk_lds = package_lds_offset(min(tid, kPkGroups - 1));
     const float *pk0 = pack + ((int64_t)c * d.Hv + h) * nch * kPackFloats;
     auto chunk_base = [&](const float *buf, int row_floats, int k0) { return buf + ((int64_t)c * T + k0) * row_floats; };
-    auto load_frag = [&](int jc, Frag &f) {
+    // chunk jc's package group, values and gate values of this thread
+    v4f pkn, vn, zn = {0.f, 0.f, 0.f, 0.f};
+    auto load_chunk = [&](int jc) {
         const int k0 = jc * BC, nc = min(BC, T - k0);
-        const __amdgpu_buffer_rsrc_t pr = rsrc(pk0 + (int64_t)jc * kPackFloats, kPackFloats * 4);
-        f.tf = load4(pr, (PK_T + 16 * l16 + 4 * g4) * 4);
-        f.cf = load4(pr, (PK_CQ + 16 * l16 + 4 * g4) * 4);
-        f.a = load4(pr, (PK_A + 4 * g4) * 4);
-        f.b = load4(pr, (PK_B + 4 * g4) * 4);
-        f.cc = load4(pr, (PK_C + 4 * g4) * 4);
-        f.w = load4(pr, (PK_W + 4 * g4) * 4);
-        f.gend = load1(pr, (PK_GEND + g4) * 4);
+        pkn = load4(rsrc(pk0 + (int64_t)jc * kPackFloats, kPackFloats * 4), pk_off);
         const __amdgpu_buffer_rsrc_t vr = rsrc(chunk_base(qkv, Ch, k0), nc * Ch * 4);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) f.v[v] = load1(vr, vo[v]);
+        for (int v = 0; v < 4; ++v) vn[v] = load1(vr, vo[v]);
         if constexpr (GATED) {
             const __amdgpu_buffer_rsrc_t zr = rsrc(chunk_base(gate_z, HvDV, k0), nc * HvDV * 4);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) f.z[v] = load1(zr, zo[v]);
+            for (int v = 0; v < 4; ++v) zn[v] = load1(zr, zo[v]);
         }
     };
     ChunkRows<DK> rows(Ch, d.Hk, kh);
     rows.load(rsrc(chunk_base(qkv, Ch, 0), min(BC, T) * Ch * 4));
-    Frag fn;
-    load_frag(0, fn);
+    load_chunk(0);
     __builtin_amdgcn_sched_barrier(0);
     const int s = __builtin_amdgcn_readfirstlane(s_v);
     const bool s_ok = s >= 0 && s < d.P;
@@ -323,26 +325,38 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
 
     for (int jc = 0; jc < nch; ++jc) {
         const int k0 = jc * BC, nc = min(BC, T - k0);
-        float *Qb = QK[jc & 1], *Kb = Qb + BC * SX;
+        float *Qb = QK[jc & 1], *Kb = Qb + BC * SX, *Pb = PK[jc & 1];
         rows.stage(Qb);
-        const Frag f = fn;
+        if (tid < kPkGroups) *reinterpret_cast<v4f *>(Pb + pk_lds) = pkn;
+        const v4f vv = vn, zz = zn;
         lds_barrier();
         if (jc + 1 < nch) {  // the next chunk's loads go out now, under this chunk's products
             rows.load(rsrc(chunk_base(qkv, Ch, k0 + BC), min(BC, T - k0 - BC) * Ch * 4));
-            load_frag(jc + 1, fn);
+            load_chunk(jc + 1);
         }
         if (wave < CT) {
-            // [K; Q] S
+            // [K; Q] S, the operands read ahead of the products
+            v4f ak[KC], aq[KC];
+#pragma unroll
+            for (int q = 0; q < KC; ++q) {
+                ak[q] = *reinterpret_cast<const v4f *>(Kb + l16 * SX + 16 * q + 4 * g4);
+                aq[q] = *reinterpret_cast<const v4f *>(Qb + l16 * SX + 16 * q + 4 * g4);
+            }
             v4f ks = {0.f, 0.f, 0.f, 0.f}, qs = ks;
 #pragma unroll
             for (int q = 0; q < KC; ++q) {
-                const v4f ak = *reinterpret_cast<const v4f *>(Kb + l16 * SX + 16 * q + 4 * g4);
-                const v4f aq = *reinterpret_cast<const v4f *>(Qb + l16 * SX + 16 * q + 4 * g4);
-                ks = mfma4(ak, sreg[q], ks);
-                qs = mfma4(aq, sreg[q], qs);
+                ks = mfma4(ak[q], sreg[q], ks);
+                qs = mfma4(aq[q], sreg[q], qs);
             }
-            // the update's left operand K^T (lane supplies K[token 4*g4 + s][16 rt + l16] in
-            // step s), read while the products run
+            // the package operands, and the update's left operand K^T (lane supplies
+            // K[token 4*g4 + s][16 rt + l16] in step s), read while the products run
+            const v4f tf = *reinterpret_cast<const v4f *>(Pb + LP_T + l16 * LP_S + 4 * g4);
+            const v4f cf = *reinterpret_cast<const v4f *>(Pb + LP_CQ + l16 * LP_S + 4 * g4);
+            const v4f pa = *reinterpret_cast<const v4f *>(Pb + LP_V + 4 * g4);
+            const v4f pb = *reinterpret_cast<const v4f *>(Pb + LP_V + BC + 4 * g4);
+            const v4f pc = *reinterpret_cast<const v4f *>(Pb + LP_V + 2 * BC + 4 * g4);
+            const v4f pw = *reinterpret_cast<const v4f *>(Pb + LP_V + 3 * BC + 4 * g4);
+            const float gend = Pb[LP_G];
             v4f kt[KC];
 #pragma unroll
             for (int rt = 0; rt < KC; ++rt)
@@ -352,27 +366,27 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
             v4f rhs, o, bw;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                rhs[v] = f.a[v] * (f.v[v] - f.b[v] * ks[v]);
-                o[v] = f.cc[v] * qs[v];
+                rhs[v] = pa[v] * (vv[v] - pb[v] * ks[v]);
+                o[v] = pc[v] * qs[v];
             }
-            const v4f dl = mfma4(f.tf, rhs, v4f{0.f, 0.f, 0.f, 0.f});
-            o = mfma4(f.cf, dl, o);
+            const v4f dl = mfma4(tf, rhs, v4f{0.f, 0.f, 0.f, 0.f});
+            o = mfma4(cf, dl, o);
             const __amdgpu_buffer_rsrc_t orr = rsrc(chunk_base(out, HvDV, k0), nc * HvDV * 4);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 if constexpr (GATED) {
-                    const float sg = fast_sigmoid(f.z[v]);
-                    o[v] *= gate_mode == 0 ? f.z[v] * sg : sg;  // silu(z) = z sigmoid(z)
+                    const float sg = fast_sigmoid(zz[v]);
+                    o[v] *= gate_mode == 0 ? zz[v] * sg : sg;  // silu(z) = z sigmoid(z)
                 }
                 // (the element goes through a scalar: this compiler's __builtin_bit_cast of a vector
                 // element lvalue reads element 0 whatever the index)
                 const float ov = o[v];
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), orr, zo[v], 0, kNonTemporal);
-                bw[v] = f.w[v] * dl[v];
+                bw[v] = pw[v] * dl[v];
             }
             // S <- G_B S + K^T diag(w) D, tile by tile of 16 d_k rows
 #pragma unroll
-            for (int rt = 0; rt < KC; ++rt) sreg[rt] = mfma4(kt[rt], bw, f.gend * sreg[rt]);
+            for (int rt = 0; rt < KC; ++rt) sreg[rt] = mfma4(kt[rt], bw, gend * sreg[rt]);
         }
     }
 
