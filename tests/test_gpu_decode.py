@@ -210,3 +210,47 @@ def test_plain_steps_equal_chain_verify_then_commit():
     e_out = max(err_metric(outs[t].np(), ov[:, t]) for t in range(k))
     assert e_out <= REC_TOL, f"output error {e_out}"
     log(f"[plain] plain vs verify+commit: out {e_out:.2e} state {e_state:.2e}")
+
+
+def test_plain_step_graph_replay_matches_eager():
+    """Two plain steps (conv step + recurrence each) captured in a HIP graph: every replay,
+    with eager work and host synchronisation between replays, is bit-identical to the
+    eager calls."""
+    C, P, Hk, Hv, dk, dv = 4, 8, 16, 32, 128, 128
+    case = synth_case(C, 2, P, Hk, Hv, dk, dv, seed=90, tree=False)
+    log("[plain] two plain steps captured and replayed")
+    g = PlainStep(case, Hk)
+    hist0, state0 = g.hist.clone(), g.state.clone()
+    sh1 = g.shape(1)
+    xs = [dev(case["x"][:, t:t + 1]) for t in range(2)]
+    bas = [dev(case["ba"][:, t]) for t in range(2)]
+    qkv = [torch.empty((C, 1, g.Ch), device="cuda") for _ in range(2)]
+    outs = [torch.empty((C, Hv, dv), device="cuda") for _ in range(2)]
+
+    def run():
+        for t in range(2):
+            gdn.conv_step(sh1, xs[t], g.conv_w, g.hist, g.slot_t, g.status, conv_out=qkv[t])
+            gdn.decode_step(sh1, qkv[t][:, 0], bas[t][:, :Hv], bas[t][:, Hv:], g.dt, g.A, g.state, g.slot_t,
+                            g.status, out=outs[t])
+
+    run()
+    torch.cuda.synchronize()
+    bufs = qkv + outs + [g.hist, g.state]
+    ref = [b.clone() for b in bufs]
+    g.hist.copy_(hist0)
+    g.state.copy_(state0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        for b in qkv + outs:
+            b.fill_(0.0)  # eager work between replays
+        g.hist.copy_(hist0)
+        g.state.copy_(state0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(g.status.item()) == 0
+        for a, b in zip(bufs, ref):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager result"

@@ -179,3 +179,48 @@ def test_prefill_is_all_or_nothing(bad):
     assert st & (gdn.STATUS_SLOT_DUP if bad == "slot_dup" else 0x100)
     assert (out.np() == np.float32(SENTINEL)).all()
     assert np.array_equal(state.cpu().numpy(), case["state"])
+
+
+def test_prompt_graph_replay_matches_eager():
+    """The prompt path (chain conv step, then prefill with a gate) captured in a HIP graph:
+    every replay, with eager work and host synchronisation between replays, is
+    bit-identical to the eager calls."""
+    C, T, P, Hk, Hv, dk, dv = 2, 40, 3, 2, 4, 64, 64
+    case = _inputs(C, T, P, Hk, Hv, dk, dv, seed=260)
+    sh = gdn.Shape(C, T, P, Hk, Hv, dk, dv)
+    log("[prefill] conv step + prefill captured and replayed")
+    x, w, ba = dev(case["x"]), dev(case["conv_w"]), dev(case["ba"])
+    hist, state, slots = dev(case["conv_hist"]), dev(case["state"]), dev(case["slot_ids"])
+    z, dt, A = dev(case["z"]), dev(case["dt_bias"]), dev(case["A"])
+    hist0, state0 = hist.clone(), state.clone()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qkv = torch.empty((C, T, sh.channels), device="cuda")
+    out = torch.empty((C, T, Hv, dv), device="cuda")
+    ws = torch.empty(gdn.prefill_workspace_size(sh) // 4, device="cuda")
+
+    def run():
+        gdn.conv_step(sh, x, w, hist, slots, status, conv_out=qkv)
+        gdn.prefill(sh, qkv, ba[..., :Hv], ba[..., Hv:], dt, A, state, slots, status, gate_z=z, gate_mode=0,
+                    out=out, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    ref = [qkv.clone(), out.clone(), hist.clone(), state.clone()]
+    hist.copy_(hist0)
+    state.copy_(state0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        qkv.fill_(0.0)  # eager work between replays
+        out.fill_(0.0)
+        ws.fill_(float("nan"))
+        hist.copy_(hist0)
+        state.copy_(state0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        for a, b in zip([qkv, out, hist, state], ref):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager result"
