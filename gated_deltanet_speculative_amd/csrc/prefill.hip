@@ -19,19 +19,21 @@
 //
 // Two launches.  Everything that does not involve the state -- norms, gates, the Gram
 // products, Lm, Cq and T = (I + Lm)^-1 -- depends on one chunk's tokens only, so the first
-// kernel computes it for every (lane, value head, chunk) at once, a workgroup per chunk,
-// into a package of kPackFloats floats in the caller's workspace.  The second kernel
+// kernel computes it for every chunk at once (a workgroup per lane, q/k head and chunk,
+// sharing the norms and Gram products among the value heads of the q/k head), into one
+// package of kPackFloats floats per value head in the caller's workspace.  The second kernel
 // carries the state through the chunks in order and does only what involves it: the
 // products [K; Q] S, D = T rhs, O = diag(c) QS + Cq D, the output gate and the update, all
 // on v_mfma_f32_16x16x4_f32 with the operand permutation of mfma4, so the state tile stays
 // in registers across chunks in exactly the layout in which the next chunk's products and
 // the update consume and produce it.
 //
-// Package of (lane c, value head h, chunk j), floats:
+// Package of (lane c, value head h, chunk j), at float offset ((c H_v + h) n_chunks + j) *
+// kPackFloats of the workspace:
 //   [0, 256)    T[t][u] row-major                  [256, 512)  Cq[t][u] row-major
 //   [512, 528)  a_t = beta_t                       [528, 544)  b_t = G_t rk_t
 //   [544, 560)  c_t = G_t rq_t / sqrt(d_k)         [560, 576)  w_t = exp(L_B - L_t) rk_t
-//   [576, 580)  G_B, four copies (so that every lane's load of it is a vector load)
+//   [576, 580)  G_B, four copies (one float4 group)
 // Padding tokens of the last chunk are zero rows: beta = 0 and no decay, so they write
 // nothing into D, O or the state.
 #include "gdn_device.h"
