@@ -117,6 +117,11 @@ def prefill_cost(wl, T, chunk=16):
     return dict(flops=flops, bytes=bytes_, conv_bytes=conv)
 
 
+def percentiles(xs):
+    """p10, median and p90 of a list of timings, rounded."""
+    return [round(float(v), 4) for v in np.percentile(np.asarray(xs, dtype=np.float64), [10, 50, 90])]
+
+
 def measured_traffic(workload, kernel):
     """Fabric bytes per launch of `kernel` from the committed counter summary
     (profiles/traffic_<workload>.json: FETCH_SIZE + WRITE_SIZE, copy-calibrated), or
@@ -496,19 +501,23 @@ def main():
         graphs[r].replay()
     torch.cuda.synchronize()
 
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
+    # K steps back to back; an event between consecutive steps gives each step's own time
+    # (events only record, they add no synchronisation)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
     for k in range(args.steps):
         graphs[k % args.rounds].replay()
-    ev1.record()
+        evs[k + 1].record()
     torch.cuda.synchronize()
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    ms_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    step_ms = [evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps)]
     assert int(status.item()) == 0, "device status bits set"
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     # per-kernel mean time per layer instance: each kernel alone over the L instances (one
     # graph of L back-to-back launches, or of one multi-layer commit launch), HIP events
     # on the stream the graph runs on
-    kern = {}
+    kern, kern_pct, cold_us = {}, {}, {}
     if not args.profile_only:
         if args.route == "fused":
             timed = [("conv_tree_verify", lambda: [conv_verify(b, 0) for b in inst])]
@@ -521,12 +530,30 @@ def main():
             g = capture(fn)
             g.replay()
             torch.cuda.synchronize()
-            ev0.record()
+            kev = [torch.cuda.Event(enable_timing=True) for _ in range(args.kernel_reps + 1)]
+            kev[0].record()
             for rep in range(args.kernel_reps):
                 g.replay()
+                kev[rep + 1].record()
+            torch.cuda.synchronize()
+            kern[name] = kev[0].elapsed_time(kev[-1]) * 1e3 / (args.kernel_reps * L)  # us per layer instance
+            kern_pct[name] = percentiles([kev[r].elapsed_time(kev[r + 1]) * 1e3 / L for r in range(args.kernel_reps)])
+        # one call each right after a 1 GiB device write has flushed the caches (eager
+        # launches; the write is still running while the call is enqueued, so the host's
+        # launch latency is not in the measurement)
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        for name, fn in timed:
+            one = {"conv_tree_verify": lambda: conv_verify(inst[0], 0), "conv_tree_step": lambda: conv(inst[0], 0),
+                   "tree_verify": lambda: verify(inst[0], 0), "replay_commit": lambda: commit(inst[0], 0)}[name]
+            one()  # the first launch of a kernel in the process also loads it: not timed
+            torch.cuda.synchronize()
+            flush.fill_(1.0)
+            ev0.record()
+            one()
             ev1.record()
             torch.cuda.synchronize()
-            kern[name] = ev0.elapsed_time(ev1) * 1e3 / (args.kernel_reps * L)  # us per layer instance
+            cold_us[name] = ev0.elapsed_time(ev1) * 1e3
+        del flush
 
     calibrate_copy(args.calibrate_copy, dev)
 
@@ -579,7 +606,10 @@ def main():
                    **({"ragged": "lane node counts uniform in 1..N, mean "
                                  + f"{np.mean(present) / C:.2f} per lane"} if args.ragged else {})},
         "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_ms_p10_p50_p90": percentiles(step_ms),
         "kernel_us": {k: round(v, 3) for k, v in kern.items()},
+        "kernel_us_p10_p50_p90": kern_pct,
+        "kernel_cold_call_us": {k: round(v, 2) for k, v in cold_us.items()},
         "kernel_gbs": {k: round(kernel_bytes[k] / (kern[k] * 1e-6) / 1e9, 1) for k in kern},
         "verify_only_tokens_per_s": (round(present[0] / (sum(v for k, v in kern.items() if k != "replay_commit")
                                                          * 1e-6), 1) if kern else None),
