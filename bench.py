@@ -517,7 +517,9 @@ def main():
     # per-kernel mean time per layer instance: each kernel alone over the L instances (one
     # graph of L back-to-back launches, or of one multi-layer commit launch), HIP events
     # on the stream the graph runs on
-    kern, kern_pct, cold_us = {}, {}, {}
+    kern, kern_pct, cold_us, copy_ref = {}, {}, {}, None
+    ab0 = algorithmic_bytes(wl, [1] * C, rounds[0].get("lane_nodes"))
+    kernel_bytes_est = {"conv_tree_verify": ab0["conv_verify"], "tree_verify": ab0["verify"]}
     if not args.profile_only:
         if args.route == "fused":
             timed = [("conv_tree_verify", lambda: [conv_verify(b, 0) for b in inst])]
@@ -554,6 +556,24 @@ def main():
             torch.cuda.synchronize()
             cold_us[name] = ev0.elapsed_time(ev1) * 1e3
         del flush
+        # context for the dominant kernel's fraction: a plain device copy moving the same
+        # number of bytes (read + write), 64 back-to-back copies of distinct buffers replayed
+        # as a graph, and an empty graph replay's cost per launch of a one-kernel graph
+        nb = int(kernel_bytes_est["conv_tree_verify" if args.route == "fused" else "tree_verify"]) // 8
+        srcs = [torch.ones(nb, dtype=torch.float32, device=dev) for _ in range(64)]
+        dsts = [torch.empty(nb, dtype=torch.float32, device=dev) for _ in range(64)]
+        g = capture(lambda: [d_.copy_(s_) for d_, s_ in zip(dsts, srcs)])
+        g.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(5):
+            g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        copy_us = ev0.elapsed_time(ev1) * 1e3 / (5 * 64)
+        copy_ref = dict(bytes=8 * nb, us=round(copy_us, 3), gbs=round(8 * nb / (copy_us * 1e-6) / 1e9, 1),
+                        what="torch device copy_ of the same byte count, 64 buffers, graph replay")
+        del srcs, dsts, g
 
     calibrate_copy(args.calibrate_copy, dev)
 
@@ -610,6 +630,7 @@ def main():
         "kernel_us": {k: round(v, 3) for k, v in kern.items()},
         "kernel_us_p10_p50_p90": kern_pct,
         "kernel_cold_call_us": {k: round(v, 2) for k, v in cold_us.items()},
+        "copy_same_bytes": copy_ref,
         "kernel_gbs": {k: round(kernel_bytes[k] / (kern[k] * 1e-6) / 1e9, 1) for k in kern},
         "verify_only_tokens_per_s": (round(present[0] / (sum(v for k, v in kern.items() if k != "replay_commit")
                                                          * 1e-6), 1) if kern else None),
