@@ -136,6 +136,17 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
 
     ChunkRows<DK> rows(d.Ch, d.Hk, kh);
     rows.load(rsrc(qkv + ((int64_t)c * T + k0) * d.Ch, nc * d.Ch * 4));
+    // gate inputs of value heads m0 .. m0 + HG - 1 for thread (m, t): a row of 16 lanes per
+    // head (the first group's go out with the rows)
+    float xb, xa, xA;
+    auto load_gates = [&](int m0) {
+        const int h = kh + d.Hk * min(m0 + (tid >> 4), R - 1);
+        const int64_t trow = (int64_t)c * T + min(k0 + (tid & 15), T - 1);
+        xb = beta_logits[trow * gate_stride + h];
+        xa = alpha_logits[trow * gate_stride + h] + dt_bias[h];
+        xA = A[h];
+    };
+    load_gates(0);
     rows.stage(QK);
     lds_barrier();
 
@@ -178,16 +189,13 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
 
     const float isd = 1.0f / sqrtf((float)DK);
     for (int m0 = 0; m0 < R; m0 += HG) {
-        // gates of value heads m0 .. m0 + HG - 1: thread (m, t), a row of 16 lanes per head,
-        // and the inclusive prefix of the log-decays over the chunk
+        // gates of value heads m0 .. m0 + HG - 1 and the inclusive prefix of the log-decays
+        // over the chunk
+        if (m0 > 0) load_gates(m0);
         {
-            const int m = m0 + (tid >> 4), t = tid & 15;
-            const int h = kh + d.Hk * min(m, R - 1);
-            const int64_t trow = (int64_t)c * T + min(k0 + t, T - 1);
-            const float xb = beta_logits[trow * gate_stride + h];
-            const float xa = alpha_logits[trow * gate_stride + h] + dt_bias[h];
+            const int t = tid & 15;
             const bool real = t < nc;
-            const float ell = real ? fast_softplus(xa) * A[h] : 0.f;  // log g
+            const float ell = real ? fast_softplus(xa) * xA : 0.f;  // log g
             const float L = group_sum_last<16>(ell);
             s_beta[tid >> 4][t] = real ? fast_sigmoid(xb) : 0.f;
             s_L[tid >> 4][t] = L;
