@@ -370,3 +370,44 @@ def test_fused_matches_split_route():
     torch.cuda.synchronize()
     assert err_metric(b.state.cpu().numpy(), a.state.cpu().numpy()) <= REC_TOL
     assert torch.equal(a.conv_hist, b.conv_hist)
+
+
+@pytest.mark.parametrize("layer", [0, 47])
+def test_stress_two_rounds_on_sampled_lanes(layer):
+    """The bandwidth-stress workload (64 lanes in 128 slots, 32-node trees) over two
+    verify -> commit rounds of one layer: the GPU runs every lane (fused route), the oracle
+    4 sampled lanes on their own slots; outputs, windows and log each round, then the
+    committed state and history, are compared."""
+    wl = WORKLOADS["stress-c64-n32-l48"]
+    sh = gdn.Shape(**wl.shape_dict())
+    lanes = np.array([3, 22, 51, 60])
+    log(f"[parity] stress two rounds, layer {layer}, lanes {lanes.tolist()}")
+    lp = layer_params(wl, layer)
+    rs = [round_structure(wl, r) for r in range(2)]
+    ri = [round_inputs(wl, layer, r) for r in range(2)]
+    g = GpuRound(sh, ri[0]["x"], ri[0]["ba"], lp["conv_w"], lp["conv_hist"], lp["state"], lp["dt_bias"], lp["A"],
+                 rs[0]["slot_ids"], rs[0]["parents"], fused=True)
+    slots = rs[0]["slot_ids"][lanes]
+    local = np.arange(len(lanes), dtype=np.int32)
+    pool, hist = lp["state"][slots].astype(np.float64), lp["conv_hist"][slots].astype(np.float64)
+    for r in range(2):
+        if r:
+            g.x.copy_(dev(ri[r]["x"]))
+            g.ba.copy_(dev(ri[r]["ba"]))
+            g.parents.copy_(dev(rs[r]["parents"]))
+        g.verify()
+        torch.cuda.synchronize()
+        assert int(g.status.item()) == 0
+        ref = oracle_round(sh, ri[r]["x"][lanes], ri[r]["ba"][lanes], lp["conv_w"], hist, pool, lp["dt_bias"],
+                           lp["A"], local, rs[r]["parents"][lanes])
+        errs = compare_verify(g, ref, lanes=lanes, ref_is_subset=True)
+        g.commit(rs[r]["accept_node"])
+        st, pool, hist = oracle_commit(sh, ref, local, rs[r]["parents"][lanes], rs[r]["accept_node"][lanes], pool,
+                                       hist)
+        assert st == 0
+        log(f"[parity] stress round {r}: {errs}")
+    torch.cuda.synchronize()
+    assert int(g.status.item()) == 0
+    e_state = err_metric(g.state.cpu().numpy()[slots], pool)
+    assert e_state <= REC_TOL, f"committed state error {e_state}"
+    assert np.array_equal(g.conv_hist.cpu().numpy()[slots], hist.astype(np.float32))
