@@ -74,9 +74,11 @@ __device__ inline v4f load4(__amdgpu_buffer_rsrc_t r, int byte_offset) {
     return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
 }
 
-template <int DK, int DV, int NP, bool FUSED>
+// WIDE: a workgroup covers all d_v columns of its value head (eight 16-column tiles, one per
+// wave, each over the whole of d_k) instead of 64 of them; see launch_np.
+template <int DK, int DV, int NP, bool FUSED, bool WIDE = false>
 struct VerifyLayout {
-    static constexpr int JB = DV < 64 ? DV : 64;  // value columns per workgroup
+    static constexpr int JB = WIDE ? DV : (DV < 64 ? DV : 64);  // value columns per workgroup
     static constexpr int NB = DV / JB;            // column blocks per head
     static constexpr int CT = JB / 16;            // 16-column tiles of the block
     static constexpr int NT = NP / 16;            // 16-row tiles of K (and of Q)
@@ -112,7 +114,10 @@ struct VerifyLayout {
     static constexpr int UNIT = RT * 256;
     static constexpr int OFF_UNIT = GPART;
     static constexpr int STAGE = FUSED ? (NP + 3) * SXS : 0;
-    static constexpr int SCR = STAGE > GPART + 8 * UNIT ? STAGE : GPART + 8 * UNIT;
+    // WIDE: every wave's state-product tiles are complete and stay in its registers
+    static constexpr int PARTS = GPART + (WIDE ? 0 : kWaves * UNIT);
+    static constexpr int SCR1 = STAGE > PARTS ? STAGE : PARTS;
+    static constexpr int SCR = SCR1 > 2 * NP * SV ? SCR1 : 2 * NP * SV;  // also the epilogue's row staging
     static constexpr int LDS_FLOATS = OFF_SCR + SCR;
 };
 
@@ -143,9 +148,10 @@ __device__ inline void hist_columns(const v4f raw[3], v4f hc[3]) {
 
 // RAGGED: the caller passed per-lane node counts (without them every lane has N nodes and
 // the count costs nothing)
-template <int DK, int DV, int NP, bool FUSED, bool RAGGED>
+template <int DK, int DV, int NP, bool FUSED, bool RAGGED, bool WIDE>
 __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
-    using Ly = VerifyLayout<DK, DV, NP, FUSED>;
+    using Ly = VerifyLayout<DK, DV, NP, FUSED, WIDE>;
+    static_assert(!WIDE || Ly::KP == 1, "wide: one wave per column tile");
     constexpr int JB = Ly::JB, NB = Ly::NB, CT = Ly::CT, NT = Ly::NT, RT = Ly::RT, KC = Ly::KC, LCG = Ly::LCG, KP = Ly::KP, LCQ = Ly::LCQ;
     constexpr int R = Ly::R, G = Ly::G, Q4 = Ly::Q4, SX = Ly::SX, SV = Ly::SV, SG = Ly::SG, SXS = Ly::SXS;
     static_assert(kThreads % G == 0 && kThreads % Q4 == 0 && 64 % G == 0, "channel groups must tile a wave");
@@ -336,13 +342,11 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     if constexpr (FUSED) {
 #pragma unroll
         for (int u = 0; u < QPT; ++u) {
-            const int f = tid + kThreads * u;
             const int i = (tid / G) * QPT + u;
             if (i < NP) *reinterpret_cast<v4f *>(stg + i * SXS + 4 * gq) = qreg[u];
         }
 #pragma unroll
         for (int u = 0; u < VPT; ++u) {
-            const int f = tid + kThreads * u;
             const int i = (tid / Q4) * VPT + u;
             if (i < NP) *reinterpret_cast<v4f *>(stg + i * SXS + 2 * DK + 4 * gv) = vreg[u];
         }
@@ -465,7 +469,8 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     lds_barrier();
 
     // ---- [K; Q] x S0 for this wave's unit (column tile pct, chunks q = pkp + KP*lc) into
-    //      LDS partial tiles in accumulator order
+    //      LDS partial tiles in accumulator order (WIDE: the complete tiles stay in sp)
+    v4f sp[Ly::RT];
     auto state_product = [&]() {
         v4f acc[RT];
 #pragma unroll
@@ -481,9 +486,14 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
                                     acc[rt]);
             }
         }
-        float *pp = scr + Ly::OFF_UNIT + wv_u * Ly::UNIT + lane * 4;
+        if constexpr (WIDE) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) *reinterpret_cast<v4f *>(pp + rt * 256) = acc[rt];
+            for (int rt = 0; rt < RT; ++rt) sp[rt] = acc[rt];
+        } else {
+            float *pp = scr + Ly::OFF_UNIT + wv_u * Ly::UNIT + lane * 4;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) *reinterpret_cast<v4f *>(pp + rt * 256) = acc[rt];
+        }
     };
 
     // ---- waves 0..3: Gram products of the raw rows, split by 16-wide chunks of d_k:
@@ -552,8 +562,16 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     // ---- waves 4..7: T = (I + Lm)^-1 by forward substitution.  Waves nt < CT: the KS and
     //      QS tiles of value columns j0 + 16nt.. from the unit partials, and rhs.
     v4f rhs[NT], qs[NT];
+    // rhs from this wave's KS tile (v, beta and the decay-norm scales are in LDS)
+    auto form_rhs = [&](int mt, int jj, const v4f &ks) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = 16 * mt + 4 * g4 + v;
+            rhs[mt][v] = s_beta[i] * (Vl[i * SV + jj] - s_gk[i] * ks[v]);
+        }
+    };
     if (wv_u < 4) {
-        if (wave < CT) {
+        if (!WIDE && wave < CT) {
             const int nt = wave, jj = 16 * nt + l16;
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) {
@@ -565,11 +583,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
                     ks += *reinterpret_cast<const v4f *>(pp + mt * 256);
                     qs[mt] += *reinterpret_cast<const v4f *>(pp + (NT + mt) * 256);
                 }
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int i = 16 * mt + 4 * g4 + v;
-                    rhs[mt][v] = s_beta[i] * (Vl[i * SV + jj] - s_gk[i] * ks[v]);
-                }
+                form_rhs(mt, jj, ks);
             }
         }
     } else if constexpr (NP == 16) {
@@ -612,11 +626,18 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     //      replay log), O = diag(gq) QS + Cq D (output).
     //      Waves 4..7, once per lane and value head: the replay-log header (g, k^) of every
     //      node (its stores go out beside the epilogue's).
-    static_assert(CT <= 4, "epilogue waves");
+    static_assert(WIDE || CT <= 4, "epilogue waves");
     static_assert(2 * NP * SV <= Ly::SCR, "output tiles fit the scratch");
     float *Ot = scr, *Dt = scr + NP * SV;  // output and delta rows of the block, [NP][SV] each
     if (wave < CT) {
         const int nt = wave, jj = 16 * nt + l16;
+        if constexpr (WIDE) {  // KS and QS of this wave's column tile are its own tiles
+#pragma unroll
+            for (int mt = 0; mt < NT; ++mt) {
+                form_rhs(mt, jj, sp[mt]);
+                qs[mt] = sp[NT + mt];
+            }
+        }
         v4f dl[NT];
 #pragma unroll
         for (int mt = 0; mt < NT; ++mt) {
@@ -673,9 +694,9 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     }
 }
 
-template <int DK, int DV, int NP, bool RAGGED>
+template <int DK, int DV, int NP, bool RAGGED, bool WIDE>
 __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs args) {
-    verify_body<DK, DV, NP, false, RAGGED>(args);
+    verify_body<DK, DV, NP, false, RAGGED, WIDE>(args);
 }
 
 // Commit windows of the fused route, written by workgroups of their own that run beside
@@ -750,45 +771,56 @@ __device__ __forceinline__ void window_body(const VerifyArgs &args, int b) {
     }
 }
 
-template <int DK, int DV, int NP, bool RAGGED>
+template <int DK, int DV, int NP, bool RAGGED, bool WIDE>
 __global__ __launch_bounds__(kThreads) void conv_tree_verify_kernel(const VerifyArgs args) {
-    constexpr int NB = VerifyLayout<DK, DV, NP, true>::NB;
-    static_assert(kThreads * 12 <= VerifyLayout<DK, DV, NP, true>::LDS_FLOATS, "window chunks fit the LDS");
+    constexpr int NB = VerifyLayout<DK, DV, NP, true, WIDE>::NB;
+    static_assert(kThreads * 12 <= VerifyLayout<DK, DV, NP, true, WIDE>::LDS_FLOATS, "window chunks fit the LDS");
     const int n_verify = NB * args.d.Hv * args.d.C;
     if ((int)blockIdx.x < n_verify)
-        verify_body<DK, DV, NP, true, RAGGED>(args);
+        verify_body<DK, DV, NP, true, RAGGED, WIDE>(args);
     else
         window_body<NP, RAGGED>(args, blockIdx.x - n_verify);
 }
 
-template <int DK, int DV, int NP, bool FUSED, bool RAGGED>
+template <int DK, int DV, int NP, bool FUSED, bool RAGGED, bool WIDE>
 hipError_t launch(const VerifyArgs &a, hipStream_t stream) {
-    using Ly = VerifyLayout<DK, DV, NP, FUSED>;
+    using Ly = VerifyLayout<DK, DV, NP, FUSED, WIDE>;
     const size_t lds = sizeof(float) * Ly::LDS_FLOATS;
     // the LDS limit is a property of the kernel, set once (also keeps stream capture clean)
-    const void *kernel = FUSED ? reinterpret_cast<const void *>(&conv_tree_verify_kernel<DK, DV, NP, RAGGED>)
-                               : reinterpret_cast<const void *>(&tree_verify_kernel<DK, DV, NP, RAGGED>);
+    const void *kernel = FUSED ? reinterpret_cast<const void *>(&conv_tree_verify_kernel<DK, DV, NP, RAGGED, WIDE>)
+                               : reinterpret_cast<const void *>(&tree_verify_kernel<DK, DV, NP, RAGGED, WIDE>);
     static const hipError_t attr = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
     // fused: the window workgroups follow the verify workgroups
     const int grid = Ly::NB * a.d.Hv * a.d.C +
                      (FUSED ? a.d.C * ((a.d.Ch + 4 * (kThreads / NP) - 1) / (4 * (kThreads / NP))) : 0);
     if constexpr (FUSED)
-        hipLaunchKernelGGL((conv_tree_verify_kernel<DK, DV, NP, RAGGED>), dim3(grid), dim3(kThreads), lds, stream, a);
+        hipLaunchKernelGGL((conv_tree_verify_kernel<DK, DV, NP, RAGGED, WIDE>), dim3(grid), dim3(kThreads), lds, stream, a);
     else
-        hipLaunchKernelGGL((tree_verify_kernel<DK, DV, NP, RAGGED>), dim3(grid), dim3(kThreads), lds, stream, a);
+        hipLaunchKernelGGL((tree_verify_kernel<DK, DV, NP, RAGGED, WIDE>), dim3(grid), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
 }
 
-template <int DK, int DV>
-hipError_t launch_np(const VerifyArgs &a, hipStream_t stream) {
+template <int DK, int DV, bool WIDE>
+hipError_t launch_wide(const VerifyArgs &a, hipStream_t stream) {
     const bool fused = a.x != nullptr;
     const bool ragged = a.lane_nodes != nullptr;
     if (a.d.N <= 16)
-        return fused ? (ragged ? launch<DK, DV, 16, true, true>(a, stream) : launch<DK, DV, 16, true, false>(a, stream))
-                     : (ragged ? launch<DK, DV, 16, false, true>(a, stream) : launch<DK, DV, 16, false, false>(a, stream));
-    return fused ? (ragged ? launch<DK, DV, 32, true, true>(a, stream) : launch<DK, DV, 32, true, false>(a, stream))
-                 : (ragged ? launch<DK, DV, 32, false, true>(a, stream) : launch<DK, DV, 32, false, false>(a, stream));
+        return fused ? (ragged ? launch<DK, DV, 16, true, true, WIDE>(a, stream) : launch<DK, DV, 16, true, false, WIDE>(a, stream))
+                     : (ragged ? launch<DK, DV, 16, false, true, WIDE>(a, stream) : launch<DK, DV, 16, false, false, WIDE>(a, stream));
+    return fused ? (ragged ? launch<DK, DV, 32, true, true, WIDE>(a, stream) : launch<DK, DV, 32, true, false, WIDE>(a, stream))
+                 : (ragged ? launch<DK, DV, 32, false, true, WIDE>(a, stream) : launch<DK, DV, 32, false, false, WIDE>(a, stream));
+}
+
+// The q/k conv, norms, Gram products and tree algebra of a (lane, value head) are repeated by
+// each of its column blocks.  While the grid fits the chip in one pass (C * H_v < 256) the
+// 64-column blocks give the parallelism; beyond it the launch is bound by arithmetic and one
+// workgroup per (lane, value head) over all 128 columns does a third less of it per byte.
+template <int DK, int DV>
+hipError_t launch_np(const VerifyArgs &a, hipStream_t stream) {
+    if constexpr (DV == 128)
+        if (a.d.C * a.d.Hv >= 256) return launch_wide<DK, DV, true>(a, stream);
+    return launch_wide<DK, DV, false>(a, stream);
 }
 
 }  // namespace
