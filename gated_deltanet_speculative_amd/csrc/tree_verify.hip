@@ -50,7 +50,8 @@
 // ancestors, then the slot's history columns), writing the results straight into the
 // product operands; the conv output never goes to memory.  The commit windows are
 // written once, by copy-only workgroups appended to the same launch (one per lane and
-// block of channels), which run beside the verify workgroups.
+// block of channels), which run beside the verify workgroups; in the wide variant with two
+// or more verify workgroups per CU, by the verify workgroups from their staged rows.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -65,6 +66,8 @@ constexpr int kWaves = kThreads / 64;
 // makes no memory access.
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kOutOfRange = 0x40000000;  // past every buffer range used here (at most 1 GiB)
+typedef int v4i __attribute__((ext_vector_type(4)));
+constexpr int kNonTemporal = 2;  // cache-policy operand of the buffer stores: nt
 
 __device__ inline float load1(__amdgpu_buffer_rsrc_t r, int byte_offset) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_offset, 0, 0));
@@ -73,6 +76,12 @@ __device__ inline float load1(__amdgpu_buffer_rsrc_t r, int byte_offset) {
 __device__ inline v4f load4(__amdgpu_buffer_rsrc_t r, int byte_offset) {
     return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, 0));
 }
+
+// Wide variant, fused route: the commit windows are written by the verify workgroups
+// themselves once the grid spans more than one workgroup per CU (two or more per CU on
+// 256 CUs); below that, copy-only workgroups in the free slots beside them write the windows
+// sooner.
+__host__ __device__ inline bool windows_in_verify(const Dims &d) { return d.C * d.Hv >= 512; }
 
 // WIDE: a workgroup covers all d_v columns of its value head (eight 16-column tiles, one per
 // wave, each over the whole of d_k) instead of 64 of them; see launch_np.
@@ -106,19 +115,22 @@ struct VerifyLayout {
     static constexpr int OFF_TAP = OFF_T + NP * SG;                   // fused: taps [NG][4] of v4f
     static constexpr int OFF_SCR = OFF_TAP + (FUSED ? NG * 16 : 0);
     static constexpr int OFF_STG = OFF_SCR;  // fused: staged rows, dead once the conv is done
-    // scratch, reused: staged rows (until the conv), Gram partials (until the
+    // scratch, reused: staged rows (until the conv; fused and wide: until the commit
+    // windows are written, after the Gram products), Gram partials (until the
     // coefficients), partial state products
+    static constexpr int STAGE = FUSED ? (NP + 3) * SXS : 0;
     static constexpr int GRAM_TILES = RT * NT;
     static constexpr int GPART = GW * GRAM_TILES * 256;
+    static constexpr int OFF_GRAM = FUSED && WIDE ? STAGE : 0;
     // state-product partials: unit u = wave u covers column tile u % CT and k part u / CT
     static constexpr int UNIT = RT * 256;
-    static constexpr int OFF_UNIT = GPART;
-    static constexpr int STAGE = FUSED ? (NP + 3) * SXS : 0;
+    static constexpr int OFF_UNIT = OFF_GRAM + GPART;
     // WIDE: every wave's state-product tiles are complete and stay in its registers
-    static constexpr int PARTS = GPART + (WIDE ? 0 : kWaves * UNIT);
+    static constexpr int PARTS = OFF_GRAM + GPART + (WIDE ? 0 : kWaves * UNIT);
     static constexpr int SCR1 = STAGE > PARTS ? STAGE : PARTS;
     static constexpr int SCR = SCR1 > 2 * NP * SV ? SCR1 : 2 * NP * SV;  // also the epilogue's row staging
     static constexpr int LDS_FLOATS = OFF_SCR + SCR;
+    static_assert(4 * LDS_FLOATS <= 160 * 1024 - 2048, "LDS of one workgroup (with the static arrays)");
 };
 
 // Tree conv + SiLU of 4 channels at one node from its sources, oldest first (x3 = the
@@ -521,7 +533,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
                     for (int at = 0; at < NT; ++at) acc[rt][at] = mfma4(av[rt], av[at], acc[rt][at]);
             }
         }
-        float *gp = scr + wave * Ly::GRAM_TILES * 256;
+        float *gp = scr + Ly::OFF_GRAM + wave * Ly::GRAM_TILES * 256;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -533,6 +545,48 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
         }
     }
     state_product();
+
+    // ---- fused, wide: waves 4..7, which have no Gram products, write the commit windows of
+    //      the workgroup's channels from the staged rows.  The window of node i and channel e
+    //      is (oldest first) its second and first nearest sources and its own token, 3 floats;
+    //      4 channels take 12 consecutive floats, stored as three 16-byte chunks (flat float f
+    //      of a group = source f % 3 of channel f / 3).  Lane l takes chunk l + 64m of a node's
+    //      row of chunks, so a store instruction writes consecutive chunks.  The q/k slab's
+    //      channel groups are split over the workgroups that share it (the value heads of the
+    //      q/k head), the value block is this workgroup's own.  No global load follows these
+    //      stores.
+    if constexpr (FUSED && WIDE) {
+        if (wv_u >= 4 && windows_in_verify(d)) {
+            const int nshare = Hv / d.Hk;
+            const int gq0 = (ws * G) / nshare, nq = ((ws + 1) * G) / nshare - gq0;
+            const int cpn = 3 * (nq + Q4);  // chunks of one node
+            const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+                args.commit_win + (int64_t)c * N * d.Ch * 3, 0, nvc * d.Ch * 12, kRsrcWord3);
+            for (int m = 0; 64 * m < cpn; ++m) {
+                const int r = lane + 64 * m, gg = r / 3, p = r - 3 * gg;
+                const bool slab = gg < nq;
+                const int g = slab ? gq0 + gg : min(gg - nq, Q4 - 1);
+                const int col = slab ? 4 * g : 2 * DK + 4 * g;
+                const int ch = slab ? (g < DK / 4 ? kh * DK + 4 * g : d.Hk * DK + kh * DK + 4 * (g - DK / 4))
+                                    : 2 * d.Hk * DK + h * DV + j0 + 4 * g;
+                const int gofs = r < cpn ? ch * 12 + 16 * p : kOutOfRange;
+                for (int i = wv_u - 4; i < nvc; i += 4) {
+                    const int sr = s_src[i];
+                    const int rb[3] = {((sr >> 8) & 255) * SXS + col, ((sr >> 16) & 255) * SXS + col, i * SXS + col};
+                    float w[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int f = 4 * p + e, src = f % 3;  // p + e = f mod 3
+                        w[e] = stg[(src == 0 ? rb[0] : src == 1 ? rb[1] : rb[2]) + f / 3];
+                    }
+                    const v4f chunk = {w[0], w[1], w[2], w[3]};
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, chunk), wr,
+                                                           gofs < kOutOfRange ? i * d.Ch * 12 + gofs : kOutOfRange, 0,
+                                                           kNonTemporal);
+                }
+            }
+        }
+    }
     lds_barrier();
 
     // ---- decayed, ancestor-masked, norm-scaled coefficients and per-node scales
@@ -541,8 +595,9 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
         const int i = p / NP, a = p - i * NP;
         const bool on = (s_anc[i] >> a) & 1u;
         const int ln = ((i & 15) >> 2) * 16 + (a & 15), v = i & 3;
-        const float *gk = scr + ((((i >> 4) * NT + (a >> 4)) * 64 + ln) * 4 + v);         // k_i . k_a
-        const float *gqk = scr + (((((NT + (i >> 4)) * NT) + (a >> 4)) * 64 + ln) * 4 + v);  // q_i . k_a
+        const float *gk = scr + Ly::OFF_GRAM + ((((i >> 4) * NT + (a >> 4)) * 64 + ln) * 4 + v);  // k_i . k_a
+        const float *gqk =
+            scr + Ly::OFF_GRAM + (((((NT + (i >> 4)) * NT) + (a >> 4)) * 64 + ln) * 4 + v);  // q_i . k_a
         float skk = 0.f, sqk = 0.f;
 #pragma unroll
         for (int w = 0; w < Ly::GW; ++w) {
@@ -778,7 +833,7 @@ __global__ __launch_bounds__(kThreads) void conv_tree_verify_kernel(const Verify
     const int n_verify = NB * args.d.Hv * args.d.C;
     if ((int)blockIdx.x < n_verify)
         verify_body<DK, DV, NP, true, RAGGED, WIDE>(args);
-    else
+    else  // present only when the verify workgroups do not write the windows
         window_body<NP, RAGGED>(args, blockIdx.x - n_verify);
 }
 
@@ -792,8 +847,9 @@ hipError_t launch(const VerifyArgs &a, hipStream_t stream) {
     static const hipError_t attr = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
     // fused: the window workgroups follow the verify workgroups
+    const bool window_wgs = FUSED && !(WIDE && windows_in_verify(a.d));
     const int grid = Ly::NB * a.d.Hv * a.d.C +
-                     (FUSED ? a.d.C * ((a.d.Ch + 4 * (kThreads / NP) - 1) / (4 * (kThreads / NP))) : 0);
+                     (window_wgs ? a.d.C * ((a.d.Ch + 4 * (kThreads / NP) - 1) / (4 * (kThreads / NP))) : 0);
     if constexpr (FUSED)
         hipLaunchKernelGGL((conv_tree_verify_kernel<DK, DV, NP, RAGGED, WIDE>), dim3(grid), dim3(kThreads), lds, stream, a);
     else

@@ -92,6 +92,10 @@ SWEEP = [
     (8, 16, 9, 16, 32, 128, 128, True),
     (16, 9, 16, 4, 16, 64, 128, True),
     (4, 25, 5, 8, 64, 32, 128, True),
+    # C * H_v >= 512 with d_v = 128: those workgroups also write the commit windows
+    (16, 16, 17, 16, 32, 128, 128, True),
+    (8, 27, 9, 2, 64, 64, 128, True),
+    (8, 25, 9, 8, 64, 32, 128, False),
 ]
 
 

@@ -21,6 +21,11 @@ CASES = [
     ("headline-heads", 4, 16, 8, 16, 32, 128, 128, True, [16, 5, 0, 11]),
     ("np32", 3, 32, 5, 2, 4, 64, 32, True, [32, 17, 1]),
     ("chains-d16", 5, 8, 7, 2, 2, 16, 16, False, [8, 3, 0, 1, 6]),
+    # C * H_v >= 256 with d_v = 128: the variant whose verify workgroups write the windows
+    ("wide", 8, 16, 9, 16, 32, 128, 128, True, [16, 5, 0, 11, 1, 16, 9, 3]),
+    ("wide-np32", 4, 32, 5, 4, 64, 64, 128, True, [32, 17, 1, 25]),
+    ("wide-windows", 16, 16, 17, 16, 32, 128, 128, True, [16, 5, 0, 11, 1, 16, 9, 3, 2, 14, 16, 7, 8, 0, 12, 6]),
+    ("wide-windows-np32", 8, 32, 9, 4, 64, 64, 128, True, [32, 17, 1, 25, 0, 32, 9, 30]),
 ]
 
 
