@@ -132,11 +132,15 @@ def test_many_lanes_small_heads(route):
 
 
 @pytest.mark.parametrize("route", ROUTES)
-def test_padding_and_invalid_lanes_write_nothing(route):
-    C, N, P, Hk, Hv, d = 6, 5, 8, 1, 2, 32
-    sh = _shape(C, N, P, Hk, Hv, d, d)
-    log(f"[lanes] padding / invalid parent / duplicate slot / slot out of range, route={route}")
-    case = synth_case(C, N, P, Hk, Hv, d, d, seed=11, slots=[2, -1, 3, 5, 5, 8])
+@pytest.mark.parametrize("C,N,P,Hk,Hv,dk,dv", [
+    (6, 5, 8, 1, 2, 32, 32),
+    (16, 5, 20, 4, 32, 64, 128),  # C * H_v = 512: the verify workgroups write the windows
+])
+def test_padding_and_invalid_lanes_write_nothing(C, N, P, Hk, Hv, dk, dv, route):
+    sh = _shape(C, N, P, Hk, Hv, dk, dv)
+    log(f"[lanes] padding / invalid parent / duplicate slot / slot out of range, C={C} H_v={Hv} route={route}")
+    slots = [2, -1, 3, 5, 5, P] + list(range(6, C))  # lanes 1..5 padding or invalid
+    case = synth_case(C, N, P, Hk, Hv, dk, dv, seed=11, slots=slots)
     case["parents"][2, 3] = 3  # not before its child
     g, ref, _ = _run_case(sh, case, route=route)
     want = gdn.STATUS_PARENT | gdn.STATUS_SLOT_DUP | gdn.STATUS_SLOT_RANGE
@@ -144,11 +148,11 @@ def test_padding_and_invalid_lanes_write_nothing(route):
     assert g.guards_intact()
     for buf in (g.conv_out, g.commit_win, g.out, g.replay_log):
         a = buf.np()
-        assert (a[1:] == np.float32(SENTINEL)).all(), "an invalid or padding lane was written"
-    compare_verify(g, ref, lanes=[0])
-    # the round's status makes the commit a no-op for every lane, including the valid one
+        assert (a[1:6] == np.float32(SENTINEL)).all(), "an invalid or padding lane was written"
+    compare_verify(g, ref, lanes=[0] + list(range(6, C)))
+    # the round's status makes the commit a no-op for every lane, including the valid ones
     state0, hist0 = g.state.clone(), g.conv_hist.clone()
-    g.commit(np.array([4, 0, 0, 0, 0, 0], np.int32))
+    g.commit(np.array([4] + [0] * (C - 1), np.int32))
     torch.cuda.synchronize()
     assert torch.equal(g.state, state0) and torch.equal(g.conv_hist, hist0)
 
