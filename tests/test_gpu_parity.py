@@ -96,6 +96,8 @@ SWEEP = [
     (16, 16, 17, 16, 32, 128, 128, True),
     (8, 27, 9, 2, 64, 64, 128, True),
     (8, 25, 9, 8, 64, 32, 128, False),
+    (16, 8, 17, 32, 32, 128, 128, False),  # H_k = H_v: each workgroup writes its whole q/k slab
+    (32, 4, 33, 4, 16, 16, 128, True),
 ]
 
 
