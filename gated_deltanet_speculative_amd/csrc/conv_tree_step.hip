@@ -33,6 +33,7 @@ __global__ __launch_bounds__(kThreads) void conv_tree_step_kernel(
     float *__restrict__ conv_out, float *__restrict__ commit_win, int32_t *__restrict__ status) {
     extern __shared__ v4f rows4[];  // [3 + N][kGroups]: history columns 0..2, then token rows
     __shared__ int s_wbits[kThreads / 64];
+    __shared__ v4f s_chunks[kThreads * 3];  // window chunks, transposed per wave
 
     const int c = blockIdx.y, tid = threadIdx.x;
     const int N = d.N, Ch = d.Ch;
@@ -102,7 +103,13 @@ __global__ __launch_bounds__(kThreads) void conv_tree_step_kernel(
     //      node i, oldest first: LDS row r < 3 is history column r, row 3 + a is the token
     //      of node a; the newest source is node i itself, then its ancestors (found with
     //      lane shuffles over the parents held by lanes 0..N-1), then history columns 2, 1, 0.
+    //      A node's windows in the block are 3 * kGroups consecutive 16-byte chunks, held by
+    //      one row of 16 lanes; they go through a wave-private transpose in LDS so that each
+    //      store instruction writes consecutive chunks from consecutive lanes (whole lines)
+    //      instead of 16-byte pieces at a 48-byte lane stride.
     const int ch = ch0 + 4 * q;
+    const int l16 = tid % kGroups;  // == q
+    v4f *chunks = s_chunks + 3 * (tid - l16);  // this row's 3 * kGroups chunks
 #pragma unroll
     for (int u = 0; u < XPT; ++u) {
         const int i = tid / kGroups + kRowsPerPass * u;
@@ -112,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void conv_tree_step_kernel(
         const int n2 = n1 >= 0 ? n2s : -1;
         const int n3s = __shfl(par, n2 >= 0 ? n2 : 0);
         const int n3 = n2 >= 0 ? n3s : -1;
-        if (i >= nv || q >= ng) continue;  // absent node (nv <= N: a bad count returned above)
+        if (i >= nv) continue;  // absent node (nv <= N: a bad count returned above); uniform per row
         const int cnt = 1 + (n1 >= 0) + (n2 >= 0) + (n3 >= 0);
         const int nn[4] = {n0, n1, n2, n3};
         int src[4];
@@ -129,13 +136,25 @@ __global__ __launch_bounds__(kThreads) void conv_tree_step_kernel(
         zc = fmaf(t0.z, wc.x, zc); zc = fmaf(t1.z, wc.y, zc); zc = fmaf(t2.z, wc.z, zc); zc = fmaf(t3.z, wc.w, zc);
         zd = fmaf(t0.w, wd.x, zd); zd = fmaf(t1.w, wd.y, zd); zd = fmaf(t2.w, wd.z, zd); zd = fmaf(t3.w, wd.w, zd);
         const int64_t row = (int64_t)c * N + i;
-        *reinterpret_cast<v4f *>(conv_out + row * Ch + ch) = v4f{silu(za), silu(zb), silu(zc), silu(zd)};
+        if (q < ng) *reinterpret_cast<v4f *>(conv_out + row * Ch + ch) = v4f{silu(za), silu(zb), silu(zc), silu(zd)};
         // commit window = taps 1..3 of each channel, [ch][3] layout: 12 floats for 4 channels
-        v4f *wdst = reinterpret_cast<v4f *>(commit_win + (row * Ch + ch) * 3);
+        chunks[3 * l16] = v4f{t1.x, t2.x, t3.x, t1.y};
+        chunks[3 * l16 + 1] = v4f{t2.y, t3.y, t1.z, t2.z};
+        chunks[3 * l16 + 2] = v4f{t3.z, t1.w, t2.w, t3.w};
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // (non-temporal: the windows are read again only by the commit, after the round)
-        __builtin_nontemporal_store(v4f{t1.x, t2.x, t3.x, t1.y}, wdst);
-        __builtin_nontemporal_store(v4f{t2.y, t3.y, t1.z, t2.z}, wdst + 1);
-        __builtin_nontemporal_store(v4f{t3.z, t1.w, t2.w, t3.w}, wdst + 2);
+        v4f *wdst = reinterpret_cast<v4f *>(commit_win + (row * Ch + ch0) * 3);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int j = l16 + kGroups * k;  // chunk j holds part j % 3 of channel group j / 3
+            if (j < 3 * ng) __builtin_nontemporal_store(chunks[j], wdst + j);
+        }
+        // the row's chunks are read before the next pass overwrites them
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
