@@ -162,6 +162,66 @@ def cpu_baseline(wl, seconds, seed):
                        f"{t_used:.1f} s")
 
 
+def cpu_baseline_decode(wl, seconds, seed):
+    """The fp64 oracle's plain decode step (conv step, then the one-token recurrence) on one
+    layer instance of the workload, repeated on its in-place history and state until
+    `seconds` of CPU work."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import gdn_oracle as O
+    from workloads import layer_params, round_inputs, round_structure
+
+    C, Ch, Hv, dv = wl.n_seqs, wl.channels, wl.n_v_heads, wl.d_v
+    slots = round_structure(wl, 0, seed)["slot_ids"]
+    lp, ri = layer_params(wl, 0, seed), round_inputs(wl, 0, 0, seed)
+    ba = ri["ba"][:, 0]
+    hist, pool = lp["conv_hist"].astype(np.float64), lp["state"].astype(np.float64)
+    conv_out, out = np.zeros((C, 1, Ch)), np.zeros((C, Hv, dv))
+    done, t_used = 0, 0.0
+    with threadpool_limits(limits=1):
+        while t_used < seconds:
+            t0 = time.perf_counter()
+            O.conv_step(ri["x"][:, :1], lp["conv_w"], hist, slots, conv_out)
+            O.decode_step(conv_out[:, 0], ba[:, :Hv], ba[:, Hv:], lp["dt_bias"], lp["A"], pool, slots, wl.n_k_heads,
+                          out)
+            t_used += time.perf_counter() - t0
+            done += 1
+    return dict(value=C * done / t_used, unit="decode tokens/s", cores=1, kind="oracle",
+                sample=f"{done} single-layer decode steps (conv step + recurrence) of {wl.name}, fp64 numpy, "
+                       f"1 BLAS thread, {t_used:.1f} s")
+
+
+def cpu_baseline_prefill(wl, seconds, seed, tokens=32):
+    """The fp64 oracle's prompt path (conv step over the prompt, then the token-by-token
+    recurrence) on `tokens`-token prompts of the workload's lanes, until `seconds` of CPU
+    work (one layer instance, its history and state carried over from prompt to prompt):
+    the oracle's cost is linear in the prompt length, so a short prompt measures its rate."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import gdn_oracle as O
+    from workloads import layer_params, round_structure
+
+    C, Ch, Hv, dv = wl.n_seqs, wl.channels, wl.n_v_heads, wl.d_v
+    slots = round_structure(wl, 0, seed)["slot_ids"]
+    lp = layer_params(wl, 0, seed)
+    rng = np.random.default_rng([seed, 7])
+    x = rng.standard_normal((C, tokens, Ch)).astype(np.float32)
+    ba = rng.standard_normal((C, tokens, 2 * Hv)).astype(np.float32)
+    hist, pool = lp["conv_hist"].astype(np.float64), lp["state"].astype(np.float64)
+    conv_out, out = np.zeros((C, tokens, Ch)), np.zeros((C, tokens, Hv, dv))
+    done, t_used = 0, 0.0
+    with threadpool_limits(limits=1):
+        while t_used < seconds:
+            t0 = time.perf_counter()
+            O.conv_step(x, lp["conv_w"], hist, slots, conv_out)
+            O.prefill(conv_out, ba[..., :Hv], ba[..., Hv:], lp["dt_bias"], lp["A"], pool, slots, wl.n_k_heads, out)
+            t_used += time.perf_counter() - t0
+            done += 1
+    return dict(value=C * tokens * done / t_used, unit="prompt tokens/s", cores=1, kind="oracle",
+                sample=f"{done} single-layer {tokens}-token prompts of {wl.name} (conv step + recurrence), "
+                       f"fp64 numpy, 1 BLAS thread, {t_used:.1f} s")
+
+
 def decode_main(args):
     """The plain decode step at the workload's head shape: one token per lane, for every
     layer instance the conv step (history written in place) and the one-token recurrence
@@ -265,6 +325,8 @@ def decode_main(args):
         "kernel_us": {k: round(v, 3) for k, v in kern.items()},
         "kernel_gbs": {k: round(kb[k] / (kern[k] * 1e-6) / 1e9, 1) for k in kern},
         "roofline": roofline,
+        "cpu_baseline": (None if args.no_cpu_baseline or args.profile_only
+                         else cpu_baseline_decode(wl, args.cpu_seconds, args.seed)),
         "setup_s": round(t_gen, 1),
     }
     print(json.dumps(line), flush=True)
@@ -380,6 +442,8 @@ def prefill_main(args):
         "kernel_gbs": ({"conv_step": round(cost["conv_bytes"] / (kern["conv_step"] * 1e-6) / 1e9, 1),
                         "prefill": round(cost["bytes"] / (kern["prefill"] * 1e-6) / 1e9, 1)} if kern else {}),
         "roofline": roofline,
+        "cpu_baseline": (None if args.no_cpu_baseline or args.profile_only
+                         else cpu_baseline_prefill(wl, args.cpu_seconds, args.seed)),
         "setup_s": round(t_gen, 1),
     }
     print(json.dumps(line), flush=True)

@@ -83,3 +83,11 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stdout + r.stderr
+
+
+@pytest.mark.parametrize("fn,unit", [("cpu_baseline", "verify tokens/s"), ("cpu_baseline_decode", "decode tokens/s"),
+                                     ("cpu_baseline_prefill", "prompt tokens/s")])
+def test_cpu_baselines_report_their_sample(fn, unit):
+    r = getattr(bench, fn)(WORKLOADS["tiny-chain"], 0.05, 0)
+    assert r["unit"] == unit and r["kind"] == "oracle" and r["cores"] == 1
+    assert r["value"] > 0 and "fp64" in r["sample"]
