@@ -54,3 +54,47 @@ def test_leaf_prefix_acceptance_on_path():
     st = round_structure(wl, 1)
     depths = [len(path_to_root(st["parents"][c], int(e))) if e >= 0 else 0 for c, e in enumerate(st["accept_node"])]
     assert min(depths) >= 0 and max(depths) <= wl.n_nodes
+
+
+def test_edge_inputs_reach_their_extremes():
+    """The edge inputs do what they are for, checked on the oracle's float64 values: keys
+    within a few degrees of each other, decays of exactly exp(-480) and of 1 - 1e-12 or
+    closer, beta saturated, q|k channels scaled and nothing else touched."""
+    from oracle import gdn_oracle as O
+    from workloads import EDGE_KINDS, edge_case, synth_case
+
+    C, N, P, Hk, Hv, d = 2, 32, 3, 2, 4, 128
+    base = synth_case(C, N, P, Hk, Hv, d, d, seed=332, tree=False)
+
+    def run(kind):
+        case = edge_case(base, kind, Hk, d, seed=1)
+        with np.errstate(over="ignore"):
+            ref = O.verify_round(case["x"], case["ba"], case["conv_w"], case["conv_hist"], case["state"],
+                                 case["dt_bias"], case["A"], case["slot_ids"], case["parents"], Hk)
+        assert ref["status"] == 0
+        return case, ref
+
+    case, ref = run("parallel_keys")
+    k = ref["conv_out"][..., Hk * d:2 * Hk * d].reshape(C, N, Hk, d)
+    kn = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    cos = np.einsum("cihd,cjhd->chij", kn, kn)
+    assert cos.min() >= 0.95, f"keys not near-parallel: min cos {cos.min():.3f}"
+    assert (ref["replay_log"][..., 0] > 1 - 1e-9).all()
+    _, ref = run("decay_zero")
+    assert (ref["replay_log"][..., 0] < 1e-200).all()
+    _, ref = run("decay_one")
+    assert (ref["replay_log"][..., 0] > 1 - 1e-9).all()
+    case, _ = run("beta_zero")
+    assert (case["ba"][..., :Hv] == -30).all() and np.array_equal(case["ba"][..., Hv:], base["ba"][..., Hv:])
+    case, _ = run("gates_mixed")
+    b = case["ba"][..., :Hv]
+    assert (b == 30).any() and (b == -30).any() and (np.abs(b) < 30).any()
+    assert (case["A"] <= -1).all() and (case["A"] >= -np.exp(3.0) - 1e-3).all()
+    for kind, s in (("qk_small", 1e-3), ("qk_large", 1e3)):
+        case, _ = run(kind)
+        qk = 2 * Hk * d
+        assert np.allclose(case["x"][..., :qk], base["x"][..., :qk] * np.float32(s), rtol=1e-6)
+        assert np.array_equal(case["x"][..., qk:], base["x"][..., qk:])
+        assert np.allclose(case["conv_hist"][:, :qk], base["conv_hist"][:, :qk] * np.float32(s), rtol=1e-6)
+    assert set(EDGE_KINDS) >= {"beta_one", "beta_zero", "decay_zero", "decay_one", "gates_mixed", "parallel_keys",
+                               "qk_small", "qk_large"}

@@ -6,6 +6,7 @@ HIP path and the CPU oracle can consume the same arrays without sharing code.
 """
 
 from .gen import (  # noqa: F401
+    EDGE_KINDS,
     WORKLOADS,
     Workload,
     layer_params,
@@ -13,4 +14,5 @@ from .gen import (  # noqa: F401
     round_structure,
     path_to_root,
     synth_case,
+    edge_case,
 )

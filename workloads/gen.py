@@ -192,3 +192,77 @@ def synth_case(C: int, N: int, P: int, Hk: int, Hv: int, dk: int, dv: int, seed:
     out["x"] = _normal(rng, 1.0, (C, N, ch))
     out["ba"] = _normal(rng, 1.0, (C, N, 2 * Hv))
     return out
+
+
+# Inputs at the extremes the gate formula and the q/k normalisation reach.  The gates are
+# beta = sigmoid(b) and g = exp(softplus(a + dt_bias) * A) ("qwen35: DSpark speculative
+# decoding", raw-gate commit message); real layers carry A = -exp(A_log) over a wide range.
+EDGE_KINDS = (
+    "beta_one",       # b = +30: beta -> 1 (the write replaces what the state held along k)
+    "beta_zero",      # b = -30: beta -> 0 (pure decay)
+    "decay_zero",     # a + dt_bias = +30 with A = -16: g = exp(-480), zero in float32
+    "decay_one",      # a + dt_bias = -30: g -> 1
+    "gates_mixed",    # per token and head one of the four above or the normal draw; A = -exp(U(0, 3))
+    "parallel_keys",  # beta -> 1, g -> 1, and k rows of every token within a few degrees of each other
+    "qk_small",       # the q|k channels of tokens and history scaled by 1e-3
+    "qk_large",       # ... and by 1e3
+)
+
+
+def edge_case(case: dict, kind: str, n_k_heads: int, d_k: int, seed: int = 0) -> dict:
+    """A copy of a `synth_case`-style dict with its inputs pushed to one extreme (EDGE_KINDS).
+
+    Touches `ba` (beta logits in the first H_v columns of a token's row, alpha logits in the
+    next H_v), `A`, and the q|k channels (the first 2 * n_k_heads * d_k) of `x`, `conv_hist`
+    and, when present, `qkv` (a chain's conv output rows).  Draw order for the kinds that
+    draw: the beta picks, the alpha picks, A (gates_mixed); the shared key direction, then
+    the per-row perturbations of x, conv_hist and qkv in that order (parallel_keys).
+    """
+    if kind not in EDGE_KINDS:
+        raise ValueError(f"unknown edge kind {kind!r}")
+    out = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in case.items()}
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 2000, EDGE_KINDS.index(kind)])))
+    Hv = out["dt_bias"].shape[0]
+    b, a = out["ba"][..., :Hv], out["ba"][..., Hv:]  # views: writes land in out["ba"]
+    dt = out["dt_bias"].astype(np.float32)
+    a_hi, a_lo = np.float32(30.0) - dt, np.float32(-30.0) - dt  # a + dt_bias = +30 / -30
+    qk = 2 * n_k_heads * d_k
+    slabs = [k for k in ("x", "conv_hist", "qkv") if k in out]
+    if kind == "beta_one":
+        b[...] = 30.0
+    elif kind == "beta_zero":
+        b[...] = -30.0
+    elif kind == "decay_zero":
+        a[...] = np.broadcast_to(a_hi, a.shape)
+        out["A"][...] = -16.0
+    elif kind == "decay_one":
+        a[...] = np.broadcast_to(a_lo, a.shape)
+    elif kind == "gates_mixed":
+        pb = rng.integers(0, 3, size=b.shape)
+        b[...] = np.where(pb == 0, 30.0, np.where(pb == 1, -30.0, b))
+        pa = rng.integers(0, 3, size=a.shape)
+        a[...] = np.where(pa == 0, np.broadcast_to(a_hi, a.shape), np.where(pa == 1, np.broadcast_to(a_lo, a.shape), a))
+        out["A"][...] = (-np.exp(rng.uniform(0.0, 3.0, Hv))).astype(np.float32)
+    elif kind == "parallel_keys":
+        b[...] = 30.0
+        a[...] = np.broadcast_to(a_lo, a.shape)
+        base = rng.standard_normal(n_k_heads * d_k)  # one direction per key channel
+        for k in slabs:
+            arr = out[k]
+            kslab = (slice(None),) * (arr.ndim - 1) + (slice(n_k_heads * d_k, qk),)
+            if k == "conv_hist":  # [P][Ch][3]: the key channels of every history column
+                kslab = (slice(None), slice(n_k_heads * d_k, qk), slice(None))
+                shape = arr[kslab].shape
+                arr[kslab] = (base[None, :, None] + 0.1 * rng.standard_normal(shape)).astype(np.float32)
+            else:
+                shape = arr[kslab].shape
+                arr[kslab] = (base + 0.1 * rng.standard_normal(shape)).astype(np.float32)
+    else:
+        s = np.float32(1e-3 if kind == "qk_small" else 1e3)
+        for k in slabs:
+            arr = out[k]
+            if k == "conv_hist":
+                arr[:, :qk, :] *= s
+            else:
+                arr[..., :qk] *= s
+    return out
