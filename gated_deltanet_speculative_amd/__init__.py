@@ -18,7 +18,9 @@ directly:
 and a prompt fills a slot with conv_step over its tokens followed by
 
     prefill         -> out; the recurrence over the prompt, each slot's state in place
-                       (prefill_workspace_size: the scratch bytes it needs)
+                       (prefill_workspace_size: the scratch bytes it needs;
+                       prefill_noalloc: the same with the library's static scratch,
+                       for callers that cannot allocate)
 
 The library is loaded on first use and must have been built
 (`python -m gated_deltanet_speculative_amd.build`); there is no fallback path.
@@ -40,7 +42,9 @@ from ._lib import (  # noqa: F401
     conv_tree_step,
     conv_tree_verify,
     decode_step,
+    STATIC_SCRATCH_BYTES,
     prefill,
+    prefill_noalloc,
     prefill_workspace_size,
     load_library,
     replay_commit,

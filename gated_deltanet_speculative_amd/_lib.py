@@ -19,11 +19,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdnverify.so")
 
 (GDN_OK, GDN_ERR_NULL, GDN_ERR_SHAPE, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP, GDN_ERR_ALIGN,
- GDN_ERR_WORKSPACE) = range(8)
+ GDN_ERR_WORKSPACE, GDN_ERR_SCRATCH) = range(9)
 STATUS_SLOT_RANGE, STATUS_SLOT_DUP, STATUS_PARENT, STATUS_ACCEPT, STATUS_NODES = 1, 2, 4, 8, 16
 EXPORTED = ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_conv_tree_verify", "gdn_replay_commit",
             "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step", "gdn_prefill", "gdn_prefill_workspace_size",
-            "gdn_strerror")
+            "gdn_prefill_noalloc", "gdn_strerror")
 MAX_CHAIN = 65536
 MAX_LAYERS = 64
 
@@ -83,10 +83,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdn_conv_step.argtypes = [sp] + [vp] * 7
     lib.gdn_decode_step.argtypes = [sp, vp, vp, vp, i64] + [vp] * 7
     lib.gdn_prefill.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, vp, vp, ctypes.c_size_t, vp, vp]
+    lib.gdn_prefill_noalloc.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, vp, vp, vp]
     lib.gdn_prefill_workspace_size.argtypes = [sp]
     lib.gdn_prefill_workspace_size.restype = ctypes.c_size_t
     for f in ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_conv_tree_verify", "gdn_replay_commit",
-              "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step", "gdn_prefill"):
+              "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step", "gdn_prefill",
+              "gdn_prefill_noalloc"):
         getattr(lib, f).restype = i32
     lib.gdn_strerror.argtypes = [ctypes.c_int]
     lib.gdn_strerror.restype = ctypes.c_char_p
@@ -427,4 +429,37 @@ def prefill(sh: Shape, qkv, beta_logits, alpha_logits, dt_bias, A, state_pool, s
     ]
     cs = sh.c_struct()
     _check(load_library().gdn_prefill(ctypes.byref(cs), *args), "gdn_prefill")
+    return out
+
+
+STATIC_SCRATCH_BYTES = 32 << 20
+
+
+def prefill_noalloc(sh: Shape, qkv, beta_logits, alpha_logits, dt_bias, A, state_pool, slot_ids, status, out,
+                    gate_z=None, gate_mode=0):
+    """prefill with its workspace in the library's static device array (for callers that
+    cannot allocate): nothing is allocated, here or in the library; `out` must be given.
+    Shapes whose workspace exceeds STATIC_SCRATCH_BYTES raise (GDN_ERR_SCRATCH).  Calls that
+    overlap on one GPU share that array and race.  Returns out."""
+    C, T, P, Hv, dk, dv = sh.n_seqs, sh.n_nodes, sh.n_slots, sh.n_v_heads, sh.d_k, sh.d_v
+    if status is None or out is None:
+        raise ValueError("prefill_noalloc needs a status word and an output tensor")
+    bp, bs = _gate_view(beta_logits, "beta_logits", sh)
+    ap, as_ = _gate_view(alpha_logits, "alpha_logits", sh)
+    if bs != as_:
+        raise ValueError("beta_logits and alpha_logits must share one row stride")
+    args = [
+        _dev(qkv, "qkv", torch.float32, (C, T, sh.channels)), bp, ap, bs,
+        _dev(dt_bias, "dt_bias", torch.float32, (Hv,)),
+        _dev(A, "A", torch.float32, (Hv,)),
+        _dev(state_pool, "state_pool", torch.float32, (P, Hv, dk, dv)),
+        _dev(slot_ids, "slot_ids", torch.int32, (C,)),
+        None if gate_z is None else _dev(gate_z, "gate_z", torch.float32, (C, T, Hv, dv)),
+        ctypes.c_int32(int(gate_mode)),
+        _dev(out, "out", torch.float32, (C, T, Hv, dv)),
+        _dev(status, "status", torch.int32, (1,)),
+        _stream(qkv),
+    ]
+    cs = sh.c_struct()
+    _check(load_library().gdn_prefill_noalloc(ctypes.byref(cs), *args), "gdn_prefill_noalloc")
     return out

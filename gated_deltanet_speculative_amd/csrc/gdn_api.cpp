@@ -272,6 +272,31 @@ size_t gdn_prefill_workspace_size(const gdn_shape *sh) {
     return gdn::prefill_workspace_floats(d) * F;
 }
 
+// Argument checks shared by gdn_prefill and gdn_prefill_noalloc (whose workspace is the
+// library's own array: no caller buffer can overlap it).
+static int prefill_args(const gdn_shape *sh, gdn::Dims *dp, const float *qkv, const float *beta_logits,
+                        const float *alpha_logits, int64_t gate_stride, const float *dt_bias, const float *A,
+                        float *state_pool, const int32_t *slot_ids, const float *gate_z, int32_t gate_mode,
+                        float *out, const float *workspace, size_t ws_b, int32_t *status) {
+    gdn::Dims &d = *dp;
+    if (int r = check_shape(sh, &d, true)) return r;
+    if (!qkv || !beta_logits || !alpha_logits || !dt_bias || !A || !state_pool || !slot_ids || !out || !status)
+        return GDN_ERR_NULL;
+    if (gate_stride < d.Hv || (gate_mode != 0 && gate_mode != 1)) return GDN_ERR_SHAPE;
+    if (!aligned({qkv, state_pool, out, gate_z, workspace}, 16) ||
+        !aligned({beta_logits, alpha_logits, dt_bias, A, slot_ids, status}, 4))
+        return GDN_ERR_ALIGN;
+    const size_t rows = (size_t)d.C * d.N;
+    const size_t gate_bytes = ((rows - 1) * (size_t)gate_stride + d.Hv) * F;
+    const size_t out_b = rows * d.Hv * d.dv * F;
+    if (any_alias({{state_pool, (size_t)d.P * d.Hv * d.dk * d.dv * F}, {out, out_b}, {workspace, ws_b}, {status, I}},
+                  {{qkv, rows * d.Ch * F}, {beta_logits, gate_bytes}, {alpha_logits, gate_bytes},
+                   {dt_bias, (size_t)d.Hv * F}, {A, (size_t)d.Hv * F}, {slot_ids, (size_t)d.C * I},
+                   {gate_z, out_b}}))
+        return GDN_ERR_ALIAS;
+    return GDN_OK;
+}
+
 int gdn_prefill(const gdn_shape *sh, const float *qkv, const float *beta_logits, const float *alpha_logits,
                 int64_t gate_stride, const float *dt_bias, const float *A, float *state_pool, const int32_t *slot_ids,
                 const float *gate_z, int32_t gate_mode, float *out, float *workspace, size_t workspace_bytes,
@@ -284,19 +309,28 @@ int gdn_prefill(const gdn_shape *sh, const float *qkv, const float *beta_logits,
     if (gate_stride < d.Hv || (gate_mode != 0 && gate_mode != 1)) return GDN_ERR_SHAPE;
     const size_t ws_b = gdn::prefill_workspace_floats(d) * F;
     if (workspace_bytes < ws_b) return GDN_ERR_WORKSPACE;
-    if (!aligned({qkv, state_pool, out, gate_z, workspace}, 16) ||
-        !aligned({beta_logits, alpha_logits, dt_bias, A, slot_ids, status}, 4))
-        return GDN_ERR_ALIGN;
-    const size_t rows = (size_t)d.C * d.N;
-    const size_t gate_bytes = ((rows - 1) * (size_t)gate_stride + d.Hv) * F;
-    const size_t out_b = rows * d.Hv * d.dv * F;
-    if (any_alias({{state_pool, (size_t)d.P * d.Hv * d.dk * d.dv * F}, {out, out_b}, {workspace, ws_b}, {status, I}},
-                  {{qkv, rows * d.Ch * F}, {beta_logits, gate_bytes}, {alpha_logits, gate_bytes},
-                   {dt_bias, (size_t)d.Hv * F}, {A, (size_t)d.Hv * F}, {slot_ids, (size_t)d.C * I},
-                   {gate_z, out_b}}))
-        return GDN_ERR_ALIAS;
+    if (int r = prefill_args(sh, &d, qkv, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids,
+                             gate_z, gate_mode, out, workspace, ws_b, status))
+        return r;
     return gdn::launch_prefill(d, d.N, qkv, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids,
                                gate_z, gate_mode, out, workspace, status, stream) == hipSuccess
+               ? GDN_OK
+               : GDN_ERR_HIP;
+}
+
+int gdn_prefill_noalloc(const gdn_shape *sh, const float *qkv, const float *beta_logits, const float *alpha_logits,
+                        int64_t gate_stride, const float *dt_bias, const float *A, float *state_pool,
+                        const int32_t *slot_ids, const float *gate_z, int32_t gate_mode, float *out, int32_t *status,
+                        hipStream_t stream) {
+    gdn::Dims d;
+    if (int r = prefill_args(sh, &d, qkv, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids,
+                             gate_z, gate_mode, out, nullptr, 0, status))
+        return r;
+    if (gdn::prefill_workspace_floats(d) > gdn::kStaticScratchFloats) return GDN_ERR_SCRATCH;
+    float *ws = nullptr;
+    if (gdn::static_scratch(stream, &ws) != hipSuccess) return GDN_ERR_HIP;
+    return gdn::launch_prefill(d, d.N, qkv, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids,
+                               gate_z, gate_mode, out, ws, status, stream) == hipSuccess
                ? GDN_OK
                : GDN_ERR_HIP;
 }
@@ -311,6 +345,7 @@ const char *gdn_strerror(int code) {
         case GDN_ERR_HIP: return "HIP kernel launch failed";
         case GDN_ERR_ALIGN: return "a buffer is misaligned (dense float buffers need 16 bytes, others 4)";
         case GDN_ERR_WORKSPACE: return "the workspace is smaller than the size query returns for this shape";
+        case GDN_ERR_SCRATCH: return "the shape needs more workspace than the static scratch of gdn_prefill_noalloc (32 MiB)";
         default: return "unknown error code";
     }
 }

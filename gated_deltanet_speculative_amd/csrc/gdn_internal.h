@@ -71,6 +71,10 @@ constexpr int kPackFloats = 580;
 inline size_t prefill_workspace_floats(const Dims &d) {
     return (size_t)d.C * d.Hv * (size_t)((d.N + kPrefillChunk - 1) / kPrefillChunk) * kPackFloats;
 }
+// The static workspace of the prefill variant that allocates nothing: the device address of
+// this GPU's copy (the stream's device, else the current one), looked up once per device.
+constexpr size_t kStaticScratchFloats = GDN_STATIC_SCRATCH_BYTES / sizeof(float);
+hipError_t static_scratch(hipStream_t stream, float **ptr);
 hipError_t launch_prefill(const Dims &d, int n_tokens, const float *qkv, const float *beta_logits,
                           const float *alpha_logits, int64_t gate_stride, const float *dt_bias, const float *A,
                           float *state_pool, const int32_t *slot_ids, const float *gate_z, int gate_mode, float *out,

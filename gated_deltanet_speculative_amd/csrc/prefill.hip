@@ -36,6 +36,8 @@
 //   [576, 580)  G_B, four copies (one float4 group)
 // Padding tokens of the last chunk are zero rows: beta = 0 and no decay, so they write
 // nothing into D, O or the state.
+#include <mutex>
+
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -429,6 +431,35 @@ hipError_t launch(const Dims &d, int T, const float *qkv, const float *beta_logi
 }
 
 }  // namespace
+
+// Workspace of gdn_prefill_noalloc: a file-scope device array, one copy per GPU the library's
+// code object is loaded on, held until the process ends.  On the host the array's name is a
+// stand-in, not a device address: kernels get each device's address from hipGetSymbolAddress.
+static __device__ __align__(256) float scratch[kStaticScratchFloats];
+
+hipError_t static_scratch(hipStream_t stream, float **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static float *addr[kMaxDevices] = {};
+    int cur = 0;
+    if (hipError_t e = hipGetDevice(&cur); e != hipSuccess) return e;
+    int dev = cur;  // the device the launches go to: the stream's, or the current one
+    if (stream)
+        if (hipError_t e = hipStreamGetDevice(stream, &dev); e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {  // once per device, with that device current
+        if (dev != cur)
+            if (hipError_t e = hipSetDevice(dev); e != hipSuccess) return e;
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) (void)hipSetDevice(cur);
+        if (e != hipSuccess) return e;
+        addr[dev] = static_cast<float *>(p);
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_prefill(const Dims &d, int n_tokens, const float *qkv, const float *beta_logits,
                           const float *alpha_logits, int64_t gate_stride, const float *dt_bias, const float *A,

@@ -25,7 +25,8 @@
  *
  * A prompt fills a slot the same way, with gdn_conv_step over its tokens and then
  *   gdn_prefill      the gated delta rule over a chain of tokens per lane, the slot's state
- *                    updated in place, with an optional closing output gate.
+ *                    updated in place, with an optional closing output gate
+ *                    (gdn_prefill_noalloc: the same without a caller workspace).
  *
  * Sources (page title, then section):
  *   "perf(qwen35): fuse the DFlash2 concurrent verify Gated DeltaNet route",
@@ -47,7 +48,8 @@
  * Conventions common to all calls
  *   - Every tensor is float32 or int32, C order (row-major), in device memory,
  *     allocated and owned by the caller.  The library allocates nothing, keeps no
- *     pointer or device state between calls, and is re-entrant.
+ *     pointer or device state between calls, and is re-entrant; the one exception is
+ *     gdn_prefill_noalloc, whose workspace is a static device array of the library.
  *   - Every call validates its arguments on the host, enqueues its kernels on
  *     `stream` and returns without synchronising.  Verify and commit of a round
  *     must be issued on the same stream (or the caller orders them).
@@ -101,6 +103,8 @@ extern "C" {
 #define GDN_ERR_ALIGN 6       /* a dense float buffer is not 16-byte aligned, or an int32 /
                                  gate buffer not 4-byte aligned                              */
 #define GDN_ERR_WORKSPACE 7   /* workspace_bytes below gdn_prefill_workspace_size()          */
+#define GDN_ERR_SCRATCH 8     /* gdn_prefill_noalloc: the shape needs more workspace than
+                                 GDN_STATIC_SCRATCH_BYTES                                    */
 
 /* Device status bits (OR-ed into *status). */
 #define GDN_STATUS_SLOT_RANGE 1 /* slot id outside [-1, P)                                   */
@@ -345,6 +349,26 @@ int gdn_prefill(const gdn_shape *sh, const float *qkv, const float *beta_logits,
 /* Bytes of workspace gdn_prefill needs for this shape (n_nodes = T tokens per lane); 0 if
    the shape is invalid for gdn_prefill.  Host only, no device call. */
 size_t gdn_prefill_workspace_size(const gdn_shape *sh);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): gdn_prefill with its workspace in a
+ * static device array of the library instead of a caller buffer.  Arguments, results and
+ * errors are those of gdn_prefill without workspace / workspace_bytes, plus
+ * GDN_ERR_SCRATCH (nothing enqueued) when gdn_prefill_workspace_size(sh) exceeds
+ * GDN_STATIC_SCRATCH_BYTES (32 MiB: e.g. 4 lanes x 1024 tokens x 32 value heads need 19 MB).
+ * The call allocates and frees nothing.  Every GPU the library runs on holds one copy of the
+ * array from the library's first use on it until the process ends; its address is looked
+ * up once per device (GDN_ERR_HIP if that fails).  All calls on one GPU share that copy:
+ * calls whose executions overlap on one GPU (different streams, or other host threads,
+ * without ordering between them) race on it and give undefined results; calls ordered on
+ * one stream are safe.  The array's contents on entry do not matter.
+ */
+#define GDN_STATIC_SCRATCH_BYTES (32u << 20)
+int gdn_prefill_noalloc(const gdn_shape *sh, const float *qkv, const float *beta_logits, const float *alpha_logits,
+                        int64_t gate_stride, const float *dt_bias, const float *A, float *state_pool,
+                        const int32_t *slot_ids, const float *gate_z, int32_t gate_mode, float *out, int32_t *status,
+                        hipStream_t stream);
 
 /* Static description of a GDN_OK / GDN_ERR_* code. */
 const char *gdn_strerror(int code);

@@ -29,14 +29,14 @@ static gdn_shape shape() {
     s.d_conv = mode == 0 ? pick(0, 5) : 4;
     return s;
 }
-static bool known(int r) { return r >= 0 && r <= 7; }
+static bool known(int r) { return r >= 0 && r <= 8; }
 int main() {
-    int counts[8] = {0};
+    int counts[9] = {0};
     for (int it = 0; it < 200000; ++it) {
         gdn_shape s = shape();
         const gdn_shape *sp = R(0, 50) ? &s : nullptr;
         long long b = R(1, 20);
-        int which = (int)R(0, 7), r = 0;
+        int which = (int)R(0, 8), r = 0;
         switch (which) {
         case 0: r = gdn_conv_tree_step(sp, cf(b), cf(b + 1), cf(b + 2), I(b + 3), I(b + 4), (int32_t *)maybe(I(b + 12)),
                                        (float *)maybe(F(b + 5)), (float *)maybe(F(b + 6)), (int32_t *)maybe(I(b + 7)), nullptr); break;
@@ -68,13 +68,17 @@ int main() {
                             I(b + 6), R(0, 1) ? cf(b + 7) : nullptr, (int32_t)R(-1, 2), (float *)maybe(F(b + 8)),
                             (float *)maybe(F(b + 9)), have, (int32_t *)maybe(I(b + 10)), nullptr); break;
         }
+        case 8: r = gdn_prefill_noalloc(sp, cf(b), cf(b + 1), cf(b + 2), R(-1, 200), cf(b + 3), cf(b + 4),
+                                        (float *)maybe(F(b + 5)), I(b + 6), R(0, 1) ? cf(b + 7) : nullptr,
+                                        (int32_t)R(-1, 2), (float *)maybe(F(b + 8)), (int32_t *)maybe(I(b + 10)),
+                                        nullptr); break;
         }
         if (!known(r)) { std::printf("unknown return %d from call %d\n", r, which); return 1; }
         ++counts[r];
         if (!gdn_strerror(r)) return 1;
     }
     std::printf("launches %d; codes:", g_launches);
-    for (int k = 0; k < 8; ++k) std::printf(" %d:%d", k, counts[k]);
+    for (int k = 0; k < 9; ++k) std::printf(" %d:%d", k, counts[k]);
     std::printf("\n");
     return 0;
 }

@@ -24,4 +24,8 @@ hipError_t launch_prefill(const Dims &, int, const float *, const float *, const
                           hipStream_t) {
     ++g_launches; return hipSuccess;
 }
+hipError_t static_scratch(hipStream_t, float **ptr) {
+    *ptr = reinterpret_cast<float *>(0x7E0000000000ull);  // a stand-in, never dereferenced
+    return hipSuccess;
+}
 }  // namespace gdn

@@ -324,3 +324,33 @@ def test_conv_step_chain_limit():
     chains are rejected before anything is enqueued."""
     assert gdn.MAX_CHAIN == 65536
     assert _conv_step(_shape(n_nodes=65537), _ptrs(5), FAKE + (1 << 40)) == _lib.GDN_ERR_UNSUPPORTED
+
+
+def test_prefill_noalloc_rejections():
+    """The prefill variant with the library's static workspace: the prefill's own checks,
+    and GDN_ERR_SCRATCH, before any device call, when the shape's workspace exceeds the
+    static array."""
+    lib = gdn.load_library()
+    st = FAKE + (1 << 40)
+
+    def call(sh, p, gate_stride=8, gate_mode=0, status=st):
+        cs = sh.c_struct()
+        return lib.gdn_prefill_noalloc(ctypes.byref(cs), p[0], p[1], p[2], gate_stride, p[3], p[4], p[5], p[6], p[7],
+                                       ctypes.c_int32(gate_mode), p[8], status, None)
+
+    p = _ptrs(9)  # qkv, beta, alpha, dt_bias, A, state_pool, slot_ids, gate_z, out
+    assert call(_shape(n_nodes=1000), p, status=None) == _lib.GDN_ERR_NULL
+    assert call(_shape(n_nodes=1000), p, gate_mode=2) == _lib.GDN_ERR_SHAPE
+    q = list(p)
+    q[8] += 4
+    assert call(_shape(n_nodes=1000), q) == _lib.GDN_ERR_ALIGN
+    q = list(p)
+    q[8] = q[7] + 16  # out overlapping the gate values
+    assert call(_shape(n_nodes=1000), q) == _lib.GDN_ERR_ALIAS
+    assert call(_shape(n_nodes=65537), p) == _lib.GDN_ERR_UNSUPPORTED
+    big = gdn.Shape(4, 2048, 8, 16, 32, 128, 128)  # 4 x 32 x 128 packages of 2320 bytes: 38 MB
+    assert gdn.prefill_workspace_size(big) > gdn.STATIC_SCRATCH_BYTES
+    assert call(big, p, gate_stride=64) == _lib.GDN_ERR_SCRATCH
+    assert "static scratch" in gdn.strerror(_lib.GDN_ERR_SCRATCH)
+    fits = gdn.Shape(4, 1024, 8, 16, 32, 128, 128)  # the prefill bench shape: 19 MB
+    assert gdn.prefill_workspace_size(fits) <= gdn.STATIC_SCRATCH_BYTES
