@@ -53,6 +53,15 @@ __device__ inline float add_row_shr(float x) {
     return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + SH, 0xF, 0xF, true));
 }
 
+// the same for a double (both halves moved by DPP; lanes before the row start add 0.0)
+template <int SH>
+__device__ inline double add_row_shr(double x) {
+    const long long b = __double_as_longlong(x);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)b, 0x110 + SH, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), 0x110 + SH, 0xF, 0xF, true);
+    return x + __longlong_as_double((long long)((unsigned long long)(unsigned)hi << 32 | (unsigned)lo));
+}
+
 // value of lane K of each row of 16 lanes, in every lane of the row (DPP row_newbcast)
 template <int K>
 __device__ inline float row_bcast(float x) {
@@ -71,8 +80,8 @@ __device__ inline float bcast_solve(float t, const v4f *Lr, std::integer_sequenc
 // Sum over aligned groups of W consecutive lanes (W = 4, 8 or 16; W = 16 is a DPP row),
 // left in the last lane of each group; with W = 16 also the inclusive prefix sum along
 // each row of 16 lanes.
-template <int W>
-__device__ inline float group_sum_last(float x) {
+template <int W, typename F>
+__device__ inline F group_sum_last(F x) {
     x = add_row_shr<1>(x);
     x = add_row_shr<2>(x);
     if constexpr (W >= 8) x = add_row_shr<4>(x);

@@ -126,7 +126,8 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
     __shared__ __align__(16) float s_gram[kWaves][2][256];
     __shared__ __align__(16) float Lm[BC * SG], Tm[BC * BC];
     __shared__ float s_rk[BC], s_rq[BC], s_kk[256], s_qk[256];
-    __shared__ float s_beta[HG][BC], s_L[HG][BC];
+    __shared__ float s_beta[HG][BC];
+    __shared__ double s_L[HG][BC];
     const float *Ql = QK, *Kl = QK + BC * SX;
 
     const int nch = (T + BC - 1) / BC;
@@ -197,8 +198,10 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
         {
             const int t = tid & 15;
             const bool real = t < nc;
-            const float ell = real ? fast_softplus(xa) * xA : 0.f;  // log g
-            const float L = group_sum_last<16>(ell);
+            // the prefix in double: a chunk of strong decays reaches hundreds, where a float
+            // sum would lose about 1e-4 of every ratio exp(L_t - L_u) formed from it
+            const double ell = real ? fast_softplus(xa) * xA : 0.f;  // log g
+            const double L = group_sum_last<16>(ell);
             s_beta[tid >> 4][t] = real ? fast_sigmoid(xb) : 0.f;
             s_L[tid >> 4][t] = L;
         }
@@ -208,17 +211,18 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
             float *pk = pack + (((int64_t)c * d.Hv + h) * nch + j) * kPackFloats;
             {
                 const int i = tid >> 4, a = tid & 15;
-                const float r = a <= i ? fast_exp(s_L[mg][i] - s_L[mg][a]) * s_rk[a] : 0.f;
+                const float r = a <= i ? fast_exp((float)(s_L[mg][i] - s_L[mg][a])) * s_rk[a] : 0.f;
                 Lm[i * SG + a] = a < i ? r * s_kk[tid] * (s_beta[mg][i] * s_rk[i]) : 0.f;
                 pk[PK_CQ + tid] = r * s_qk[tid] * (s_rq[i] * isd);
             }
             if (tid < BC) {
-                const float G = fast_exp(s_L[mg][tid]), Lend = s_L[mg][BC - 1];  // padding adds no decay
+                const float G = fast_exp((float)s_L[mg][tid]);
+                const double Lend = s_L[mg][BC - 1];  // padding adds no decay
                 pk[PK_A + tid] = s_beta[mg][tid];
                 pk[PK_B + tid] = G * s_rk[tid];
                 pk[PK_C + tid] = G * s_rq[tid] * isd;
-                pk[PK_W + tid] = fast_exp(Lend - s_L[mg][tid]) * s_rk[tid];
-                if (tid < 4) pk[PK_GEND + tid] = fast_exp(Lend);
+                pk[PK_W + tid] = fast_exp((float)(Lend - s_L[mg][tid])) * s_rk[tid];
+                if (tid < 4) pk[PK_GEND + tid] = fast_exp((float)Lend);
             }
             lds_barrier();
             // T = (I + Lm)^-1: lane (column a, row i) over rows of 16 lanes

@@ -175,7 +175,10 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     float *Tm = lds + Ly::OFF_T;     // T = (I + Lm)^-1
     float *scr = lds + Ly::OFF_SCR;
     __shared__ int s_wbits[kWaves];
-    __shared__ float s_beta[NP], s_g[NP], s_L[NP], s_G[NP], s_gk[NP], s_gq[NP], s_r[2 * NP];
+    __shared__ float s_beta[NP], s_g[NP], s_G[NP], s_gk[NP], s_gq[NP], s_r[2 * NP];
+    // cumulative log-decays in double: along a path of strong decays they reach hundreds, and
+    // a float sum would then lose about 1e-4 of every ratio exp(L_i - L_a) formed from them
+    __shared__ double s_L[NP];
     __shared__ float s_ssq[2 * NP][Ly::NPART];
     __shared__ unsigned int s_anc[NP];
     // conv sources of node i, oldest first, as staged rows (node rows, or NP + j for
@@ -318,9 +321,9 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
         const bool real = lane < nvc;
         const int a1 = real ? par : -1;
         int jump = a1;
-        float L = 0.f;
+        double L = 0.0;
         if (real) L = fast_softplus(araw) * Ah;  // log g = softplus(a + dt_bias) * A
-        if (lane < NP) s_g[lane] = real ? fast_exp(L) : 0.f;
+        if (lane < NP) s_g[lane] = real ? fast_exp((float)L) : 0.f;
         unsigned int anc = real ? 1u << lane : 0u;
         const int a2s = __shfl(a1, a1 >= 0 ? a1 : 0);
         const int a2 = a1 >= 0 ? a2s : -1;
@@ -329,7 +332,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
 #pragma unroll
         for (int r = 1; r < NP; r <<= 1) {
             const int srcl = jump < 0 ? lane : jump;
-            const float Lj = __shfl(L, srcl);
+            const double Lj = __shfl(L, srcl);
             const unsigned int aj = __shfl(anc, srcl);
             const int jj = __shfl(jump, srcl);
             if (jump >= 0) {
@@ -340,7 +343,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
         }
         if (lane < NP) {
             s_L[lane] = L;
-            s_G[lane] = real ? fast_exp(L) : 0.f;
+            s_G[lane] = real ? fast_exp((float)L) : 0.f;
             s_anc[lane] = anc;
             s_beta[lane] = real ? fast_sigmoid(braw) : 0.f;
             const int r2 = a1 >= 0 ? a1 : NP + 2;
@@ -604,7 +607,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
             skk += gk[w * Ly::GRAM_TILES * 256];
             sqk += gqk[w * Ly::GRAM_TILES * 256];
         }
-        const float r = on ? fast_exp(s_L[i] - s_L[a]) * s_r[a] : 0.f;
+        const float r = on ? fast_exp((float)(s_L[i] - s_L[a])) * s_r[a] : 0.f;
         Lm[i * SG + a] = (on && a != i) ? r * skk * (s_r[i] * s_beta[i]) : 0.f;
         Cq[i * SG + a] = r * sqk * (s_r[NP + i] * isd);
     }
