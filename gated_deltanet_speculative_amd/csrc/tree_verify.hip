@@ -129,9 +129,31 @@ struct VerifyLayout {
     static constexpr int PARTS = OFF_GRAM + GPART + (WIDE ? 0 : kWaves * UNIT);
     static constexpr int SCR1 = STAGE > PARTS ? STAGE : PARTS;
     static constexpr int SCR = SCR1 > 2 * NP * SV ? SCR1 : 2 * NP * SV;  // also the epilogue's row staging
-    static constexpr int LDS_FLOATS = OFF_SCR + SCR;
+    // SPLIT: the state product [K; Q] x S0 as three bf16 products of hi/lo parts (see
+    // state_product); the raw rows' bf16 parts [2NP][SXB] are staged beside XQK.  Used where
+    // the extra LDS keeps two workgroups per CU: 64-column blocks over at most 16 nodes.
+    static constexpr bool SPLIT = !WIDE && NP == 16 && DK % 32 == 0 && (DK / 32) % KP == 0;
+    static constexpr int SXB = DK + 8;  // bf16 row stride: 16 rows read with ds_read_b128 hit distinct banks
+    static constexpr int LC3 = SPLIT ? DK / 32 / KP : 0;  // state product: 32-wide chunks per wave
+    static constexpr int OFF_XH = OFF_SCR + SCR;          // hi parts, then lo parts (2 bf16 per float)
+    static constexpr int LDS_FLOATS = OFF_XH + (SPLIT ? 2 * NP * SXB : 0);
     static_assert(4 * LDS_FLOATS <= 160 * 1024 - 2048, "LDS of one workgroup (with the static arrays)");
 };
+
+typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+
+// x = hi + lo + r with hi = bf16(x), lo = bf16(x - hi) (round to nearest even) and
+// |r| <= 2^-18 |x|: three bf16 products hi.hi + hi.lo + lo.hi, accumulated in float32, give a
+// product to about 2^-17 relative (the dropped lo.lo and r terms)
+template <int K>
+__device__ inline void split_bf16(const float (&x)[K], __bf16 (&h)[K], __bf16 (&l)[K]) {
+#pragma unroll
+    for (int e = 0; e < K; ++e) {
+        h[e] = (__bf16)x[e];
+        l[e] = (__bf16)(x[e] - (float)h[e]);
+    }
+}
 
 // Tree conv + SiLU of 4 channels at one node from its sources, oldest first (x3 = the
 // node's own tokens); w[e] holds the 4 taps of channel e (tap 0 = oldest), summed from
@@ -174,6 +196,8 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     float *Cq = lds + Ly::OFF_CQ;    // output coefficients (1/sqrt(d_k) folded in)
     float *Tm = lds + Ly::OFF_T;     // T = (I + Lm)^-1
     float *scr = lds + Ly::OFF_SCR;
+    __bf16 *XH = reinterpret_cast<__bf16 *>(lds + Ly::OFF_XH);  // SPLIT: bf16 parts of the raw rows
+    __bf16 *XL = XH + 2 * NP * Ly::SXB;
     __shared__ int s_wbits[kWaves];
     __shared__ float s_beta[NP], s_g[NP], s_G[NP], s_gk[NP], s_gq[NP], s_r[2 * NP];
     // cumulative log-decays in double: along a path of strong decays they reach hundreds, and
@@ -395,6 +419,8 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     //      are requested only now, once the token rows have arrived, so that the rows the
     //      conv and the tree algebra need first do not queue behind the state in HBM; the
     //      state is first needed after the conv.
+    //      SPLIT: the 32-wide chunks m = pkp + KP*l3 of the bf16 products instead, lane group g4
+    //      holding rows 32m + 8*g4 + 0..7 (in sreg[2*l3][0..3], sreg[2*l3 + 1][0..3])
     float sreg[LCQ][4];
     {
         const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
@@ -403,7 +429,8 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
 #pragma unroll
         for (int lc = 0; lc < LCQ; ++lc) {
             const int q = pkp + KP * lc;
-            const int base = (KC % KP == 0 || q < KC) ? ((16 * q + 4 * g4) * DV + j0 + 16 * pct + l16) * 4 : kOutOfRange;
+            const int row0 = Ly::SPLIT ? 32 * (pkp + KP * (lc / 2)) + 8 * g4 + 4 * (lc % 2) : 16 * q + 4 * g4;
+            const int base = (Ly::SPLIT || KC % KP == 0 || q < KC) ? (row0 * DV + j0 + 16 * pct + l16) * 4 : kOutOfRange;
 #pragma unroll
             for (int e = 0; e < 4; ++e) sreg[lc][e] = load1(sr, base + e * DV * 4);
         }
@@ -471,6 +498,13 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
                 const int row = isq ? NP + i : i;
                 *reinterpret_cast<v4f *>(XQK + row * SX + 4 * cg) = yq[u];
                 if ((cg & 15) == (DK / 4 < 16 ? DK / 4 : 16) - 1) s_ssq[row][cg >> 4] = ss;
+                if constexpr (Ly::SPLIT) {
+                    const float y[4] = {yq[u].x, yq[u].y, yq[u].z, yq[u].w};
+                    __bf16 hi[4], lo[4];
+                    split_bf16(y, hi, lo);
+                    *reinterpret_cast<bf4 *>(XH + row * Ly::SXB + 4 * cg) = bf4{hi[0], hi[1], hi[2], hi[3]};
+                    *reinterpret_cast<bf4 *>(XL + row * Ly::SXB + 4 * cg) = bf4{lo[0], lo[1], lo[2], lo[3]};
+                }
             }
         }
         if (has_v) {
@@ -486,19 +520,44 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     // ---- [K; Q] x S0 for this wave's unit (column tile pct, chunks q = pkp + KP*lc) into
     //      LDS partial tiles in accumulator order (WIDE: the complete tiles stay in sp)
     v4f sp[Ly::RT];
+    //      SPLIT: per 32-wide chunk three v_mfma_f32_16x16x32_bf16 on the hi/lo parts of both
+    //      operands (hi.hi + hi.lo + lo.hi), lane group g4 supplying rows 32m + 8*g4 + 0..7 of
+    //      the chunk in both operands; the float32 accumulators have the layout of mfma4's
     auto state_product = [&]() {
         v4f acc[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) acc[rt] = v4f{0.f, 0.f, 0.f, 0.f};
+        if constexpr (Ly::SPLIT) {
 #pragma unroll
-        for (int lc = 0; lc < LCQ; ++lc) {
-            const int q = pkp + KP * lc;
-            if (KC % KP == 0 || q < KC) {
-                const v4f bv = {sreg[lc][0], sreg[lc][1], sreg[lc][2], sreg[lc][3]};
+            for (int l3 = 0; l3 < Ly::LC3; ++l3) {
+                const int m = pkp + KP * l3;
+                const float x[8] = {sreg[2 * l3][0],     sreg[2 * l3][1],     sreg[2 * l3][2],     sreg[2 * l3][3],
+                                    sreg[2 * l3 + 1][0], sreg[2 * l3 + 1][1], sreg[2 * l3 + 1][2], sreg[2 * l3 + 1][3]};
+                __bf16 bh[8], bl[8];
+                split_bf16(x, bh, bl);
+                const bf8 vbh = {bh[0], bh[1], bh[2], bh[3], bh[4], bh[5], bh[6], bh[7]};
+                const bf8 vbl = {bl[0], bl[1], bl[2], bl[3], bl[4], bl[5], bl[6], bl[7]};
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-                    acc[rt] = mfma4(*reinterpret_cast<const v4f *>(XQK + (16 * rt + l16) * SX + 16 * q + 4 * g4), bv,
-                                    acc[rt]);
+                for (int rt = 0; rt < RT; ++rt) {
+                    const int off = (16 * rt + l16) * Ly::SXB + 32 * m + 8 * g4;
+                    const bf8 ah = *reinterpret_cast<const bf8 *>(XH + off);
+                    const bf8 al = *reinterpret_cast<const bf8 *>(XL + off);
+                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, vbh, acc[rt], 0, 0, 0);
+                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, vbl, acc[rt], 0, 0, 0);
+                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, vbh, acc[rt], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int lc = 0; lc < LCQ; ++lc) {
+                const int q = pkp + KP * lc;
+                if (KC % KP == 0 || q < KC) {
+                    const v4f bv = {sreg[lc][0], sreg[lc][1], sreg[lc][2], sreg[lc][3]};
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        acc[rt] = mfma4(*reinterpret_cast<const v4f *>(XQK + (16 * rt + l16) * SX + 16 * q + 4 * g4),
+                                        bv, acc[rt]);
+                }
             }
         }
         if constexpr (WIDE) {
