@@ -62,6 +62,9 @@ def parse():
                          "without a draft (conv step + one-token recurrence per instance, state in place); "
                          "or a prompt filling the slots (conv step + chunked prefill per instance)")
     ap.add_argument("--prompt", type=int, default=1024, help="--mode prefill: prompt tokens per lane")
+    ap.add_argument("--lanes", type=int, default=None,
+                    help="verify mode: run the workload's head shape and trees with this many lanes "
+                         "(slots = max(lanes, the workload's pool)); the workload is then named <name>-lanes<N>")
     return ap.parse_args()
 
 
@@ -137,29 +140,66 @@ def measured_traffic(workload, kernel):
     return int(round(rec["read_bytes"] + rec["write_bytes"]))
 
 
-def cpu_baseline(wl, seconds, seed):
-    """The fp64 oracle on single-layer instances of the workload, until `seconds` of CPU work."""
-    from threadpoolctl import threadpool_limits
+def host_description():
+    """The host the CPU baseline ran on: logical CPUs, those this process may use, the CPU
+    model, and the BLAS libraries numpy loaded with the thread count each uses inside the
+    baseline (limited to one)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    with threadpool_limits(limits=1):
+        blas = [dict(library=i.get("internal_api"), threads=i.get("num_threads")) for i in threadpool_info()
+                if i.get("user_api") == "blas"]
+    return dict(host_cpu_count=os.cpu_count(), host_cpus_usable=len(os.sched_getaffinity(0)), cpu_model=model,
+                blas_in_baseline=blas)
+
+
+def _oracle_round_seconds(wl, layer, seed):
+    """Seconds of one single-layer round (conv + verify + commit) of the fp64 oracle."""
     from oracle import gdn_oracle as O
     from workloads import layer_params, round_inputs, round_structure
 
     st = round_structure(wl, 0, seed)
+    lp, ri = layer_params(wl, layer, seed), round_inputs(wl, layer, 0, seed)
+    t0 = time.perf_counter()
+    r = O.verify_round(ri["x"], ri["ba"], lp["conv_w"], lp["conv_hist"], lp["state"], lp["dt_bias"], lp["A"],
+                       st["slot_ids"], st["parents"], wl.n_k_heads)
+    pool, hist = lp["state"].astype(np.float64), lp["conv_hist"].astype(np.float64)
+    O.replay_commit(r["replay_log"], r["commit_win"], st["slot_ids"], st["parents"], st["accept_node"], pool, hist)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(wl, seconds, seed):
+    """The fp64 oracle on single-layer instances of the workload, until `seconds` of CPU work,
+    and on one layer of the single-lane grouped chain (median of 3 after a warm-up)."""
+    from threadpoolctl import threadpool_limits
+
+    from workloads import WORKLOADS
+
     done, t_used = 0, 0.0
     with threadpool_limits(limits=1):
         while t_used < seconds:
-            lp, ri = layer_params(wl, done, seed), round_inputs(wl, done, 0, seed)
-            t0 = time.perf_counter()
-            r = O.verify_round(ri["x"], ri["ba"], lp["conv_w"], lp["conv_hist"], lp["state"], lp["dt_bias"], lp["A"],
-                               st["slot_ids"], st["parents"], wl.n_k_heads)
-            pool, hist = lp["state"].astype(np.float64), lp["conv_hist"].astype(np.float64)
-            O.replay_commit(r["replay_log"], r["commit_win"], st["slot_ids"], st["parents"], st["accept_node"], pool,
-                            hist)
-            t_used += time.perf_counter() - t0
+            t_used += _oracle_round_seconds(wl, done, seed)
             done += 1
+        c1 = WORKLOADS["grouped-chain-n8"]
+        _oracle_round_seconds(c1, 0, seed)
+        t1 = float(np.median([_oracle_round_seconds(c1, k, seed) for k in range(3)]))
     return dict(value=wl.n_seqs * wl.n_nodes * done / t_used, unit="verify tokens/s", cores=1, kind="oracle",
                 sample=f"{done} single-layer rounds (conv+verify+commit) of {wl.name}, fp64 numpy, 1 BLAS thread, "
-                       f"{t_used:.1f} s")
+                       f"{t_used:.1f} s",
+                grouped_chain_n8=dict(value=round(c1.n_seqs * c1.n_nodes / t1, 1), unit="verify tokens/s",
+                                      sample="one layer (1 lane, 8-token chain, H_k 16, H_v 32, d 128; "
+                                             "conv+verify+commit), median of 3 after a warm-up",
+                                      seconds=round(t1, 4)),
+                **host_description())
 
 
 def cpu_baseline_decode(wl, seconds, seed):
@@ -188,7 +228,7 @@ def cpu_baseline_decode(wl, seconds, seed):
             done += 1
     return dict(value=C * done / t_used, unit="decode tokens/s", cores=1, kind="oracle",
                 sample=f"{done} single-layer decode steps (conv step + recurrence) of {wl.name}, fp64 numpy, "
-                       f"1 BLAS thread, {t_used:.1f} s")
+                       f"1 BLAS thread, {t_used:.1f} s", **host_description())
 
 
 def cpu_baseline_prefill(wl, seconds, seed, tokens=32):
@@ -219,7 +259,7 @@ def cpu_baseline_prefill(wl, seconds, seed, tokens=32):
             done += 1
     return dict(value=C * tokens * done / t_used, unit="prompt tokens/s", cores=1, kind="oracle",
                 sample=f"{done} single-layer {tokens}-token prompts of {wl.name} (conv step + recurrence), "
-                       f"fp64 numpy, 1 BLAS thread, {t_used:.1f} s")
+                       f"fp64 numpy, 1 BLAS thread, {t_used:.1f} s", **host_description())
 
 
 def decode_main(args):
@@ -470,6 +510,11 @@ def main():
     from workloads import WORKLOADS, layer_params, path_to_root, round_inputs, round_structure
 
     wl = WORKLOADS[args.workload]
+    if args.lanes is not None:
+        import dataclasses
+
+        wl = dataclasses.replace(wl, name=f"{wl.name}-lanes{args.lanes}", n_seqs=args.lanes,
+                                 n_slots=max(args.lanes, wl.n_slots))
     sh = gdn.Shape(**wl.shape_dict())
     C, N, P, Ch, Hv, dk, dv = sh.n_seqs, sh.n_nodes, sh.n_slots, sh.channels, sh.n_v_heads, sh.d_k, sh.d_v
     L = args.instances
@@ -581,7 +626,7 @@ def main():
     # per-kernel mean time per layer instance: each kernel alone over the L instances (one
     # graph of L back-to-back launches, or of one multi-layer commit launch), HIP events
     # on the stream the graph runs on
-    kern, kern_pct, cold_us, copy_ref = {}, {}, {}, None
+    kern, kern_pct, cold_us, copy_ref, floor = {}, {}, {}, None, None
     ab0 = algorithmic_bytes(wl, [1] * C, rounds[0].get("lane_nodes"))
     kernel_bytes_est = {"conv_tree_verify": ab0["conv_verify"], "tree_verify": ab0["verify"]}
     if not args.profile_only:
@@ -641,6 +686,36 @@ def main():
         copy_ref = dict(bytes=8 * nb, us=round(copy_us, 3), gbs=round(8 * nb / (copy_us * 1e-6) / 1e9, 1),
                         what="torch device copy_ of the same byte count, 64 buffers, graph replay")
         del srcs, dsts, g
+        # the dispatch floor on this machine: 64 launches of an empty one-workgroup kernel (torch's
+        # clock spin for 0 cycles), and 64 launches of the fused kernel's own grid with every lane
+        # a padding lane (its workgroups issue their slot-independent loads and return)
+        g = capture(lambda: [torch.cuda._sleep(0) for _ in range(64)])
+        g.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(5):
+            g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        floor = dict(empty_kernel_us=round(ev0.elapsed_time(ev1) * 1e3 / (5 * 64), 3))
+        if args.route == "fused":
+            pad = torch.full((C,), -1, dtype=torch.int32, device=dev)
+            g = capture(lambda: [gdn.conv_tree_verify(sh, b["x"], b["conv_w"], b["conv_hist"], b["beta"], b["alpha"],
+                                                      b["dt_bias"], b["A"], b["state"], pad, parents[0], out=b["out"],
+                                                      replay_log=b["log"], commit_win=b["commit_win"], status=status,
+                                                      lane_nodes=counts[0]) for b in inst])
+            g.replay()
+            torch.cuda.synchronize()
+            ev0.record()
+            for _ in range(5):
+                g.replay()
+            ev1.record()
+            torch.cuda.synchronize()
+            floor["padding_lanes_same_grid_us"] = round(ev0.elapsed_time(ev1) * 1e3 / (5 * L), 3)
+        floor["what"] = ("per launch in graph replays of back-to-back launches: an empty one-workgroup kernel, and "
+                         "the fused launch with every lane a padding lane (same grid; each workgroup issues its "
+                         "slot-independent loads, then returns)")
+        del g
 
     calibrate_copy(args.calibrate_copy, dev)
 
@@ -648,9 +723,10 @@ def main():
     # per-kernel times are taken on round 0: with ragged lanes its node counts set the bytes
     ab = algorithmic_bytes(wl, [int(round(mean_depths))] * C, rounds[0].get("lane_nodes"))
     ab_rounds = [algorithmic_bytes(wl, dd, rd.get("lane_nodes")) for dd, rd in zip(depths, rounds)]
-    commit_bytes = float(np.mean([a["commit"] for a in ab_rounds]))
+    commit_bytes = float(np.mean([a["commit"] for a in ab_rounds]))  # a step's commit: the rounds cycle
+    # the per-kernel loop times every kernel on round 0's trees and accepted paths
     kernel_bytes = {"conv_tree_step": ab["conv"], "tree_verify": ab["verify"], "conv_tree_verify": ab["conv_verify"],
-                    "replay_commit": commit_bytes}
+                    "replay_commit": ab_rounds[0]["commit"]}
     roofline = None
     if kern:
         dom = max(kern, key=lambda k: kern[k])
@@ -698,6 +774,7 @@ def main():
         "kernel_us_p10_p50_p90": kern_pct,
         "kernel_cold_call_us": {k: round(v, 2) for k, v in cold_us.items()},
         "copy_same_bytes": copy_ref,
+        "dispatch_floor": floor,
         "kernel_gbs": {k: round(kernel_bytes[k] / (kern[k] * 1e-6) / 1e9, 1) for k in kern},
         "verify_only_tokens_per_s": (round(present[0] / (sum(v for k, v in kern.items() if k != "replay_commit")
                                                          * 1e-6), 1) if kern else None),

@@ -113,6 +113,11 @@ extern "C" {
 #define GDN_STATUS_ACCEPT 8     /* accept_node[c] outside [-1, N_c) (commit only)            */
 #define GDN_STATUS_NODES 16     /* lane_nodes[c] outside [0, N]                              */
 
+/* Draft nodes per lane (N).  The largest verify batch the pages use is a tree of 17 to 32
+   nodes: "qwen35: DSpark speculative decoding (Qwen3.8-27B drafters)", the commit message on
+   the quantized-GEMM tile choice, names N = 17..32 batches for the DDTree budgets; chains there
+   are 8 or 16 wide.  The fused verify keeps a (2N) x (d_k + N) block per workgroup in LDS, so
+   N is bounded by that largest tree (GDN_ERR_UNSUPPORTED above it). */
 #define GDN_MAX_NODES 32
 #define GDN_MAX_CHAIN 65536 /* tokens per lane of gdn_conv_step and gdn_prefill */
 #define GDN_MAX_SEQS 1024

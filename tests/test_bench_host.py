@@ -91,3 +91,11 @@ def test_cpu_baselines_report_their_sample(fn, unit):
     r = getattr(bench, fn)(WORKLOADS["tiny-chain"], 0.05, 0)
     assert r["unit"] == unit and r["kind"] == "oracle" and r["cores"] == 1
     assert r["value"] > 0 and "fp64" in r["sample"]
+    # the host it ran on: logical CPUs, usable CPUs, model, and one BLAS thread in the baseline
+    assert r["host_cpu_count"] == os.cpu_count() and 1 <= r["host_cpus_usable"] <= r["host_cpu_count"]
+    assert "cpu_model" in r
+    assert all(b["threads"] == 1 for b in r["blas_in_baseline"])
+    if fn == "cpu_baseline":  # also one layer of the single-lane grouped chain
+        c1 = r["grouped_chain_n8"]
+        assert c1["unit"] == "verify tokens/s" and c1["value"] > 0
+        assert abs(c1["value"] - 8 / c1["seconds"]) / c1["value"] < 1e-2

@@ -26,7 +26,8 @@ def _bench(*extra):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("extra,workload", [((), "tree-c4-n16"), (("--mode", "decode", "--instances", "8"),
-                                                                    "tree-c4-n16-decode")])
+                                                                    "tree-c4-n16-decode"),
+                                            (("--lanes", "8", "--instances", "8"), "tree-c4-n16-lanes8")])
 def test_bench_line(extra, workload):
     d = _bench(*extra)
     assert d["n_gpus"] == 1 and d["steps"] == 2 and d["warmup"] == 1 and d["higher_is_better"] is True
@@ -36,3 +37,8 @@ def test_bench_line(extra, workload):
     assert rl["bound"] == "hbm" and rl["unit"] == "GB/s" and rl["peak"] == 8000.0
     assert abs(rl["frac"] - rl["achieved"] / rl["peak"]) < 1e-3
     assert abs(rl["achieved"] - rl["bytes_per_launch"] / (rl["us_per_launch"] * 1e3)) / rl["achieved"] < 1e-2
+    if "lanes8" in workload:
+        assert d["config"]["lanes"] == 8 and d["config"]["slots"] == 8
+    if "decode" not in workload:  # the dispatch floor of this machine, beside the kernel times
+        fl = d["dispatch_floor"]
+        assert 0 < fl["empty_kernel_us"] < fl["padding_lanes_same_grid_us"] < rl["us_per_launch"]
