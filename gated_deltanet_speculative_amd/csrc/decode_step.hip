@@ -143,49 +143,55 @@ __global__ __launch_bounds__(kThreads) void conv_step_kernel(Dims d, const float
     }
 }
 
-// ---- decode step: workgroup = (lane c = blockIdx.y, value head h, block of JB value
-//      columns); thread (r, q) = (tid / Q4, tid % Q4) holds the 4 columns q of the rows
-//      r, r + RG, ... of the block, so one load instruction covers whole rows.
+// ---- decode step: workgroup = one wave = (lane c = blockIdx.y, value head h, block of JB value
+//      columns).  Thread (r, q) = (lane / Q4, lane % Q4) holds the 4 columns q of the RPL
+//      consecutive rows r*RPL.. of the block, so one load instruction covers RG whole row
+//      segments of the block.  The wave owns every row of its columns: the column sums
+//      S^T k^ and S^T q^ reduce across its lanes (DPP rotations and permlane swaps), with no
+//      cross-wave exchange, and the wave writes its columns back as soon as its own loads
+//      have arrived.
 template <int DK, int DV>
 struct DecodeCfg {
-    static constexpr int JB = DV < 32 ? DV : 32;  // value columns per workgroup
+    static constexpr int JB = DV < 32 ? DV : 32;  // value columns per wave
     static constexpr int NB = DV / JB;
-    static constexpr int Q4 = JB / 4;             // 4-column groups
-    static constexpr int RG = kThreads / Q4;      // row groups
-    static constexpr int RPT = (DK + RG - 1) / RG;  // rows per thread
+    static constexpr int Q4 = JB / 4;             // 4-column groups (4 or 8)
+    static constexpr int RG = 64 / Q4;            // row groups
+    static constexpr int RPL = DK / RG;           // consecutive rows per thread
+    static_assert(RPL >= 1 && RG * RPL == DK, "rows tile the wave");
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(kThreads) void decode_step_kernel(
+__global__ __launch_bounds__(64) void decode_step_kernel(
     Dims d, const float *__restrict__ qkv, const float *__restrict__ beta_logits,
     const float *__restrict__ alpha_logits, int64_t gate_stride, const float *__restrict__ dt_bias,
     const float *__restrict__ A, float *__restrict__ state_pool, const int32_t *__restrict__ slot_ids,
     float *__restrict__ out, int32_t *__restrict__ status) {
     using Cfg = DecodeCfg<DK, DV>;
-    constexpr int JB = Cfg::JB, NB = Cfg::NB, Q4 = Cfg::Q4, RG = Cfg::RG, RPT = Cfg::RPT;
-    static_assert(DK / 4 <= 64, "q and k rows staged by one wave each");
+    constexpr int JB = Cfg::JB, NB = Cfg::NB, Q4 = Cfg::Q4, RPL = Cfg::RPL;
     __shared__ unsigned int s_bitmap[kBitmapSlots / 32];
     __shared__ int s_word;
-    __shared__ float s_q[DK], s_k[DK], s_dot[3];
-    __shared__ v4f s_part[kThreads / 64][2][Q4];
 
     const int c = blockIdx.y, h = blockIdx.x / NB, jb = blockIdx.x - h * NB, j0 = jb * JB;
     const int kh = h % d.Hk;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int q = tid % Q4, r = tid / Q4;
+    const int lane = threadIdx.x;
+    const int q = lane % Q4, r = lane / Q4, i0 = r * RPL;
     // loads in the order they are needed, all issued before any is consumed: this lane's
     // slot id (a vector load, so that its wait does not hold up the loads behind it),
-    // the preflight's slot ids, q / k rows, value columns and gates, then the state block
+    // the preflight's slot ids, this thread's q / k rows, value columns and gates, then the
+    // state block
     const int s_v = __builtin_bit_cast(
         int, __builtin_amdgcn_raw_buffer_load_b32(
                  __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(slot_ids), 0, 4 * d.C, 0x00020000), 4 * c, 0,
                  0));
-    const LaneSlots lanes(slot_ids, d.C);
+    const LaneSlotsT<64> lanes(slot_ids, d.C);
     const int st_in = *status;
     const float *row = qkv + (int64_t)c * d.Ch;
-    v4f qk4 = {0.f, 0.f, 0.f, 0.f};
-    if (wave < 2 && lane < DK / 4)  // wave 0: q row, wave 1: k row of q/k head kh
-        qk4 = reinterpret_cast<const v4f *>(row + wave * d.Hk * DK + kh * DK)[lane];
+    float kq[RPL], qq[RPL];
+#pragma unroll
+    for (int e = 0; e < RPL; ++e) {
+        qq[e] = row[kh * DK + i0 + e];
+        kq[e] = row[d.Hk * DK + kh * DK + i0 + e];
+    }
     const v4f v = reinterpret_cast<const v4f *>(row + 2 * d.Hk * DK + h * DV + j0)[q];
     const float braw = beta_logits[(int64_t)c * gate_stride + h];
     const float araw = alpha_logits[(int64_t)c * gate_stride + h] + dt_bias[h];
@@ -194,78 +200,54 @@ __global__ __launch_bounds__(kThreads) void decode_step_kernel(
     const int s = __builtin_amdgcn_readfirstlane(s_v);
     const bool s_ok = s >= 0 && s < d.P;
     v4f *S4 = reinterpret_cast<v4f *>(state_pool + ((int64_t)(s_ok ? s : 0) * d.Hv + h) * DK * DV + j0) + q;
-    v4f sv[RPT];  // the state block (slot clamped into range; written back only if the step commits)
+    v4f sv[RPL];  // the state block (slot clamped into range; written back only if the step commits)
 #pragma unroll
-    for (int k = 0; k < RPT; ++k) sv[k] = S4[min(r + RG * k, DK - 1) * (DV / 4)];
+    for (int e = 0; e < RPL; ++e) sv[e] = S4[(i0 + e) * (DV / 4)];
 
-    if (wave < 2 && lane < DK / 4) reinterpret_cast<v4f *>(wave == 0 ? s_q : s_k)[lane] = qk4;
-    const int bits = slot_preflight<kThreads>(lanes, slot_ids, d.C, d.P, s_bitmap, &s_word);  // its barriers also publish s_q / s_k
+    const int bits = slot_preflight<64>(lanes, slot_ids, d.C, d.P, s_bitmap, &s_word);
     if (bits || st_in) {
-        if (bits && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) atomicOr(status, bits);
+        if (bits && blockIdx.x == 0 && blockIdx.y == 0 && lane == 0) atomicOr(status, bits);
         return;
     }
-    if (s < 0) return;  // padding lane (uniform over the workgroup)
+    if (s < 0) return;  // padding lane (uniform over the wave)
 
-    // |q|^2, |k|^2 and q . k, one wave each
-    if (wave < 3) {
-        const float *u = wave == 1 ? s_k : s_q;
-        const float *w = wave == 0 ? s_q : s_k;
-        float acc = 0.f;
-        for (int e = lane; e < DK; e += 64) acc = fmaf(u[e], w[e], acc);
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-        if (lane == 0) s_dot[wave] = acc;
-    }
-    lds_barrier();
-    const float rq = inv_norm(s_dot[0]), rk = inv_norm(s_dot[1]);
-    const float qk = s_dot[2] * rq * rk;  // q^ . k^
-
-    // column sums of k^_i S[i][j] and q^_i S[i][j] over this thread's rows, then over the
-    // row groups: lanes of a wave that share q, then the waves through LDS
+    // |q|^2, |k|^2, q . k and the column sums of k_i S[i][j], q_i S[i][j] over this thread's
+    // rows, then over the row groups (the lanes sharing q)
+    float ssq = 0.f, ssk = 0.f, sqk = 0.f;
     v4f pu = {0.f, 0.f, 0.f, 0.f}, pw = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < RPT; ++k) {
-        const int i = r + RG * k;
-        if (RG * RPT == DK || i < DK) {
-            pu += (s_k[i] * rk) * sv[k];
-            pw += (s_q[i] * rq) * sv[k];
-        }
+    for (int e = 0; e < RPL; ++e) {
+        ssq = fmaf(qq[e], qq[e], ssq);
+        ssk = fmaf(kq[e], kq[e], ssk);
+        sqk = fmaf(qq[e], kq[e], sqk);
+        pu += kq[e] * sv[e];
+        pw += qq[e] * sv[e];
     }
+    ssq = sum_lanes_sharing<Q4>(ssq);
+    ssk = sum_lanes_sharing<Q4>(ssk);
+    sqk = sum_lanes_sharing<Q4>(sqk);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         pu[e] = sum_lanes_sharing<Q4>(pu[e]);
         pw[e] = sum_lanes_sharing<Q4>(pw[e]);
     }
-    if (lane < Q4) {
-        s_part[wave][0][q] = pu;
-        s_part[wave][1][q] = pw;
-    }
-    lds_barrier();
-    v4f U = s_part[0][0][q], W = s_part[0][1][q];
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) {
-        U += s_part[w][0][q];
-        W += s_part[w][1][q];
-    }
+    const float rq = inv_norm(ssq), rk = inv_norm(ssk);
     // S' = g S;  delta = beta (v - S'^T k^);  S_new = S' + k^ delta^T;
     // o = S_new^T q^ / sqrt(d_k) = (g S^T q^ + (q^ . k^) delta) / sqrt(d_k)
     const float g = fast_exp(fast_softplus(araw) * Ah), beta = fast_sigmoid(braw);
-    const v4f delta = beta * (v - g * U);
+    const v4f delta = beta * (v - (g * rk) * pu);
 #pragma unroll
-    for (int k = 0; k < RPT; ++k) {
-        const int i = r + RG * k;
-        if (RG * RPT == DK || i < DK) __builtin_nontemporal_store(g * sv[k] + (s_k[i] * rk) * delta, S4 + i * (DV / 4));
-    }
+    for (int e = 0; e < RPL; ++e) __builtin_nontemporal_store(g * sv[e] + (kq[e] * rk) * delta, S4 + (i0 + e) * (DV / 4));
     if (r == 0)
         reinterpret_cast<v4f *>(out + ((int64_t)c * d.Hv + h) * DV + j0)[q] =
-            (g * W + qk * delta) * (1.0f / sqrtf((float)DK));
+            ((g * rq) * pw + (sqk * rq * rk) * delta) * (1.0f / sqrtf((float)DK));
 }
 
 template <int DK, int DV>
 hipError_t launch_decode(const Dims &d, const float *qkv, const float *beta_logits, const float *alpha_logits,
                          int64_t gate_stride, const float *dt_bias, const float *A, float *state_pool,
                          const int32_t *slot_ids, float *out, int32_t *status, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_step_kernel<DK, DV>), dim3(DecodeCfg<DK, DV>::NB * d.Hv, d.C), dim3(kThreads), 0,
+    hipLaunchKernelGGL((decode_step_kernel<DK, DV>), dim3(DecodeCfg<DK, DV>::NB * d.Hv, d.C), dim3(64), 0,
                        stream, d, qkv, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids, out,
                        status);
     return hipGetLastError();

@@ -102,7 +102,8 @@ struct LaneSlotsT {
     int v[kPerThread];
     __device__ LaneSlotsT(const int32_t *__restrict__ slot_ids, int C) {
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k) v[k] = slot_ids[min((int)threadIdx.x + THREADS * k, C - 1)];
+        for (int k = 0; k < kPerThread; ++k)  // (a uniform test: no load issued past the lane count)
+            v[k] = THREADS * k < C ? slot_ids[min((int)threadIdx.x + THREADS * k, C - 1)] : -1;
     }
 };
 
