@@ -820,7 +820,8 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs 
 // the verify workgroups of the same launch, so that these stores drain while the verify
 // workgroups compute.  Workgroup b covers lane b / blocks_per_lane and a block of
 // 4 * (kThreads / NP) channels; thread t covers node t / (kThreads / NP) and one 4-channel
-// group.  The window of node i is the last 3 sources of its extended sequence, oldest
+// group (NP = 8 for trees of at most 8 nodes, the pages' width-8 chains, else the verify's
+// padded node count).  The window of node i is the last 3 sources of its extended sequence, oldest
 // first: the tokens of its parent and grandparent, or the slot's newest history columns
 // in their place past the root, then the node's own tokens ("perf(qwen35): fuse the
 // DFlash2 concurrent verify Gated DeltaNet route", Optimizations, first bullet).
@@ -895,7 +896,9 @@ __global__ __launch_bounds__(kThreads) void conv_tree_verify_kernel(const Verify
     const int n_verify = NB * args.d.Hv * args.d.C;
     if ((int)blockIdx.x < n_verify)
         verify_body<DK, DV, NP, true, RAGGED, WIDE>(args);
-    else  // present only when the verify workgroups do not write the windows
+    else if (args.d.N <= 8)  // present only when the verify workgroups do not write the windows
+        window_body<8, RAGGED>(args, blockIdx.x - n_verify);  // chains of 8: a wave per node
+    else
         window_body<NP, RAGGED>(args, blockIdx.x - n_verify);
 }
 
@@ -910,8 +913,8 @@ hipError_t launch(const VerifyArgs &a, hipStream_t stream) {
     if (attr != hipSuccess) return attr;
     // fused: the window workgroups follow the verify workgroups
     const bool window_wgs = FUSED && !(WIDE && windows_in_verify(a.d));
-    const int grid = Ly::NB * a.d.Hv * a.d.C +
-                     (window_wgs ? a.d.C * ((a.d.Ch + 4 * (kThreads / NP) - 1) / (4 * (kThreads / NP))) : 0);
+    const int gpb = kThreads / (a.d.N <= 8 ? 8 : NP);  // window workgroups: 4-channel groups per workgroup
+    const int grid = Ly::NB * a.d.Hv * a.d.C + (window_wgs ? a.d.C * ((a.d.Ch + 4 * gpb - 1) / (4 * gpb)) : 0);
     if constexpr (FUSED)
         hipLaunchKernelGGL((conv_tree_verify_kernel<DK, DV, NP, RAGGED, WIDE>), dim3(grid), dim3(kThreads), lds, stream, a);
     else
