@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true", help="skip the CPU oracle and per-kernel loops")
+    ap.add_argument("--no-floor", action="store_true",
+                    help="skip the dispatch-floor launches (so a kernel trace holds only the kernels' real launches)")
     ap.add_argument("--eager", action="store_true", help="launch every call directly instead of replaying graphs")
     ap.add_argument("--route", choices=("fused", "split"), default="fused",
                     help="fused conv + verify call, or the separate conv step and verify calls")
@@ -686,6 +688,7 @@ def main():
         copy_ref = dict(bytes=8 * nb, us=round(copy_us, 3), gbs=round(8 * nb / (copy_us * 1e-6) / 1e9, 1),
                         what="torch device copy_ of the same byte count, 64 buffers, graph replay")
         del srcs, dsts, g
+    if not args.profile_only and not args.no_floor:
         # the dispatch floor on this machine: 64 launches of an empty one-workgroup kernel (torch's
         # clock spin for 0 cycles), and 64 launches of the fused kernel's own grid with every lane
         # a padding lane (its workgroups issue their slot-independent loads and return)
@@ -733,7 +736,7 @@ def main():
         bytes_per = kernel_bytes[dom]
         layers_per_launch = L if (dom == "replay_commit" and args.commit == "layers") else 1
         achieved = bytes_per / (kern[dom] * 1e-6) / 1e9
-        traffic = measured_traffic(wl.name, dom)
+        traffic = measured_traffic(wl.name + ("-split" if args.route == "split" else ""), dom)
         roofline = dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                         frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                         bytes_per_launch=int(bytes_per * layers_per_launch),
