@@ -84,8 +84,9 @@ __device__ inline v4f load4(__amdgpu_buffer_rsrc_t r, int byte_offset) {
 __host__ __device__ inline bool windows_in_verify(const Dims &d) { return d.C * d.Hv >= 512; }
 
 // WIDE: a workgroup covers all d_v columns of its value head (eight 16-column tiles, one per
-// wave, each over the whole of d_k) instead of 64 of them; see launch_np.
-template <int DK, int DV, int NP, bool FUSED, bool WIDE = false>
+// wave, each over the whole of d_k) instead of 64 of them; see launch_np.  WINV (fused, wide):
+// the verify workgroups also write the commit windows, so the staged rows stay until then.
+template <int DK, int DV, int NP, bool FUSED, bool WIDE = false, bool WINV = false>
 struct VerifyLayout {
     static constexpr int JB = WIDE ? DV : (DV < 64 ? DV : 64);  // value columns per workgroup
     static constexpr int NB = DV / JB;            // column blocks per head
@@ -121,7 +122,19 @@ struct VerifyLayout {
     static constexpr int STAGE = FUSED ? (NP + 3) * SXS : 0;
     static constexpr int GRAM_TILES = RT * NT;
     static constexpr int GPART = GW * GRAM_TILES * 256;
-    static constexpr int OFF_GRAM = FUSED && WIDE ? STAGE : 0;
+    // SPLIT: the state product [K; Q] x S0 as three bf16 products of hi/lo parts (see
+    // state_product), from the raw rows' bf16 parts [2NP][SXB] in LDS.  SPLIT_B (64-column blocks
+    // over at most 16 nodes): the parts are written during the conv, beside the scratch (two
+    // workgroups per CU still fit).  SPLIT_W (wide, windows written elsewhere, at most 16 nodes):
+    // they are converted after the conv into the staging area, dead by then, and the Gram
+    // partials follow them there.
+    static constexpr bool SPLIT_B = !WIDE && NP == 16 && DK % 32 == 0 && (DK / 32) % KP == 0;
+    static constexpr bool SPLIT_W = WIDE && !(FUSED && WINV) && NP == 16 && DK % 32 == 0;
+    static constexpr bool SPLIT = SPLIT_B || SPLIT_W;
+    static constexpr int SXB = DK + 8;  // bf16 row stride: 16 rows read with ds_read_b128 hit distinct banks
+    static constexpr int XHF = 2 * NP * SXB;  // floats of the hi and lo parts (two bf16 per float)
+    static constexpr int LC3 = SPLIT ? DK / 32 / KP : 0;  // state product: 32-wide chunks per wave
+    static constexpr int OFF_GRAM = FUSED && WIDE && WINV ? STAGE : (SPLIT_W ? XHF : 0);
     // state-product partials: unit u = wave u covers column tile u % CT and k part u / CT
     static constexpr int UNIT = RT * 256;
     static constexpr int OFF_UNIT = OFF_GRAM + GPART;
@@ -129,14 +142,8 @@ struct VerifyLayout {
     static constexpr int PARTS = OFF_GRAM + GPART + (WIDE ? 0 : kWaves * UNIT);
     static constexpr int SCR1 = STAGE > PARTS ? STAGE : PARTS;
     static constexpr int SCR = SCR1 > 2 * NP * SV ? SCR1 : 2 * NP * SV;  // also the epilogue's row staging
-    // SPLIT: the state product [K; Q] x S0 as three bf16 products of hi/lo parts (see
-    // state_product); the raw rows' bf16 parts [2NP][SXB] are staged beside XQK.  Used where
-    // the extra LDS keeps two workgroups per CU: 64-column blocks over at most 16 nodes.
-    static constexpr bool SPLIT = !WIDE && NP == 16 && DK % 32 == 0 && (DK / 32) % KP == 0;
-    static constexpr int SXB = DK + 8;  // bf16 row stride: 16 rows read with ds_read_b128 hit distinct banks
-    static constexpr int LC3 = SPLIT ? DK / 32 / KP : 0;  // state product: 32-wide chunks per wave
-    static constexpr int OFF_XH = OFF_SCR + SCR;          // hi parts, then lo parts (2 bf16 per float)
-    static constexpr int LDS_FLOATS = OFF_XH + (SPLIT ? 2 * NP * SXB : 0);
+    static constexpr int OFF_XH = SPLIT_W ? OFF_SCR : OFF_SCR + SCR;  // hi parts, then lo parts
+    static constexpr int LDS_FLOATS = OFF_SCR + SCR + (SPLIT_B ? XHF : 0);
     static_assert(4 * LDS_FLOATS <= 160 * 1024 - 2048, "LDS of one workgroup (with the static arrays)");
 };
 
@@ -182,9 +189,9 @@ __device__ inline void hist_columns(const v4f raw[3], v4f hc[3]) {
 
 // RAGGED: the caller passed per-lane node counts (without them every lane has N nodes and
 // the count costs nothing)
-template <int DK, int DV, int NP, bool FUSED, bool RAGGED, bool WIDE>
+template <int DK, int DV, int NP, bool FUSED, bool RAGGED, bool WIDE, bool WINV>
 __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
-    using Ly = VerifyLayout<DK, DV, NP, FUSED, WIDE>;
+    using Ly = VerifyLayout<DK, DV, NP, FUSED, WIDE, WINV>;
     static_assert(!WIDE || Ly::KP == 1, "wide: one wave per column tile");
     constexpr int JB = Ly::JB, NB = Ly::NB, CT = Ly::CT, NT = Ly::NT, RT = Ly::RT, KC = Ly::KC, LCG = Ly::LCG, KP = Ly::KP, LCQ = Ly::LCQ;
     constexpr int R = Ly::R, G = Ly::G, Q4 = Ly::Q4, SX = Ly::SX, SV = Ly::SV, SG = Ly::SG, SXS = Ly::SXS;
@@ -498,7 +505,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
                 const int row = isq ? NP + i : i;
                 *reinterpret_cast<v4f *>(XQK + row * SX + 4 * cg) = yq[u];
                 if ((cg & 15) == (DK / 4 < 16 ? DK / 4 : 16) - 1) s_ssq[row][cg >> 4] = ss;
-                if constexpr (Ly::SPLIT) {
+                if constexpr (Ly::SPLIT_B) {
                     const float y[4] = {yq[u].x, yq[u].y, yq[u].z, yq[u].w};
                     __bf16 hi[4], lo[4];
                     split_bf16(y, hi, lo);
@@ -605,7 +612,22 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
             if constexpr (Ly::NPART > 1) sq += s_ssq[tid][1];
             s_r[tid] = inv_norm(sq);
         }
+    } else if constexpr (Ly::SPLIT_W) {
+        // waves 4..7, beside the Gram products: the bf16 parts of the raw [K; Q] rows into the
+        // staging area, dead since the conv (16 floats of a row per thread)
+        constexpr int TPR = 256 / (2 * NP);  // threads per row
+        const int t = tid - 256, row = t / TPR, c0 = (t % TPR) * (DK / TPR);
+#pragma unroll
+        for (int k = 0; k < DK / TPR; k += 4) {
+            const v4f x = *reinterpret_cast<const v4f *>(XQK + row * SX + c0 + k);
+            const float y[4] = {x.x, x.y, x.z, x.w};
+            __bf16 hi[4], lo[4];
+            split_bf16(y, hi, lo);
+            *reinterpret_cast<bf4 *>(XH + row * Ly::SXB + c0 + k) = bf4{hi[0], hi[1], hi[2], hi[3]};
+            *reinterpret_cast<bf4 *>(XL + row * Ly::SXB + c0 + k) = bf4{lo[0], lo[1], lo[2], lo[3]};
+        }
     }
+    if constexpr (Ly::SPLIT_W) lds_barrier();  // the bf16 parts are complete
     state_product();
 
     // ---- fused, wide: waves 4..7, which have no Gram products, write the commit windows of
@@ -618,7 +640,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     //      q/k head), the value block is this workgroup's own.  No global load follows these
     //      stores.
     if constexpr (FUSED && WIDE) {
-        if (wv_u >= 4 && windows_in_verify(d)) {
+        if (wv_u >= 4 && WINV) {
             const int nshare = Hv / d.Hk;
             const int gq0 = (ws * G) / nshare, nq = ((ws + 1) * G) / nshare - gq0;
             const int cpn = 3 * (nq + Q4);  // chunks of one node
@@ -813,7 +835,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
 
 template <int DK, int DV, int NP, bool RAGGED, bool WIDE>
 __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs args) {
-    verify_body<DK, DV, NP, false, RAGGED, WIDE>(args);
+    verify_body<DK, DV, NP, false, RAGGED, WIDE, false>(args);
 }
 
 // Commit windows of the fused route, written by workgroups of their own that run beside
@@ -889,54 +911,68 @@ __device__ __forceinline__ void window_body(const VerifyArgs &args, int b) {
     }
 }
 
-template <int DK, int DV, int NP, bool RAGGED, bool WIDE>
+template <int DK, int DV, int NP, bool RAGGED, bool WIDE, bool WINV>
 __global__ __launch_bounds__(kThreads) void conv_tree_verify_kernel(const VerifyArgs args) {
-    constexpr int NB = VerifyLayout<DK, DV, NP, true, WIDE>::NB;
-    static_assert(kThreads * 12 <= VerifyLayout<DK, DV, NP, true, WIDE>::LDS_FLOATS, "window chunks fit the LDS");
+    constexpr int NB = VerifyLayout<DK, DV, NP, true, WIDE, WINV>::NB;
+    static_assert(kThreads * 12 <= VerifyLayout<DK, DV, NP, true, WIDE, WINV>::LDS_FLOATS, "window chunks fit the LDS");
     const int n_verify = NB * args.d.Hv * args.d.C;
     if ((int)blockIdx.x < n_verify)
-        verify_body<DK, DV, NP, true, RAGGED, WIDE>(args);
+        verify_body<DK, DV, NP, true, RAGGED, WIDE, WINV>(args);
     else if (args.d.N <= 8)  // present only when the verify workgroups do not write the windows
         window_body<8, RAGGED>(args, blockIdx.x - n_verify);  // chains of 8: a wave per node
     else
         window_body<NP, RAGGED>(args, blockIdx.x - n_verify);
 }
 
-template <int DK, int DV, int NP, bool FUSED, bool RAGGED, bool WIDE>
+template <int DK, int DV, int NP, bool FUSED, bool RAGGED, bool WIDE, bool WINV>
 hipError_t launch(const VerifyArgs &a, hipStream_t stream) {
-    using Ly = VerifyLayout<DK, DV, NP, FUSED, WIDE>;
+    using Ly = VerifyLayout<DK, DV, NP, FUSED, WIDE, WINV>;
     const size_t lds = sizeof(float) * Ly::LDS_FLOATS;
     // the LDS limit is a property of the kernel, set once (also keeps stream capture clean)
-    const void *kernel = FUSED ? reinterpret_cast<const void *>(&conv_tree_verify_kernel<DK, DV, NP, RAGGED, WIDE>)
+    const void *kernel = FUSED ? reinterpret_cast<const void *>(&conv_tree_verify_kernel<DK, DV, NP, RAGGED, WIDE, WINV>)
                                : reinterpret_cast<const void *>(&tree_verify_kernel<DK, DV, NP, RAGGED, WIDE>);
     static const hipError_t attr = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
     // fused: the window workgroups follow the verify workgroups
-    const bool window_wgs = FUSED && !(WIDE && windows_in_verify(a.d));
+    const bool window_wgs = FUSED && !(WIDE && WINV);
     const int gpb = kThreads / (a.d.N <= 8 ? 8 : NP);  // window workgroups: 4-channel groups per workgroup
     const int grid = Ly::NB * a.d.Hv * a.d.C + (window_wgs ? a.d.C * ((a.d.Ch + 4 * gpb - 1) / (4 * gpb)) : 0);
     if constexpr (FUSED)
-        hipLaunchKernelGGL((conv_tree_verify_kernel<DK, DV, NP, RAGGED, WIDE>), dim3(grid), dim3(kThreads), lds, stream, a);
+        hipLaunchKernelGGL((conv_tree_verify_kernel<DK, DV, NP, RAGGED, WIDE, WINV>), dim3(grid), dim3(kThreads), lds,
+                           stream, a);
     else
         hipLaunchKernelGGL((tree_verify_kernel<DK, DV, NP, RAGGED, WIDE>), dim3(grid), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
 }
 
-template <int DK, int DV, bool WIDE>
-hipError_t launch_wide(const VerifyArgs &a, hipStream_t stream) {
+// Fused wide launches whose grid spans two or more workgroups per CU have the verify
+// workgroups write the commit windows (windows_in_verify); otherwise window workgroups do.
+template <int DK, int DV, int NP, bool WIDE>
+hipError_t launch_variant(const VerifyArgs &a, hipStream_t stream) {
     const bool fused = a.x != nullptr;
     const bool ragged = a.lane_nodes != nullptr;
-    if (a.d.N <= 16)
-        return fused ? (ragged ? launch<DK, DV, 16, true, true, WIDE>(a, stream) : launch<DK, DV, 16, true, false, WIDE>(a, stream))
-                     : (ragged ? launch<DK, DV, 16, false, true, WIDE>(a, stream) : launch<DK, DV, 16, false, false, WIDE>(a, stream));
-    return fused ? (ragged ? launch<DK, DV, 32, true, true, WIDE>(a, stream) : launch<DK, DV, 32, true, false, WIDE>(a, stream))
-                 : (ragged ? launch<DK, DV, 32, false, true, WIDE>(a, stream) : launch<DK, DV, 32, false, false, WIDE>(a, stream));
+    if (!fused)
+        return ragged ? launch<DK, DV, NP, false, true, WIDE, false>(a, stream)
+                      : launch<DK, DV, NP, false, false, WIDE, false>(a, stream);
+    if constexpr (WIDE)
+        if (windows_in_verify(a.d))
+            return ragged ? launch<DK, DV, NP, true, true, true, true>(a, stream)
+                          : launch<DK, DV, NP, true, false, true, true>(a, stream);
+    return ragged ? launch<DK, DV, NP, true, true, WIDE, false>(a, stream)
+                  : launch<DK, DV, NP, true, false, WIDE, false>(a, stream);
+}
+
+template <int DK, int DV, bool WIDE>
+hipError_t launch_wide(const VerifyArgs &a, hipStream_t stream) {
+    return a.d.N <= 16 ? launch_variant<DK, DV, 16, WIDE>(a, stream) : launch_variant<DK, DV, 32, WIDE>(a, stream);
 }
 
 // The q/k conv, norms, Gram products and tree algebra of a (lane, value head) are repeated by
 // each of its column blocks.  While the grid fits the chip in one pass (C * H_v < 256) the
 // 64-column blocks give the parallelism; beyond it the launch is bound by arithmetic and one
 // workgroup per (lane, value head) over all 128 columns does a third less of it per byte.
+// (Between 128 and 256, where some CUs run two 64-column workgroups, the wide workgroups were
+// measured slower even with the split state product: 10.1 against 9.6 us on 5 lanes x 32 heads.)
 template <int DK, int DV>
 hipError_t launch_np(const VerifyArgs &a, hipStream_t stream) {
     if constexpr (DV == 128)

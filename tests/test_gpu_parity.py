@@ -88,6 +88,10 @@ SWEEP = [
     (3, 31, 5, 2, 4, 64, 32, True),
     (5, 12, 9, 3, 3, 32, 128, True),
     (2, 16, 2, 4, 8, 128, 32, True),
+    # 256 <= C * H_v < 512 with d_v = 128 and at most 16 nodes: one workgroup per (lane, value
+    # head), split state product, window workgroups
+    (9, 13, 10, 8, 32, 128, 128, True),
+    (7, 16, 8, 4, 40, 32, 128, True),
     # C * H_v >= 256 with d_v = 128: one workgroup per (lane, value head) over all columns
     (8, 16, 9, 16, 32, 128, 128, True),
     (16, 9, 16, 4, 16, 64, 128, True),
