@@ -25,6 +25,21 @@ __device__ inline void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+
+// x = hi + lo + r with hi = bf16(x), lo = bf16(x - hi) (round to nearest even) and
+// |r| <= 2^-18 |x|: three bf16 products hi.hi + hi.lo + lo.hi, accumulated in float32, give a
+// product to about 2^-17 relative (the dropped lo.lo and r terms)
+template <int K>
+__device__ inline void split_bf16(const float (&x)[K], __bf16 (&h)[K], __bf16 (&l)[K]) {
+#pragma unroll
+    for (int e = 0; e < K; ++e) {
+        h[e] = (__bf16)x[e];
+        l[e] = (__bf16)(x[e] - (float)h[e]);
+    }
+}
+
 // 1 / max(|x|, 1e-6) from |x|^2, and the gate nonlinearities, on the hardware
 // transcendental units (about 1 ulp each; the outputs they feed carry a 2e-4 tolerance)
 __device__ inline float inv_norm(float sq) { return fminf(__builtin_amdgcn_rsqf(sq), 1e6f); }

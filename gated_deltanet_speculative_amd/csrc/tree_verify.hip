@@ -147,21 +147,6 @@ struct VerifyLayout {
     static_assert(4 * LDS_FLOATS <= 160 * 1024 - 2048, "LDS of one workgroup (with the static arrays)");
 };
 
-typedef __bf16 bf4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
-
-// x = hi + lo + r with hi = bf16(x), lo = bf16(x - hi) (round to nearest even) and
-// |r| <= 2^-18 |x|: three bf16 products hi.hi + hi.lo + lo.hi, accumulated in float32, give a
-// product to about 2^-17 relative (the dropped lo.lo and r terms)
-template <int K>
-__device__ inline void split_bf16(const float (&x)[K], __bf16 (&h)[K], __bf16 (&l)[K]) {
-#pragma unroll
-    for (int e = 0; e < K; ++e) {
-        h[e] = (__bf16)x[e];
-        l[e] = (__bf16)(x[e] - (float)h[e]);
-    }
-}
-
 // Tree conv + SiLU of 4 channels at one node from its sources, oldest first (x3 = the
 // node's own tokens); w[e] holds the 4 taps of channel e (tap 0 = oldest), summed from
 // the oldest source.
