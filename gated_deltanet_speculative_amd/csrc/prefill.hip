@@ -71,6 +71,7 @@ __device__ inline int tile_index(int i, int a) { return (16 * (i >> 2) + a) * 4 
 // a store there is dropped, without a memory access.
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kNonTemporal = 2;  // cache-policy operand of the buffer stores: nt
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 __device__ inline __amdgpu_buffer_rsrc_t rsrc(const float *base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, bytes, kRsrcWord3);
@@ -272,6 +273,7 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     __shared__ int s_word;
     __shared__ __align__(16) float QK[2][2 * BC * SX];  // per buffer: q rows, then k rows
     __shared__ __align__(16) float PK[2][LP_FLOATS];
+    __shared__ __align__(16) float OT[2][BC * JB];      // per buffer: a chunk's output rows of the block
 
     const int n_groups = d.C * d.Hk;
     const int grp = blockIdx.x % n_groups, ws = blockIdx.x / n_groups;
@@ -339,8 +341,23 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     }
     if (s < 0) return;  // padding lane (uniform over the workgroup)
 
-    for (int jc = 0; jc < nch; ++jc) {
+    // a chunk's outputs wait in OT[jc % 2] until the next barrier, then every thread stores a
+    // 16-byte piece of whole rows of the block (JB consecutive floats of a row): a row's lines
+    // are written by one store instruction instead of a 64-byte segment by each of CT waves
+    constexpr int OG = JB / 4;  // 16-byte pieces of a block row
+    const int o_row = tid / OG, o_grp = tid - o_row * OG;
+    const int o_off = (o_row * HvDV + h * DV + j0 + 4 * o_grp) * 4;
+    auto store_outputs = [&](int jc) {
         const int k0 = jc * BC, nc = min(BC, T - k0);
+        if (tid < BC * OG) {
+            const v4f ov = *reinterpret_cast<const v4f *>(&OT[jc & 1][o_row * JB + 4 * o_grp]);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, ov), rsrc(chunk_base(out, HvDV, k0), nc * HvDV * 4),
+                                                   o_off, 0, kNonTemporal);
+        }
+    };
+
+    for (int jc = 0; jc < nch; ++jc) {
+        const int k0 = jc * BC;
         float *Qb = QK[jc & 1], *Kb = Qb + BC * SX, *Pb = PK[jc & 1];
         rows.stage(Qb);
         if (tid < kPkGroups) *reinterpret_cast<v4f *>(Pb + pk_lds) = pkn;
@@ -350,6 +367,7 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
             rows.load(rsrc(chunk_base(qkv, Ch, k0 + BC), min(BC, T - k0 - BC) * Ch * 4));
             load_chunk(jc + 1);
         }
+        if (jc > 0) store_outputs(jc - 1);  // complete since the barrier
         if (wave < CT) {
             // [K; Q] S, the operands read ahead of the products
             v4f ak[KC], aq[KC];
@@ -387,7 +405,6 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
             }
             const v4f dl = mfma4(tf, rhs, v4f{0.f, 0.f, 0.f, 0.f});
             o = mfma4(cf, dl, o);
-            const __amdgpu_buffer_rsrc_t orr = rsrc(chunk_base(out, HvDV, k0), nc * HvDV * 4);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 if constexpr (GATED) {
@@ -397,7 +414,7 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
                 // (the element goes through a scalar: this compiler's __builtin_bit_cast of a vector
                 // element lvalue reads element 0 whatever the index)
                 const float ov = o[v];
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), orr, zo[v], 0, kNonTemporal);
+                OT[jc & 1][(4 * g4 + v) * JB + 16 * cw + l16] = ov;
                 bw[v] = pw[v] * dl[v];
             }
             // S <- G_B S + K^T diag(w) D, tile by tile of 16 d_k rows
@@ -405,6 +422,9 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
             for (int rt = 0; rt < KC; ++rt) sreg[rt] = mfma4(kt[rt], bw, gend * sreg[rt]);
         }
     }
+
+    lds_barrier();
+    store_outputs(nch - 1);
 
     // ---- the slot's state, in place
     if (wave < CT) {
