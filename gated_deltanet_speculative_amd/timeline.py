@@ -15,8 +15,11 @@ changed, and nothing in the library loads this build.
 `run` (on the GPU) replays the launch over the workload's layer instances as the bench
 does, reads the stamps of the last launch and prints, per phase, the median, p10 and p90
 over the verify workgroups.  The shader clock runs per XCD, so only differences within one
-workgroup are meaningful.  The stamps cost time themselves (each waits for the LDS
-counters); the launch time printed last is the instrumented one.
+workgroup are meaningful; the constant clock is common to the chip and places every
+workgroup's start and end (verify and window workgroups) on one time line.  Wave 4 also
+stamps the start of its state product, once its state chunks are all back (it waits for
+them there anyway).  The stamps cost time themselves (each waits
+for the LDS counters); the launch time printed last is the instrumented one.
 """
 
 from __future__ import annotations
@@ -49,6 +52,9 @@ _STAMP_DEFS = f"""
 __device__ unsigned long long gdn_tl_stamps[GDN_TL_MAX_WG][16];
 #define GDN_STAMP(k) do {{ if (threadIdx.x == 0 && blockIdx.x < GDN_TL_MAX_WG) \\
     __builtin_nontemporal_store(__builtin_amdgcn_s_memtime(), &gdn_tl_stamps[blockIdx.x][k]); }} while (0)
+#define GDN_STAMP_ARRIVAL(r) do {{ if (threadIdx.x == 256 && blockIdx.x < GDN_TL_MAX_WG) {{ \
+    asm volatile("" :: "v"(r[0][0]), "v"(r[LCQ - 1][3])); \
+    __builtin_nontemporal_store(__builtin_amdgcn_s_memtime(), &gdn_tl_stamps[blockIdx.x][11]); }} }} while (0)
 #define GDN_RSTAMP(k) do {{ if (threadIdx.x == 0 && blockIdx.x < GDN_TL_MAX_WG) \\
     __builtin_nontemporal_store(__builtin_amdgcn_s_memrealtime(), &gdn_tl_stamps[blockIdx.x][k]); }} while (0)
 extern "C" int gdn_timeline_read(unsigned long long *host) {{
@@ -80,6 +86,7 @@ def _instrument(src: str) -> str:
     close = part.rindex("}\n", 0, part.rindex("template <int DK, int DV, int NP, bool RAGGED, bool WIDE>"))
     part = part[:close] + "    GDN_STAMP(10); GDN_RSTAMP(13);\n" + part[close:]
     src = src[:body] + part + src[end:]
+    sub("    auto state_product = [&]() {\n", "    auto state_product = [&]() {\n        GDN_STAMP_ARRIVAL(sreg);\n")
     sub("    const Dims d = args.d;\n    // every kernel argument used for an address",
         "    GDN_STAMP(0); GDN_RSTAMP(12);\n    const Dims d = args.d;\n    // every kernel argument used for an address")
     sub("    // fused: stage the raw token rows for the tree conv\n",
@@ -87,7 +94,7 @@ def _instrument(src: str) -> str:
     sub("    constexpr int GPB = kThreads / NP;  // 4-channel groups per workgroup\n",
         "    constexpr int GPB = kThreads / NP;  // 4-channel groups per workgroup\n    GDN_STAMP(0); GDN_RSTAMP(12);\n")
     wb = src.index("void window_body")
-    wend = src.index("__global__ __launch_bounds__(kThreads) void conv_tree_verify_kernel")
+    wend = src.index("void conv_tree_verify_kernel(")
     wclose = src.rindex("}\n", wb, src.rindex("template", wb, wend))
     src = src[:wclose] + "    GDN_STAMP(10); GDN_RSTAMP(13);\n" + src[wclose:]
     return src
@@ -189,6 +196,20 @@ def run(workload: str, instances: int) -> None:
         prev = s[:, slot]
     span = (s[:, 10] - s[:, 0]) / per_us
     print(f"{'whole body':32s} {np.median(span):7.2f} {np.percentile(span, 10):7.2f} {np.percentile(span, 90):7.2f}")
+    arr = (s[:, 11] - s[:, 2]) / per_us
+    print(f"{'state product starts, from staging':32s} {np.median(arr):7.2f} {np.percentile(arr, 10):7.2f} "
+          f"{np.percentile(arr, 90):7.2f}  (wave 4)")
+    # the common clock: every workgroup's start and end against the first start of the launch
+    n_window = 0 if (wide and C * Hv >= 512) else C * -(-Ch // (4 * (512 // (8 if N <= 8 else (16 if N <= 16 else 32)))))
+    allw = stamps[:n_verify + n_window].astype(np.int64)
+    t0 = allw[:, 12].min()
+    print(f"{'common clock (us from first start)':36s} {'start p10/p50/p90':>20s} {'end p10/p50/p90':>20s}")
+    for name, blk in (("verify workgroups", allw[:n_verify]), ("window workgroups", allw[n_verify:])):
+        if len(blk) == 0:
+            continue
+        st, en = (blk[:, 12] - t0) / 100.0, (blk[:, 13] - t0) / 100.0
+        print(f"{name:36s} {np.percentile(st, 10):6.2f} {np.median(st):6.2f} {np.percentile(st, 90):6.2f} "
+              f"{np.percentile(en, 10):6.2f} {np.median(en):6.2f} {np.percentile(en, 90):6.2f}  (last {en.max():.2f})")
     print(f"instrumented launch: {e0.elapsed_time(e1) * 1e3 / instances:.2f} us (graph of {instances})")
 
 

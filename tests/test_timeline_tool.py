@@ -16,5 +16,7 @@ def test_instrumentation_inserts_every_stamp():
     stamps = re.findall(r"GDN_STAMP\((\d+)\);", out)
     # verify body: entry, first loads, six barriers, end; window body: entry, end
     assert sorted(int(k) for k in stamps) == sorted([0, 1, 2, 3, 4, 5, 6, 7, 10, 0, 10])
-    stripped = re.sub(r"^[ \t]*GDN_R?STAMP\(\d+\);( GDN_R?STAMP\(\d+\);)?\n", "", out, flags=re.M)
+    assert out.count("GDN_STAMP_ARRIVAL(sreg);") == 1
+    stripped = re.sub(r"^[ \t]*(GDN_R?STAMP\(\d+\);( GDN_R?STAMP\(\d+\);)?|GDN_STAMP_ARRIVAL\(sreg\);)\n", "", out,
+                      flags=re.M)
     assert stripped.replace(timeline._STAMP_DEFS + "\n", "") == src
