@@ -264,6 +264,31 @@ def cpu_baseline_prefill(wl, seconds, seed, tokens=32):
                        f"fp64 numpy, 1 BLAS thread, {t_used:.1f} s", **host_description())
 
 
+def copy_reference(nbytes, dev):
+    """A plain device copy moving `nbytes` (half read, half written): 64 back-to-back copies of
+    distinct buffers replayed as a graph; microseconds per copy and the rate."""
+    import torch
+
+    nb = int(nbytes) // 8
+    srcs = [torch.ones(nb, dtype=torch.float32, device=dev) for _ in range(64)]
+    dsts = [torch.empty(nb, dtype=torch.float32, device=dev) for _ in range(64)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for d_, s_ in zip(dsts, srcs):
+            d_.copy_(s_)
+    g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(5):
+        g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    copy_us = ev0.elapsed_time(ev1) * 1e3 / (5 * 64)
+    return dict(bytes=8 * nb, us=round(copy_us, 3), gbs=round(8 * nb / (copy_us * 1e-6) / 1e9, 1),
+                what="torch device copy_ of the same byte count, 64 buffers, graph replay")
+
+
 def decode_main(args):
     """The plain decode step at the workload's head shape: one token per lane, for every
     layer instance the conv step (history written in place) and the one-token recurrence
@@ -338,6 +363,8 @@ def decode_main(args):
     assert int(status.item()) == 0, "device status bits set"
     calibrate_copy(args.calibrate_copy, dev)
     kb = decode_bytes(wl)
+    # context for the recurrence: a plain copy of its bytes (the state block read and written)
+    copy_ref = None if args.profile_only else copy_reference(kb["decode_step"], dev)
     roofline = None
     if kern:
         dom = max(kern, key=lambda k: kern[k])
@@ -366,6 +393,7 @@ def decode_main(args):
         "step_gbs": round(L * (kb["conv_step"] + kb["decode_step"]) / (ms_step * 1e-3) / 1e9, 1),
         "kernel_us": {k: round(v, 3) for k, v in kern.items()},
         "kernel_gbs": {k: round(kb[k] / (kern[k] * 1e-6) / 1e9, 1) for k in kern},
+        "copy_same_bytes": copy_ref,
         "roofline": roofline,
         "cpu_baseline": (None if args.no_cpu_baseline or args.profile_only
                          else cpu_baseline_decode(wl, args.cpu_seconds, args.seed)),
@@ -673,21 +701,7 @@ def main():
         # context for the dominant kernel's fraction: a plain device copy moving the same
         # number of bytes (read + write), 64 back-to-back copies of distinct buffers replayed
         # as a graph, and an empty graph replay's cost per launch of a one-kernel graph
-        nb = int(kernel_bytes_est["conv_tree_verify" if args.route == "fused" else "tree_verify"]) // 8
-        srcs = [torch.ones(nb, dtype=torch.float32, device=dev) for _ in range(64)]
-        dsts = [torch.empty(nb, dtype=torch.float32, device=dev) for _ in range(64)]
-        g = capture(lambda: [d_.copy_(s_) for d_, s_ in zip(dsts, srcs)])
-        g.replay()
-        torch.cuda.synchronize()
-        ev0.record()
-        for _ in range(5):
-            g.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-        copy_us = ev0.elapsed_time(ev1) * 1e3 / (5 * 64)
-        copy_ref = dict(bytes=8 * nb, us=round(copy_us, 3), gbs=round(8 * nb / (copy_us * 1e-6) / 1e9, 1),
-                        what="torch device copy_ of the same byte count, 64 buffers, graph replay")
-        del srcs, dsts, g
+        copy_ref = copy_reference(kernel_bytes_est["conv_tree_verify" if args.route == "fused" else "tree_verify"], dev)
     if not args.profile_only and not args.no_floor:
         # the dispatch floor on this machine: 64 launches of an empty one-workgroup kernel (torch's
         # clock spin for 0 cycles), and 64 launches of the fused kernel's own grid with every lane

@@ -39,6 +39,8 @@ def test_bench_line(extra, workload):
     assert abs(rl["achieved"] - rl["bytes_per_launch"] / (rl["us_per_launch"] * 1e3)) / rl["achieved"] < 1e-2
     if "lanes8" in workload:
         assert d["config"]["lanes"] == 8 and d["config"]["slots"] == 8
+    cp = d["copy_same_bytes"]  # a plain copy of the dominant kernel's bytes in the same run
+    assert cp["bytes"] > 0 and cp["us"] > 0 and abs(cp["bytes"] - rl["bytes_per_launch"]) <= 8
     if "decode" not in workload:  # the dispatch floor of this machine, beside the kernel times
         fl = d["dispatch_floor"]
         assert 0 < fl["empty_kernel_us"] < fl["padding_lanes_same_grid_us"] < rl["us_per_launch"]
