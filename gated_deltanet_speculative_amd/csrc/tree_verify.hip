@@ -125,12 +125,15 @@ struct VerifyLayout {
     // SPLIT: the state product [K; Q] x S0 as three bf16 products of hi/lo parts (see
     // state_product), from the raw rows' bf16 parts [2NP][SXB] in LDS.  SPLIT_B (64-column blocks
     // over at most 16 nodes): the parts are written during the conv, beside the scratch (two
-    // workgroups per CU still fit).  SPLIT_W (wide, windows written elsewhere, at most 16 nodes):
-    // they are converted after the conv into the staging area, dead by then, and the Gram
-    // partials follow them there.
+    // workgroups per CU still fit).  SPLIT_W (wide, windows written elsewhere): waves 4..7
+    // convert them beside the Gram products into the staging area, dead after the conv, and the
+    // Gram partials follow them there.  SPLIT_R (wide, windows written by the verify
+    // workgroups, so the staging area stays in use and the LDS is full): each wave splits the
+    // fp32 rows it reads in registers instead.
     static constexpr bool SPLIT_B = !WIDE && NP == 16 && DK % 32 == 0 && (DK / 32) % KP == 0;
-    static constexpr bool SPLIT_W = WIDE && !(FUSED && WINV) && NP == 16 && DK % 32 == 0;
-    static constexpr bool SPLIT = SPLIT_B || SPLIT_W;
+    static constexpr bool SPLIT_W = WIDE && !(FUSED && WINV) && DK % 32 == 0;
+    static constexpr bool SPLIT_R = WIDE && FUSED && WINV && DK % 32 == 0;
+    static constexpr bool SPLIT = SPLIT_B || SPLIT_W || SPLIT_R;
     static constexpr int SXB = DK + 8;  // bf16 row stride: 16 rows read with ds_read_b128 hit distinct banks
     static constexpr int XHF = 2 * NP * SXB;  // floats of the hi and lo parts (two bf16 per float)
     static constexpr int LC3 = SPLIT ? DK / 32 / KP : 0;  // state product: 32-wide chunks per wave
@@ -428,6 +431,62 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
         }
     }
 
+    // SPLIT_W: the bf16 parts of the raw [K; Q] rows, by 256 threads (t = 0..255), TPR of them
+    // per row
+    auto convert_rows = [&](int t) {
+        constexpr int TPR = 256 / (2 * NP) < DK / 4 ? 256 / (2 * NP) : DK / 4;  // threads per row
+        if (t >= 2 * NP * TPR) return;
+        const int row = t / TPR, c0 = (t % TPR) * (DK / TPR);
+#pragma unroll
+        for (int k = 0; k < DK / TPR; k += 4) {
+            const v4f x = *reinterpret_cast<const v4f *>(XQK + row * SX + c0 + k);
+            const float y[4] = {x.x, x.y, x.z, x.w};
+            __bf16 hi[4], lo[4];
+            split_bf16(y, hi, lo);
+            *reinterpret_cast<bf4 *>(XH + row * Ly::SXB + c0 + k) = bf4{hi[0], hi[1], hi[2], hi[3]};
+            *reinterpret_cast<bf4 *>(XL + row * Ly::SXB + c0 + k) = bf4{lo[0], lo[1], lo[2], lo[3]};
+        }
+    };
+    // ---- fused, wide, windows by the verify workgroups: waves 4..7, which have no Gram
+    //      products, write the commit windows of the workgroup's channels from the staged rows.  The window of node i and channel e
+    //      is (oldest first) its second and first nearest sources and its own token, 3 floats;
+    //      4 channels take 12 consecutive floats, stored as three 16-byte chunks (flat float f
+    //      of a group = source f % 3 of channel f / 3).  Lane l takes chunk l + 64m of a node's
+    //      row of chunks, so a store instruction writes consecutive chunks.  The q/k slab's
+    //      channel groups are split over the workgroups that share it (the value heads of the
+    //      q/k head), the value block is this workgroup's own.  No global load follows these
+    //      stores.
+    auto write_windows = [&]() {
+        const int nshare = Hv / d.Hk;
+        const int gq0 = (ws * G) / nshare, nq = ((ws + 1) * G) / nshare - gq0;
+        const int cpn = 3 * (nq + Q4);  // chunks of one node
+        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+            args.commit_win + (int64_t)c * N * d.Ch * 3, 0, nvc * d.Ch * 12, kRsrcWord3);
+        for (int m = 0; 64 * m < cpn; ++m) {
+            const int r = lane + 64 * m, gg = r / 3, p = r - 3 * gg;
+            const bool slab = gg < nq;
+            const int g = slab ? gq0 + gg : min(gg - nq, Q4 - 1);
+            const int col = slab ? 4 * g : 2 * DK + 4 * g;
+            const int ch = slab ? (g < DK / 4 ? kh * DK + 4 * g : d.Hk * DK + kh * DK + 4 * (g - DK / 4))
+                                : 2 * d.Hk * DK + h * DV + j0 + 4 * g;
+            const int gofs = r < cpn ? ch * 12 + 16 * p : kOutOfRange;
+            for (int i = wv_u - 4; i < nvc; i += 4) {
+                const int sr = s_src[i];
+                const int rb[3] = {((sr >> 8) & 255) * SXS + col, ((sr >> 16) & 255) * SXS + col, i * SXS + col};
+                float w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int f = 4 * p + e, src = f % 3;  // p + e = f mod 3
+                    w[e] = stg[(src == 0 ? rb[0] : src == 1 ? rb[1] : rb[2]) + f / 3];
+                }
+                const v4f chunk = {w[0], w[1], w[2], w[3]};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, chunk), wr,
+                                                       gofs < kOutOfRange ? i * d.Ch * 12 + gofs : kOutOfRange, 0,
+                                                       kNonTemporal);
+            }
+        }
+    };
+
     // ---- conv + SiLU (fused) of the block's channels, or the loaded conv rows as they are:
     //      raw q/k rows into XQK with their squared norms, value rows into Vl
     {
@@ -531,9 +590,20 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
                 const bf8 vbl = {bl[0], bl[1], bl[2], bl[3], bl[4], bl[5], bl[6], bl[7]};
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
-                    const int off = (16 * rt + l16) * Ly::SXB + 32 * m + 8 * g4;
-                    const bf8 ah = *reinterpret_cast<const bf8 *>(XH + off);
-                    const bf8 al = *reinterpret_cast<const bf8 *>(XL + off);
+                    bf8 ah, al;
+                    if constexpr (Ly::SPLIT_R) {
+                        const float *xr = XQK + (16 * rt + l16) * SX + 32 * m + 8 * g4;
+                        const v4f a0 = *reinterpret_cast<const v4f *>(xr), a1 = *reinterpret_cast<const v4f *>(xr + 4);
+                        const float xa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                        __bf16 h[8], l[8];
+                        split_bf16(xa, h, l);
+                        ah = bf8{h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]};
+                        al = bf8{l[0], l[1], l[2], l[3], l[4], l[5], l[6], l[7]};
+                    } else {
+                        const int off = (16 * rt + l16) * Ly::SXB + 32 * m + 8 * g4;
+                        ah = *reinterpret_cast<const bf8 *>(XH + off);
+                        al = *reinterpret_cast<const bf8 *>(XL + off);
+                    }
                     acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, vbh, acc[rt], 0, 0, 0);
                     acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, vbl, acc[rt], 0, 0, 0);
                     acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, vbh, acc[rt], 0, 0, 0);
@@ -599,63 +669,13 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
         }
     } else if constexpr (Ly::SPLIT_W) {
         // waves 4..7, beside the Gram products: the bf16 parts of the raw [K; Q] rows into the
-        // staging area, dead since the conv (16 floats of a row per thread)
-        constexpr int TPR = 256 / (2 * NP);  // threads per row
-        const int t = tid - 256, row = t / TPR, c0 = (t % TPR) * (DK / TPR);
-#pragma unroll
-        for (int k = 0; k < DK / TPR; k += 4) {
-            const v4f x = *reinterpret_cast<const v4f *>(XQK + row * SX + c0 + k);
-            const float y[4] = {x.x, x.y, x.z, x.w};
-            __bf16 hi[4], lo[4];
-            split_bf16(y, hi, lo);
-            *reinterpret_cast<bf4 *>(XH + row * Ly::SXB + c0 + k) = bf4{hi[0], hi[1], hi[2], hi[3]};
-            *reinterpret_cast<bf4 *>(XL + row * Ly::SXB + c0 + k) = bf4{lo[0], lo[1], lo[2], lo[3]};
-        }
+        // staging area, dead since the conv
+        convert_rows(tid - 256);
     }
     if constexpr (Ly::SPLIT_W) lds_barrier();  // the bf16 parts are complete
     state_product();
-
-    // ---- fused, wide: waves 4..7, which have no Gram products, write the commit windows of
-    //      the workgroup's channels from the staged rows.  The window of node i and channel e
-    //      is (oldest first) its second and first nearest sources and its own token, 3 floats;
-    //      4 channels take 12 consecutive floats, stored as three 16-byte chunks (flat float f
-    //      of a group = source f % 3 of channel f / 3).  Lane l takes chunk l + 64m of a node's
-    //      row of chunks, so a store instruction writes consecutive chunks.  The q/k slab's
-    //      channel groups are split over the workgroups that share it (the value heads of the
-    //      q/k head), the value block is this workgroup's own.  No global load follows these
-    //      stores.
-    if constexpr (FUSED && WIDE) {
-        if (wv_u >= 4 && WINV) {
-            const int nshare = Hv / d.Hk;
-            const int gq0 = (ws * G) / nshare, nq = ((ws + 1) * G) / nshare - gq0;
-            const int cpn = 3 * (nq + Q4);  // chunks of one node
-            const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-                args.commit_win + (int64_t)c * N * d.Ch * 3, 0, nvc * d.Ch * 12, kRsrcWord3);
-            for (int m = 0; 64 * m < cpn; ++m) {
-                const int r = lane + 64 * m, gg = r / 3, p = r - 3 * gg;
-                const bool slab = gg < nq;
-                const int g = slab ? gq0 + gg : min(gg - nq, Q4 - 1);
-                const int col = slab ? 4 * g : 2 * DK + 4 * g;
-                const int ch = slab ? (g < DK / 4 ? kh * DK + 4 * g : d.Hk * DK + kh * DK + 4 * (g - DK / 4))
-                                    : 2 * d.Hk * DK + h * DV + j0 + 4 * g;
-                const int gofs = r < cpn ? ch * 12 + 16 * p : kOutOfRange;
-                for (int i = wv_u - 4; i < nvc; i += 4) {
-                    const int sr = s_src[i];
-                    const int rb[3] = {((sr >> 8) & 255) * SXS + col, ((sr >> 16) & 255) * SXS + col, i * SXS + col};
-                    float w[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int f = 4 * p + e, src = f % 3;  // p + e = f mod 3
-                        w[e] = stg[(src == 0 ? rb[0] : src == 1 ? rb[1] : rb[2]) + f / 3];
-                    }
-                    const v4f chunk = {w[0], w[1], w[2], w[3]};
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, chunk), wr,
-                                                           gofs < kOutOfRange ? i * d.Ch * 12 + gofs : kOutOfRange, 0,
-                                                           kNonTemporal);
-                }
-            }
-        }
-    }
+    if constexpr (FUSED && WIDE && WINV)
+        if (wv_u >= 4) write_windows();
     lds_barrier();
 
     // ---- decayed, ancestor-masked, norm-scaled coefficients and per-node scales
@@ -717,31 +737,33 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4) Lr[k4] = *reinterpret_cast<const v4f *>(Lm + i * SG + 4 * k4);
         Tm[i * SG + a] = bcast_solve(i == a ? 1.f : 0.f, Lr, std::make_integer_sequence<int, 16>());
-    } else if (wv_u == 4) {
-        if (lane < NP) {
-            // one column per lane; row i + 1 of Lm is read while row i is being solved
-            const int a = lane;
-            float t[NP];
-            v4f cur[NP / 4], nxt[NP / 4];
-            cur[0] = *reinterpret_cast<const v4f *>(Lm);
+    } else {
+        // 32 nodes, waves 4..7: the diagonal 16 x 16 blocks T11 = (I + L11)^-1 and
+        // T22 = (I + L22)^-1 by the same substitution (block pb on pass pb), T12 = 0; then
+        // T21 = -T22 L21 T11 below
 #pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                if (i + 1 < NP)
+        for (int pb = 0; pb < 2; ++pb) {
+            const int a = 4 * (wv_u - 4) + (lane >> 4), i = lane & 15, o = 16 * pb;
+            v4f Lr[4];
 #pragma unroll
-                    for (int m4 = 0; m4 <= (i + 1) / 4; ++m4)
-                        nxt[m4] = *reinterpret_cast<const v4f *>(Lm + (i + 1) * SG + 4 * m4);
-                float s0 = 0.f, s1 = 0.f;
+            for (int k4 = 0; k4 < 4; ++k4) Lr[k4] = *reinterpret_cast<const v4f *>(Lm + (o + i) * SG + o + 4 * k4);
+            Tm[(o + i) * SG + o + a] = bcast_solve(i == a ? 1.f : 0.f, Lr, std::make_integer_sequence<int, 16>());
+            if (pb == 0) Tm[i * SG + 16 + a] = 0.f;
+        }
+    }
+    if constexpr (NP == 32) lds_barrier();  // the diagonal blocks of T are complete
+    if constexpr (NP == 32) {
+        // wave 4: M = L21 T11, then T21 = -T22 M (two 16 x 16 products; the accumulator of the
+        // first is the right operand of the second)
+        if (wv_u == 4) {
+            v4f t11;
 #pragma unroll
-                for (int m = 0; m < i; ++m) {
-                    if (m & 1) s1 = fmaf(cur[m / 4][m % 4], t[m], s1);
-                    else s0 = fmaf(cur[m / 4][m % 4], t[m], s0);
-                }
-                t[i] = i < a ? 0.f : (i == a ? 1.f : -(s0 + s1));
+            for (int e = 0; e < 4; ++e) t11[e] = Tm[(4 * g4 + e) * SG + l16];
+            const v4f zero = {0.f, 0.f, 0.f, 0.f};
+            const v4f mm = mfma4(*reinterpret_cast<const v4f *>(Lm + (16 + l16) * SG + 4 * g4), t11, zero);
+            const v4f t21 = mfma4(*reinterpret_cast<const v4f *>(Tm + (16 + l16) * SG + 16 + 4 * g4), mm, zero);
 #pragma unroll
-                for (int m4 = 0; m4 < NP / 4; ++m4) cur[m4] = nxt[m4];
-            }
-#pragma unroll
-            for (int i = 0; i < NP; ++i) Tm[i * SG + a] = t[i];
+            for (int e = 0; e < 4; ++e) Tm[(16 + 4 * g4 + e) * SG + l16] = -t21[e];
         }
     }
     lds_barrier();
