@@ -447,15 +447,15 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
             *reinterpret_cast<bf4 *>(XL + row * Ly::SXB + c0 + k) = bf4{lo[0], lo[1], lo[2], lo[3]};
         }
     };
-    // ---- fused, wide, windows by the verify workgroups: waves 4..7, which have no Gram
-    //      products, write the commit windows of the workgroup's channels from the staged rows.  The window of node i and channel e
-    //      is (oldest first) its second and first nearest sources and its own token, 3 floats;
-    //      4 channels take 12 consecutive floats, stored as three 16-byte chunks (flat float f
-    //      of a group = source f % 3 of channel f / 3).  Lane l takes chunk l + 64m of a node's
-    //      row of chunks, so a store instruction writes consecutive chunks.  The q/k slab's
-    //      channel groups are split over the workgroups that share it (the value heads of the
-    //      q/k head), the value block is this workgroup's own.  No global load follows these
-    //      stores.
+    // ---- fused, wide, windows by the verify workgroups: after their state product, waves 4..7
+    //      (32 nodes: every wave) write the commit windows of the workgroup's channels from the
+    //      staged rows.  The window of node i and channel e is (oldest first) its second and first
+    //      nearest sources and its own token, 3 floats; 4 channels take 12 consecutive floats,
+    //      stored as three 16-byte chunks (flat float f of a group = source f % 3 of channel
+    //      f / 3).  Lane l takes chunk l + 64m of a node's row of chunks, so a store instruction
+    //      writes consecutive chunks.  The q/k slab's channel groups are split over the workgroups
+    //      that share it (the value heads of the q/k head), the value block is this workgroup's
+    //      own.  No global load follows these stores.
     auto write_windows = [&]() {
         const int nshare = Hv / d.Hk;
         const int gq0 = (ws * G) / nshare, nq = ((ws + 1) * G) / nshare - gq0;
@@ -470,7 +470,8 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
             const int ch = slab ? (g < DK / 4 ? kh * DK + 4 * g : d.Hk * DK + kh * DK + 4 * (g - DK / 4))
                                 : 2 * d.Hk * DK + h * DV + j0 + 4 * g;
             const int gofs = r < cpn ? ch * 12 + 16 * p : kOutOfRange;
-            for (int i = wv_u - 4; i < nvc; i += 4) {
+            constexpr int WW = NP == 32 ? kWaves : 4;  // waves writing windows: the last WW
+            for (int i = wv_u - (kWaves - WW); i < nvc; i += WW) {
                 const int sr = s_src[i];
                 const int rb[3] = {((sr >> 8) & 255) * SXS + col, ((sr >> 16) & 255) * SXS + col, i * SXS + col};
                 float w[4];
@@ -674,9 +675,27 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
     }
     if constexpr (Ly::SPLIT_W) lds_barrier();  // the bf16 parts are complete
     state_product();
+    // (32 nodes: by every wave, once its product is done -- 146-147 against 151 us on the stress
+    // layer; 16 nodes: by waves 4..7, 19.8 against 20.4-20.8 us at 16 lanes)
     if constexpr (FUSED && WIDE && WINV)
-        if (wv_u >= 4) write_windows();
+        if (NP == 32 || wv_u >= 4) write_windows();
     lds_barrier();
+
+    // the replay-log header (g, k^) of every node, once per lane and value head (jb == 0), by
+    // 256 threads (t = 0..255): wide workgroups from waves 0..3 in the solve phase, the others
+    // from waves 4..7 beside the epilogue (its stores go out beside the epilogue's)
+    auto write_log_header = [&](int t) {
+        float *logc = args.replay_log + ((int64_t)c * N * Hv + h) * R;
+        for (int f = t; f < nvc * (DK / 4); f += 256) {
+            const int i = f / (DK / 4), e4 = f - i * (DK / 4);
+            float sq = s_ssq[i][0];
+            if constexpr (Ly::NPART > 1) sq += s_ssq[i][1];
+            float *lrow = logc + (int64_t)i * Hv * R;
+            __builtin_nontemporal_store(*reinterpret_cast<const v4f *>(XQK + i * SX + 4 * e4) * inv_norm(sq),
+                                        reinterpret_cast<v4u *>(lrow + 1 + 4 * e4));
+            if (e4 == 0) __builtin_nontemporal_store(s_g[i], lrow);
+        }
+    };
 
     // ---- decayed, ancestor-masked, norm-scaled coefficients and per-node scales
     const float isd = 1.0f / sqrtf((float)DK);
@@ -715,7 +734,8 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
         }
     };
     if (wv_u < 4) {
-        if (!WIDE && wave < CT) {
+        if constexpr (WIDE) write_log_header(tid);  // (these waves have nothing else here)
+        else if (wave < CT) {
             const int nt = wave, jj = 16 * nt + l16;
 #pragma unroll
             for (int mt = 0; mt < NT; ++mt) {
@@ -770,8 +790,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
 
     // ---- epilogue: wave nt < CT owns value columns j0 + 16nt..: D = T rhs (delta rows,
     //      replay log), O = diag(gq) QS + Cq D (output).
-    //      Waves 4..7, once per lane and value head: the replay-log header (g, k^) of every
-    //      node (its stores go out beside the epilogue's).
+    //      Column blocks: waves 4..7 write the replay-log header beside it.
     static_assert(WIDE || CT <= 4, "epilogue waves");
     static_assert(2 * NP * SV <= Ly::SCR, "output tiles fit the scratch");
     float *Ot = scr, *Dt = scr + NP * SV;  // output and delta rows of the block, [NP][SV] each
@@ -809,19 +828,7 @@ __device__ __forceinline__ void verify_body(const VerifyArgs &args) {
             }
         }
     }
-    // waves 4..7, once per lane and value head: the replay-log header (g, k^) of every node
-    if (wv_u >= 4 && jb == 0) {
-        float *logc = args.replay_log + ((int64_t)c * N * Hv + h) * R;
-        for (int f = tid - 256; f < nvc * (DK / 4); f += kThreads - 256) {
-            const int i = f / (DK / 4), e4 = f - i * (DK / 4);
-            float sq = s_ssq[i][0];
-            if constexpr (Ly::NPART > 1) sq += s_ssq[i][1];
-            float *lrow = logc + (int64_t)i * Hv * R;
-            __builtin_nontemporal_store(*reinterpret_cast<const v4f *>(XQK + i * SX + 4 * e4) * inv_norm(sq),
-                                        reinterpret_cast<v4u *>(lrow + 1 + 4 * e4));
-            if (e4 == 0) __builtin_nontemporal_store(s_g[i], lrow);
-        }
-    }
+    if (!WIDE && wv_u >= 4 && jb == 0) write_log_header(tid - 256);
     lds_barrier();
     // output rows and the log's delta rows of the block, in 16-byte chunks from consecutive
     // lanes (whole lines per store instruction; a log row is 1 + d_k + d_v floats, so its
