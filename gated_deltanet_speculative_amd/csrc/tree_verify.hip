@@ -925,8 +925,10 @@ __device__ __forceinline__ void window_body(const VerifyArgs &args, int b) {
     }
 }
 
+// (16-node trees: two workgroups side by side on a CU -- a verify and a window workgroup, or two
+// wide verify workgroups -- so at least four waves per SIMD, at most 128 VGPRs)
 template <int DK, int DV, int NP, bool RAGGED, bool WIDE, bool WINV>
-__global__ __launch_bounds__(kThreads) void conv_tree_verify_kernel(const VerifyArgs args) {
+__global__ __launch_bounds__(kThreads, NP == 16 ? 4 : 1) void conv_tree_verify_kernel(const VerifyArgs args) {
     constexpr int NB = VerifyLayout<DK, DV, NP, true, WIDE, WINV>::NB;
     static_assert(kThreads * 12 <= VerifyLayout<DK, DV, NP, true, WIDE, WINV>::LDS_FLOATS, "window chunks fit the LDS");
     const int n_verify = NB * args.d.Hv * args.d.C;

@@ -1,7 +1,7 @@
 """Per-phase timeline of the fused conv + verify launch, from an instrumented build.
 
     python -m gated_deltanet_speculative_amd.timeline build
-    python -m gated_deltanet_speculative_amd.timeline run [--workload tree-c4-n16] [--instances 64]
+    python -m gated_deltanet_speculative_amd.timeline run [--workload tree-c4-n16] [--instances 64] [--lanes N]
 
 `build` (no GPU needed) writes a copy of csrc/tree_verify.hip in which thread 0 of every
 workgroup records the shader clock (s_memtime) at the start of the verify body, once its
@@ -126,7 +126,9 @@ def build() -> str:
     return LIB
 
 
-def run(workload: str, instances: int) -> None:
+def run(workload: str, instances: int, lanes: int | None = None) -> None:
+    import dataclasses
+
     import numpy as np
     import torch
 
@@ -142,6 +144,8 @@ def run(workload: str, instances: int) -> None:
     _lib._lib = lib  # the binding's calls go to the instrumented build
     lib.gdn_timeline_read.argtypes = [ctypes.c_void_p]
     wl = WORKLOADS[workload]
+    if lanes is not None:  # the workload's head shape and trees with this many lanes, as in bench.py
+        wl = dataclasses.replace(wl, name=f"{wl.name}-lanes{lanes}", n_seqs=lanes, n_slots=max(lanes, wl.n_slots))
     sh = gdn.Shape(**wl.shape_dict())
     C, N, Ch, Hv, dv = sh.n_seqs, sh.n_nodes, sh.channels, sh.n_v_heads, sh.d_v
     dev = torch.device("cuda:0")
@@ -187,7 +191,7 @@ def run(workload: str, instances: int) -> None:
     n_verify = (1 if wide else max(dv // 64, 1)) * Hv * C
     s = stamps[:n_verify].astype(np.int64)
     per_us = np.median((s[:, 10] - s[:, 0]) / ((s[:, 13] - s[:, 12]) / 100.0))  # shader cycles per us
-    print(f"{workload}: {n_verify} verify workgroups, shader clock {per_us / 1e3:.2f} GHz")
+    print(f"{wl.name}: {n_verify} verify workgroups, shader clock {per_us / 1e3:.2f} GHz")
     print(f"{'phase':32s} {'median':>7s} {'p10':>7s} {'p90':>7s}  (us, per verify workgroup)")
     prev = s[:, 0]
     for slot, name in PHASES:
@@ -218,11 +222,12 @@ def main() -> None:
     ap.add_argument("mode", choices=("build", "run"))
     ap.add_argument("--workload", default="tree-c4-n16")
     ap.add_argument("--instances", type=int, default=64)
+    ap.add_argument("--lanes", type=int, default=None, help="this many lanes at the workload's head shape")
     args = ap.parse_args()
     if args.mode == "build":
         build()
     else:
-        run(args.workload, args.instances)
+        run(args.workload, args.instances, args.lanes)
 
 
 if __name__ == "__main__":
