@@ -38,6 +38,7 @@ EDGE_SHAPES = [
     (2, 32, 3, 2, 4, 128, False),     # 32-node chains
     (8, 32, 9, 16, 32, 128, True),    # C * H_v = 256: one workgroup per (lane, value head)
     (16, 16, 17, 16, 32, 128, True),  # C * H_v = 512: those workgroups also write the windows
+    (16, 32, 17, 16, 32, 128, True),  # the same with 32-node trees (the stress layer's variant)
 ]
 
 
