@@ -23,10 +23,10 @@
 // sharing the norms and Gram products among the value heads of the q/k head), into one
 // package of kPackFloats floats per value head in the caller's workspace.  The second kernel
 // carries the state through the chunks in order and does only what involves it: the
-// products [K; Q] S, D = T rhs, O = diag(c) QS + Cq D, the output gate and the update, all
-// on v_mfma_f32_16x16x4_f32 with the operand permutation of mfma4, so the state tile stays
-// in registers across chunks in exactly the layout in which the next chunk's products and
-// the update consume and produce it.
+// products [K; Q] S (split bf16), D = T rhs, O = diag(c) QS + Cq D, the output gate and the
+// update (float32), with the operand permutation of mfma4, so the state tile stays in
+// registers across chunks in exactly the layout in which the next chunk's products and the
+// update consume and produce it.
 //
 // Package of (lane c, value head h, chunk j), at float offset ((c H_v + h) n_chunks + j) *
 // kPackFloats of the workspace:
@@ -256,12 +256,23 @@ __device__ inline int package_lds_offset(int t) {  // float offset of package gr
 // ---- kernel 2: the state through the chunks.  One workgroup (4 waves) per (lane, value
 // head, block of 64 value columns); wave w owns the 16-column tile w of the state for the
 // whole prompt.  Workgroup ids are ordered so that the workgroups sharing one (lane, q/k
-// head) are congruent modulo C * H_k and read the shared q/k rows through one L2.  One
-// barrier per chunk: the rows and the package of chunk j are staged in LDS buffer j % 2,
-// so staging chunk j + 1 never overlaps a wave still reading chunk j - 1.  Every per-chunk
-// buffer (rows, values, gate values, outputs, package) is addressed by a per-lane offset
-// that is the same for every chunk and a chunk base that moves by a uniform step; its
-// range ends at the chunk's last real token.
+// head) are congruent modulo C * H_k and read the shared q/k rows through one L2.
+//
+// Per chunk, in order: the products [K; Q] S in split bf16 (three bf16 products of hi / lo
+// parts, accumulated in float32), then D = T rhs, O = diag(c) QS + Cq D, the output gate and
+// the update S <- G_B S + K^T diag(w) D on float32 MFMA.  On this chip the float32 matrix
+// instructions and the vector ALU share one arithmetic rate, so the chunk costs the sum of
+// its float32 MFMA and VALU work: the split form replaces [K; Q] S's 64 float32 MFMAs per
+// wave with 24 bf16 ones and the split of the state tile (the q / k rows are split once per
+// workgroup at staging); the update stays float32.
+//
+// One barrier per chunk: chunk j's rows (bf16 parts, float32 k rows), package, values and
+// gate values are staged in LDS buffers j % 2 from registers loaded during the iteration
+// before, so a stage never overlaps a wave still reading chunk j - 1.  Every global access of
+// the loop is a raw buffer access whose range ends at the chunk's last real token and is
+// empty past the last chunk, so no load or store needs a branch; the values, gate values and
+// package are one 16-byte load per thread each (a wave's vector memory instructions, not
+// their bytes, set the address unit's time).
 template <int DK, int DV, bool GATED>
 __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     Dims d, int T, const float *__restrict__ qkv, const float *__restrict__ pack, float *__restrict__ state_pool,
@@ -269,11 +280,19 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     int32_t *__restrict__ status) {
     using Cfg = PrefillCfg<DK, DV>;
     constexpr int JB = Cfg::JB, NB = Cfg::NB, CT = Cfg::CT, KC = Cfg::KC, SX = Cfg::SX;
+    constexpr int OG = JB / 4;               // 16-byte groups of a block row
+    constexpr int VW = JB + 4;               // value rows in LDS (16 lanes of a row group on distinct banks)
+    constexpr int VROWS = kThreads / OG;     // rows written by the staging threads (>= BC)
+    constexpr int KM = (DK + 31) / 32;       // 32-wide chunks of d_k in the bf16 products (d_k = 16: one, half zero)
+    constexpr int SXB = 32 * KM + 8;         // bf16 row stride (16 rows read with ds_read_b128 hit distinct banks)
+    constexpr int XSB = 2 * BC * SXB;        // bf16 parts of one buffer: q rows, then k rows
     __shared__ unsigned int s_bitmap[kBitmapSlots / 32];
     __shared__ int s_word;
-    __shared__ __align__(16) float QK[2][2 * BC * SX];  // per buffer: q rows, then k rows
+    __shared__ __align__(16) float KF[2][BC * SX];        // per buffer: a chunk's k rows
+    __shared__ __align__(16) __bf16 XS[2][2][XSB];        // per buffer: hi parts, lo parts of the q and k rows
     __shared__ __align__(16) float PK[2][LP_FLOATS];
-    __shared__ __align__(16) float OT[2][BC * JB];      // per buffer: a chunk's output rows of the block
+    __shared__ __align__(16) float VZ[2][2][VROWS * VW];  // per buffer: value rows, gate value rows
+    __shared__ __align__(16) float OT[2][BC * JB];        // per buffer: a chunk's output rows of the block
 
     const int n_groups = d.C * d.Hk;
     const int grp = blockIdx.x % n_groups, ws = blockIdx.x / n_groups;
@@ -293,35 +312,43 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     const LaneSlotsT<kThreads> lanes(slot_ids, d.C);
     const int st_in = *status;
 
-    // per-lane byte offsets within a chunk: value (and gate value / output) rows 4 g4 + v;
-    // this thread's package group
-    int vo[4], zo[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        vo[v] = ((4 * g4 + v) * Ch + 2 * d.Hk * DK + h * DV + jj) * 4;
-        zo[v] = ((4 * g4 + v) * HvDV + h * DV + jj) * 4;
-    }
-    const int pk_off = tid < kPkGroups ? 16 * tid : kPackFloats * 4;  // past the range: reads zero
+    // Per-thread pieces of the chunk buffers: thread t holds 16-byte group t % OG of block row
+    // t / OG of the values, gate values and outputs (rows past BC read as zero and store
+    // nothing) and package group t.
+    const int b_row = tid / OG, b_grp = tid - b_row * OG;
+    constexpr int kPast = 0x7ffffff0;  // a byte offset past every range: loads read zero, stores drop
+    const int v_off = b_row < BC ? (b_row * Ch + 2 * d.Hk * DK + h * DV + j0 + 4 * b_grp) * 4 : kPast;
+    const int z_off = b_row < BC ? (b_row * HvDV + h * DV + j0 + 4 * b_grp) * 4 : kPast;
+    const int vz_lds = b_row * VW + 4 * b_grp;
+    const int pk_off = tid < kPkGroups ? 16 * tid : kPast;
     const int pk_lds = package_lds_offset(min(tid, kPkGroups - 1));
     const float *pk0 = pack + ((int64_t)c * d.Hv + h) * nch * kPackFloats;
-    auto chunk_base = [&](const float *buf, int row_floats, int k0) { return buf + ((int64_t)c * T + k0) * row_floats; };
-    // chunk jc's package group, values and gate values of this thread
-    v4f pkn, vn, zn = {0.f, 0.f, 0.f, 0.f};
-    auto load_chunk = [&](int jc) {
-        const int k0 = jc * BC, nc = min(BC, T - k0);
-        pkn = load4(rsrc(pk0 + (int64_t)jc * kPackFloats, kPackFloats * 4), pk_off);
-        const __amdgpu_buffer_rsrc_t vr = rsrc(chunk_base(qkv, Ch, k0), nc * Ch * 4);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) vn[v] = load1(vr, vo[v]);
-        if constexpr (GATED) {
-            const __amdgpu_buffer_rsrc_t zr = rsrc(chunk_base(gate_z, HvDV, k0), nc * HvDV * 4);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) zn[v] = load1(zr, zo[v]);
-        }
+    // chunk jc's tokens (0 past the end), and a buffer resource over rows of `row_floats`
+    // floats of chunk jc of this lane, empty past the end
+    auto chunk_len = [&](int jc) { return jc < nch ? min(BC, T - jc * BC) : 0; };
+    auto chunk_rsrc = [&](const float *buf, int row_floats, int jc) {
+        const int jcc = min(jc, nch - 1);
+        return rsrc(buf + ((int64_t)c * T + jcc * BC) * row_floats, chunk_len(jc) * row_floats * 4);
     };
-    ChunkRows<DK> rows(Ch, d.Hk, kh);
-    rows.load(rsrc(chunk_base(qkv, Ch, 0), min(BC, T) * Ch * 4));
-    load_chunk(0);
+    // Two chunks' loads are in flight at a time (register sets A and B, loaded two iterations
+    // before their chunk is staged): one iteration does not cover the loads' latency.
+    constexpr int QPT = Cfg::QPT;
+    struct ChunkRegs {
+        v4f x[QPT];   // the chunk's q / k row groups of this thread (ChunkRows' order)
+        v4f pk, v, z;  // package group, values, gate values
+    };
+    const ChunkRows<DK> rows(Ch, d.Hk, kh);  // (its per-thread offsets)
+    auto load_chunk = [&](ChunkRegs &r, int jc) {  // rows, package, values and gate values of chunk jc
+        const __amdgpu_buffer_rsrc_t rr = chunk_rsrc(qkv, Ch, jc);
+#pragma unroll
+        for (int u = 0; u < QPT; ++u) r.x[u] = load4(rr, rows.off[u]);
+        r.pk = load4(rsrc(pk0 + (int64_t)min(jc, nch - 1) * kPackFloats, jc < nch ? kPackFloats * 4 : 0), pk_off);
+        r.v = load4(chunk_rsrc(qkv, Ch, jc), v_off);
+        if constexpr (GATED) r.z = load4(chunk_rsrc(gate_z, HvDV, jc), z_off);
+    };
+    ChunkRegs ra, rb;
+    load_chunk(ra, 0);
+    load_chunk(rb, 1);
     __builtin_amdgcn_sched_barrier(0);
     const int s = __builtin_amdgcn_readfirstlane(s_v);
     const bool s_ok = s >= 0 && s < d.P;
@@ -344,63 +371,112 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     // a chunk's outputs wait in OT[jc % 2] until the next barrier, then every thread stores a
     // 16-byte piece of whole rows of the block (JB consecutive floats of a row): a row's lines
     // are written by one store instruction instead of a 64-byte segment by each of CT waves
-    constexpr int OG = JB / 4;  // 16-byte pieces of a block row
-    const int o_row = tid / OG, o_grp = tid - o_row * OG;
-    const int o_off = (o_row * HvDV + h * DV + j0 + 4 * o_grp) * 4;
-    auto store_outputs = [&](int jc) {
-        const int k0 = jc * BC, nc = min(BC, T - k0);
-        if (tid < BC * OG) {
-            const v4f ov = *reinterpret_cast<const v4f *>(&OT[jc & 1][o_row * JB + 4 * o_grp]);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, ov), rsrc(chunk_base(out, HvDV, k0), nc * HvDV * 4),
-                                                   o_off, 0, kNonTemporal);
-        }
+    const int o_off = b_row < BC ? (b_row * HvDV + h * DV + j0 + 4 * b_grp) * 4 : kPast;
+    const int o_lds = min(b_row, BC - 1) * JB + 4 * b_grp;
+    auto store_outputs = [&](int jc) {  // chunk jc's outputs (none for jc < 0)
+        const v4f ov = *reinterpret_cast<const v4f *>(&OT[jc & 1][o_lds]);
+        const int jcc = max(jc, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(v4i, ov),
+            rsrc(out + ((int64_t)c * T + jcc * BC) * HvDV, jc >= 0 ? chunk_len(jcc) * HvDV * 4 : 0), o_off, 0,
+            kNonTemporal);
     };
 
-    for (int jc = 0; jc < nch; ++jc) {
-        const int k0 = jc * BC;
-        float *Qb = QK[jc & 1], *Kb = Qb + BC * SX, *Pb = PK[jc & 1];
-        rows.stage(Qb);
-        if (tid < kPkGroups) *reinterpret_cast<v4f *>(Pb + pk_lds) = pkn;
-        const v4f vv = vn, zz = zn;
-        lds_barrier();
-        if (jc + 1 < nch) {  // the next chunk's loads go out now, under this chunk's products
-            rows.load(rsrc(chunk_base(qkv, Ch, k0 + BC), min(BC, T - k0 - BC) * Ch * 4));
-            load_chunk(jc + 1);
+    // Staging of a chunk: the k rows as float32 (the update's left operand), the q and k rows
+    // as their bf16 hi / lo parts (the products with the state), the package, the values and
+    // the gate values.  In the bf16 parts the columns of each 32-wide chunk m of d_k are
+    // permuted so that lane group g of a product supplies, in slots 8g .. 8g + 7, the columns
+    // 32m + 4g + 0..3 and 32m + 16 + 4g + 0..3: the same d_k rows as the state tile's
+    // registers sreg[2m] and sreg[2m + 1] (column 32m + 16h + 4g + e sits at 32m + 8g + 4h + e).
+    constexpr int QK4 = Cfg::QK4;
+    int kf_at[QPT], xs_at[QPT];
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+        const int f = min(tid + kThreads * u, 2 * QK4 - 1);
+        const int m = f / QK4, r = f - m * QK4, t = r / (DK / 4), p = r - t * (DK / 4);
+        kf_at[u] = m == 1 ? t * SX + 4 * p : -1;
+        xs_at[u] = (m * BC + t) * SXB + 32 * (p >> 3) + 8 * (p & 3) + 4 * ((p >> 2) & 1);
+    }
+    auto stage_chunk = [&](int buf, const ChunkRegs &r) {
+        __bf16 *xh = XS[buf][0];
+#pragma unroll
+        for (int u = 0; u < QPT; ++u) {
+            if (tid + kThreads * u >= 2 * QK4) continue;
+            const v4f x = r.x[u];
+            if (kf_at[u] >= 0) *reinterpret_cast<v4f *>(KF[buf] + kf_at[u]) = x;
+            const float xa[4] = {x[0], x[1], x[2], x[3]};
+            __bf16 hi[4], lo[4];
+            split_bf16(xa, hi, lo);
+            *reinterpret_cast<bf4 *>(xh + xs_at[u]) = bf4{hi[0], hi[1], hi[2], hi[3]};
+            *reinterpret_cast<bf4 *>(xh + XSB + xs_at[u]) = bf4{lo[0], lo[1], lo[2], lo[3]};
         }
-        if (jc > 0) store_outputs(jc - 1);  // complete since the barrier
+        if (tid < kPkGroups) *reinterpret_cast<v4f *>(PK[buf] + pk_lds) = r.pk;
+        *reinterpret_cast<v4f *>(VZ[buf][0] + vz_lds) = r.v;
+        if constexpr (GATED) *reinterpret_cast<v4f *>(VZ[buf][1] + vz_lds) = r.z;
+    };
+    if constexpr (DK < 32) {  // the missing half of the one 32-wide chunk reads as zero
+        for (int i = tid; i < 2 * 2 * XSB; i += kThreads) (&XS[0][0][0])[i] = (__bf16)0.f;
+        lds_barrier();
+    }
+
+    // one chunk: stage it from its register set, which then loads the chunk two ahead
+    auto step = [&](int jc, ChunkRegs &r) {
+        const int buf = jc & 1;
+        stage_chunk(buf, r);
+        lds_barrier();
+        v4f ks = {0.f, 0.f, 0.f, 0.f}, qs = ks;
         if (wave < CT) {
-            // [K; Q] S, the operands read ahead of the products
-            v4f ak[KC], aq[KC];
+            // [K; Q] S: per 32-wide chunk m of d_k, the state tile's rows split into bf16 hi /
+            // lo parts in registers, against the staged parts of the rows
+            const __bf16 *xh = XS[buf][0];
 #pragma unroll
-            for (int q = 0; q < KC; ++q) {
-                ak[q] = *reinterpret_cast<const v4f *>(Kb + l16 * SX + 16 * q + 4 * g4);
-                aq[q] = *reinterpret_cast<const v4f *>(Qb + l16 * SX + 16 * q + 4 * g4);
-            }
-            v4f ks = {0.f, 0.f, 0.f, 0.f}, qs = ks;
+            for (int m = 0; m < KM; ++m) {
+                const v4f s1 = 2 * m + 1 < KC ? sreg[min(2 * m + 1, KC - 1)] : v4f{0.f, 0.f, 0.f, 0.f};
+                const float x[8] = {sreg[2 * m][0], sreg[2 * m][1], sreg[2 * m][2], sreg[2 * m][3],
+                                    s1[0],          s1[1],          s1[2],          s1[3]};
+                __bf16 bh[8], bl[8];
+                split_bf16(x, bh, bl);
+                const bf8 vbh = {bh[0], bh[1], bh[2], bh[3], bh[4], bh[5], bh[6], bh[7]};
+                const bf8 vbl = {bl[0], bl[1], bl[2], bl[3], bl[4], bl[5], bl[6], bl[7]};
 #pragma unroll
-            for (int q = 0; q < KC; ++q) {
-                ks = mfma4(ak[q], sreg[q], ks);
-                qs = mfma4(aq[q], sreg[q], qs);
+                for (int rt = 0; rt < 2; ++rt) {  // q rows, k rows
+                    const int off = (BC * rt + l16) * SXB + 32 * m + 8 * g4;
+                    const bf8 ah = *reinterpret_cast<const bf8 *>(xh + off);
+                    const bf8 al = *reinterpret_cast<const bf8 *>(xh + XSB + off);
+                    v4f &acc = rt ? ks : qs;
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, vbh, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, vbl, acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, vbh, acc, 0, 0, 0);
+                }
             }
-            // the package operands, and the update's left operand K^T (lane supplies
-            // K[token 4*g4 + s][16 rt + l16] in step s), read while the products run
+        }
+        // the loads of the chunk two ahead and the previous chunk's output store go out under
+        // the products (every wave, at one point of the program, so that no wait for them is
+        // placed before their registers are read two iterations on)
+        load_chunk(r, jc + 2);
+        store_outputs(jc - 1);  // complete since the barrier
+        if (wave < CT) {
+            // the package operands, the values, and the update's left operand K^T (lane
+            // supplies K[token 4*g4 + s][16 rt + l16] in step s)
+            const float *Pb = PK[buf], *Vb = VZ[buf][0], *Zb = VZ[buf][1], *Kb = KF[buf];
             const v4f tf = *reinterpret_cast<const v4f *>(Pb + LP_T + l16 * LP_S + 4 * g4);
             const v4f cf = *reinterpret_cast<const v4f *>(Pb + LP_CQ + l16 * LP_S + 4 * g4);
             const v4f pa = *reinterpret_cast<const v4f *>(Pb + LP_V + 4 * g4);
             const v4f pb = *reinterpret_cast<const v4f *>(Pb + LP_V + BC + 4 * g4);
             const v4f pc = *reinterpret_cast<const v4f *>(Pb + LP_V + 2 * BC + 4 * g4);
             const v4f pw = *reinterpret_cast<const v4f *>(Pb + LP_V + 3 * BC + 4 * g4);
-            const float gend = Pb[LP_G];
+            const float gend = jc < nch ? Pb[LP_G] : 1.f;  // (past the last chunk: S unchanged)
             v4f kt[KC];
 #pragma unroll
             for (int rt = 0; rt < KC; ++rt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) kt[rt][e] = Kb[(4 * g4 + e) * SX + 16 * rt + l16];
             // D = T rhs, O = diag(c) QS + Cq D, the gate; outputs of padding tokens are dropped
+            // at the store
             v4f rhs, o, bw;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                rhs[v] = pa[v] * (vv[v] - pb[v] * ks[v]);
+                rhs[v] = pa[v] * (Vb[(4 * g4 + v) * VW + 16 * cw + l16] - pb[v] * ks[v]);
                 o[v] = pc[v] * qs[v];
             }
             const v4f dl = mfma4(tf, rhs, v4f{0.f, 0.f, 0.f, 0.f});
@@ -408,23 +484,35 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 if constexpr (GATED) {
-                    const float sg = fast_sigmoid(zz[v]);
-                    o[v] *= gate_mode == 0 ? zz[v] * sg : sg;  // silu(z) = z sigmoid(z)
+                    const float zz = Zb[(4 * g4 + v) * VW + 16 * cw + l16];
+                    const float sg = fast_sigmoid(zz);
+                    o[v] *= gate_mode == 0 ? zz * sg : sg;  // silu(z) = z sigmoid(z)
                 }
                 // (the element goes through a scalar: this compiler's __builtin_bit_cast of a vector
                 // element lvalue reads element 0 whatever the index)
                 const float ov = o[v];
-                OT[jc & 1][(4 * g4 + v) * JB + 16 * cw + l16] = ov;
+                OT[buf][(4 * g4 + v) * JB + 16 * cw + l16] = ov;
                 bw[v] = pw[v] * dl[v];
             }
             // S <- G_B S + K^T diag(w) D, tile by tile of 16 d_k rows
 #pragma unroll
             for (int rt = 0; rt < KC; ++rt) sreg[rt] = mfma4(kt[rt], bw, gend * sreg[rt]);
         }
+    };
+    // the state tile and the first two chunks are in before the loop: a load still pending at
+    // the loop's entry would have the compiler wait for every younger load in each iteration
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), lgkmcnt and expcnt left open
+    // Steps in pairs, with no branch between them (a conditional step would have the compiler
+    // wait for every pending load at the loop's head): an odd count ends with a step past the
+    // last chunk, whose buffers are zero (beta = 0, so D = 0) and whose decay is taken as 1,
+    // so it leaves the state as it is and stores nothing.
+    for (int jc = 0; jc < nch; jc += 2) {
+        step(jc, ra);
+        step(jc + 1, rb);
     }
 
     lds_barrier();
-    store_outputs(nch - 1);
+    store_outputs(((nch + 1) & ~1) - 1);  // the last step's outputs (none past the last chunk)
 
     // ---- the slot's state, in place
     if (wave < CT) {
