@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     __shared__ int s_word;
     __shared__ __align__(16) float KF[2][BC * SX];        // per buffer: a chunk's k rows
     __shared__ __align__(16) __bf16 XS[2][2][XSB];        // per buffer: hi parts, lo parts of the q and k rows
-    __shared__ __align__(16) float PK[2][LP_FLOATS];
+    __shared__ __align__(16) float PK[2][LP_FLOATS + 4];  // (+ a slot the threads without a package group write)
     __shared__ __align__(16) float VZ[2][2][VROWS * VW];  // per buffer: value rows, gate value rows
     __shared__ __align__(16) float OT[2][BC * JB];        // per buffer: a chunk's output rows of the block
 
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     const int z_off = b_row < BC ? (b_row * HvDV + h * DV + j0 + 4 * b_grp) * 4 : kPast;
     const int vz_lds = b_row * VW + 4 * b_grp;
     const int pk_off = tid < kPkGroups ? 16 * tid : kPast;
-    const int pk_lds = package_lds_offset(min(tid, kPkGroups - 1));
+    const int pk_lds = tid < kPkGroups ? package_lds_offset(tid) : LP_FLOATS;
     const float *pk0 = pack + ((int64_t)c * d.Hv + h) * nch * kPackFloats;
     // chunk jc's tokens (0 past the end), and a buffer resource over rows of `row_floats`
     // floats of chunk jc of this lane, empty past the end
@@ -375,11 +375,11 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     const int o_lds = min(b_row, BC - 1) * JB + 4 * b_grp;
     auto store_outputs = [&](int jc) {  // chunk jc's outputs (none for jc < 0)
         const v4f ov = *reinterpret_cast<const v4f *>(&OT[jc & 1][o_lds]);
-        const int jcc = max(jc, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(
-            __builtin_bit_cast(v4i, ov),
-            rsrc(out + ((int64_t)c * T + jcc * BC) * HvDV, jc >= 0 ? chunk_len(jcc) * HvDV * 4 : 0), o_off, 0,
-            kNonTemporal);
+        const int jcc = max(jc, 0), live = jc >= 0;  // (a product, not a select: no branch)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, ov),
+                                               rsrc(out + ((int64_t)c * T + jcc * BC) * HvDV,
+                                                    live * chunk_len(jcc) * HvDV * 4),
+                                               o_off, 0, kNonTemporal);
     };
 
     // Staging of a chunk: the k rows as float32 (the update's left operand), the q and k rows
@@ -397,20 +397,24 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
         kf_at[u] = m == 1 ? t * SX + 4 * p : -1;
         xs_at[u] = (m * BC + t) * SXB + 32 * (p >> 3) + 8 * (p & 3) + 4 * ((p >> 2) & 1);
     }
+    // (when a chunk's q rows fill whole rounds of the threads, whether item u is a q or a k
+    // group, and whether it exists, is known per u at compile time: no branch)
+    constexpr bool kWholeRounds = QK4 % kThreads == 0;
     auto stage_chunk = [&](int buf, const ChunkRegs &r) {
         __bf16 *xh = XS[buf][0];
 #pragma unroll
         for (int u = 0; u < QPT; ++u) {
-            if (tid + kThreads * u >= 2 * QK4) continue;
+            if (!kWholeRounds && tid + kThreads * u >= 2 * QK4) continue;
             const v4f x = r.x[u];
-            if (kf_at[u] >= 0) *reinterpret_cast<v4f *>(KF[buf] + kf_at[u]) = x;
+            if (kWholeRounds ? kThreads * u >= QK4 : kf_at[u] >= 0)
+                *reinterpret_cast<v4f *>(KF[buf] + kf_at[u]) = x;
             const float xa[4] = {x[0], x[1], x[2], x[3]};
             __bf16 hi[4], lo[4];
             split_bf16(xa, hi, lo);
             *reinterpret_cast<bf4 *>(xh + xs_at[u]) = bf4{hi[0], hi[1], hi[2], hi[3]};
             *reinterpret_cast<bf4 *>(xh + XSB + xs_at[u]) = bf4{lo[0], lo[1], lo[2], lo[3]};
         }
-        if (tid < kPkGroups) *reinterpret_cast<v4f *>(PK[buf] + pk_lds) = r.pk;
+        *reinterpret_cast<v4f *>(PK[buf] + pk_lds) = r.pk;
         *reinterpret_cast<v4f *>(VZ[buf][0] + vz_lds) = r.v;
         if constexpr (GATED) *reinterpret_cast<v4f *>(VZ[buf][1] + vz_lds) = r.z;
     };
@@ -424,8 +428,11 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
         const int buf = jc & 1;
         stage_chunk(buf, r);
         lds_barrier();
+        // (every wave computes: with fewer tiles than waves, CT < 4, the waves past the last
+        // tile repeat tile CT - 1's arithmetic and write the same values; no branch, so that the
+        // products, the loads and the update share one scheduling region)
         v4f ks = {0.f, 0.f, 0.f, 0.f}, qs = ks;
-        if (wave < CT) {
+        {
             // [K; Q] S: per 32-wide chunk m of d_k, the state tile's rows split into bf16 hi /
             // lo parts in registers, against the staged parts of the rows
             const __bf16 *xh = XS[buf][0];
@@ -450,12 +457,7 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
                 }
             }
         }
-        // the loads of the chunk two ahead and the previous chunk's output store go out under
-        // the products (every wave, at one point of the program, so that no wait for them is
-        // placed before their registers are read two iterations on)
-        load_chunk(r, jc + 2);
-        store_outputs(jc - 1);  // complete since the barrier
-        if (wave < CT) {
+        {
             // the package operands, the values, and the update's left operand K^T (lane
             // supplies K[token 4*g4 + s][16 rt + l16] in step s)
             const float *Pb = PK[buf], *Vb = VZ[buf][0], *Zb = VZ[buf][1], *Kb = KF[buf];
@@ -465,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
             const v4f pb = *reinterpret_cast<const v4f *>(Pb + LP_V + BC + 4 * g4);
             const v4f pc = *reinterpret_cast<const v4f *>(Pb + LP_V + 2 * BC + 4 * g4);
             const v4f pw = *reinterpret_cast<const v4f *>(Pb + LP_V + 3 * BC + 4 * g4);
-            const float gend = jc < nch ? Pb[LP_G] : 1.f;  // (past the last chunk: S unchanged)
+            const float gp = Pb[LP_G], gend = jc < nch ? gp : 1.f;  // (past the last chunk: S unchanged)
             v4f kt[KC];
 #pragma unroll
             for (int rt = 0; rt < KC; ++rt)
@@ -494,9 +496,18 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
                 OT[buf][(4 * g4 + v) * JB + 16 * cw + l16] = ov;
                 bw[v] = pw[v] * dl[v];
             }
-            // S <- G_B S + K^T diag(w) D, tile by tile of 16 d_k rows
+            // S <- G_B S + K^T diag(w) D, tile by tile of 16 d_k rows, with the loads of the
+            // chunk two ahead and the previous chunk's output store spread between its products
+            // (issued in a cluster they stall the wave on the address unit)
+            load_chunk(r, jc + 2);
+            store_outputs(jc - 1);  // complete since the barrier
 #pragma unroll
             for (int rt = 0; rt < KC; ++rt) sreg[rt] = mfma4(kt[rt], bw, gend * sreg[rt]);
+#pragma unroll
+            for (int i = 0; i < QPT + 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 4 * KC / (QPT + 4) > 0 ? 4 * KC / (QPT + 4) : 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+            }
         }
     };
     // the state tile and the first two chunks are in before the loop: a load still pending at
