@@ -352,8 +352,8 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     __builtin_amdgcn_sched_barrier(0);
     const int s = __builtin_amdgcn_readfirstlane(s_v);
     const bool s_ok = s >= 0 && s < d.P;
-    // the state tile of this wave in the MFMA operand layout:
-    // sreg[q][e] = S[16q + 4*g4 + e][jj]   (waves w < CT)
+    // the state tile of this wave in the MFMA operand layout (waves past the last tile, CT < 4,
+    // hold tile CT - 1): sreg[q][e] = S[16q + 4*g4 + e][jj]
     float *Sp = state_pool + ((int64_t)(s_ok ? s : 0) * d.Hv + h) * DK * DV + jj;
     v4f sreg[KC];
 #pragma unroll
