@@ -93,16 +93,19 @@ def test_prefill_parity(C, T, P, Hk, Hv, dk, dv, pad, gate):
     log(f"[prefill] out {e_out:.2e} state {e_state:.2e}")
 
 
-def test_prefill_long_prompt():
-    """512 tokens (32 chunks) at d = 128: the error stays within the bar."""
-    case = _inputs(1, 512, 2, 1, 2, 128, 128, seed=210)
-    log("[prefill] 512-token prompt")
+@pytest.mark.parametrize("T", [512, 513])
+def test_prefill_long_prompt(T):
+    """512 tokens (32 chunks) and 513 (33 chunks, a one-token tail: the chunk loop runs in
+    pairs, so an odd count ends with a step past the last chunk) at d = 128: the error stays
+    within the bar."""
+    case = _inputs(1, T, 2, 1, 2, 128, 128, seed=210 + T % 2)
+    log(f"[prefill] {T}-token prompt")
     state, out, status = _gpu_prefill(case, 1)
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     pool, ref = _oracle_prefill(case, 1)
     e_out, e_state = _check(case, state, out, pool, ref, "long prompt")
-    log(f"[prefill] 512 tokens: out {e_out:.2e} state {e_state:.2e}")
+    log(f"[prefill] {T} tokens: out {e_out:.2e} state {e_state:.2e}")
 
 
 def test_prompt_conv_then_prefill():
