@@ -10,7 +10,7 @@ its end (the window workgroups at their start and end), plus the constant 100 MH
 (s_memrealtime) at start and end to convert cycles to microseconds.  Stamps go to a
 fixed device array with ordinary vector stores.  The copy is linked with the other
 sources into libgdntimeline.so beside this file; the library's own sources are not
-changed, and nothing in the library loads this build.
+changed, and nothing in the library loads the instrumented copy.
 
 `run` (on the GPU) replays the launch over the workload's layer instances as the bench
 does, reads the stamps of the last launch and prints, per phase, the median, p10 and p90
