@@ -916,12 +916,15 @@ __device__ __forceinline__ void window_body(const VerifyArgs &args, int b) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int gi = tid % GPB;
-    v4f *dst = reinterpret_cast<v4f *>(args.commit_win + (((int64_t)c * N + ic) * d.Ch + ch0) * 3);
+    // (a buffer resource that ends at the row's last channel: chunks of channel groups past it
+    // are dropped by the range check; immediate offsets, no per-store address arithmetic)
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        args.commit_win + (((int64_t)c * N + ic) * d.Ch + ch0) * 3, 0, (d.Ch - ch0) * 12, kRsrcWord3);
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
         const int j = GPB * u + gi;  // chunk j holds part j % 3 of channel group j / 3
         const v4f v = chunks[3 * (tid - gi) + j];
-        if (i < nv && ch0 + 4 * (j / 3) < d.Ch) __builtin_nontemporal_store(v, dst + j);
+        if (i < nv) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), wr, 16 * j, 0, kNonTemporal);
     }
 }
 
