@@ -367,7 +367,9 @@ def decode_main(args):
     copy_ref = None if args.profile_only else copy_reference(kb["decode_step"], dev)
     roofline = None
     if kern:
-        dom = max(kern, key=lambda k: kern[k])
+        # the recurrence moves 14x the conv step's bytes; both launches are near the dispatch floor, so
+        # which one times longer over a few replays is noise, and the roofline stays with the recurrence
+        dom = "decode_step"
         achieved = kb[dom] / (kern[dom] * 1e-6) / 1e9
         roofline = dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                         frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(wl.name + "-decode", dom),
