@@ -67,7 +67,7 @@ hipError_t launch_decode_step(const Dims &d, const float *qkv, const float *beta
 // every (lane, value head, chunk of kPrefillChunk tokens) into `workspace`
 // (kPackFloats floats each), then the state recurrence over the chunks.
 constexpr int kPrefillChunk = 16;
-constexpr int kPackFloats = 580;
+constexpr int kPackFloats = 372;
 inline size_t prefill_workspace_floats(const Dims &d) {
     return (size_t)d.C * d.Hv * (size_t)((d.N + kPrefillChunk - 1) / kPrefillChunk) * kPackFloats;
 }

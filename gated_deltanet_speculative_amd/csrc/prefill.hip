@@ -29,11 +29,15 @@
 // update consume and produce it.
 //
 // Package of (lane c, value head h, chunk j), at float offset ((c H_v + h) n_chunks + j) *
-// kPackFloats of the workspace:
-//   [0, 256)    T[t][u] row-major                  [256, 512)  Cq[t][u] row-major
-//   [512, 528)  a_t = beta_t                       [528, 544)  b_t = G_t rk_t
-//   [544, 560)  c_t = G_t rq_t / sqrt(d_k)         [560, 576)  w_t = exp(L_B - L_t) rk_t
-//   [576, 580)  G_B, four copies (one float4 group)
+// kPackFloats of the workspace.  T is unit lower triangular (the substitution leaves its
+// diagonal exactly 1 and the part above it exactly 0) and Cq lower triangular, so each row
+// travels only as far as the 4-float groups that hold its entries below (T) or on and below
+// (Cq) the diagonal: row t of T as its first 4 ceil(t / 4) floats, row t of Cq as its first
+// 4 ceil((t + 1) / 4), rows one after another (every group is a 16-byte piece of one row):
+//   [0, 144)    T row segments                     [144, 304)  Cq row segments
+//   [304, 320)  a_t = beta_t                       [320, 336)  b_t = G_t rk_t
+//   [336, 352)  c_t = G_t rq_t / sqrt(d_k)         [352, 368)  w_t = exp(L_B - L_t) rk_t
+//   [368]       G_B                                [369, 372)  unused
 // Padding tokens of the last chunk are zero rows: beta = 0 and no decay, so they write
 // nothing into D, O or the state.
 #include <mutex>
@@ -48,7 +52,19 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int BC = kPrefillChunk;  // tokens per chunk
 static_assert(BC == 16, "one 16 x 16 MFMA tile of tokens per chunk");
-constexpr int PK_T = 0, PK_CQ = 256, PK_A = 512, PK_B = 528, PK_C = 544, PK_W = 560, PK_GEND = 576;
+// row segments of the packed T (strictly lower) and Cq (lower) rows: length and start, with
+// ceil_sum(n) = sum over s = 1..n of ceil(s / 4) = (m + 1) (2m + r) for n = 4m + r
+__host__ __device__ constexpr int seg_t(int t) { return (t + 3) / 4 * 4; }
+__host__ __device__ constexpr int seg_c(int t) { return (t + 4) / 4 * 4; }
+__host__ __device__ constexpr int ceil_sum(int n) { return n <= 0 ? 0 : (n / 4 + 1) * (2 * (n / 4) + n % 4); }
+__host__ __device__ constexpr int seg_t_start(int t) { return 4 * ceil_sum(t - 1); }
+__host__ __device__ constexpr int seg_c_start(int t) { return 4 * ceil_sum(t); }
+static_assert(seg_t_start(2) == 4 && seg_t_start(5) == 16 && seg_c_start(1) == 4 && seg_c_start(4) == 16 &&
+                  seg_c_start(5) == 24,
+              "row segment starts");
+constexpr int PK_T = 0, PK_CQ = seg_t_start(BC), PK_A = PK_CQ + seg_c_start(BC), PK_B = PK_A + BC, PK_C = PK_B + BC,
+              PK_W = PK_C + BC, PK_GEND = PK_W + BC;
+static_assert(PK_CQ == 144 && PK_A == 304, "package layout");
 static_assert(PK_GEND + 4 == kPackFloats && kPackFloats % 4 == 0, "package layout");
 
 template <int DK, int DV>
@@ -214,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
                 const int i = tid >> 4, a = tid & 15;
                 const float r = a <= i ? fast_exp((float)(s_L[mg][i] - s_L[mg][a])) * s_rk[a] : 0.f;
                 Lm[i * SG + a] = a < i ? r * s_kk[tid] * (s_beta[mg][i] * s_rk[i]) : 0.f;
-                pk[PK_CQ + tid] = r * s_qk[tid] * (s_rq[i] * isd);
+                if (a < seg_c(i)) pk[PK_CQ + seg_c_start(i) + a] = r * s_qk[tid] * (s_rq[i] * isd);
             }
             if (tid < BC) {
                 const float G = fast_exp((float)s_L[mg][tid]);
@@ -223,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
                 pk[PK_B + tid] = G * s_rk[tid];
                 pk[PK_C + tid] = G * s_rq[tid] * isd;
                 pk[PK_W + tid] = fast_exp((float)(Lend - s_L[mg][tid])) * s_rk[tid];
-                if (tid < 4) pk[PK_GEND + tid] = fast_exp((float)Lend);
+                if (tid == 0) pk[PK_GEND] = fast_exp((float)Lend);
             }
             lds_barrier();
             // T = (I + Lm)^-1: lane (column a, row i) over rows of 16 lanes
@@ -235,8 +251,12 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
                 Tm[i * BC + a] = bcast_solve(i == a ? 1.f : 0.f, Lr, std::make_integer_sequence<int, 16>());
             }
             lds_barrier();
-            if (tid < BC * BC / 4)
-                *reinterpret_cast<v4f *>(pk + PK_T + 4 * tid) = *reinterpret_cast<const v4f *>(Tm + 4 * tid);
+            {  // T's row segments: thread (row i, group a4) stores a 16-byte group of row i
+                const int i = tid >> 2, a4 = tid & 3;
+                if (tid < 4 * BC && 4 * a4 < seg_t(i))
+                    *reinterpret_cast<v4f *>(pk + PK_T + seg_t_start(i) + 4 * a4) =
+                        *reinterpret_cast<const v4f *>(Tm + i * BC + 4 * a4);
+            }
         }
         lds_barrier();  // s_beta / s_L of this group consumed
     }
@@ -244,13 +264,25 @@ __global__ __launch_bounds__(kThreads) void prefill_prep_kernel(
 
 // A chunk's package in LDS: T and Cq with rows of LP_S floats (so that 16 lanes reading a
 // 16-byte piece of one row each hit distinct banks), then the four per-token vectors and
-// G_B.  Thread t < kPkGroups stages float4 group t of the package.
+// G_B.  T's diagonal and the parts of both matrices past their rows' segments are set once
+// (1 on T's diagonal, 0 elsewhere) and never staged; thread t < kPkGroups stages group t of
+// the package, a 16-byte piece of one row.
 constexpr int LP_S = BC + 4, LP_T = 0, LP_CQ = BC * LP_S, LP_V = 2 * BC * LP_S, LP_G = LP_V + 4 * BC;
 constexpr int LP_FLOATS = LP_G + 4, kPkGroups = kPackFloats / 4;
 static_assert(kPkGroups <= kThreads, "one package group per thread");
-__device__ inline int package_lds_offset(int t) {  // float offset of package group t in LDS
-    return t < 64 ? LP_T + (t >> 2) * LP_S + 4 * (t & 3)
-                  : t < 128 ? LP_CQ + ((t - 64) >> 2) * LP_S + 4 * (t & 3) : LP_V + 4 * (t - 128);
+__device__ inline int package_lds_offset(int g) {  // float offset in LDS of package group g
+    const int f = 4 * g;
+    if (f < PK_CQ) {  // a segment of T's row t
+        int t = 1;
+        while (seg_t_start(t + 1) <= f) ++t;
+        return LP_T + t * LP_S + (f - seg_t_start(t));
+    }
+    if (f < PK_A) {  // a segment of Cq's row t
+        int t = 0;
+        while (seg_c_start(t + 1) <= f - PK_CQ) ++t;
+        return LP_CQ + t * LP_S + (f - PK_CQ - seg_c_start(t));
+    }
+    return f < PK_GEND ? LP_V + (f - PK_A) : LP_G;  // the vectors; G_B and the unused floats
 }
 
 // ---- kernel 2: the state through the chunks.  One workgroup (4 waves) per (lane, value
@@ -418,10 +450,15 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
         *reinterpret_cast<v4f *>(VZ[buf][0] + vz_lds) = r.v;
         if constexpr (GATED) *reinterpret_cast<v4f *>(VZ[buf][1] + vz_lds) = r.z;
     };
-    if constexpr (DK < 32) {  // the missing half of the one 32-wide chunk reads as zero
-        for (int i = tid; i < 2 * 2 * XSB; i += kThreads) (&XS[0][0][0])[i] = (__bf16)0.f;
-        lds_barrier();
+    // T's diagonal (1) and the parts above T's and Cq's diagonals (0) in both package buffers,
+    // once; (d_k = 16) the missing half of the one 32-wide chunk of the bf16 parts reads as zero
+    for (int i = tid; i < 2 * 2 * BC * LP_S; i += kThreads) {
+        const int b = i / (2 * BC * LP_S), r = i - b * 2 * BC * LP_S, row = (r / LP_S) % BC, col = r % LP_S;
+        PK[b][r] = r < BC * LP_S && col == row ? 1.f : 0.f;
     }
+    if constexpr (DK < 32)
+        for (int i = tid; i < 2 * 2 * XSB; i += kThreads) (&XS[0][0][0])[i] = (__bf16)0.f;
+    lds_barrier();
 
     // one chunk: stage it from its register set, which then loads the chunk two ahead
     auto step = [&](int jc, ChunkRegs &r) {

@@ -341,7 +341,7 @@ int gdn_decode_step(const gdn_shape *sh, const float *qkv, const float *beta_log
  *   workspace      device scratch of at least gdn_prefill_workspace_size(sh) bytes,
  *                  16-byte aligned, overlapping nothing else; its contents on entry do
  *                  not matter and are undefined afterwards.  It holds the per-chunk
- *                  coefficients of the chunked form (C * H_v * ceil(T / 16) * 2320 bytes)
+ *                  coefficients of the chunked form (C * H_v * ceil(T / 16) * 1488 bytes)
  *                  and must not be used by another call until this one has run.
  *   workspace_bytes its size (GDN_ERR_WORKSPACE if too small)
  *   status         int32*, REQUIRED (GDN_ERR_NULL otherwise)
@@ -361,7 +361,7 @@ size_t gdn_prefill_workspace_size(const gdn_shape *sh);
  * static device array of the library instead of a caller buffer.  Arguments, results and
  * errors are those of gdn_prefill without workspace / workspace_bytes, plus
  * GDN_ERR_SCRATCH (nothing enqueued) when gdn_prefill_workspace_size(sh) exceeds
- * GDN_STATIC_SCRATCH_BYTES (32 MiB: e.g. 4 lanes x 1024 tokens x 32 value heads need 19 MB).
+ * GDN_STATIC_SCRATCH_BYTES (32 MiB: e.g. 4 lanes x 1024 tokens x 32 value heads need 12.2 MB).
  * The call allocates and frees nothing.  Every GPU the library runs on holds one copy of the
  * array from the library's first use on it until the process ends; its address is looked
  * up once per device (GDN_ERR_HIP if that fails).  All calls on one GPU share that copy:

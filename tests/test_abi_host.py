@@ -310,11 +310,11 @@ def test_prefill_rejections():
 
 
 def test_prefill_workspace_size():
-    """One package of 580 floats per (lane, value head, chunk of 16 tokens); 0 for shapes the
+    """One package of 372 floats per (lane, value head, chunk of 16 tokens); 0 for shapes the
     prefill rejects."""
     sh = _shape(n_nodes=37)
-    assert gdn.prefill_workspace_size(sh) == sh.n_seqs * sh.n_v_heads * 3 * 580 * 4
-    assert gdn.prefill_workspace_size(_shape(n_nodes=16)) == _shape().n_seqs * _shape().n_v_heads * 580 * 4
+    assert gdn.prefill_workspace_size(sh) == sh.n_seqs * sh.n_v_heads * 3 * 372 * 4
+    assert gdn.prefill_workspace_size(_shape(n_nodes=16)) == _shape().n_seqs * _shape().n_v_heads * 372 * 4
     assert gdn.prefill_workspace_size(_shape(n_nodes=65537)) == 0
     assert gdn.prefill_workspace_size(_shape(d_k=24)) == 0
 
@@ -348,9 +348,9 @@ def test_prefill_noalloc_rejections():
     q[8] = q[7] + 16  # out overlapping the gate values
     assert call(_shape(n_nodes=1000), q) == _lib.GDN_ERR_ALIAS
     assert call(_shape(n_nodes=65537), p) == _lib.GDN_ERR_UNSUPPORTED
-    big = gdn.Shape(4, 2048, 8, 16, 32, 128, 128)  # 4 x 32 x 128 packages of 2320 bytes: 38 MB
+    big = gdn.Shape(4, 4096, 8, 16, 32, 128, 128)  # 4 x 32 x 256 packages of 1488 bytes: 49 MB
     assert gdn.prefill_workspace_size(big) > gdn.STATIC_SCRATCH_BYTES
     assert call(big, p, gate_stride=64) == _lib.GDN_ERR_SCRATCH
     assert "static scratch" in gdn.strerror(_lib.GDN_ERR_SCRATCH)
-    fits = gdn.Shape(4, 1024, 8, 16, 32, 128, 128)  # the prefill bench shape: 19 MB
+    fits = gdn.Shape(4, 1024, 8, 16, 32, 128, 128)  # the prefill bench shape: 12.2 MB
     assert gdn.prefill_workspace_size(fits) <= gdn.STATIC_SCRATCH_BYTES

@@ -60,15 +60,15 @@ def test_noalloc_prefill_matches_caller_workspace():
 
 
 def test_noalloc_prefill_rejects_an_oversized_shape():
-    sh = gdn.Shape(4, 2048, 8, 16, 32, 128, 128)
+    sh = gdn.Shape(4, 4096, 8, 16, 32, 128, 128)  # 49 MB of packages against 32 MiB
     t = torch.zeros(1, device="cuda")
     with pytest.raises(gdn.GdnError) as ei:
-        gdn.prefill_noalloc(sh, torch.zeros((4, 2048, sh.channels), device="cuda"),
-                            torch.zeros((4, 2048, 32), device="cuda"), torch.zeros((4, 2048, 32), device="cuda"),
+        gdn.prefill_noalloc(sh, torch.zeros((4, 4096, sh.channels), device="cuda"),
+                            torch.zeros((4, 4096, 32), device="cuda"), torch.zeros((4, 4096, 32), device="cuda"),
                             torch.zeros(32, device="cuda"), torch.zeros(32, device="cuda"),
                             torch.zeros((8, 32, 128, 128), device="cuda"), torch.arange(4, dtype=torch.int32,
                                                                                         device="cuda"),
                             torch.zeros(1, dtype=torch.int32, device="cuda"),
-                            torch.zeros((4, 2048, 32, 128), device="cuda"))
+                            torch.zeros((4, 4096, 32, 128), device="cuda"))
     assert ei.value.code == gdn._lib.GDN_ERR_SCRATCH
     del t
