@@ -23,10 +23,10 @@
 // sharing the norms and Gram products among the value heads of the q/k head), into one
 // package of kPackFloats floats per value head in the caller's workspace.  The second kernel
 // carries the state through the chunks in order and does only what involves it: the
-// products [K; Q] S (split bf16), D = T rhs, O = diag(c) QS + Cq D, the output gate and the
-// update (float32), with the operand permutation of mfma4, so the state tile stays in
-// registers across chunks in exactly the layout in which the next chunk's products and the
-// update consume and produce it.
+// products [K; Q] S (split bf16), D = T rhs, O = diag(c) QS + Cq D (float32), the output gate
+// and the update (split bf16, three parts), with the operand permutation of mfma4, so the
+// state tile stays in float32 registers across chunks in exactly the layout in which the next
+// chunk's products and the update consume and produce it.
 //
 // Package of (lane c, value head h, chunk j), at float offset ((c H_v + h) n_chunks + j) *
 // kPackFloats of the workspace.  T is unit lower triangular (the substitution leaves its
@@ -79,6 +79,25 @@ struct PrefillCfg {
     static constexpr int QPT = (2 * QK4 + kThreads - 1) / kThreads;
 };
 
+// x = hi + mid + lo + r, each part the bf16 rounding (to nearest even) of what the parts
+// before it leave (so hi and mid are also the two-part split), |r| <= 2^-26 |x|; by pairs of
+// consecutive values, each part of a pair as one packed word (element 0 in the low half)
+__device__ inline void split3_bf16(const float (&x)[4], unsigned (&h)[2], unsigned (&m)[2], unsigned (&l)[2]) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        unsigned u = __builtin_bit_cast(unsigned, bf2{(__bf16)x[2 * e], (__bf16)x[2 * e + 1]});
+        asm("" : "+v"(u));  // (opaque: keeps one packed conversion per pair)
+        const float r0 = x[2 * e] - __builtin_bit_cast(float, u << 16);
+        const float r1 = x[2 * e + 1] - __builtin_bit_cast(float, u & 0xffff0000u);
+        unsigned v = __builtin_bit_cast(unsigned, bf2{(__bf16)r0, (__bf16)r1});
+        asm("" : "+v"(v));
+        const float s0 = r0 - __builtin_bit_cast(float, v << 16), s1 = r1 - __builtin_bit_cast(float, v & 0xffff0000u);
+        h[e] = u;
+        m[e] = v;
+        l[e] = __builtin_bit_cast(unsigned, bf2{(__bf16)s0, (__bf16)s1});
+    }
+}
+
 // element (i, a) of a 16 x 16 accumulator tile stored lane-major (lane * 4 + component)
 __device__ inline int tile_index(int i, int a) { return (16 * (i >> 2) + a) * 4 + (i & 3); }
 
@@ -88,6 +107,8 @@ __device__ inline int tile_index(int i, int a) { return (16 * (i >> 2) + a) * 4 
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kNonTemporal = 2;  // cache-policy operand of the buffer stores: nt
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 __device__ inline __amdgpu_buffer_rsrc_t rsrc(const float *base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), 0, bytes, kRsrcWord3);
@@ -97,6 +118,9 @@ __device__ inline float load1(__amdgpu_buffer_rsrc_t r, int off) {
 }
 __device__ inline v4f load4(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ inline v2f load2(__amdgpu_buffer_rsrc_t r, int off, int soff) {
+    return __builtin_bit_cast(v2f, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
 }
 
 // The q and k rows of q/k head kh of one chunk, as float4 groups: item u of a thread is
@@ -291,14 +315,17 @@ __device__ inline int package_lds_offset(int g) {  // float offset in LDS of pac
 // head) are congruent modulo C * H_k and read the shared q/k rows through one L2.
 //
 // Per chunk, in order: the products [K; Q] S in split bf16 (three bf16 products of hi / lo
-// parts, accumulated in float32), then D = T rhs, O = diag(c) QS + Cq D, the output gate and
-// the update S <- G_B S + K^T diag(w) D on float32 MFMA.  On this chip the float32 matrix
-// instructions and the vector ALU share one arithmetic rate, so the chunk costs the sum of
-// its float32 MFMA and VALU work: the split form replaces [K; Q] S's 64 float32 MFMAs per
-// wave with 24 bf16 ones and the split of the state tile (the q / k rows are split once per
-// workgroup at staging); the update stays float32.
+// parts, accumulated in float32), then D = T rhs, O = diag(c) QS + Cq D and the output gate on
+// float32 MFMA, and the update S <- G_B S + K^T diag(w) D as three bf16 products of
+// three-part splits (accumulated in float32).  On this chip the float32 matrix instructions
+// and the vector ALU share one arithmetic rate, so the chunk costs the sum of its float32 MFMA
+// and VALU work: the split forms replace [K; Q] S's 64 float32 MFMAs per wave with 24 bf16
+// ones and the split of the state tile, and the update's 32 with 24 bf16 ones and the split
+// of diag(w) D (the q / k rows and K^T are split once per workgroup at staging).  A two-part
+// split of the update would drop terms near 2^-17 of it, which a prompt of near-parallel keys
+// accumulates to about 1e-4 of the state; the three-part form keeps every term above 2^-24.
 //
-// One barrier per chunk: chunk j's rows (bf16 parts, float32 k rows), package, values and
+// One barrier per chunk: chunk j's rows (bf16 parts of q / k rows and of K^T), package, values and
 // gate values are staged in LDS buffers j % 2 from registers loaded during the iteration
 // before, so a stage never overlaps a wave still reading chunk j - 1.  Every global access of
 // the loop is a raw buffer access whose range ends at the chunk's last real token and is
@@ -311,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     const int32_t *__restrict__ slot_ids, const float *__restrict__ gate_z, int gate_mode, float *__restrict__ out,
     int32_t *__restrict__ status) {
     using Cfg = PrefillCfg<DK, DV>;
-    constexpr int JB = Cfg::JB, NB = Cfg::NB, CT = Cfg::CT, KC = Cfg::KC, SX = Cfg::SX;
+    constexpr int JB = Cfg::JB, NB = Cfg::NB, CT = Cfg::CT, KC = Cfg::KC;
     constexpr int OG = JB / 4;               // 16-byte groups of a block row
     constexpr int VW = JB + 4;               // value rows in LDS (16 lanes of a row group on distinct banks)
     constexpr int VROWS = kThreads / OG;     // rows written by the staging threads (>= BC)
@@ -320,8 +347,10 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     constexpr int XSB = 2 * BC * SXB;        // bf16 parts of one buffer: q rows, then k rows
     __shared__ unsigned int s_bitmap[kBitmapSlots / 32];
     __shared__ int s_word;
-    __shared__ __align__(16) float KF[2][BC * SX];        // per buffer: a chunk's k rows
+    constexpr int KAS = 8 * (BC / 4) + 8;    // K^T rows (d_k index) of the update's operands, in bf16
     __shared__ __align__(16) __bf16 XS[2][2][XSB];        // per buffer: hi parts, lo parts of the q and k rows
+    __shared__ __align__(16) __bf16 KA[2][DK * KAS];      // per buffer: K^T as [hi | mid] per 4 tokens
+    __shared__ __align__(16) __bf16 KB[2][DK * KAS];      // per buffer: K^T as [lo | hi] per 4 tokens
     __shared__ __align__(16) float PK[2][LP_FLOATS + 4];  // (+ a slot the threads without a package group write)
     __shared__ __align__(16) float VZ[2][2][VROWS * VW];  // per buffer: value rows, gate value rows
     __shared__ __align__(16) float OT[2][BC * JB];        // per buffer: a chunk's output rows of the block
@@ -362,18 +391,48 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
         const int jcc = min(jc, nch - 1);
         return rsrc(buf + ((int64_t)c * T + jcc * BC) * row_floats, chunk_len(jc) * row_floats * 4);
     };
+    // Per-thread pieces of a chunk's q and k rows.  k: half-block b = tid + kThreads u (u < KPT),
+    // tokens 4 qd .. 4 qd + 3 of the columns 2 cp, 2 cp + 1 (qd = b / (DK / 2), cp = b % (DK / 2)),
+    // four 8-byte loads (a wave's load covers whole rows); q: group f = tid + kThreads u
+    // (u < QPT), columns 4 p .. 4 p + 3 of token t (t = f / (DK / 4), p = f % (DK / 4)).  Pieces
+    // past the end (d_k < 128) load a real piece again and are not staged.
+    constexpr int NKB = BC / 4 * (DK / 2), KPT = (NKB + kThreads - 1) / kThreads;
+    constexpr int NQG = BC * DK / 4, QPT = (NQG + kThreads - 1) / kThreads;
+    // In the bf16 parts of the rows (the products with the state) the columns of each 32-wide
+    // chunk m of d_k are permuted so that lane group g of a product supplies, in slots 8g ..
+    // 8g + 7, the columns 32m + 4g + 0..3 and 32m + 16 + 4g + 0..3: the same d_k rows as the
+    // state tile's registers sreg[2m] and sreg[2m + 1] (column 32m + 16h + 4g + e sits at
+    // 32m + 8g + 4h + e).
+    auto xs_col = [](int col) { return 32 * (col >> 5) + 8 * ((col >> 2) & 3) + 4 * ((col >> 4) & 1) + (col & 3); };
+    int k_off[KPT], ka_at[KPT], kx_at[KPT], q_off[QPT], qx_at[QPT];
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+        const int b = min(tid + kThreads * u, NKB - 1), qd = b / (DK / 2), col = 2 * (b - qd * (DK / 2));
+        k_off[u] = (4 * qd * Ch + d.Hk * DK + kh * DK + col) * 4;
+        ka_at[u] = col * KAS + 8 * qd;
+        kx_at[u] = (BC + 4 * qd) * SXB + xs_col(col);
+    }
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) {
+        const int f = min(tid + kThreads * u, NQG - 1), t = f / (DK / 4), col = 4 * (f - t * (DK / 4));
+        q_off[u] = (t * Ch + kh * DK + col) * 4;
+        qx_at[u] = t * SXB + xs_col(col);
+    }
     // Two chunks' loads are in flight at a time (register sets A and B, loaded two iterations
     // before their chunk is staged): one iteration does not cover the loads' latency.
-    constexpr int QPT = Cfg::QPT;
     struct ChunkRegs {
-        v4f x[QPT];   // the chunk's q / k row groups of this thread (ChunkRows' order)
-        v4f pk, v, z;  // package group, values, gate values
+        v2f kx[KPT][4];  // the k half-blocks of this thread: kx[u][s] = token 4 qd + s
+        v4f qx[QPT];     // the q groups
+        v4f pk, v, z;    // package group, values, gate values
     };
-    const ChunkRows<DK> rows(Ch, d.Hk, kh);  // (its per-thread offsets)
     auto load_chunk = [&](ChunkRegs &r, int jc) {  // rows, package, values and gate values of chunk jc
         const __amdgpu_buffer_rsrc_t rr = chunk_rsrc(qkv, Ch, jc);
 #pragma unroll
-        for (int u = 0; u < QPT; ++u) r.x[u] = load4(rr, rows.off[u]);
+        for (int u = 0; u < KPT; ++u)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) r.kx[u][s] = load2(rr, k_off[u], s * Ch * 4);
+#pragma unroll
+        for (int u = 0; u < QPT; ++u) r.qx[u] = load4(rr, q_off[u]);
         r.pk = load4(rsrc(pk0 + (int64_t)min(jc, nch - 1) * kPackFloats, jc < nch ? kPackFloats * 4 : 0), pk_off);
         r.v = load4(chunk_rsrc(qkv, Ch, jc), v_off);
         if constexpr (GATED) r.z = load4(chunk_rsrc(gate_z, HvDV, jc), z_off);
@@ -414,37 +473,42 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
                                                o_off, 0, kNonTemporal);
     };
 
-    // Staging of a chunk: the k rows as float32 (the update's left operand), the q and k rows
-    // as their bf16 hi / lo parts (the products with the state), the package, the values and
-    // the gate values.  In the bf16 parts the columns of each 32-wide chunk m of d_k are
-    // permuted so that lane group g of a product supplies, in slots 8g .. 8g + 7, the columns
-    // 32m + 4g + 0..3 and 32m + 16 + 4g + 0..3: the same d_k rows as the state tile's
-    // registers sreg[2m] and sreg[2m + 1] (column 32m + 16h + 4g + e sits at 32m + 8g + 4h + e).
-    constexpr int QK4 = Cfg::QK4;
-    int kf_at[QPT], xs_at[QPT];
-#pragma unroll
-    for (int u = 0; u < QPT; ++u) {
-        const int f = min(tid + kThreads * u, 2 * QK4 - 1);
-        const int m = f / QK4, r = f - m * QK4, t = r / (DK / 4), p = r - t * (DK / 4);
-        kf_at[u] = m == 1 ? t * SX + 4 * p : -1;
-        xs_at[u] = (m * BC + t) * SXB + 32 * (p >> 3) + 8 * (p & 3) + 4 * ((p >> 2) & 1);
-    }
-    // (when a chunk's q rows fill whole rounds of the threads, whether item u is a q or a k
-    // group, and whether it exists, is known per u at compile time: no branch)
-    constexpr bool kWholeRounds = QK4 % kThreads == 0;
+    // Staging of a chunk: the q and k rows as their bf16 hi / lo parts (the products with the
+    // state), K^T in three bf16 parts (the update's left operand), the package, the values and
+    // the gate values.  The k rows' hi / lo parts are the hi / mid of their three-part split.
     auto stage_chunk = [&](int buf, const ChunkRegs &r) {
-        __bf16 *xh = XS[buf][0];
+        __bf16 *xh = XS[buf][0], *xl = XS[buf][1];
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            if (NKB % kThreads != 0 && tid + kThreads * u >= NKB) continue;
+            unsigned hi[2][2], mi[2][2], lo[2][2];  // [column j][token pair], packed bf16 pairs
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float c4[4] = {r.kx[u][0][j], r.kx[u][1][j], r.kx[u][2][j], r.kx[u][3][j]};
+                split3_bf16(c4, hi[j], mi[j], lo[j]);
+                *reinterpret_cast<v4u *>(KA[buf] + ka_at[u] + j * KAS) = v4u{hi[j][0], hi[j][1], mi[j][0], mi[j][1]};
+                *reinterpret_cast<v4u *>(KB[buf] + ka_at[u] + j * KAS) = v4u{lo[j][0], lo[j][1], hi[j][0], hi[j][1]};
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {  // token 4 qd + s: its two columns' hi and mid parts
+                const int w = s >> 1;
+                const unsigned h = s & 1 ? (hi[0][w] >> 16) | (hi[1][w] & 0xffff0000u)
+                                         : (hi[0][w] & 0xffffu) | (hi[1][w] << 16);
+                const unsigned m = s & 1 ? (mi[0][w] >> 16) | (mi[1][w] & 0xffff0000u)
+                                         : (mi[0][w] & 0xffffu) | (mi[1][w] << 16);
+                *reinterpret_cast<unsigned *>(xh + kx_at[u] + s * SXB) = h;
+                *reinterpret_cast<unsigned *>(xl + kx_at[u] + s * SXB) = m;
+            }
+        }
 #pragma unroll
         for (int u = 0; u < QPT; ++u) {
-            if (!kWholeRounds && tid + kThreads * u >= 2 * QK4) continue;
-            const v4f x = r.x[u];
-            if (kWholeRounds ? kThreads * u >= QK4 : kf_at[u] >= 0)
-                *reinterpret_cast<v4f *>(KF[buf] + kf_at[u]) = x;
+            if (NQG % kThreads != 0 && tid + kThreads * u >= NQG) continue;
+            const v4f x = r.qx[u];
             const float xa[4] = {x[0], x[1], x[2], x[3]};
             __bf16 hi[4], lo[4];
             split_bf16(xa, hi, lo);
-            *reinterpret_cast<bf4 *>(xh + xs_at[u]) = bf4{hi[0], hi[1], hi[2], hi[3]};
-            *reinterpret_cast<bf4 *>(xh + XSB + xs_at[u]) = bf4{lo[0], lo[1], lo[2], lo[3]};
+            *reinterpret_cast<bf4 *>(xh + qx_at[u]) = bf4{hi[0], hi[1], hi[2], hi[3]};
+            *reinterpret_cast<bf4 *>(xl + qx_at[u]) = bf4{lo[0], lo[1], lo[2], lo[3]};
         }
         *reinterpret_cast<v4f *>(PK[buf] + pk_lds) = r.pk;
         *reinterpret_cast<v4f *>(VZ[buf][0] + vz_lds) = r.v;
@@ -495,9 +559,8 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
             }
         }
         {
-            // the package operands, the values, and the update's left operand K^T (lane
-            // supplies K[token 4*g4 + s][16 rt + l16] in step s)
-            const float *Pb = PK[buf], *Vb = VZ[buf][0], *Zb = VZ[buf][1], *Kb = KF[buf];
+            // the package operands and the values
+            const float *Pb = PK[buf], *Vb = VZ[buf][0], *Zb = VZ[buf][1];
             const v4f tf = *reinterpret_cast<const v4f *>(Pb + LP_T + l16 * LP_S + 4 * g4);
             const v4f cf = *reinterpret_cast<const v4f *>(Pb + LP_CQ + l16 * LP_S + 4 * g4);
             const v4f pa = *reinterpret_cast<const v4f *>(Pb + LP_V + 4 * g4);
@@ -505,11 +568,6 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
             const v4f pc = *reinterpret_cast<const v4f *>(Pb + LP_V + 2 * BC + 4 * g4);
             const v4f pw = *reinterpret_cast<const v4f *>(Pb + LP_V + 3 * BC + 4 * g4);
             const float gp = Pb[LP_G], gend = jc < nch ? gp : 1.f;  // (past the last chunk: S unchanged)
-            v4f kt[KC];
-#pragma unroll
-            for (int rt = 0; rt < KC; ++rt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) kt[rt][e] = Kb[(4 * g4 + e) * SX + 16 * rt + l16];
             // D = T rhs, O = diag(c) QS + Cq D, the gate; outputs of padding tokens are dropped
             // at the store
             v4f rhs, o, bw;
@@ -533,16 +591,36 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
                 OT[buf][(4 * g4 + v) * JB + 16 * cw + l16] = ov;
                 bw[v] = pw[v] * dl[v];
             }
-            // S <- G_B S + K^T diag(w) D, tile by tile of 16 d_k rows, with the loads of the
-            // chunk two ahead and the previous chunk's output store spread between its products
-            // (issued in a cluster they stall the wave on the address unit)
+            // S <- G_B S + K^T diag(w) D, tile by tile of 16 d_k rows, in three bf16 products
+            // over 32 slots: lane group g supplies tokens 4g .. 4g + 3 twice, in two parts each,
+            // so that with K^T = Kh + Km + Kl and diag(w) D = Bh + Bm + Bl the products
+            // [Kh | Km] [Bh; Bh], [Kh | Km] [Bm; Bm] and [Kl | Kh] [Bh; Bl] sum the six terms that
+            // matter (all but those below 2^-24 of the product).  The loads of the chunk two
+            // ahead and the previous chunk's output store are spread between the products
+            // (issued in a cluster they stall the wave on the address unit).
+            unsigned bh[2], bm[2], bl[2];
+            {
+                const float bwa[4] = {bw[0], bw[1], bw[2], bw[3]};
+                split3_bf16(bwa, bh, bm, bl);
+            }
+            const bf8 b1 = __builtin_bit_cast(bf8, v4u{bh[0], bh[1], bh[0], bh[1]});
+            const bf8 b2 = __builtin_bit_cast(bf8, v4u{bm[0], bm[1], bm[0], bm[1]});
+            const bf8 b3 = __builtin_bit_cast(bf8, v4u{bh[0], bh[1], bl[0], bl[1]});
             load_chunk(r, jc + 2);
             store_outputs(jc - 1);  // complete since the barrier
 #pragma unroll
-            for (int rt = 0; rt < KC; ++rt) sreg[rt] = mfma4(kt[rt], bw, gend * sreg[rt]);
+            for (int rt = 0; rt < KC; ++rt) {
+                const int at = (16 * rt + l16) * KAS + 8 * g4;
+                const bf8 a1 = *reinterpret_cast<const bf8 *>(KA[buf] + at);
+                const bf8 a2 = *reinterpret_cast<const bf8 *>(KB[buf] + at);
+                v4f acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b3, gend * sreg[rt], 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b2, acc, 0, 0, 0);
+                sreg[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc, 0, 0, 0);
+            }
+            constexpr int kVmem = 4 * KPT + QPT + 4;  // loads and the store of one step
 #pragma unroll
-            for (int i = 0; i < QPT + 4; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 4 * KC / (QPT + 4) > 0 ? 4 * KC / (QPT + 4) : 1, 0);
+            for (int i = 0; i < kVmem; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 3 * KC / kVmem > 0 ? 3 * KC / kVmem : 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
             }
         }

@@ -9,8 +9,8 @@
 each by what the same counter reads for the calibration copy (M MiB read and M MiB
 written by one plain copy kernel), and writes both a markdown table and a JSON
 record that bench.py uses for the roofline's `traffic` field.  The JSON carries the
-SHA-256 of each kernel's source file, so a later change to a kernel makes bench.py
-report its traffic as unknown instead of stale.
+SHA-256 of each kernel's source file and the project headers it includes, so a later
+change to a kernel makes bench.py report its traffic as unknown instead of stale.
 """
 
 from __future__ import annotations
@@ -20,6 +20,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import statistics
 from collections import defaultdict
 
@@ -34,11 +35,35 @@ KERNEL_SOURCES = {  # (matched in this order: conv_tree_verify before tree_verif
     "prefill_state": "csrc/prefill.hip",
     "conv_step": "csrc/decode_step.hip",
 }
+INCLUDE_DIRS = (os.path.join(PKG, "csrc"), os.path.join(os.path.dirname(PKG), "include"))
+
+
+def source_files(kernel: str) -> list:
+    """The kernel's source file and every project header it includes, directly or through
+    another header (quoted includes found in csrc/ or include/), in a fixed order."""
+    out, todo = [], [os.path.join(PKG, KERNEL_SOURCES[kernel])]
+    while todo:
+        path = todo.pop(0)
+        if path in out:
+            continue
+        out.append(path)
+        with open(path, encoding="utf-8") as f:
+            for name in re.findall(r'^\s*#\s*include\s+"([^"]+)"', f.read(), re.M):
+                for d in INCLUDE_DIRS:
+                    if os.path.exists(os.path.join(d, name)):
+                        todo.append(os.path.join(d, name))
+                        break
+    return out
 
 
 def source_sha256(kernel: str) -> str:
-    with open(os.path.join(PKG, KERNEL_SOURCES[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the kernel's source and the project headers it includes: a counter summary
+    taken under another hash no longer describes the built kernel."""
+    h = hashlib.sha256()
+    for path in source_files(kernel):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def short_name(name: str) -> str:

@@ -60,3 +60,19 @@ def test_stats_table(tmp_path):
                         "--workload", "w", "--cmd", "c"], capture_output=True, text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 0, r.stderr
     assert "| replay_commit | 3 | 10.000 | 9.000 | 11.000 | 75.0% |" in r.stdout
+
+
+def test_source_hash_covers_included_headers():
+    """A kernel's recorded hash covers the headers it includes, so a change to a shared
+    device helper invalidates the counter summaries of every kernel built from it."""
+    sys.path.insert(0, ROOT)
+    from gated_deltanet_speculative_amd import rocprof_summary as rs
+
+    for k in rs.KERNEL_SOURCES:
+        names = [os.path.basename(p) for p in rs.source_files(k)]
+        assert names[0] == os.path.basename(rs.KERNEL_SOURCES[k])
+        assert {"gdn_device.h", "gdn_internal.h", "gdn_verify.h"} <= set(names), (k, names)
+        assert len(names) == len(set(names))
+    # kernels built from the same file share a hash; different files differ
+    assert rs.source_sha256("prefill_prep") == rs.source_sha256("prefill_state")
+    assert rs.source_sha256("prefill_prep") != rs.source_sha256("decode_step")
