@@ -348,6 +348,10 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     __shared__ unsigned int s_bitmap[kBitmapSlots / 32];
     __shared__ int s_word;
     constexpr int KAS = 8 * (BC / 4) + 8;    // K^T rows (d_k index) of the update's operands, in bf16
+    // the 16-byte groups of a K^T row sit at group index (token quad) ^ ((row >> KSW) & 3), so
+    // that neither the staging writes (rows 2i and 2i + 1 by lane i) nor the operand reads (rows
+    // 16 rt + l by lane group l) of 16 lanes share a bank
+    constexpr int KSW = 4;
     __shared__ __align__(16) __bf16 XS[2][2][XSB];        // per buffer: hi parts, lo parts of the q and k rows
     __shared__ __align__(16) __bf16 KA[2][DK * KAS];      // per buffer: K^T as [hi | mid] per 4 tokens
     __shared__ __align__(16) __bf16 KB[2][DK * KAS];      // per buffer: K^T as [lo | hi] per 4 tokens
@@ -409,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
     for (int u = 0; u < KPT; ++u) {
         const int b = min(tid + kThreads * u, NKB - 1), qd = b / (DK / 2), col = 2 * (b - qd * (DK / 2));
         k_off[u] = (4 * qd * Ch + d.Hk * DK + kh * DK + col) * 4;
-        ka_at[u] = col * KAS + 8 * qd;
+        ka_at[u] = col * KAS + 8 * (qd ^ ((col >> KSW) & 3));  // (rows col and col + 1 alike)
         kx_at[u] = (BC + 4 * qd) * SXB + xs_col(col);
     }
 #pragma unroll
@@ -610,7 +614,7 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
             store_outputs(jc - 1);  // complete since the barrier
 #pragma unroll
             for (int rt = 0; rt < KC; ++rt) {
-                const int at = (16 * rt + l16) * KAS + 8 * g4;
+                const int row = 16 * rt + l16, at = row * KAS + 8 * (g4 ^ ((row >> KSW) & 3));
                 const bf8 a1 = *reinterpret_cast<const bf8 *>(KA[buf] + at);
                 const bf8 a2 = *reinterpret_cast<const bf8 *>(KB[buf] + at);
                 v4f acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b3, gend * sreg[rt], 0, 0, 0);
