@@ -610,23 +610,34 @@ __global__ __launch_bounds__(kThreads) void prefill_state_kernel(
             const bf8 b1 = __builtin_bit_cast(bf8, v4u{bh[0], bh[1], bh[0], bh[1]});
             const bf8 b2 = __builtin_bit_cast(bf8, v4u{bm[0], bm[1], bm[0], bm[1]});
             const bf8 b3 = __builtin_bit_cast(bf8, v4u{bh[0], bh[1], bl[0], bl[1]});
+            __builtin_amdgcn_sched_barrier(0);  // the update and the memory operations in a region of their own
             load_chunk(r, jc + 2);
             store_outputs(jc - 1);  // complete since the barrier
+            bf8 a1[KC], a2[KC];
 #pragma unroll
             for (int rt = 0; rt < KC; ++rt) {
                 const int row = 16 * rt + l16, at = row * KAS + 8 * (g4 ^ ((row >> KSW) & 3));
-                const bf8 a1 = *reinterpret_cast<const bf8 *>(KA[buf] + at);
-                const bf8 a2 = *reinterpret_cast<const bf8 *>(KB[buf] + at);
-                v4f acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2, b3, gend * sreg[rt], 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b2, acc, 0, 0, 0);
-                sreg[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc, 0, 0, 0);
+                a1[rt] = *reinterpret_cast<const bf8 *>(KA[buf] + at);
+                a2[rt] = *reinterpret_cast<const bf8 *>(KB[buf] + at);
             }
-            constexpr int kVmem = 4 * KPT + QPT + 4;  // loads and the store of one step
 #pragma unroll
-            for (int i = 0; i < kVmem; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 3 * KC / kVmem > 0 ? 3 * KC / kVmem : 1, 0);
+            for (int rt = 0; rt < KC; ++rt) {
+                v4f acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a2[rt], b3, gend * sreg[rt], 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[rt], b2, acc, 0, 0, 0);
+                sreg[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[rt], b1, acc, 0, 0, 0);
+            }
+            // the operand reads of tiles 0 and 1 first; then per tile its three products, the
+            // reads of the tile two ahead and a share of the loads and the store
+            constexpr int kVmem = 4 * KPT + QPT + 4;  // loads and the store of one step
+            constexpr int kAhead = KC < 2 ? KC : 2;
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead + 1, 0);  // (+ the output row read)
+#pragma unroll
+            for (int rt = 0; rt < KC; ++rt) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+                if (rt + kAhead < KC) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                 __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
             }
+            if constexpr (kVmem > KC) __builtin_amdgcn_sched_group_barrier(0x010, kVmem > KC ? kVmem - KC : 1, 0);
         }
     };
     // the state tile and the first two chunks are in before the loop: a load still pending at
