@@ -59,6 +59,12 @@ __device__ inline unsigned int path_mask(int par, int lane, int N, int e) {
     return (e >= 0 && e < N) ? __shfl(anc, e) : 0u;
 }
 
+// Raw buffer resources: word 3 of the descriptor for the gfx9 family (32-bit data,
+// unswizzled); a load past num_records reads zero and a store there is dropped.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;  // cache-policy operand of the buffer stores: nt
+typedef int v4i __attribute__((ext_vector_type(4)));
+
 template <int DK, int DV>
 __global__ __launch_bounds__(kThreads) void replay_commit_kernel(
     Dims d, const LayerPtrs lp, const int32_t *__restrict__ slot_ids, const int32_t *__restrict__ parents,
@@ -222,7 +228,20 @@ __global__ __launch_bounds__(kThreads) void replay_commit_kernel(
         const int n4 = d.Ch * 3 / 4;
         const v4f *src = reinterpret_cast<const v4f *>(lp.commit_win[layer] + ((int64_t)c * N + e) * d.Ch * 3);
         v4f *dst = reinterpret_cast<v4f *>(lp.conv_hist[layer] + (int64_t)s * d.Ch * 3);
-        for (int idx = rb * kThreads + tid; idx < n4; idx += Cfg::NB * kThreads) __builtin_nontemporal_store(src[idx], dst + idx);
+        // batches of kCopy loads, then their stores (one at a time, each store waited for its
+        // load: a memory round trip per element), through raw buffer resources over the
+        // window and the history row, so the elements past the end need no branch (their
+        // loads read zero and their stores are dropped)
+        constexpr int kCopy = 8, kStride = Cfg::NB * kThreads;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<v4f *>(src), 0, n4 * 16, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst, 0, n4 * 16, kRsrcWord3);
+        for (int i0 = rb * kThreads + tid; i0 < n4; i0 += kCopy * kStride) {
+            v4i buf[kCopy];
+#pragma unroll
+            for (int j = 0; j < kCopy; ++j) buf[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (i0 + j * kStride), 0, 0);
+#pragma unroll
+            for (int j = 0; j < kCopy; ++j) __builtin_amdgcn_raw_buffer_store_b128(buf[j], rd, 16 * (i0 + j * kStride), 0, kNonTemporal);
+        }
         return;
     }
 
