@@ -108,12 +108,14 @@ __global__ __launch_bounds__(kThreads) void replay_commit_kernel(
     }
     const int s = slot_ids[c], e = accept_node[c];
     const int st_in = *status;
-    // ---- the state block (slot clamped into range; used only if the round commits)
+    // ---- the state block (slot clamped into range; used only if the round commits), read
+    //      non-temporal like its write-back: each line is used once, and cached loads had the
+    //      state displace the logged rows and windows in L2 (3.48 -> 3.15 us per layer)
     const bool s_ok = s >= 0 && s < d.P;
     v4f *S4 = reinterpret_cast<v4f *>(state_pool + (((int64_t)(s_ok ? s : 0) * Hv + h) * DK + r0) * DV);
     v4f sv[FPT];
 #pragma unroll
-    for (int u = 0; u < FPT; ++u) sv[u] = S4[row_of(u) * Q4 + q];
+    for (int u = 0; u < FPT; ++u) sv[u] = __builtin_nontemporal_load(S4 + row_of(u) * Q4 + q);
 
     // ---- accepted path (every wave computes it) and the replay of its logged rows.
     //      The transitions are linear, so S_final = G S0 + A with G the product of the
