@@ -51,7 +51,7 @@ def parse():
                     help="skip the dispatch-floor launches (so a kernel trace holds only the kernels' real launches)")
     ap.add_argument("--eager", action="store_true", help="launch every call directly instead of replaying graphs")
     ap.add_argument("--route", choices=("fused", "split"), default="fused",
-                    help="fused conv + verify call, or the separate conv step and verify calls")
+                    help="fused conv + verify (decode mode: conv + recurrence) call, or the separate calls")
     ap.add_argument("--commit", choices=("layers", "per-layer"), default="layers",
                     help="one multi-layer commit launch per round, or one commit launch per instance")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -106,7 +106,8 @@ def decode_bytes(wl):
     W = wl.d_conv - 1
     conv = 4 * Ch * (C * (W + 1 + 1 + W) + wl.d_conv)
     decode = 4 * (2 * C * Hv * dk * dv + C * Ch + 2 * C * Hv + 2 * Hv + C * Hv * dv)
-    return dict(conv_step=conv, decode_step=decode)
+    # the fused call: the conv output row is neither written nor read back
+    return dict(conv_step=conv, decode_step=decode, conv_decode=conv + decode - 2 * 4 * C * Ch)
 
 
 def prefill_cost(wl, T, chunk=16):
@@ -292,7 +293,8 @@ def copy_reference(nbytes, dev):
 def decode_main(args):
     """The plain decode step at the workload's head shape: one token per lane, for every
     layer instance the conv step (history written in place) and the one-token recurrence
-    (state updated in place).  value = C * L / step time."""
+    (state updated in place), in one fused launch (--route split: the two calls).
+    value = C * L / step time."""
     import torch
 
     import gated_deltanet_speculative_amd as gdn
@@ -311,6 +313,7 @@ def decode_main(args):
     t_gen = time.time()
     slot_ids = d(round_structure(wl, 0, args.seed)["slot_ids"])
     status = torch.zeros(1, dtype=torch.int32, device=dev)
+    sync = torch.zeros((C, wl.n_k_heads, gdn.SYNC_STRIDE), dtype=torch.int32, device=dev)  # the fused call's counters
     inst = []
     for l in range(L):
         lp, ri = layer_params(wl, l, args.seed), round_inputs(wl, l, 0, args.seed)
@@ -328,10 +331,17 @@ def decode_main(args):
         gdn.decode_step(sh, b["qkv"][:, 0], b["beta"], b["alpha"], b["dt_bias"], b["A"], b["state"], slot_ids,
                         status, out=b["out"])
 
+    def fused(b):
+        gdn.conv_decode_step(sh, b["x"][:, 0], b["conv_w"], b["conv_hist"], b["beta"], b["alpha"], b["dt_bias"],
+                             b["A"], b["state"], slot_ids, sync, status, out=b["out"])
+
     def step():
         for b in inst:
-            conv(b)
-            rec(b)
+            if args.route == "fused":
+                fused(b)
+            else:
+                conv(b)
+                rec(b)
 
     for _ in range(args.warmup):
         step()
@@ -358,21 +368,27 @@ def decode_main(args):
     ms_step = timed_graph(step, args.steps)
     kern = {}
     if not args.profile_only:
-        kern["conv_step"] = timed_graph(lambda: [conv(b) for b in inst], args.kernel_reps) * 1e3 / L
-        kern["decode_step"] = timed_graph(lambda: [rec(b) for b in inst], args.kernel_reps) * 1e3 / L
+        if args.route == "fused":
+            kern["conv_decode"] = timed_graph(lambda: [fused(b) for b in inst], args.kernel_reps) * 1e3 / L
+        else:
+            kern["conv_step"] = timed_graph(lambda: [conv(b) for b in inst], args.kernel_reps) * 1e3 / L
+            kern["decode_step"] = timed_graph(lambda: [rec(b) for b in inst], args.kernel_reps) * 1e3 / L
     assert int(status.item()) == 0, "device status bits set"
+    assert not sync.any(), "sync counters left non-zero"
     calibrate_copy(args.calibrate_copy, dev)
     kb = decode_bytes(wl)
-    # context for the recurrence: a plain copy of its bytes (the state block read and written)
-    copy_ref = None if args.profile_only else copy_reference(kb["decode_step"], dev)
+    # split: the recurrence moves 14x the conv step's bytes; both launches are near the dispatch
+    # floor, so which one times longer over a few replays is noise, and the roofline stays with
+    # the recurrence
+    dom = "conv_decode" if args.route == "fused" else "decode_step"
+    # context for the dominant kernel: a plain copy of its bytes (mostly the state block read and written)
+    copy_ref = None if args.profile_only else copy_reference(kb[dom], dev)
     roofline = None
     if kern:
-        # the recurrence moves 14x the conv step's bytes; both launches are near the dispatch floor, so
-        # which one times longer over a few replays is noise, and the roofline stays with the recurrence
-        dom = "decode_step"
         achieved = kb[dom] / (kern[dom] * 1e-6) / 1e9
+        traffic_wl = wl.name + ("-decode" if args.route == "fused" else "-decode-split")
         roofline = dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(wl.name + "-decode", dom),
+                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(traffic_wl, dom),
                         bytes_per_launch=int(kb[dom]), us_per_launch=round(kern[dom], 3))
     line = {
         "metric": "GDN plain decode tokens/s (one token per lane, state committed in place)",
@@ -391,8 +407,11 @@ def decode_main(args):
                   + "; inputs resident in HBM",
         "config": {"workload": wl.name + "-decode", "lanes": C, "tokens_per_lane": 1, "slots": P,
                    "k_heads": wl.n_k_heads, "v_heads": Hv, "d_k": dk, "d_v": dv, "conv_channels": Ch,
-                   "layer_instances": L, "step": "conv step + one-token recurrence per instance"},
-        "step_gbs": round(L * (kb["conv_step"] + kb["decode_step"]) / (ms_step * 1e-3) / 1e9, 1),
+                   "layer_instances": L,
+                   "step": ("fused conv step + one-token recurrence per instance" if args.route == "fused"
+                            else "conv step + one-token recurrence per instance")},
+        "step_gbs": round(L * (kb["conv_decode"] if args.route == "fused" else kb["conv_step"] + kb["decode_step"])
+                          / (ms_step * 1e-3) / 1e9, 1),
         "kernel_us": {k: round(v, 3) for k, v in kern.items()},
         "kernel_gbs": {k: round(kb[k] / (kern[k] * 1e-6) / 1e9, 1) for k in kern},
         "copy_same_bytes": copy_ref,

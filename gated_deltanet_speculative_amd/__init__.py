@@ -14,6 +14,7 @@ directly:
 
     conv_step       -> conv_out; writes each slot's conv history in place
     decode_step     -> out; applies one token to each slot's state in place
+    conv_decode_step -> out; the two above for one token, fused in one launch
 
 and a prompt fills a slot with conv_step over its tokens followed by
 
@@ -38,6 +39,8 @@ from ._lib import (  # noqa: F401
     STATUS_PARENT,
     STATUS_SLOT_DUP,
     STATUS_SLOT_RANGE,
+    SYNC_STRIDE,
+    conv_decode_step,
     conv_step,
     conv_tree_step,
     conv_tree_verify,

@@ -22,10 +22,11 @@ LIB_PATH = os.path.join(_HERE, "libgdnverify.so")
  GDN_ERR_WORKSPACE, GDN_ERR_SCRATCH) = range(9)
 STATUS_SLOT_RANGE, STATUS_SLOT_DUP, STATUS_PARENT, STATUS_ACCEPT, STATUS_NODES = 1, 2, 4, 8, 16
 EXPORTED = ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_conv_tree_verify", "gdn_replay_commit",
-            "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step", "gdn_prefill", "gdn_prefill_workspace_size",
-            "gdn_prefill_noalloc", "gdn_strerror")
+            "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step", "gdn_conv_decode_step", "gdn_prefill",
+            "gdn_prefill_workspace_size", "gdn_prefill_noalloc", "gdn_strerror")
 MAX_CHAIN = 65536
 MAX_LAYERS = 64
+SYNC_STRIDE = 32  # int32 per counter of conv_decode_step (one 128-byte line)
 
 
 class GdnError(RuntimeError):
@@ -82,12 +83,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdn_replay_commit_layers.argtypes = [sp, i32] + [vp] * 10
     lib.gdn_conv_step.argtypes = [sp] + [vp] * 7
     lib.gdn_decode_step.argtypes = [sp, vp, vp, vp, i64] + [vp] * 7
+    lib.gdn_conv_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, i64] + [vp] * 8
     lib.gdn_prefill.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, vp, vp, ctypes.c_size_t, vp, vp]
     lib.gdn_prefill_noalloc.argtypes = [sp, vp, vp, vp, i64, vp, vp, vp, vp, vp, i32, vp, vp, vp]
     lib.gdn_prefill_workspace_size.argtypes = [sp]
     lib.gdn_prefill_workspace_size.restype = ctypes.c_size_t
     for f in ("gdn_conv_tree_step", "gdn_tree_verify", "gdn_conv_tree_verify", "gdn_replay_commit",
-              "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step", "gdn_prefill",
+              "gdn_replay_commit_layers", "gdn_conv_step", "gdn_decode_step", "gdn_conv_decode_step", "gdn_prefill",
               "gdn_prefill_noalloc"):
         getattr(lib, f).restype = i32
     lib.gdn_strerror.argtypes = [ctypes.c_int]
@@ -380,6 +382,40 @@ def decode_step(sh: Shape, qkv, beta_logits, alpha_logits, dt_bias, A, state_poo
     ]
     cs = sh.c_struct()
     _check(load_library().gdn_decode_step(ctypes.byref(cs), *args), "gdn_decode_step")
+    return out
+
+
+def conv_decode_step(sh: Shape, x, conv_w, conv_hist, beta_logits, alpha_logits, dt_bias, A, state_pool, slot_ids,
+                     sync, status, out=None):
+    """conv_step over one token per lane and decode_step on its output, in one launch (the
+    same results; n_nodes must be 1).  x is [C, Ch]; sync is a [C, H_k, SYNC_STRIDE] int32
+    array that is zero on entry and left zero (not shared by calls that overlap).  A transaction on the
+    status word.  Returns out [C, H_v, d_v]."""
+    C, P, Hk, Hv, dk, dv, Ch = sh.n_seqs, sh.n_slots, sh.n_k_heads, sh.n_v_heads, sh.d_k, sh.d_v, sh.channels
+    if status is None:
+        raise ValueError("conv_decode_step needs a status word (it mutates the pools)")
+    if out is None:
+        out = torch.empty((C, Hv, dv), dtype=torch.float32, device=x.device)
+    bp, bs = _row_gate_view(beta_logits, "beta_logits", sh)
+    ap, as_ = _row_gate_view(alpha_logits, "alpha_logits", sh)
+    if bs != as_:
+        raise ValueError("beta_logits and alpha_logits must share one row stride")
+    args = [
+        _dev(x, "x", torch.float32, (C, Ch)),
+        _dev(conv_w, "conv_w", torch.float32, (Ch, sh.d_conv)),
+        _dev(conv_hist, "conv_hist", torch.float32, (P, Ch, sh.d_conv - 1)),
+        bp, ap, bs,
+        _dev(dt_bias, "dt_bias", torch.float32, (Hv,)),
+        _dev(A, "A", torch.float32, (Hv,)),
+        _dev(state_pool, "state_pool", torch.float32, (P, Hv, dk, dv)),
+        _dev(slot_ids, "slot_ids", torch.int32, (C,)),
+        _dev(sync, "sync", torch.int32, (C, Hk, SYNC_STRIDE)),
+        _dev(out, "out", torch.float32, (C, Hv, dv)),
+        _dev(status, "status", torch.int32, (1,)),
+        _stream(x),
+    ]
+    cs = sh.c_struct()
+    _check(load_library().gdn_conv_decode_step(ctypes.byref(cs), *args), "gdn_conv_decode_step")
     return out
 
 

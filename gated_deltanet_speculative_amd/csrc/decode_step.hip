@@ -160,6 +160,46 @@ struct DecodeCfg {
     static_assert(RPL >= 1 && RG * RPL == DK, "rows tile the wave");
 };
 
+// The recurrence of one token on a wave's block once its inputs are in registers: this
+// thread's q / k rows qq, kq, value columns v, raw gates and state rows sv (loaded from S4);
+// writes the rows back and, in row group 0, the output columns to *o4.
+template <int DK, int DV>
+__device__ __forceinline__ void decode_block(const float (&qq)[DecodeCfg<DK, DV>::RPL],
+                                             const float (&kq)[DecodeCfg<DK, DV>::RPL], v4f v, float braw, float araw,
+                                             float Ah, const v4f (&sv)[DecodeCfg<DK, DV>::RPL], v4f *S4, int i0, int r,
+                                             v4f *o4) {
+    constexpr int Q4 = DecodeCfg<DK, DV>::Q4, RPL = DecodeCfg<DK, DV>::RPL;
+    // |q|^2, |k|^2, q . k and the column sums of k_i S[i][j], q_i S[i][j] over this thread's
+    // rows, then over the row groups (the lanes sharing q)
+    float ssq = 0.f, ssk = 0.f, sqk = 0.f;
+    v4f pu = {0.f, 0.f, 0.f, 0.f}, pw = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < RPL; ++e) {
+        ssq = fmaf(qq[e], qq[e], ssq);
+        ssk = fmaf(kq[e], kq[e], ssk);
+        sqk = fmaf(qq[e], kq[e], sqk);
+        pu += kq[e] * sv[e];
+        pw += qq[e] * sv[e];
+    }
+    ssq = sum_lanes_sharing<Q4>(ssq);
+    ssk = sum_lanes_sharing<Q4>(ssk);
+    sqk = sum_lanes_sharing<Q4>(sqk);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        pu[e] = sum_lanes_sharing<Q4>(pu[e]);
+        pw[e] = sum_lanes_sharing<Q4>(pw[e]);
+    }
+    const float rq = inv_norm(ssq), rk = inv_norm(ssk);
+    // S' = g S;  delta = beta (v - S'^T k^);  S_new = S' + k^ delta^T;
+    // o = S_new^T q^ / sqrt(d_k) = (g S^T q^ + (q^ . k^) delta) / sqrt(d_k)
+    const float g = fast_exp(fast_softplus(araw) * Ah), beta = fast_sigmoid(braw);
+    const v4f delta = beta * (v - (g * rk) * pu);
+#pragma unroll
+    for (int e = 0; e < RPL; ++e) __builtin_nontemporal_store(g * sv[e] + (kq[e] * rk) * delta, S4 + (i0 + e) * (DV / 4));
+    if (r == 0) *o4 = ((g * rq) * pw + (sqk * rq * rk) * delta) * (1.0f / sqrtf((float)DK));
+}
+
+
 template <int DK, int DV>
 __global__ __launch_bounds__(64) void decode_step_kernel(
     Dims d, const float *__restrict__ qkv, const float *__restrict__ beta_logits,
@@ -213,36 +253,148 @@ __global__ __launch_bounds__(64) void decode_step_kernel(
     }
     if (s < 0) return;  // padding lane (uniform over the wave)
 
-    // |q|^2, |k|^2, q . k and the column sums of k_i S[i][j], q_i S[i][j] over this thread's
-    // rows, then over the row groups (the lanes sharing q)
-    float ssq = 0.f, ssk = 0.f, sqk = 0.f;
-    v4f pu = {0.f, 0.f, 0.f, 0.f}, pw = {0.f, 0.f, 0.f, 0.f};
+    decode_block<DK, DV>(qq, kq, v, braw, araw, Ah, sv, S4, i0, r, reinterpret_cast<v4f *>(out + ((int64_t)c * d.Hv + h) * DV + j0) + q);
+}
+
+// ---- fused plain step: the waves of decode_step_kernel, each first forming the conv output of
+//      the channels it needs (the 2 d_k channels of its q/k head and the JB value channels of
+//      its block) from the slot's history, the token and the taps, into LDS.  The history is
+//      updated in place once every reader is done with it: a wave writes its value channels'
+//      new history itself (no other wave reads them); the q/k channels are read by the
+//      R * NB waves of their (lane, q/k head), so the wave that arrives last at
+//      sync[(c * H_k + kh) * GDN_SYNC_STRIDE] -- an atomic count taken after the wave's
+//      history reads are back -- writes their new history and sets the count back to zero.
+//      One counter per 128-byte line: packed into two lines, the 512 counts of the bench
+//      shape queued on one L2 channel (2.4 us of a 9.3 us launch).
+template <int DK, int DV>
+__global__ __launch_bounds__(64) void conv_decode_kernel(
+    Dims d, const float *__restrict__ x, const float *__restrict__ conv_w, float *__restrict__ conv_hist,
+    const float *__restrict__ beta_logits, const float *__restrict__ alpha_logits, int64_t gate_stride,
+    const float *__restrict__ dt_bias, const float *__restrict__ A, float *__restrict__ state_pool,
+    const int32_t *__restrict__ slot_ids, int32_t *__restrict__ sync, float *__restrict__ out,
+    int32_t *__restrict__ status) {
+    using Cfg = DecodeCfg<DK, DV>;
+    constexpr int JB = Cfg::JB, NB = Cfg::NB, Q4 = Cfg::Q4, RPL = Cfg::RPL;
+    constexpr int GQK = DK / 2, GV = JB / 4, NI = (GQK + GV + 63) / 64;  // 4-channel groups; per lane
+    __shared__ unsigned int s_bitmap[kBitmapSlots / 32];
+    __shared__ int s_word;
+    __shared__ __align__(16) float s_y[2 * DK + JB];  // conv outputs: q rows, k rows, value columns
+
+    const int c = blockIdx.y, h = blockIdx.x / NB, jb = blockIdx.x - h * NB, j0 = jb * JB;
+    const int kh = h % d.Hk;
+    const int lane = threadIdx.x;
+    const int q = lane % Q4, r = lane / Q4, i0 = r * RPL;
+    // loads in the order they are needed, as in decode_step_kernel: slot id, the preflight's
+    // slot ids, the taps and token of this lane's channel groups (item u = group lane + 64 u
+    // of the q/k slab, then of the value block), the gates; then the history and the state
+    const int s_v = __builtin_bit_cast(
+        int, __builtin_amdgcn_raw_buffer_load_b32(
+                 __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(slot_ids), 0, 4 * d.C, 0x00020000), 4 * c, 0,
+                 0));
+    const LaneSlotsT<64> lanes(slot_ids, d.C);
+    const int st_in = *status;
+    int ch[NI], at[NI];
+    v4f w[NI][4], xv[NI];
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+        const int f = min(lane + 64 * u, GQK + GV - 1);
+        ch[u] = f < DK / 4 ? kh * DK + 4 * f
+                : f < GQK  ? d.Hk * DK + kh * DK + 4 * (f - DK / 4)
+                           : 2 * d.Hk * DK + h * DV + j0 + 4 * (f - GQK);
+        at[u] = f < GQK ? 4 * f : 2 * DK + 4 * (f - GQK);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[u][e] = reinterpret_cast<const v4f *>(conv_w)[ch[u] + e];
+        xv[u] = *reinterpret_cast<const v4f *>(x + (int64_t)c * d.Ch + ch[u]);
+    }
+    const float braw = beta_logits[(int64_t)c * gate_stride + h];
+    const float araw = alpha_logits[(int64_t)c * gate_stride + h] + dt_bias[h];
+    const float Ah = A[h];
+    __builtin_amdgcn_sched_barrier(0);
+    const int s = __builtin_amdgcn_readfirstlane(s_v);
+    const bool s_ok = s >= 0 && s < d.P;
+    v4f hv[NI][3];  // history of the item's 4 channels, layout [ch][3]: 12 consecutive floats
+#pragma unroll
+    for (int u = 0; u < NI; ++u)
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            hv[u][k] = reinterpret_cast<const v4f *>(conv_hist + ((int64_t)(s_ok ? s : 0) * d.Ch + ch[u]) * 3)[k];
+    v4f *S4 = reinterpret_cast<v4f *>(state_pool + ((int64_t)(s_ok ? s : 0) * d.Hv + h) * DK * DV + j0) + q;
+    v4f sv[RPL];
+#pragma unroll
+    for (int e = 0; e < RPL; ++e) sv[e] = __builtin_nontemporal_load(S4 + (i0 + e) * (DV / 4));
+
+    // conv + SiLU of the items' channels (the conv step's order of taps and accumulation)
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+        if (GQK + GV < 64 * NI && lane + 64 * u >= GQK + GV) continue;
+        const v4f h0 = hv[u][0], h1 = hv[u][1], h2 = hv[u][2];
+        const v4f a = v4f{h0.x, h0.w, h1.z, h2.y}, b = v4f{h0.y, h1.x, h1.w, h2.z}, cc = v4f{h0.z, h1.y, h2.x, h2.w};
+        v4f y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float z = a[e] * w[u][e][0];
+            z = fmaf(b[e], w[u][e][1], z);
+            z = fmaf(cc[e], w[u][e][2], z);
+            z = fmaf(xv[u][e], w[u][e][3], z);
+            y[e] = fast_silu(z);
+        }
+        *reinterpret_cast<v4f *>(s_y + at[u]) = y;
+    }
+    // Count this wave among the readers of its q/k history as soon as its reads are back (the
+    // conv above consumed them, and the count is not moved above those stores); its return
+    // is needed only at the end.  Every wave of the group counts, whatever the verdict, so
+    // the last one can always set the count back to zero.
+    asm volatile("" ::: "memory");
+    int last = 0;
+    if (lane == 0) last = atomicAdd(&sync[(c * d.Hk + kh) * GDN_SYNC_STRIDE], 1) == (d.Hv / d.Hk) * NB - 1;
+    lds_barrier();
+    float qq[RPL], kq[RPL];
 #pragma unroll
     for (int e = 0; e < RPL; ++e) {
-        ssq = fmaf(qq[e], qq[e], ssq);
-        ssk = fmaf(kq[e], kq[e], ssk);
-        sqk = fmaf(qq[e], kq[e], sqk);
-        pu += kq[e] * sv[e];
-        pw += qq[e] * sv[e];
+        qq[e] = s_y[i0 + e];
+        kq[e] = s_y[DK + i0 + e];
     }
-    ssq = sum_lanes_sharing<Q4>(ssq);
-    ssk = sum_lanes_sharing<Q4>(ssk);
-    sqk = sum_lanes_sharing<Q4>(sqk);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        pu[e] = sum_lanes_sharing<Q4>(pu[e]);
-        pw[e] = sum_lanes_sharing<Q4>(pw[e]);
+    const v4f v = *reinterpret_cast<const v4f *>(s_y + 2 * DK + 4 * q);
+
+    const int bits = slot_preflight<64>(lanes, slot_ids, d.C, d.P, s_bitmap, &s_word);
+    if (bits || st_in || s < 0) {  // rejected step, or a padding lane (uniform over the wave)
+        if (bits && blockIdx.x == 0 && blockIdx.y == 0 && lane == 0) atomicOr(status, bits);
+        if (__builtin_amdgcn_readfirstlane(last) && lane == 0) atomicExch(&sync[(c * d.Hk + kh) * GDN_SYNC_STRIDE], 0);
+        return;
     }
-    const float rq = inv_norm(ssq), rk = inv_norm(ssk);
-    // S' = g S;  delta = beta (v - S'^T k^);  S_new = S' + k^ delta^T;
-    // o = S_new^T q^ / sqrt(d_k) = (g S^T q^ + (q^ . k^) delta) / sqrt(d_k)
-    const float g = fast_exp(fast_softplus(araw) * Ah), beta = fast_sigmoid(braw);
-    const v4f delta = beta * (v - (g * rk) * pu);
+
+    // the new history [column 1, column 2, token] of item u's channels
+    auto write_hist = [&](int u) {
+        const v4f h0 = hv[u][0], h1 = hv[u][1], h2 = hv[u][2];
+        const v4f b = v4f{h0.y, h1.x, h1.w, h2.z}, cc = v4f{h0.z, h1.y, h2.x, h2.w}, xt = xv[u];
+        v4f *hp = reinterpret_cast<v4f *>(conv_hist + ((int64_t)s * d.Ch + ch[u]) * 3);
+        hp[0] = v4f{b.x, cc.x, xt.x, b.y};
+        hp[1] = v4f{cc.y, xt.y, b.z, cc.z};
+        hp[2] = v4f{xt.z, b.w, cc.w, xt.w};
+    };
 #pragma unroll
-    for (int e = 0; e < RPL; ++e) __builtin_nontemporal_store(g * sv[e] + (kq[e] * rk) * delta, S4 + (i0 + e) * (DV / 4));
-    if (r == 0)
-        reinterpret_cast<v4f *>(out + ((int64_t)c * d.Hv + h) * DV + j0)[q] =
-            ((g * rq) * pw + (sqk * rq * rk) * delta) * (1.0f / sqrtf((float)DK));
+    for (int u = 0; u < NI; ++u) {
+        const int f = lane + 64 * u;
+        if (f >= GQK && f < GQK + GV) write_hist(u);  // this wave's value channels
+    }
+    decode_block<DK, DV>(qq, kq, v, braw, araw, Ah, sv, S4, i0, r, reinterpret_cast<v4f *>(out + ((int64_t)c * d.Hv + h) * DV + j0) + q);
+    if (__builtin_amdgcn_readfirstlane(last)) {  // the last reader of the q/k history
+#pragma unroll
+        for (int u = 0; u < NI; ++u)
+            if (lane + 64 * u < GQK) write_hist(u);
+        if (lane == 0) atomicExch(&sync[(c * d.Hk + kh) * GDN_SYNC_STRIDE], 0);
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch_conv_decode(const Dims &d, const float *x, const float *conv_w, float *conv_hist,
+                              const float *beta_logits, const float *alpha_logits, int64_t gate_stride,
+                              const float *dt_bias, const float *A, float *state_pool, const int32_t *slot_ids,
+                              int32_t *sync, float *out, int32_t *status, hipStream_t stream) {
+    hipLaunchKernelGGL((conv_decode_kernel<DK, DV>), dim3(DecodeCfg<DK, DV>::NB * d.Hv, d.C), dim3(64), 0, stream, d,
+                       x, conv_w, conv_hist, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids,
+                       sync, out, status);
+    return hipGetLastError();
 }
 
 template <int DK, int DV>
@@ -277,6 +429,21 @@ hipError_t launch_decode_step(const Dims &d, const float *qkv, const float *beta
     GDN_DECODE_ROW(16) GDN_DECODE_ROW(32) GDN_DECODE_ROW(64) GDN_DECODE_ROW(128)
 #undef GDN_DECODE_ROW
 #undef GDN_DECODE_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_conv_decode_step(const Dims &d, const float *x, const float *conv_w, float *conv_hist,
+                                   const float *beta_logits, const float *alpha_logits, int64_t gate_stride,
+                                   const float *dt_bias, const float *A, float *state_pool, const int32_t *slot_ids,
+                                   int32_t *sync, float *out, int32_t *status, hipStream_t stream) {
+#define GDN_FUSED_CASE(K, V)                                                                                       \
+    if (d.dk == K && d.dv == V)                                                                                    \
+        return launch_conv_decode<K, V>(d, x, conv_w, conv_hist, beta_logits, alpha_logits, gate_stride, dt_bias, A, \
+                                        state_pool, slot_ids, sync, out, status, stream);
+#define GDN_FUSED_ROW(K) GDN_FUSED_CASE(K, 16) GDN_FUSED_CASE(K, 32) GDN_FUSED_CASE(K, 64) GDN_FUSED_CASE(K, 128)
+    GDN_FUSED_ROW(16) GDN_FUSED_ROW(32) GDN_FUSED_ROW(64) GDN_FUSED_ROW(128)
+#undef GDN_FUSED_ROW
+#undef GDN_FUSED_CASE
     return hipErrorInvalidValue;
 }
 

@@ -266,6 +266,33 @@ int gdn_decode_step(const gdn_shape *sh, const float *qkv, const float *beta_log
                : GDN_ERR_HIP;
 }
 
+int gdn_conv_decode_step(const gdn_shape *sh, const float *x, const float *conv_w, float *conv_hist,
+                         const float *beta_logits, const float *alpha_logits, int64_t gate_stride,
+                         const float *dt_bias, const float *A, float *state_pool, const int32_t *slot_ids,
+                         int32_t *sync, float *out, int32_t *status, hipStream_t stream) {
+    gdn::Dims d;
+    if (int r = check_shape(sh, &d)) return r;
+    if (d.N != 1) return GDN_ERR_UNSUPPORTED;
+    if (!x || !conv_w || !conv_hist || !beta_logits || !alpha_logits || !dt_bias || !A || !state_pool || !slot_ids ||
+        !sync || !out || !status)
+        return GDN_ERR_NULL;
+    if (gate_stride < d.Hv) return GDN_ERR_SHAPE;
+    if (!aligned({x, conv_w, conv_hist, state_pool, out}, 16) ||
+        !aligned({beta_logits, alpha_logits, dt_bias, A, slot_ids, sync, status}, 4))
+        return GDN_ERR_ALIGN;
+    const size_t gate_bytes = ((size_t)(d.C - 1) * (size_t)gate_stride + d.Hv) * F;
+    if (any_alias({{conv_hist, (size_t)d.P * d.Ch * 3 * F}, {state_pool, (size_t)d.P * d.Hv * d.dk * d.dv * F},
+                   {out, (size_t)d.C * d.Hv * d.dv * F}, {sync, (size_t)d.C * d.Hk * GDN_SYNC_STRIDE * I}, {status, I}},
+                  {{x, (size_t)d.C * d.Ch * F}, {conv_w, (size_t)d.Ch * 4 * F}, {beta_logits, gate_bytes},
+                   {alpha_logits, gate_bytes}, {dt_bias, (size_t)d.Hv * F}, {A, (size_t)d.Hv * F},
+                   {slot_ids, (size_t)d.C * I}}))
+        return GDN_ERR_ALIAS;
+    return gdn::launch_conv_decode_step(d, x, conv_w, conv_hist, beta_logits, alpha_logits, gate_stride, dt_bias, A,
+                                        state_pool, slot_ids, sync, out, status, stream) == hipSuccess
+               ? GDN_OK
+               : GDN_ERR_HIP;
+}
+
 size_t gdn_prefill_workspace_size(const gdn_shape *sh) {
     gdn::Dims d;
     if (check_shape(sh, &d, true)) return 0;

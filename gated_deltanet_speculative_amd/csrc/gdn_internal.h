@@ -61,6 +61,11 @@ hipError_t launch_conv_step(const Dims &d, const float *x, const float *conv_w, 
 hipError_t launch_decode_step(const Dims &d, const float *qkv, const float *beta_logits, const float *alpha_logits,
                               int64_t gate_stride, const float *dt_bias, const float *A, float *state_pool,
                               const int32_t *slot_ids, float *out, int32_t *status, hipStream_t stream);
+// Both in one launch; sync holds C * H_k zero counters GDN_SYNC_STRIDE apart, left zero.
+hipError_t launch_conv_decode_step(const Dims &d, const float *x, const float *conv_w, float *conv_hist,
+                                   const float *beta_logits, const float *alpha_logits, int64_t gate_stride,
+                                   const float *dt_bias, const float *A, float *state_pool, const int32_t *slot_ids,
+                                   int32_t *sync, float *out, int32_t *status, hipStream_t stream);
 
 // Prefill: the recurrence over a chain of d.N tokens per lane, state updated in place,
 // optional output gate (gate_z may be null).  Two launches: the chunk coefficients of

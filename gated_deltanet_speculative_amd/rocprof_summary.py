@@ -30,6 +30,7 @@ KERNEL_SOURCES = {  # (matched in this order: conv_tree_verify before tree_verif
     "conv_tree_step": "csrc/conv_tree_step.hip",
     "tree_verify": "csrc/tree_verify.hip",
     "replay_commit": "csrc/replay_commit.hip",
+    "conv_decode": "csrc/decode_step.hip",  # the fused plain step (conv_decode_kernel)
     "decode_step": "csrc/decode_step.hip",
     "prefill_prep": "csrc/prefill.hip",
     "prefill_state": "csrc/prefill.hip",

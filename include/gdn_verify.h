@@ -21,7 +21,8 @@
  *   gdn_conv_step    causal conv + SiLU over a chain of tokens per lane, writing each
  *                    slot's new conv history in place;
  *   gdn_decode_step  one token of the gated delta rule applied to each slot's state in
- *                    place, with the output row.
+ *                    place, with the output row
+ *                    (gdn_conv_decode_step: both for one token in one launch).
  *
  * A prompt fills a slot the same way, with gdn_conv_step over its tokens and then
  *   gdn_prefill      the gated delta rule over a chain of tokens per lane, the slot's state
@@ -314,6 +315,38 @@ int gdn_conv_step(const gdn_shape *sh, const float *x, const float *conv_w, floa
 int gdn_decode_step(const gdn_shape *sh, const float *qkv, const float *beta_logits, const float *alpha_logits,
                     int64_t gate_stride, const float *dt_bias, const float *A, float *state_pool,
                     const int32_t *slot_ids, float *out, int32_t *status, hipStream_t stream);
+
+/*
+ * Plain decode step in one launch: gdn_conv_step over one token per lane followed by
+ * gdn_decode_step on its output, with the same results bit for bit (the conv output stays
+ * on chip and is not written).  Same sources as those two calls.  The pages fuse only the
+ * verify route ("perf(qwen35): fuse the DFlash2 concurrent verify Gated DeltaNet route",
+ * Summary: fewer launches and less temporary traffic); this call applies the same fusion
+ * to the plain step, as gdn_conv_tree_verify does to the verify.
+ *
+ * n_nodes must be 1 (GDN_ERR_UNSUPPORTED otherwise).  A transaction with the preflight of
+ * gdn_conv_step: on a bad slot or a non-zero *status nothing is written at all.
+ *
+ *   x              [C][Ch]             the token of each lane                 (read)
+ *   conv_w         [Ch][4]             depthwise taps                         (read)
+ *   conv_hist      [P][Ch][3]          history pool, updated in place
+ *   beta_logits, alpha_logits, gate_stride, dt_bias, A   as in gdn_decode_step
+ *   state_pool     [P][H_v][d_k][d_v]  updated in place
+ *   slot_ids       [C]                 int32, -1 = padding lane               (read)
+ *   sync           [C][H_k][GDN_SYNC_STRIDE]  int32 counters (element [c][kh][0] of each
+ *                                      128-byte line), all zero on entry; every call leaves
+ *                                      them zero.  The in-place history of a q/k channel is
+ *                                      read by all the workgroups of its (lane, q/k head); the
+ *                                      last of them to count itself here writes it.  Calls
+ *                                      that overlap in time must not share one sync array.
+ *   out            [C][H_v][d_v]       written for non-padding lanes
+ *   status         int32*, REQUIRED (GDN_ERR_NULL otherwise)
+ */
+#define GDN_SYNC_STRIDE 32 /* int32 per counter of gdn_conv_decode_step: one 128-byte line */
+int gdn_conv_decode_step(const gdn_shape *sh, const float *x, const float *conv_w, float *conv_hist,
+                         const float *beta_logits, const float *alpha_logits, int64_t gate_stride,
+                         const float *dt_bias, const float *A, float *state_pool, const int32_t *slot_ids,
+                         int32_t *sync, float *out, int32_t *status, hipStream_t stream);
 
 /*
  * Prefill ("Feature/support dflash2", first-version commit message: prefill's recurrence

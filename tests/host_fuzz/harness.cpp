@@ -36,7 +36,7 @@ int main() {
         gdn_shape s = shape();
         const gdn_shape *sp = R(0, 50) ? &s : nullptr;
         long long b = R(1, 20);
-        int which = (int)R(0, 8), r = 0;
+        int which = (int)R(0, 9), r = 0;
         switch (which) {
         case 0: r = gdn_conv_tree_step(sp, cf(b), cf(b + 1), cf(b + 2), I(b + 3), I(b + 4), (int32_t *)maybe(I(b + 12)),
                                        (float *)maybe(F(b + 5)), (float *)maybe(F(b + 6)), (int32_t *)maybe(I(b + 7)), nullptr); break;
@@ -72,6 +72,10 @@ int main() {
                                         (float *)maybe(F(b + 5)), I(b + 6), R(0, 1) ? cf(b + 7) : nullptr,
                                         (int32_t)R(-1, 2), (float *)maybe(F(b + 8)), (int32_t *)maybe(I(b + 10)),
                                         nullptr); break;
+        case 9: r = gdn_conv_decode_step(sp, cf(b), cf(b + 1), (float *)maybe(F(b + 2)), cf(b + 3), cf(b + 4), R(-1, 200),
+                                         cf(b + 5), cf(b + 6), (float *)maybe(F(b + 7)), I(b + 8),
+                                         (int32_t *)maybe(I(b + 9)), (float *)maybe(F(b + 10)),
+                                         (int32_t *)maybe(I(b + 11)), nullptr); break;
         }
         if (!known(r)) { std::printf("unknown return %d from call %d\n", r, which); return 1; }
         ++counts[r];

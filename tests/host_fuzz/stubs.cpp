@@ -19,6 +19,11 @@ hipError_t launch_decode_step(const Dims &, const float *, const float *, const 
                               const float *, float *, const int32_t *, float *, int32_t *, hipStream_t) {
     ++g_launches; return hipSuccess;
 }
+hipError_t launch_conv_decode_step(const Dims &, const float *, const float *, float *, const float *, const float *,
+                                   int64_t, const float *, const float *, float *, const int32_t *, int32_t *, float *,
+                                   int32_t *, hipStream_t) {
+    ++g_launches; return hipSuccess;
+}
 hipError_t launch_prefill(const Dims &, int, const float *, const float *, const float *, int64_t, const float *,
                           const float *, float *, const int32_t *, const float *, int, float *, float *, int32_t *,
                           hipStream_t) {

@@ -76,6 +76,9 @@ def test_decode_bytes_tensor_by_tensor():
     assert db["conv_step"] == 4 * (2 * C * Ch * W + C * Ch + C * Ch + Ch * wl.d_conv)
     # recurrence: state read and written, conv row, two gates, dt and A, output row
     assert db["decode_step"] == 4 * (2 * C * Hv * dk * dv + C * Ch + 2 * C * Hv + 2 * Hv + C * Hv * dv)
+    # fused: both, without the conv row written by one and read by the other
+    assert db["conv_decode"] == 4 * (2 * C * Ch * W + C * Ch + Ch * wl.d_conv + 2 * C * Hv * dk * dv + 2 * C * Hv
+                                     + 2 * Hv + C * Hv * dv)
 
 
 def test_more_than_one_gpu_is_refused():

@@ -27,6 +27,8 @@ def _bench(*extra):
 @pytest.mark.gpu
 @pytest.mark.parametrize("extra,workload", [((), "tree-c4-n16"), (("--mode", "decode", "--instances", "8"),
                                                                     "tree-c4-n16-decode"),
+                                            (("--mode", "decode", "--route", "split", "--instances", "8"),
+                                             "tree-c4-n16-decode"),
                                             (("--lanes", "8", "--instances", "8"), "tree-c4-n16-lanes8")])
 def test_bench_line(extra, workload):
     d = _bench(*extra)
@@ -37,6 +39,8 @@ def test_bench_line(extra, workload):
     assert rl["bound"] == "hbm" and rl["unit"] == "GB/s" and rl["peak"] == 8000.0
     assert abs(rl["frac"] - rl["achieved"] / rl["peak"]) < 1e-3
     assert abs(rl["achieved"] - rl["bytes_per_launch"] / (rl["us_per_launch"] * 1e3)) / rl["achieved"] < 1e-2
+    if "decode" in workload:
+        assert rl["kernel"] == ("decode_step" if "split" in extra else "conv_decode")
     if "lanes8" in workload:
         assert d["config"]["lanes"] == 8 and d["config"]["slots"] == 8
     cp = d["copy_same_bytes"]  # a plain copy of the dominant kernel's bytes in the same run

@@ -52,6 +52,18 @@ class PlainStep:
         return qkv, out
 
 
+    def fused(self, t):
+        """conv_decode_step on token t (both parts in one launch)."""
+        if not hasattr(self, "sync"):
+            self.sync = torch.zeros((self.C, self.Hk, gdn.SYNC_STRIDE), dtype=torch.int32, device="cuda")
+        ba = dev(self.case["ba"][:, t])
+        out = Guarded((self.C, self.Hv, self.dv))
+        gdn.conv_decode_step(self.shape(1), dev(self.case["x"][:, t]), self.conv_w, self.hist, ba[:, :self.Hv],
+                             ba[:, self.Hv:], self.dt, self.A, self.state, self.slot_t, self.sync, self.status,
+                             out=out.t)
+        return out
+
+
 class OraclePlain:
     """The same steps in the oracle, on float64 copies of the pools."""
 
@@ -254,3 +266,79 @@ def test_plain_step_graph_replay_matches_eager():
         assert int(g.status.item()) == 0
         for a, b in zip(bufs, ref):
             assert torch.equal(a, b), f"replay {rep} differs from the eager result"
+
+
+# ---------------------------------------------------------------- fused plain step
+FUSED_SHAPES = DECODE_SHAPES + [(2, 3, 2, 6, 16, 128, None)]  # value heads 3 per q/k head, 4 column blocks
+
+
+@pytest.mark.parametrize("C,P,Hk,Hv,dk,dv,pad", FUSED_SHAPES)
+def test_fused_plain_steps_equal_separate_calls(C, P, Hk, Hv, dk, dv, pad):
+    """conv_decode_step against conv_step + decode_step, GPU against GPU, over 5
+    consecutive tokens: outputs, state and history bit for bit, untouched slots and padding
+    lanes unchanged, and the sync counters back to zero after every call."""
+    T = 5
+    case = synth_case(C, T, P, Hk, Hv, dk, dv, seed=90 + C + dk + dv, tree=False)
+    slots = case["slot_ids"].copy()
+    if pad is not None:
+        slots[pad] = -1
+    log(f"[plain] fused vs separate C={C} P={P} Hk={Hk} Hv={Hv} dk={dk} dv={dv} slots={slots.tolist()}")
+    a, b = PlainStep(case, Hk, slots), PlainStep(case, Hk, slots)
+    for t in range(T):
+        _, oa = a.decode(t)
+        ob = b.fused(t)
+        torch.cuda.synchronize()
+        assert int(a.status.item()) == 0 and int(b.status.item()) == 0
+        assert np.array_equal(oa.np(), ob.np()), f"out of token {t}"
+        assert ob.guards_intact()
+        assert not b.sync.any(), f"sync counters left non-zero after token {t}"
+    assert torch.equal(a.state, b.state) and torch.equal(a.hist, b.hist)
+
+
+def test_fused_plain_step_parity():
+    """conv_decode_step at the headline head shape against the fp64 oracle over 3 tokens."""
+    C, P, Hk, Hv, dk, dv, T = 4, 8, 16, 32, 128, 128, 3
+    case = synth_case(C, T, P, Hk, Hv, dk, dv, seed=97, tree=False)
+    slots = case["slot_ids"].copy()
+    slots[2] = -1
+    log(f"[plain] fused parity slots={slots.tolist()}")
+    g, r = PlainStep(case, Hk, slots), OraclePlain(case, Hk, slots)
+    worst = 0.0
+    for t in range(T):
+        go = g.fused(t)
+        _, ro = r.decode(t)
+        torch.cuda.synchronize()
+        worst = max(worst, _compare_rows(go, ro, slots, REC_TOL, f"out token {t}"))
+    assert int(g.status.item()) == 0
+    e_state = _check_pools(g, r, "fused steps")
+    log(f"[plain] fused: out {worst:.2e} state {e_state:.2e}")
+
+
+@pytest.mark.parametrize("bad", ["slot_dup", "slot_range", "status_in"])
+def test_fused_plain_step_is_all_or_nothing(bad):
+    """A rejected fused step writes nothing and leaves the sync counters at zero, so the next
+    call on the same counters is exact."""
+    C, P, Hk, Hv, dk, dv = 3, 5, 1, 2, 32, 32
+    case = synth_case(C, 2, P, Hk, Hv, dk, dv, seed=98, tree=False)
+    slots = {"slot_dup": [0, 3, 3], "slot_range": [0, 5, 2], "status_in": [0, 3, 2]}[bad]
+    bit = {"slot_dup": gdn.STATUS_SLOT_DUP, "slot_range": gdn.STATUS_SLOT_RANGE, "status_in": 0x100}[bad]
+    log(f"[plain] fused transaction {bad}: slots={slots}")
+    g = PlainStep(case, Hk, slots)
+    if bad == "status_in":
+        g.status.fill_(0x100)
+    go = g.fused(0)
+    torch.cuda.synchronize()
+    assert int(g.status.item()) & bit
+    assert (go.np() == np.float32(SENTINEL)).all()
+    assert np.array_equal(g.hist.cpu().numpy(), case["conv_hist"])
+    assert np.array_equal(g.state.cpu().numpy(), case["state"])
+    assert not g.sync.any()
+    # the same counters then serve a valid step exactly
+    ok = [0, 3, 2]
+    a, b = PlainStep(case, Hk, ok), PlainStep(case, Hk, ok)
+    b.sync = g.sync
+    _, oa = a.decode(1)
+    ob = b.fused(1)
+    torch.cuda.synchronize()
+    assert int(b.status.item()) == 0 and np.array_equal(oa.np(), ob.np())
+    assert torch.equal(a.state, b.state) and torch.equal(a.hist, b.hist) and not b.sync.any()
