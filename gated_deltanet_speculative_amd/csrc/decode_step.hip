@@ -4,10 +4,13 @@
 //   conv_step_kernel    causal conv + SiLU over a chain of tokens per lane, writing the
 //                       slot's new history (the last 3 columns) back in place;
 //   decode_step_kernel  one token of the gated delta rule applied to the slot's state
-//                       in place, with the output row.
-// The conv must finish before the recurrence reads its output: a q/k channel feeds
-// every value head of its group, so one launch could not write the history in place
-// while other workgroups still read it.
+//                       in place, with the output row;
+// or, for one token, both in one:
+//   conv_decode_kernel  each workgroup forms the conv output of the channels it needs,
+//                       then runs the recurrence.  A q/k channel feeds every value head of
+//                       its group, so its history may be rewritten in place only once
+//                       every workgroup of the group has read it: the last of them to
+//                       count itself on a caller-provided counter writes it.
 //
 // What is computed: "Feature/support dflash2", deferred-state commit message (a step the
 // drafter did not draft for commits its post-step state to the slot immediately);

@@ -9,8 +9,9 @@
 each by what the same counter reads for the calibration copy (M MiB read and M MiB
 written by one plain copy kernel), and writes both a markdown table and a JSON
 record that bench.py uses for the roofline's `traffic` field.  The JSON carries the
-SHA-256 of each kernel's source file and the project headers it includes, so a later
-change to a kernel makes bench.py report its traffic as unknown instead of stale.
+SHA-256 of each kernel's source file and the project headers it includes (comments
+removed), so a later change to a kernel's code makes bench.py report its traffic as unknown
+instead of stale.
 """
 
 from __future__ import annotations
@@ -57,13 +58,23 @@ def source_files(kernel: str) -> list:
     return out
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
+def strip_comments(text: str) -> str:
+    """The source with its // and /* */ comments removed (line breaks kept), so that a
+    comment edit leaves the hash alone.  (A '//' inside a string literal would be cut too,
+    the same way every time, which keeps the hash deterministic.)"""
+    return _COMMENT.sub(lambda m: "\n" * m.group(0).count("\n"), text)
+
+
 def source_sha256(kernel: str) -> str:
-    """sha256 over the kernel's source and the project headers it includes: a counter summary
-    taken under another hash no longer describes the built kernel."""
+    """sha256 over the kernel's source and the project headers it includes, comments removed:
+    a counter summary taken under another hash no longer describes the built kernel."""
     h = hashlib.sha256()
     for path in source_files(kernel):
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(strip_comments(f.read()).encode())
     return h.hexdigest()
 
 

@@ -76,3 +76,18 @@ def test_source_hash_covers_included_headers():
     # kernels built from the same file share a hash; different files differ
     assert rs.source_sha256("prefill_prep") == rs.source_sha256("prefill_state")
     assert rs.source_sha256("prefill_prep") != rs.source_sha256("decode_step")
+
+
+def test_source_hash_ignores_comments_only():
+    """Comments do not enter the hash; code does."""
+    sys.path.insert(0, ROOT)
+    from gated_deltanet_speculative_amd import rocprof_summary as rs
+
+    base = "int f(int x) {\n    return x + 1;  // one more\n}\n/* a\n   block */\n"
+    same = "int f(int x) {\n    return x + 1;  // one MORE, reworded\n}\n/* another\n   block */\n"
+    other = "int f(int x) {\n    return x + 2;  // one more\n}\n/* a\n   block */\n"
+    assert rs.strip_comments(base) == rs.strip_comments(same)
+    assert rs.strip_comments(base) != rs.strip_comments(other)
+    assert "return x + 1;" in rs.strip_comments(base) and "one more" not in rs.strip_comments(base)
+    assert rs.strip_comments(base).count("\n") == base.count("\n")
+
