@@ -389,14 +389,135 @@ __global__ __launch_bounds__(64) void conv_decode_kernel(
     }
 }
 
+// ---- fused plain step, one workgroup per (lane, q/k head): its 8 waves share one conv of
+//      the group's channels (the q/k slab once, the value channels of every block of the
+//      group), so after the workgroup's barrier every reader of the history is done and each
+//      conv thread writes its channels' new history itself; wave w then runs the recurrence
+//      of blocks w, w + 8, ... (value head, column block) of the group.  For groups of at most
+//      kGroupBlocks blocks; larger ones take conv_decode_kernel.
+constexpr int kGroupWaves = 8, kGroupBlocks = 16;
+template <int DK, int DV>
+__global__ __launch_bounds__(64 * kGroupWaves) void conv_decode_group_kernel(
+    Dims d, const float *__restrict__ x, const float *__restrict__ conv_w, float *__restrict__ conv_hist,
+    const float *__restrict__ beta_logits, const float *__restrict__ alpha_logits, int64_t gate_stride,
+    const float *__restrict__ dt_bias, const float *__restrict__ A, float *__restrict__ state_pool,
+    const int32_t *__restrict__ slot_ids, float *__restrict__ out, int32_t *__restrict__ status) {
+    using Cfg = DecodeCfg<DK, DV>;
+    constexpr int JB = Cfg::JB, NB = Cfg::NB, Q4 = Cfg::Q4, RPL = Cfg::RPL, kT = 64 * kGroupWaves;
+    constexpr int GQK = DK / 2, GVB = JB / 4;  // 4-channel groups: the q/k slab, one value block
+    static_assert(GQK + kGroupBlocks * GVB <= kT, "one channel group per thread");
+    __shared__ unsigned int s_bitmap[kBitmapSlots / 32];
+    __shared__ int s_word;
+    __shared__ __align__(16) float s_y[2 * DK + kGroupBlocks * JB];  // q rows, k rows, value columns
+
+    const int c = blockIdx.y, kh = blockIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int nblk = (d.Hv / d.Hk) * NB;  // (value head, column block) pairs of the group
+    const int q = lane % Q4, r = lane / Q4, i0 = r * RPL;
+    const int s_v = __builtin_bit_cast(
+        int, __builtin_amdgcn_raw_buffer_load_b32(
+                 __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(slot_ids), 0, 4 * d.C, 0x00020000), 4 * c, 0,
+                 0));
+    const LaneSlotsT<kT> lanes(slot_ids, d.C);
+    const int st_in = *status;
+    // this thread's channel group: tid < GQK the q/k slab, then GVB groups per block
+    const int nitems = GQK + nblk * GVB;
+    const int f = min(tid, nitems - 1);
+    const int vb = (f - GQK) / GVB, vg = f - GQK - vb * GVB;
+    const int ch = f < DK / 4 ? kh * DK + 4 * f
+                   : f < GQK  ? d.Hk * DK + kh * DK + 4 * (f - DK / 4)
+                              : 2 * d.Hk * DK + (kh + d.Hk * (vb / NB)) * DV + (vb % NB) * JB + 4 * vg;
+    const int at = f < GQK ? 4 * f : 2 * DK + vb * JB + 4 * vg;
+    v4f w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = reinterpret_cast<const v4f *>(conv_w)[ch + e];
+    const v4f xv = *reinterpret_cast<const v4f *>(x + (int64_t)c * d.Ch + ch);
+    // this wave's first block: its gates
+    const int blk0 = min(wave, nblk - 1), h0 = kh + d.Hk * (blk0 / NB);
+    float braw = beta_logits[(int64_t)c * gate_stride + h0];
+    float araw = alpha_logits[(int64_t)c * gate_stride + h0] + dt_bias[h0];
+    float Ah = A[h0];
+    __builtin_amdgcn_sched_barrier(0);
+    const int s = __builtin_amdgcn_readfirstlane(s_v);
+    const bool s_ok = s >= 0 && s < d.P;
+    v4f hv[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        hv[k] = reinterpret_cast<const v4f *>(conv_hist + ((int64_t)(s_ok ? s : 0) * d.Ch + ch) * 3)[k];
+    auto state_rows = [&](int blk) {
+        return reinterpret_cast<v4f *>(state_pool + ((int64_t)(s_ok ? s : 0) * d.Hv + kh + d.Hk * (blk / NB)) * DK * DV +
+                                       (blk % NB) * JB) + q;
+    };
+    v4f sv[RPL];
+    {
+        v4f *S4 = state_rows(blk0);
+#pragma unroll
+        for (int e = 0; e < RPL; ++e) sv[e] = __builtin_nontemporal_load(S4 + (i0 + e) * (DV / 4));
+    }
+    // conv + SiLU of this thread's channel group (the conv step's order of taps and accumulation)
+    const v4f ha = v4f{hv[0].x, hv[0].w, hv[1].z, hv[2].y}, hb = v4f{hv[0].y, hv[1].x, hv[1].w, hv[2].z},
+              hc = v4f{hv[0].z, hv[1].y, hv[2].x, hv[2].w};
+    if (tid < nitems) {
+        v4f y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float z = ha[e] * w[e][0];
+            z = fmaf(hb[e], w[e][1], z);
+            z = fmaf(hc[e], w[e][2], z);
+            z = fmaf(xv[e], w[e][3], z);
+            y[e] = fast_silu(z);
+        }
+        *reinterpret_cast<v4f *>(s_y + at) = y;
+    }
+    // (the preflight's barriers also order the conv's LDS stores before the reads below, and
+    // every history read of the workgroup before the history writes)
+    const int bits = slot_preflight<kT>(lanes, slot_ids, d.C, d.P, s_bitmap, &s_word);
+    if (bits || st_in) {
+        if (bits && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) atomicOr(status, bits);
+        return;
+    }
+    if (s < 0) return;  // padding lane (uniform over the workgroup)
+    if (tid < nitems) {  // the new history [column 1, column 2, token] of this thread's channels
+        v4f *hp = reinterpret_cast<v4f *>(conv_hist + ((int64_t)s * d.Ch + ch) * 3);
+        hp[0] = v4f{hb.x, hc.x, xv.x, hb.y};
+        hp[1] = v4f{hc.y, xv.y, hb.z, hc.z};
+        hp[2] = v4f{xv.z, hb.w, hc.w, xv.w};
+    }
+    float qq[RPL], kq[RPL];
+#pragma unroll
+    for (int e = 0; e < RPL; ++e) {
+        qq[e] = s_y[i0 + e];
+        kq[e] = s_y[DK + i0 + e];
+    }
+    for (int blk = wave; blk < nblk; blk += kGroupWaves) {
+        const int h = kh + d.Hk * (blk / NB), j0 = (blk % NB) * JB;
+        v4f *S4 = state_rows(blk);
+        if (blk != blk0) {  // a second block of this wave (groups of more than 8 blocks)
+            braw = beta_logits[(int64_t)c * gate_stride + h];
+            araw = alpha_logits[(int64_t)c * gate_stride + h] + dt_bias[h];
+            Ah = A[h];
+#pragma unroll
+            for (int e = 0; e < RPL; ++e) sv[e] = __builtin_nontemporal_load(S4 + (i0 + e) * (DV / 4));
+        }
+        const v4f v = *reinterpret_cast<const v4f *>(s_y + 2 * DK + blk * JB + 4 * q);
+        decode_block<DK, DV>(qq, kq, v, braw, araw, Ah, sv, S4, i0, r,
+                             reinterpret_cast<v4f *>(out + ((int64_t)c * d.Hv + h) * DV + j0) + q);
+    }
+}
+
 template <int DK, int DV>
 hipError_t launch_conv_decode(const Dims &d, const float *x, const float *conv_w, float *conv_hist,
                               const float *beta_logits, const float *alpha_logits, int64_t gate_stride,
                               const float *dt_bias, const float *A, float *state_pool, const int32_t *slot_ids,
                               int32_t *sync, float *out, int32_t *status, hipStream_t stream) {
-    hipLaunchKernelGGL((conv_decode_kernel<DK, DV>), dim3(DecodeCfg<DK, DV>::NB * d.Hv, d.C), dim3(64), 0, stream, d,
-                       x, conv_w, conv_hist, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool, slot_ids,
-                       sync, out, status);
+    if ((d.Hv / d.Hk) * DecodeCfg<DK, DV>::NB <= kGroupBlocks)
+        hipLaunchKernelGGL((conv_decode_group_kernel<DK, DV>), dim3(d.Hk, d.C), dim3(64 * kGroupWaves), 0, stream, d,
+                           x, conv_w, conv_hist, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool,
+                           slot_ids, out, status);
+    else
+        hipLaunchKernelGGL((conv_decode_kernel<DK, DV>), dim3(DecodeCfg<DK, DV>::NB * d.Hv, d.C), dim3(64), 0, stream,
+                           d, x, conv_w, conv_hist, beta_logits, alpha_logits, gate_stride, dt_bias, A, state_pool,
+                           slot_ids, sync, out, status);
     return hipGetLastError();
 }
 

@@ -269,7 +269,10 @@ def test_plain_step_graph_replay_matches_eager():
 
 
 # ---------------------------------------------------------------- fused plain step
-FUSED_SHAPES = DECODE_SHAPES + [(2, 3, 2, 6, 16, 128, None)]  # value heads 3 per q/k head, 4 column blocks
+FUSED_SHAPES = DECODE_SHAPES + [
+    (2, 3, 2, 6, 16, 128, None),   # 3 value heads per q/k head x 4 column blocks: waves with two blocks
+    (2, 3, 1, 8, 32, 128, 0),      # 32 blocks per group: one workgroup per block, with the counters
+]
 
 
 @pytest.mark.parametrize("C,P,Hk,Hv,dk,dv,pad", FUSED_SHAPES)
