@@ -31,7 +31,7 @@ KERNEL_SOURCES = {  # (matched in this order: conv_tree_verify before tree_verif
     "conv_tree_step": "csrc/conv_tree_step.hip",
     "tree_verify": "csrc/tree_verify.hip",
     "replay_commit": "csrc/replay_commit.hip",
-    "conv_decode": "csrc/decode_step.hip",  # the fused plain step (conv_decode_kernel)
+    "conv_decode": "csrc/decode_step.hip",  # the fused plain step (conv_decode_group_kernel, or conv_decode_kernel)
     "decode_step": "csrc/decode_step.hip",
     "prefill_prep": "csrc/prefill.hip",
     "prefill_state": "csrc/prefill.hip",
@@ -78,7 +78,14 @@ def source_sha256(kernel: str) -> str:
     return h.hexdigest()
 
 
+# kernels reported under another kernel's name (the same call, another launch shape)
+KERNEL_ALIASES = {"conv_decode_group": "conv_decode"}
+
+
 def short_name(name: str) -> str:
+    for k, v in KERNEL_ALIASES.items():
+        if k + "_kernel" in name:
+            return v
     for k in KERNEL_SOURCES:
         if k + "_kernel" in name:
             return k
