@@ -6,11 +6,14 @@
 //   decode_step_kernel  one token of the gated delta rule applied to the slot's state
 //                       in place, with the output row;
 // or, for one token, both in one:
-//   conv_decode_kernel  each workgroup forms the conv output of the channels it needs,
-//                       then runs the recurrence.  A q/k channel feeds every value head of
-//                       its group, so its history may be rewritten in place only once
-//                       every workgroup of the group has read it: the last of them to
-//                       count itself on a caller-provided counter writes it.
+//   conv_decode_group_kernel  one workgroup per (lane, q/k head) forms the conv output of
+//                       the group's channels once, writes their new history after its
+//                       barrier, and runs the recurrence of every value block of the group;
+//   conv_decode_kernel  (groups of more than 16 blocks) one wave per value block, each
+//                       forming the conv of the channels it needs.  A q/k channel then
+//                       feeds several workgroups, so its history may be rewritten in place
+//                       only once all of them have read it: the last of them to count
+//                       itself on a caller-provided counter writes it.
 //
 // What is computed: "Feature/support dflash2", deferred-state commit message (a step the
 // drafter did not draft for commits its post-step state to the slot immediately);

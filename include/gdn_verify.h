@@ -335,10 +335,13 @@ int gdn_decode_step(const gdn_shape *sh, const float *qkv, const float *beta_log
  *   slot_ids       [C]                 int32, -1 = padding lane               (read)
  *   sync           [C][H_k][GDN_SYNC_STRIDE]  int32 counters (element [c][kh][0] of each
  *                                      128-byte line), all zero on entry; every call leaves
- *                                      them zero.  The in-place history of a q/k channel is
- *                                      read by all the workgroups of its (lane, q/k head); the
- *                                      last of them to count itself here writes it.  Calls
- *                                      that overlap in time must not share one sync array.
+ *                                      them zero.  Where a q/k head has more than 16
+ *                                      (value head, 32-column block) pairs (H_v / H_k value
+ *                                      heads of d_v / 32 blocks each), the in-place history of a
+ *                                      q/k channel is read by several workgroups, and the last
+ *                                      of them to count itself here writes it.  Required in
+ *                                      every call; calls that overlap in time must not share
+ *                                      one sync array.
  *   out            [C][H_v][d_v]       written for non-padding lanes
  *   status         int32*, REQUIRED (GDN_ERR_NULL otherwise)
  */
