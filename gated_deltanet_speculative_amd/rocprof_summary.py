@@ -9,9 +9,9 @@
 each by what the same counter reads for the calibration copy (M MiB read and M MiB
 written by one plain copy kernel), and writes both a markdown table and a JSON
 record that bench.py uses for the roofline's `traffic` field.  The JSON carries the
-SHA-256 of each kernel's source file and the project headers it includes (comments
-removed), so a later change to a kernel's code makes bench.py report its traffic as unknown
-instead of stale.
+SHA-256 of each kernel's source file and the project headers it includes (comments and
+layout removed), so a later change to a kernel's code makes bench.py report its traffic as
+unknown instead of stale.
 """
 
 from __future__ import annotations
@@ -62,10 +62,11 @@ _COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
 
 
 def strip_comments(text: str) -> str:
-    """The source with its // and /* */ comments removed (line breaks kept), so that a
-    comment edit leaves the hash alone.  (A '//' inside a string literal would be cut too,
-    the same way every time, which keeps the hash deterministic.)"""
-    return _COMMENT.sub(lambda m: "\n" * m.group(0).count("\n"), text)
+    """The source with its // and /* */ comments removed and every run of white space made
+    one space, so that an edit of comments or layout leaves the hash alone.  (A '//' inside a
+    string literal would be cut too, the same way every time, which keeps the hash
+    deterministic.)"""
+    return " ".join(_COMMENT.sub(" ", text).split())
 
 
 def source_sha256(kernel: str) -> str:

@@ -79,7 +79,7 @@ def test_source_hash_covers_included_headers():
 
 
 def test_source_hash_ignores_comments_only():
-    """Comments do not enter the hash; code does."""
+    """Comments and layout do not enter the hash; code does."""
     sys.path.insert(0, ROOT)
     from gated_deltanet_speculative_amd import rocprof_summary as rs
 
@@ -89,5 +89,6 @@ def test_source_hash_ignores_comments_only():
     assert rs.strip_comments(base) == rs.strip_comments(same)
     assert rs.strip_comments(base) != rs.strip_comments(other)
     assert "return x + 1;" in rs.strip_comments(base) and "one more" not in rs.strip_comments(base)
-    assert rs.strip_comments(base).count("\n") == base.count("\n")
+    relaid = "int f(int x)\n{\n    return x + 1;\n\n}\n"
+    assert rs.strip_comments(base) == rs.strip_comments(relaid)
 
