@@ -122,7 +122,7 @@ def test_edge_verify_and_commit(kind, shape, route):
 @pytest.mark.parametrize("kind", EDGE_KINDS)
 def test_edge_decode_steps(kind):
     """Three plain steps (conv step + one-token recurrence in place) at the headline head
-    shape on edge inputs."""
+    shape on edge inputs, and the fused call beside them, bit for bit."""
     C, T, P, Hk, Hv, d = 4, 3, 8, 16, 32, 128
     case = edge_case(synth_case(C, T, P, Hk, Hv, d, d, seed=320, tree=False), kind, Hk, d, seed=2)
     sh1 = gdn.Shape(C, 1, P, Hk, Hv, d, d)
@@ -132,8 +132,14 @@ def test_edge_decode_steps(kind):
     w, dt, A, slot_t = dev(case["conv_w"]), dev(case["dt_bias"]), dev(case["A"]), dev(slots)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     rhist, rstate = case["conv_hist"].astype(np.float64), case["state"].astype(np.float64)
+    # the fused call on its own copies of the pools: bit for bit the two calls
+    fhist, fstate = dev(case["conv_hist"]), dev(case["state"])
+    sync = torch.zeros((C, Hk, gdn.SYNC_STRIDE), dtype=torch.int32, device="cuda")
     worst_conv = worst_out = 0.0
     for t in range(T):
+        ba_f = dev(case["ba"][:, t])
+        fout = gdn.conv_decode_step(sh1, dev(case["x"][:, t]), w, fhist, ba_f[:, :Hv], ba_f[:, Hv:], dt, A, fstate,
+                                    slot_t, sync, status)
         qkv = Guarded((C, 1, sh1.channels))
         gdn.conv_step(sh1, dev(case["x"][:, t:t + 1]), w, hist, slot_t, status, conv_out=qkv.t)
         ba = dev(case["ba"][:, t])
@@ -147,6 +153,7 @@ def test_edge_decode_steps(kind):
             assert O.conv_step(case["x"][:, t:t + 1], case["conv_w"], rhist, slots, rq) == 0
             assert O.decode_step(rq[:, 0], case["ba"][:, t, :Hv], case["ba"][:, t, Hv:], case["dt_bias"], case["A"],
                                  rstate, slots, Hk, ro) == 0
+        assert torch.equal(fout, out.t), f"fused step, token {t}"
         worst_conv = max(worst_conv, _conv_err(qkv.np(), rq, kind, Hk, d))
         worst_out = max(worst_out, err_metric(out.np(), ro))
         assert qkv.guards_intact() and out.guards_intact()
@@ -155,6 +162,7 @@ def test_edge_decode_steps(kind):
     assert np.array_equal(hist.cpu().numpy(), rhist.astype(np.float32))
     e_state = err_metric(state.cpu().numpy(), rstate)
     assert e_state <= REC_TOL, f"state error {e_state}"
+    assert torch.equal(fhist, hist) and torch.equal(fstate, state) and not sync.any()
     log(f"[edge] decode {kind}: conv {worst_conv:.2e} out {worst_out:.2e} state {e_state:.2e}")
 
 
